@@ -1,0 +1,315 @@
+"""Pins for the CPU oracle (no GPU).
+
+Each test ties an oracle function to something other than itself: values
+printed on the pages, a second plain definition, brute force, closed forms,
+special cases that reduce to a dense computation, or finite differences.
+"""
+import json
+import os
+
+import numpy as np
+import pytest
+
+from oracle import moe_oracle as O
+from dropless_moe_dispatch_amd import synth
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
+
+
+def _rand_ids(rng, T, E, K):
+    return np.stack([rng.permutation(E)[:K] for _ in range(T)]).astype(np.int32)
+
+
+# --------------------------------------------------------------------------
+# index (a3)
+# --------------------------------------------------------------------------
+
+def test_figure2_worked_example():
+    g = json.load(open(os.path.join(GOLDEN, "moeblaze_figure2.json")))
+    ids = np.array(g["assignments"], dtype=np.int32)
+    ix = O.build_index(ids, g["E"])
+    assert ix["expert_token_indices"].tolist() == g["printed"]["expert_token_indices"]
+    assert ix["offsets"].tolist() == g["printed"]["expert_token_offsets"]
+    assert ix["token_index_map"][0:2].tolist() == g["printed"]["token_index_map_token0"]
+    for e, toks in g["printed"]["experts_tokens"].items():
+        e = int(e)
+        seg = ix["expert_token_indices"][ix["offsets"][e]:ix["offsets"][e + 1]]
+        assert seg.tolist() == toks
+    assert ix["token_expert_indices"].tolist() == g["derived"]["token_expert_indices"]
+    assert ix["token_index_map"].tolist() == g["derived"]["token_index_map"]
+
+
+def _reference_semantics_index(ids, E):
+    """Second plain definition: the sort/permute pipeline of the
+    'A reference implementation' section (stable argsort of the flattened
+    expert ids, token = order // K, counts by bincount)."""
+    T, K = ids.shape
+    flat = ids.reshape(-1)
+    order = np.argsort(flat, kind="stable")
+    counts = np.bincount(flat, minlength=E)
+    offsets = np.concatenate([[0], np.cumsum(counts)])
+    pos = np.empty_like(order)
+    pos[order] = np.arange(len(order))
+    return counts, offsets, order // K, pos
+
+
+@pytest.mark.parametrize("T,E,K", [(1, 1, 1), (1, 8, 8), (7, 4, 2), (33, 8, 3), (64, 16, 16), (100, 32, 5)])
+def test_index_matches_stable_sort_definition(T, E, K):
+    rng = np.random.default_rng(T * 131 + E * 7 + K)
+    ids = _rand_ids(rng, T, E, K)
+    ix = O.build_index(ids, E)
+    counts, offsets, src_tok, pos = _reference_semantics_index(ids, E)
+    assert ix["counts"].tolist() == counts.tolist()
+    assert ix["offsets"].tolist() == offsets.tolist()
+    assert ix["expert_token_indices"].tolist() == src_tok.tolist()
+    assert ix["token_index_map"].tolist() == pos.tolist()
+
+
+@pytest.mark.parametrize("kind", ["gaussian", "one_expert_set", "zero_rows", "ties", "hot_expert", "all_equal"])
+def test_index_invariants(kind):
+    T, E, K = 200, 16, 4
+    z = synth.structured_logits(T, E, K, kind, seed=3)
+    ids = O.topk_select(z, K)
+    ix = O.build_index(ids, E)
+    off, eti, tim = ix["offsets"], ix["expert_token_indices"], ix["token_index_map"]
+    assert off[0] == 0 and off[E] == T * K
+    assert ix["counts"].sum() == T * K
+    assert np.all(np.diff(off) == ix["counts"])
+    # the reverse map is a bijection onto the T*K positions
+    assert sorted(tim.tolist()) == list(range(T * K))
+    for t in range(T):
+        # expert ids per token are unique
+        assert len(set(ids[t].tolist())) == K
+        for k in range(K):
+            p = tim[t * K + k]
+            e = ids[t, k]
+            assert eti[p] == t
+            assert off[e] <= p < off[e + 1]
+    for e in range(E):
+        seg = eti[off[e]:off[e + 1]]
+        assert np.all(np.diff(seg) > 0)     # strictly increasing token ids (stable)
+    # every token appears exactly K times
+    assert np.all(np.bincount(eti, minlength=T) == K)
+
+
+# --------------------------------------------------------------------------
+# top-K and weights (a2)
+# --------------------------------------------------------------------------
+
+def _brute_topk(z, K):
+    T, E = z.shape
+    return np.array([sorted(range(E), key=lambda e: (-z[t, e], e))[:K] for t in range(T)], dtype=np.int32)
+
+
+@pytest.mark.parametrize("kind", ["gaussian", "ties", "all_equal", "hot_expert"])
+@pytest.mark.parametrize("E,K", [(8, 2), (8, 8), (16, 1), (64, 6)])
+def test_topk_matches_full_sort(kind, E, K):
+    z = synth.structured_logits(50, E, K, kind, seed=E + K)
+    ids = O.topk_select(z, K)
+    assert ids.tolist() == _brute_topk(z, K).tolist()
+
+
+def test_topk_special_cases():
+    z = synth.structured_logits(40, 8, 8, "gaussian", seed=5)
+    ids, w = O.route(z, 8)
+    # K = E: all experts in descending order; renormalisation is a no-op
+    assert np.all(np.diff(np.take_along_axis(z, ids.astype(np.int64), 1), axis=1) <= 0)
+    np.testing.assert_allclose(w, np.take_along_axis(O.softmax(z), ids.astype(np.int64), 1), rtol=1e-12)
+    ids1, w1 = O.route(z, 1)
+    assert np.all(w1 == 1.0)
+    assert ids1[:, 0].tolist() == np.argmax(z, axis=1).tolist()
+
+
+def test_topk_weights_closed_form():
+    z = synth.structured_logits(64, 32, 4, "gaussian", seed=9).astype(np.float64) * 3
+    ids, w = O.route(z, 4)
+    np.testing.assert_allclose(w.sum(axis=1), 1.0, rtol=0, atol=1e-12)
+    zs = np.take_along_axis(z, ids.astype(np.int64), 1)
+    ez = np.exp(zs - zs.max(axis=1, keepdims=True))
+    np.testing.assert_allclose(w, ez / ez.sum(axis=1, keepdims=True), rtol=1e-12)
+    assert np.all(np.diff(w, axis=1) <= 0)   # slot order = descending weight
+
+
+# --------------------------------------------------------------------------
+# storage rounding
+# --------------------------------------------------------------------------
+
+def test_round_bf16_known_values():
+    v = np.array([1.0, 1.0 + 2 ** -8, 1.0 + 3 * 2 ** -8, 1.0 + 2 ** -7, -2.5, 1.0 + 2 ** -8 + 2 ** -20,
+                  3.0e-3, 65504.0])
+    r = O.round_bf16(v)
+    assert r[0] == 1.0
+    assert r[1] == 1.0                      # tie -> even
+    assert r[2] == 1.0 + 2 ** -6            # tie -> even (up)
+    assert r[3] == 1.0 + 2 ** -7            # representable
+    assert r[4] == -2.5
+    assert r[5] == 1.0 + 2 ** -7            # above the tie -> up
+    # independent implementation: float32 bit-rounding of the input generator
+    for x in v[[0, 4, 6, 7]]:
+        assert O.round_bf16(np.array([x]))[0] == synth.round_to_bf16(np.array([x], np.float32))[0]
+    rng = np.random.default_rng(0)
+    f32 = (rng.standard_normal(10000) * 10).astype(np.float32)
+    np.testing.assert_array_equal(O.round_bf16(f32.astype(np.float64)), synth.round_to_bf16(f32).astype(np.float64))
+
+
+# --------------------------------------------------------------------------
+# forward (a4, a5)
+# --------------------------------------------------------------------------
+
+def _small_layer(T=24, d=16, E=4, K=2, h=12, seed=0, scale_router=1.0):
+    rng = np.random.default_rng(seed)
+    x = rng.standard_normal((T, d))
+    wg = rng.standard_normal((E, d)) / np.sqrt(d) * scale_router
+    wgt = rng.standard_normal((E, h, d)) / np.sqrt(d)
+    wup = rng.standard_normal((E, h, d)) / np.sqrt(d)
+    wdn = rng.standard_normal((E, d, h)) / np.sqrt(h)
+    dy = rng.standard_normal((T, d))
+    return x, wg, wgt, wup, wdn, dy
+
+
+def test_forward_reduces_to_dense_swiglu_when_single_expert():
+    x, wg, wgt, wup, wdn, dy = _small_layer(E=1, K=1)
+    z = O.router_logits(x, wg)
+    ids, w = O.route(z, 1)
+    assert np.all(w == 1.0)
+    f = O.moe_forward(x, ids, w, wgt, wup, wdn, dtype=None)
+    a = x @ wgt[0].T
+    b = x @ wup[0].T
+    dense = ((a / (1 + np.exp(-a))) * b) @ wdn[0].T
+    np.testing.assert_allclose(f["out"], dense, rtol=1e-12, atol=1e-12)
+
+
+def test_forward_dense_mixture_when_k_equals_e():
+    x, wg, wgt, wup, wdn, dy = _small_layer(E=3, K=3)
+    z = O.router_logits(x, wg)
+    ids, w = O.route(z, 3)
+    f = O.moe_forward(x, ids, w, wgt, wup, wdn, dtype=None)
+    p = np.exp(z - z.max(1, keepdims=True))
+    p /= p.sum(1, keepdims=True)
+    mix = sum(p[:, e:e + 1] * (((x @ wgt[e].T) / (1 + np.exp(-(x @ wgt[e].T)))) * (x @ wup[e].T)) @ wdn[e].T
+              for e in range(3))
+    np.testing.assert_allclose(f["out"], mix, rtol=1e-12, atol=1e-12)
+
+
+def test_forward_linear_in_down_projection_and_token_equivariant():
+    x, wg, wgt, wup, wdn, dy = _small_layer(T=30)
+    z = O.router_logits(x, wg)
+    ids, w = O.route(z, 2)
+    f1 = O.moe_forward(x, ids, w, wgt, wup, wdn, dtype=None)["out"]
+    f2 = O.moe_forward(x, ids, w, wgt, wup, 2.0 * wdn, dtype=None)["out"]
+    np.testing.assert_array_equal(f2, 2.0 * f1)
+    perm = np.random.default_rng(1).permutation(30)
+    fp = O.moe_forward(x[perm], ids[perm], w[perm], wgt, wup, wdn, dtype=None)["out"]
+    np.testing.assert_allclose(fp, f1[perm], rtol=1e-13, atol=1e-13)
+    # duplicating an expert and splitting its tokens between the copies leaves out unchanged
+    wgt2 = np.concatenate([wgt, wgt[:1]])
+    wup2 = np.concatenate([wup, wup[:1]])
+    wdn2 = np.concatenate([wdn, wdn[:1]])
+    ids2 = ids.copy()
+    sel = (ids2 == 0) & (np.arange(30)[:, None] % 2 == 1)
+    ids2[sel] = 4
+    f3 = O.moe_forward(x, ids2, w, wgt2, wup2, wdn2, dtype=None)["out"]
+    np.testing.assert_allclose(f3, f1, rtol=1e-13, atol=1e-13)
+
+
+def test_silu_zero_and_gradient():
+    assert O.silu(np.array([0.0]))[0] == 0.0
+    u = np.linspace(-6, 6, 101)
+    eps = 1e-6
+    fd = (O.silu(u + eps) - O.silu(u - eps)) / (2 * eps)
+    np.testing.assert_allclose(O.silu_grad(u), fd, rtol=1e-7, atol=1e-9)
+
+
+def test_storage_rounding_mirror_points():
+    x, wg, wgt, wup, wdn, dy = _small_layer()
+    x = O.round_bf16(x)
+    z = O.router_logits(x, wg)
+    ids, w = O.route(z, 2)
+    f = O.moe_forward(x, ids, w, wgt, wup, wdn, dtype="bf16")
+    for key in ("a_s", "b_s", "y_s", "out"):
+        np.testing.assert_array_equal(f[key], O.round_bf16(f[key]))
+    fp = O.moe_forward(x, ids, w, wgt, wup, wdn, dtype=None)
+    rel = np.abs(f["out"] - fp["out"]).max() / np.abs(fp["out"]).max()
+    assert 0 < rel < 2e-2
+
+
+# --------------------------------------------------------------------------
+# backward (a6 .. a10)
+# --------------------------------------------------------------------------
+
+def _margin(z, K):
+    s = -np.sort(-z, axis=1)
+    return (s[:, K - 1] - s[:, K]).min() if K < z.shape[1] else np.inf
+
+
+@pytest.mark.parametrize("E,K", [(4, 2), (5, 1), (3, 3)])
+def test_backward_finite_differences(E, K):
+    T, d, h = 16, 8, 8
+    x, wg, wgt, wup, wdn, dy = _small_layer(T=T, d=d, E=E, K=K, h=h, seed=E * 10 + K, scale_router=3.0)
+    bias = np.linspace(-0.3, 0.3, E)
+    z, ids, w, f, b = O.layer_grads(x, wg, bias, wgt, wup, wdn, dy, K)
+    assert _margin(z, K) > 1e-3
+    eps = 1e-6
+    rng = np.random.default_rng(42)
+    params = dict(x=x, wg=wg, w_gate=wgt, w_up=wup, w_down=wdn)
+    grads = dict(x=b["dx"], wg=b["dwg"], w_gate=b["dw_gate"], w_up=b["dw_up"], w_down=b["dw_down"])
+    for name, P in params.items():
+        for trial in range(3):
+            V = rng.standard_normal(P.shape)
+            args = dict(params)
+            args[name] = P + eps * V
+            lp = O.layer_loss(args["x"], args["wg"], bias, args["w_gate"], args["w_up"], args["w_down"], dy, ids)
+            args[name] = P - eps * V
+            lm = O.layer_loss(args["x"], args["wg"], bias, args["w_gate"], args["w_up"], args["w_down"], dy, ids)
+            fd = (lp - lm) / (2 * eps)
+            an = float((grads[name] * V).sum())
+            assert abs(fd - an) <= 1e-6 * max(1.0, abs(an)), (name, fd, an)
+
+
+def test_router_score_gradient_identities():
+    x, wg, wgt, wup, wdn, dy = _small_layer(T=40, E=6, K=3, seed=3)
+    z, ids, w, f, b = O.layer_grads(x, wg, None, wgt, wup, wdn, dy, 3)
+    # <dO, Y> = <dA', y>  (score gradient over h instead of d)
+    np.testing.assert_allclose(b["ds"], b["ds_alt"], rtol=1e-11, atol=1e-12)
+    dz_closed = O.router_backward_closed(w, ids, b["ds"], 6)
+    np.testing.assert_array_equal(b["dz"], dz_closed)
+    np.testing.assert_allclose(b["dz_long"], dz_closed, rtol=1e-10, atol=1e-13)
+    # zero off the chosen set, and shift invariance of the softmax
+    mask = np.zeros_like(b["dz"], dtype=bool)
+    np.put_along_axis(mask, ids.astype(np.int64), True, axis=1)
+    assert np.all(dz_closed[~mask] == 0.0)
+    np.testing.assert_allclose(b["dz"].sum(axis=1), 0.0, atol=1e-13)
+
+
+def test_zero_row_experts_get_exact_zero_weight_gradients():
+    x, wg, wgt, wup, wdn, dy = _small_layer(T=20, E=6, K=2, seed=4)
+    wg[4:] = -10.0 * np.abs(wg[4:])
+    x = np.abs(x)
+    bias = np.array([0, 0, 0, 0, -100.0, -100.0])
+    z, ids, w, f, b = O.layer_grads(x, wg, bias, wgt, wup, wdn, dy, 2)
+    assert not np.isin(ids, [4, 5]).any()
+    for key in ("dw_gate", "dw_up", "dw_down"):
+        assert np.all(b[key][4:] == 0.0)
+    assert np.all(b["dwg"][4:] == 0.0)
+
+
+def test_backward_matches_explicit_per_token_loop():
+    """Independent restatement of the backward for one token, written as
+    plain per-assignment vector algebra (Algorithm 1 order)."""
+    x, wg, wgt, wup, wdn, dy = _small_layer(T=6, E=4, K=2, seed=8)
+    z, ids, w, f, b = O.layer_grads(x, wg, None, wgt, wup, wdn, dy, 2)
+    t = 3
+    dx_t = np.zeros(x.shape[1])
+    for k in range(2):
+        e = ids[t, k]
+        a = wgt[e] @ x[t]
+        bb = wup[e] @ x[t]
+        s = 1 / (1 + np.exp(-a))
+        y = a * s * bb
+        grad_y = w[t, k] * (wdn[e].T @ dy[t])          # grad of Y_swi
+        grad_a = grad_y * bb * (s + a * s * (1 - s))
+        grad_b = grad_y * a * s
+        dx_t += wgt[e].T @ grad_a + wup[e].T @ grad_b
+        np.testing.assert_allclose(b["ds"][t, k], dy[t] @ (wdn[e] @ y), rtol=1e-12)
+    dx_t += b["dz"][t] @ wg
+    np.testing.assert_allclose(b["dx"][t], dx_t, rtol=1e-11, atol=1e-12)
