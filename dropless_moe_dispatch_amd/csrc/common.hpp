@@ -1,0 +1,79 @@
+// Shared device helpers for the dropless MoE kernels (gfx950 / CDNA4).
+//
+// Element storage: bf16 as raw uint16_t bits, fp32 as float.  Accumulation is
+// always fp32 (MFMA accumulators).  Conversions to bf16 round to nearest even.
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#define MOE_DEV __device__ __forceinline__
+
+typedef uint16_t bf16_t;
+typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+typedef float f32x16_t __attribute__((ext_vector_type(16)));
+typedef float f32x4_t __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2_t __attribute__((ext_vector_type(2)));
+
+MOE_DEV float bf16_to_f32(uint32_t v) { return __uint_as_float(v << 16); }
+
+MOE_DEV uint32_t f32_to_bf16(float f) {
+  uint32_t u = __float_as_uint(f);
+  if ((u & 0x7fffffffu) > 0x7f800000u) return (u >> 16) | 0x40u;  // quiet NaN
+  u += 0x7fffu + ((u >> 16) & 1u);
+  return u >> 16;
+}
+
+template <typename T> struct ElemT;
+template <> struct ElemT<float> {
+  static MOE_DEV float to_f32(float v) { return v; }
+  static MOE_DEV float from_f32(float v) { return v; }
+  static MOE_DEV float load(const float* p) { return *p; }
+  static MOE_DEV void store(float* p, float v) { *p = v; }
+};
+template <> struct ElemT<bf16_t> {
+  static MOE_DEV float load(const bf16_t* p) { return bf16_to_f32(*p); }
+  static MOE_DEV void store(bf16_t* p, float v) { *p = (bf16_t)f32_to_bf16(v); }
+};
+
+MOE_DEV float sigmoidf_(float u) { return 1.0f / (1.0f + expf(-u)); }
+
+MOE_DEV int lane_id() { return (int)(threadIdx.x & 63); }
+
+// ---------------------------------------------------------------------------
+// MFMA: one 32x32 output fragment per instruction, K consumed 16 at a time.
+//
+// Operand layout (both operands are staged in LDS as [row][k] with k
+// contiguous): lane l supplies row (l % 32), k = 8*(l/32) .. 8*(l/32)+7.
+// The accumulator of lane l holds column (l % 32), rows
+// 8*(r/4) + 4*(l/32) + (r%4) for r = 0..15.
+// ---------------------------------------------------------------------------
+template <typename TIN> struct Mfma;
+
+template <> struct Mfma<bf16_t> {
+  // 16 B per lane per k-step: 8 bf16 values.
+  struct Frag { u32x4_t v; };
+  static MOE_DEV Frag lds_read(const char* p) { Frag f; f.v = *(const u32x4_t*)p; return f; }
+  static MOE_DEV void mma(f32x16_t& acc, const Frag& a, const Frag& b) {
+    acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8_t, a.v),
+                                                  __builtin_bit_cast(bf16x8_t, b.v), acc, 0, 0, 0);
+  }
+};
+
+template <> struct Mfma<float> {
+  // 32 B per lane per 16-k step: 8 fp32 values, consumed by 8 K=2 MFMAs.
+  struct Frag { f32x4_t lo, hi; };
+  static MOE_DEV Frag lds_read(const char* p) {
+    Frag f; f.lo = *(const f32x4_t*)p; f.hi = *(const f32x4_t*)(p + 16); return f;
+  }
+  static MOE_DEV void mma(f32x16_t& acc, const Frag& a, const Frag& b) {
+#pragma unroll
+    for (int s = 0; s < 4; ++s) acc = __builtin_amdgcn_mfma_f32_32x32x2f32(a.lo[s], b.lo[s], acc, 0, 0, 0);
+#pragma unroll
+    for (int s = 0; s < 4; ++s) acc = __builtin_amdgcn_mfma_f32_32x32x2f32(a.hi[s], b.hi[s], acc, 0, 0, 0);
+  }
+};
+
+// Row of accumulator register r for lane l inside a 32x32 fragment.
+MOE_DEV int frag_row(int r, int l) { return 8 * (r >> 2) + 4 * (l >> 5) + (r & 3); }
+MOE_DEV int frag_col(int l) { return l & 31; }

@@ -1,0 +1,657 @@
+// Expert GEMMs of the dropless MoE layer: forward gate/up with the SwiGLU
+// epilogue, the down projection with the ordered weighted combine, and the
+// backward kernels.  All are grouped GEMMs over the expert-sorted position
+// space p in [0, T*K) defined by expert_token_offsets; token rows are read in
+// place through expert_token_indices (no permuted copy of x or dY).
+//
+//  forward (MoEBlaze analysis page, "Memory-Efficient Token Routing: Forward
+//  Pass" and "Fused SwiGLU Kernel with Activation Checkpoint"; MoEBlaze
+//  reading notes sec. 5.2 Algorithm 1):
+//    a = x W_gate^T, b = x W_up^T        (one kernel, x loaded once)
+//    y = SiLU(a) * b                     (epilogue, from the fp32 a, b)
+//    store a, b, y  (Algorithm 1 keeps A, B and Y_swi for the backward)
+//    out[t] = sum_k w_{t,k} y_{p(t,k)} W_down^T    (owner-ordered combine)
+//  backward (same pages, "Backward Pass" and Algorithm 1 backward; SonicMoE
+//  analysis page sec. 3.4.1 for dS = <dA', y> and dA = s * dA'):
+//    dA' = dO W_down;  dS = <dA', y>;  dy = w dA'
+//    sigma, SiLU recomputed from the stored a:  da = dy b SiLU'(a), db = dy SiLU(a)
+//    dW_down[e] = sum_p (w_p dO_p)^T y_p;  dW_gate/up[e] = sum_p da/db_p^T x_p
+//    dX[t] = sum_k (da W_gate + db W_up)_{p(t,k)} + router term
+#include "gemm.hpp"
+#include "layout.hpp"
+
+namespace moe {
+
+template <typename T> MOE_DEV float ld_f(const T* p) { return ElemT<T>::load(p); }
+template <typename T> MOE_DEV void st_f(T* p, float v) { ElemT<T>::store(p, v); }
+
+// ===========================================================================
+// Forward gate/up: M = rows of expert e, N = 64 gate + 64 up columns, K = d.
+// ===========================================================================
+template <class C>
+__global__ __launch_bounds__(NTHREADS, 2) void gate_up_kernel(const typename C::T* __restrict__ x,
+                                                              const int32_t* __restrict__ offsets,
+                                                              const int32_t* __restrict__ eti,
+                                                              const int32_t* __restrict__ mb_off,
+                                                              const typename C::T* __restrict__ w_gate,
+                                                              const typename C::T* __restrict__ w_up,
+                                                              typename C::T* __restrict__ h_ab,
+                                                              typename C::T* __restrict__ y_swi, int d, int E,
+                                                              int h, int nbn, int nblk) {
+  __shared__ __attribute__((aligned(16))) char smem[C::LDS_BYTES];
+  using TIN = typename C::T;
+  const int id = xcd_swizzle(blockIdx.x, nblk);
+  const int g = id / nbn, nb = id % nbn;
+  if (g >= mb_off[E]) return;
+  const RowTile rt = decode_row_tile<C::BM>(mb_off, offsets, E, g);
+  const int wave = threadIdx.x >> 6, wm = wave / C::WN, wn = wave % C::WN;
+  const size_t ldx = (size_t)d * sizeof(TIN);
+  const int j0 = nb * (C::BN / 2);  // first gate/up column of this tile
+  RowLoader<C::BM> la;
+  RowLoader<C::BN> lb;
+#pragma unroll
+  for (int i = 0; i < RowLoader<C::BM>::CPT; ++i) {
+    const int p = rt.r0 + RowLoader<C::BM>::my_row(i);
+    la.row_ptr[i] = p < rt.r1 ? (const char*)x + (size_t)eti[p] * ldx : nullptr;
+  }
+#pragma unroll
+  for (int i = 0; i < RowLoader<C::BN>::CPT; ++i) {
+    const int r = RowLoader<C::BN>::my_row(i);
+    const TIN* w = r < C::BN / 2 ? w_gate : w_up;
+    const int j = j0 + (r % (C::BN / 2));
+    lb.row_ptr[i] = (const char*)(w + ((size_t)rt.e * h + j) * d);
+  }
+  f32x16_t acc[C::FM][C::FN];
+  gemm_mainloop<C>(la, lb, d / C::BK, smem, acc, wm, wn);
+  const int l = lane_id();
+  const int j = j0 + wn * 32 + frag_col(l);
+#pragma unroll
+  for (int fm = 0; fm < C::FM; ++fm)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      const int p = rt.r0 + C::a_row0(wm, fm) + frag_row(r, l);
+      if (p >= rt.r1) continue;
+      const float a = acc[fm][0][r];
+      const float b = acc[fm][1][r];
+      st_f(h_ab + (size_t)p * 2 * h + j, a);
+      st_f(h_ab + (size_t)p * 2 * h + h + j, b);
+      st_f(y_swi + (size_t)p * h + j, a * sigmoidf_(a) * b);
+    }
+}
+
+template <typename TIN>
+static hipError_t gate_up_t(const Shape& s, const void* x, const int32_t* offsets, const int32_t* eti,
+                            const void* w_gate, const void* w_up, void* h_ab, void* y_swi, const ExpertWs& ws,
+                            hipStream_t st) {
+  using C = Cfg<TIN, 128, 128, 2, 2, true>;
+  const int nbn = s.h / (C::BN / 2);
+  long long nblk = max_row_blocks(s) * nbn;
+  nblk = (nblk + 7) / 8 * 8;
+  gate_up_kernel<C><<<dim3((unsigned)nblk), dim3(NTHREADS), 0, st>>>(
+      (const TIN*)x, offsets, eti, ws.mb_off, (const TIN*)w_gate, (const TIN*)w_up, (TIN*)h_ab, (TIN*)y_swi, s.d,
+      s.E, s.h, nbn, (int)nblk);
+  return hipGetLastError();
+}
+
+hipError_t launch_gate_up(const Shape& s, const void* x, const int32_t* offsets, const int32_t* eti,
+                          const void* w_gate, const void* w_up, void* h_ab, void* y_swi, const ExpertWs& ws,
+                          hipStream_t st) {
+  timing_mark(st, "gate_up", true);
+  hipError_t e = s.bf16 ? gate_up_t<bf16_t>(s, x, offsets, eti, w_gate, w_up, h_ab, y_swi, ws, st)
+                        : gate_up_t<float>(s, x, offsets, eti, w_gate, w_up, h_ab, y_swi, ws, st);
+  timing_mark(st, "gate_up", false);
+  return e;
+}
+
+// ===========================================================================
+// Ordered fold: the owner-computes weighted combine through the reverse index.
+//
+// Every output row out[t] (per 128-column block) receives K contributions
+// from K different expert tiles.  Tiles are claimed through a ticket counter
+// in ascending (expert, row-block, column-block) order, and a contribution of
+// rank r (the position of its expert among the token's experts, ascending)
+// is applied only after turn[t][block] == r; it then bumps the turn.  All
+// predecessors of a contribution live in tiles with smaller tickets, held by
+// running workgroups, so the waits always drain.  The fp32 accumulator sees
+// the K contributions in ascending expert order: deterministic, with integer
+// flags only (no float atomics).  The last rank writes the output row.
+//
+// INIT_FIRST: rank 0 writes the accumulator (forward); otherwise the
+// accumulator is pre-initialised and every rank adds (backward dX, where the
+// router term is the initial value).
+// ===========================================================================
+template <class C, bool INIT_FIRST>
+MOE_DEV void fold_epilogue(const f32x16_t (&acc)[C::FM][C::FN], const RowTile& rt, int nb, int NB, int wm, int wn,
+                           const int32_t* __restrict__ eti, const float* __restrict__ w_pos,
+                           const int32_t* __restrict__ rank_pos, int K, int d, int32_t* turn,
+                           float* __restrict__ accws, typename C::T* __restrict__ out, int32_t* counters,
+                           int spin_limit, char* smem) {
+  int* s_t = (int*)smem;
+  float* s_w = (float*)(smem + 4 * C::BM);
+  int* s_rank = (int*)(smem + 8 * C::BM);
+  const int tid = threadIdx.x;
+  const int rows = rt.r1 - rt.r0;
+  __syncthreads();  // LDS stages are reused below
+  if (tid < rows) {
+    const int p = rt.r0 + tid;
+    const int t = eti[p];
+    const int rank = rank_pos[p];
+    s_t[tid] = t;
+    s_w[tid] = w_pos ? w_pos[p] : 1.0f;
+    s_rank[tid] = rank;
+    int32_t* f = turn + (size_t)t * NB + nb;
+    int spins = 0;
+    while (__hip_atomic_load(f, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) < rank) {
+      if (++spins > spin_limit) {
+        __hip_atomic_store(counters, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        break;
+      }
+      __builtin_amdgcn_s_sleep(2);
+    }
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
+  }
+  __syncthreads();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
+  const int l = lane_id();
+#pragma unroll
+  for (int fm = 0; fm < C::FM; ++fm)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      const int row = C::a_row0(wm, fm) + frag_row(r, l);
+      if (row >= rows) continue;
+      const int t = s_t[row];
+      const float w = s_w[row];
+      const int rank = s_rank[row];
+#pragma unroll
+      for (int fn = 0; fn < C::FN; ++fn) {
+        const int col = nb * C::BN + C::b_row0(wn, fn) + frag_col(l);
+        const size_t o = (size_t)t * d + col;
+        const float v = w * acc[fm][fn][r];
+        if (rank == K - 1) {
+          const float prev = (INIT_FIRST && rank == 0) ? 0.0f : accws[o];
+          ElemT<typename C::T>::store(out + o, prev + v);
+        } else if (INIT_FIRST && rank == 0) {
+          accws[o] = v;
+        } else {
+          accws[o] = accws[o] + v;
+        }
+      }
+    }
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");
+  __syncthreads();
+  if (tid < rows) {
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");
+    __hip_atomic_store(turn + (size_t)s_t[tid] * NB + nb, s_rank[tid] + 1, __ATOMIC_RELAXED,
+                       __HIP_MEMORY_SCOPE_AGENT);
+  }
+}
+
+MOE_DEV int claim_ticket(int32_t* counters, char* smem) {
+  int* s = (int*)smem;
+  if (threadIdx.x == 0) *s = atomicAdd(counters + 1, 1);
+  __syncthreads();
+  const int v = *s;
+  __syncthreads();
+  return v;
+}
+
+// ===========================================================================
+// Down projection + combine: M = rows of expert e, N = 128 output columns, K = h.
+// ===========================================================================
+template <class C>
+__global__ __launch_bounds__(NTHREADS, 2) void down_combine_kernel(
+    const typename C::T* __restrict__ y_swi, const typename C::T* __restrict__ w_down,
+    const int32_t* __restrict__ offsets, const int32_t* __restrict__ eti, const int32_t* __restrict__ mb_off,
+    const float* __restrict__ w_pos, const int32_t* __restrict__ rank_pos, int32_t* turn, float* accws,
+    typename C::T* __restrict__ out, int32_t* counters, int d, int E, int K, int h, int spin_limit) {
+  __shared__ __attribute__((aligned(16))) char smem[C::LDS_BYTES];
+  using TIN = typename C::T;
+  const int NB = d / C::BN;
+  const int tile = claim_ticket(counters, smem);
+  const int g = tile / NB, nb = tile % NB;
+  if (g >= mb_off[E]) return;
+  const RowTile rt = decode_row_tile<C::BM>(mb_off, offsets, E, g);
+  const int wave = threadIdx.x >> 6, wm = wave / C::WN, wn = wave % C::WN;
+  const size_t ldy = (size_t)h * sizeof(TIN);
+  RowLoader<C::BM> la;
+  RowLoader<C::BN> lb;
+#pragma unroll
+  for (int i = 0; i < RowLoader<C::BM>::CPT; ++i) {
+    const int p = rt.r0 + RowLoader<C::BM>::my_row(i);
+    la.row_ptr[i] = p < rt.r1 ? (const char*)y_swi + (size_t)p * ldy : nullptr;
+  }
+#pragma unroll
+  for (int i = 0; i < RowLoader<C::BN>::CPT; ++i) {
+    const int n = nb * C::BN + RowLoader<C::BN>::my_row(i);
+    lb.row_ptr[i] = (const char*)(w_down + ((size_t)rt.e * d + n) * h);
+  }
+  f32x16_t acc[C::FM][C::FN];
+  gemm_mainloop<C>(la, lb, h / C::BK, smem, acc, wm, wn);
+  fold_epilogue<C, true>(acc, rt, nb, NB, wm, wn, eti, w_pos, rank_pos, K, d, turn, accws, out, counters,
+                         spin_limit, smem);
+}
+
+template <typename TIN>
+static hipError_t down_combine_t(const Shape& s, const void* y_swi, const void* w_down, const int32_t* offsets,
+                                 const int32_t* eti, void* out, const ExpertWs& ws, int spin_limit, hipStream_t st) {
+  using C = Cfg<TIN, 128, 128, 2, 2>;
+  const long long nblk = max_row_blocks(s) * (s.d / C::BN);
+  down_combine_kernel<C><<<dim3((unsigned)nblk), dim3(NTHREADS), 0, st>>>(
+      (const TIN*)y_swi, (const TIN*)w_down, offsets, eti, ws.mb_off, ws.w_pos, ws.rank_pos, ws.turn, ws.acc,
+      (TIN*)out, ws.counters, s.d, s.E, s.K, s.h, spin_limit);
+  return hipGetLastError();
+}
+
+hipError_t launch_down_combine(const Shape& s, const void* y_swi, const void* w_down, const int32_t* offsets,
+                               const int32_t* eti, void* out, const ExpertWs& ws, int spin_limit, hipStream_t st) {
+  timing_mark(st, "down_combine", true);
+  hipError_t e = s.bf16 ? down_combine_t<bf16_t>(s, y_swi, w_down, offsets, eti, out, ws, spin_limit, st)
+                        : down_combine_t<float>(s, y_swi, w_down, offsets, eti, out, ws, spin_limit, st);
+  timing_mark(st, "down_combine", false);
+  return e;
+}
+
+// ===========================================================================
+// Backward
+// ===========================================================================
+
+// k-row sources for the transposed loaders -----------------------------------
+template <typename T>
+struct SrcWeightKN {   // B[k][n] = W[k * ld + n0 + n]
+  const char* base;    // &W[0][n0]
+  size_t ld_bytes;
+  MOE_DEV const char* ptr(int k, float&) const { return base + (size_t)k * ld_bytes; }
+};
+template <typename T>
+struct SrcWeightKN2 {  // k < h: W1[k][n0+n], else W2[k-h][n0+n]
+  const char* b1;
+  const char* b2;
+  size_t ld_bytes;
+  int h;
+  MOE_DEV const char* ptr(int k, float&) const {
+    return k < h ? b1 + (size_t)k * ld_bytes : b2 + (size_t)(k - h) * ld_bytes;
+  }
+};
+template <typename T>
+struct SrcRowsContig {  // rows p = p0 + k < p1 of a [rows, ld] array, columns from col0
+  const char* base;     // &A[0][col0]
+  size_t ld_bytes;
+  int p0, p1;
+  const float* scale;   // optional per-row scale
+  MOE_DEV const char* ptr(int k, float& s) const {
+    const int p = p0 + k;
+    if (p >= p1) return nullptr;
+    if (scale) s = scale[p];
+    return base + (size_t)p * ld_bytes;
+  }
+};
+template <typename T>
+struct SrcRowsGather {  // rows eti[p], p = p0 + k < p1, optional scale w_pos[p]
+  const char* base;     // &X[0][col0]
+  size_t ld_bytes;
+  int p0, p1;
+  const int32_t* eti;
+  const float* scale;
+  MOE_DEV const char* ptr(int k, float& s) const {
+    const int p = p0 + k;
+    if (p >= p1) return nullptr;
+    if (scale) s = scale[p];
+    return base + (size_t)eti[p] * ld_bytes;
+  }
+};
+
+// dH kernel: dA' = dO W_down (M rows of e, N = 128 of h, K = d) + SwiGLU backward
+template <class C>
+__global__ __launch_bounds__(NTHREADS, 2) void dh_kernel(
+    const typename C::T* __restrict__ dout, const typename C::T* __restrict__ w_down,
+    const typename C::T* __restrict__ h_ab, const typename C::T* __restrict__ y_swi,
+    const int32_t* __restrict__ offsets, const int32_t* __restrict__ eti, const int32_t* __restrict__ mb_off,
+    const float* __restrict__ w_pos, typename C::T* __restrict__ dh, float* __restrict__ ds_part, int d, int E,
+    int h, int nbn, int nblk) {
+  __shared__ __attribute__((aligned(16))) char smem[C::LDS_BYTES];
+  using TIN = typename C::T;
+  const int id = xcd_swizzle(blockIdx.x, nblk);
+  const int g = id / nbn, nb = id % nbn;
+  if (g >= mb_off[E]) return;
+  const RowTile rt = decode_row_tile<C::BM>(mb_off, offsets, E, g);
+  const int wave = threadIdx.x >> 6, wm = wave / C::WN, wn = wave % C::WN;
+  const size_t ldd = (size_t)d * sizeof(TIN);
+  RowLoader<C::BM> la;
+#pragma unroll
+  for (int i = 0; i < RowLoader<C::BM>::CPT; ++i) {
+    const int p = rt.r0 + RowLoader<C::BM>::my_row(i);
+    la.row_ptr[i] = p < rt.r1 ? (const char*)dout + (size_t)eti[p] * ldd : nullptr;
+  }
+  KRowLoader<TIN, SrcWeightKN<TIN>, false> lb;
+  lb.src.base = (const char*)(w_down + (size_t)rt.e * d * h + nb * C::BN);
+  lb.src.ld_bytes = (size_t)h * sizeof(TIN);
+  f32x16_t acc[C::FM][C::FN];
+  gemm_mainloop<C>(la, lb, d / C::BK, smem, acc, wm, wn);
+
+  const int l = lane_id();
+  float* s_ds = (float*)smem;  // [WN][BM]
+  float rs[C::FM][16];
+#pragma unroll
+  for (int fm = 0; fm < C::FM; ++fm)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      const int p = rt.r0 + C::a_row0(wm, fm) + frag_row(r, l);
+      float dsum = 0.0f;
+      if (p < rt.r1) {
+        const float w = w_pos[p];
+#pragma unroll
+        for (int fn = 0; fn < C::FN; ++fn) {
+          const int j = nb * C::BN + C::b_row0(wn, fn) + frag_col(l);
+          const float dap = acc[fm][fn][r];
+          const float a = ld_f(h_ab + (size_t)p * 2 * h + j);
+          const float b = ld_f(h_ab + (size_t)p * 2 * h + h + j);
+          const float y = ld_f(y_swi + (size_t)p * h + j);
+          dsum += dap * y;
+          const float dy = w * dap;
+          const float sg = sigmoidf_(a);
+          st_f(dh + (size_t)p * 2 * h + j, dy * b * sg * (1.0f + a * (1.0f - sg)));
+          st_f(dh + (size_t)p * 2 * h + h + j, dy * a * sg);
+        }
+      }
+      rs[fm][r] = dsum;
+    }
+  // reduce each row's partial over the 32 columns of the half-wave, fixed order
+#pragma unroll
+  for (int fm = 0; fm < C::FM; ++fm)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      float v = rs[fm][r];
+      v += __shfl_xor(v, 16, 32);
+      v += __shfl_xor(v, 8, 32);
+      v += __shfl_xor(v, 4, 32);
+      v += __shfl_xor(v, 2, 32);
+      v += __shfl_xor(v, 1, 32);
+      rs[fm][r] = v;
+    }
+  __syncthreads();
+  if ((l & 31) == 0) {
+#pragma unroll
+    for (int fm = 0; fm < C::FM; ++fm)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) s_ds[wn * C::BM + C::a_row0(wm, fm) + frag_row(r, l)] = rs[fm][r];
+  }
+  __syncthreads();
+  const int tid = threadIdx.x;
+  if (tid < rt.r1 - rt.r0) {
+    float v = 0.0f;
+#pragma unroll
+    for (int w = 0; w < C::WN; ++w) v += s_ds[w * C::BM + tid];
+    ds_part[(size_t)(rt.r0 + tid) * nbn + nb] = v;
+  }
+}
+
+// router backward per token: dS, dz (closed form), and the router term of dX
+//   dz[t,S_k] = w_k (dS_k - sum_j w_j dS_j)          (renormalised softmax)
+//   dX_router[t] = sum_k dz[t,S_k] Wg[S_k]          -> fold accumulator init
+template <typename TIN>
+__global__ __launch_bounds__(256) void router_bwd_kernel(const int32_t* __restrict__ ids,
+                                                         const float* __restrict__ topk_w,
+                                                         const int32_t* __restrict__ tim,
+                                                         const float* __restrict__ ds_part, int nbh,
+                                                         const TIN* __restrict__ wg, float* __restrict__ dz_pos,
+                                                         float* __restrict__ ds_out, float* __restrict__ accws,
+                                                         int T, int d, int K) {
+  const int t = blockIdx.x;
+  __shared__ float s_dz[32];
+  __shared__ int s_e[32];
+  if (threadIdx.x == 0) {
+    float dsv[32], wv[32];
+    float c = 0.0f;
+    for (int k = 0; k < K; ++k) {
+      const int p = tim[(size_t)t * K + k];
+      float v = 0.0f;
+      for (int nb = 0; nb < nbh; ++nb) v += ds_part[(size_t)p * nbh + nb];
+      dsv[k] = v;
+      wv[k] = topk_w[(size_t)t * K + k];
+      c += wv[k] * v;
+    }
+    for (int k = 0; k < K; ++k) {
+      const int p = tim[(size_t)t * K + k];
+      const float dz = wv[k] * (dsv[k] - c);
+      dz_pos[p] = dz;
+      if (ds_out) ds_out[(size_t)t * K + k] = dsv[k];
+      s_dz[k] = dz;
+      s_e[k] = ids[(size_t)t * K + k];
+    }
+  }
+  __syncthreads();
+  for (int i = threadIdx.x; i < d; i += 256) {
+    float v = 0.0f;
+    for (int k = 0; k < K; ++k) v += s_dz[k] * ElemT<TIN>::load(wg + (size_t)s_e[k] * d + i);
+    accws[(size_t)t * d + i] = v;
+  }
+}
+
+// dWg[e] = sum_{p in e} dz_p x[eti[p]]: one workgroup per (expert, 512 columns);
+// each wave strides over rows, fixed-order reduction across the 4 waves.
+template <typename TIN>
+__global__ __launch_bounds__(256) void dwg_kernel(const TIN* __restrict__ x, const int32_t* __restrict__ offsets,
+                                                  const int32_t* __restrict__ eti, const float* __restrict__ dz_pos,
+                                                  float* __restrict__ dwg, int d) {
+  constexpr int VPL = 16 / sizeof(TIN);  // values per lane per row
+  const int e = blockIdx.x;
+  const int c0 = blockIdx.y * 64 * VPL;
+  const int wave = threadIdx.x >> 6, l = lane_id();
+  const int col = c0 + l * VPL;
+  float acc[VPL];
+#pragma unroll
+  for (int v = 0; v < VPL; ++v) acc[v] = 0.0f;
+  const int p0 = offsets[e], p1 = offsets[e + 1];
+  if (col < d) {
+    for (int p = p0 + wave; p < p1; p += 4) {
+      const float z = dz_pos[p];
+      const TIN* row = x + (size_t)eti[p] * d + col;
+#pragma unroll
+      for (int v = 0; v < VPL; ++v) acc[v] += z * ElemT<TIN>::load(row + v);
+    }
+  }
+  __shared__ float s[4][64 * VPL];
+#pragma unroll
+  for (int v = 0; v < VPL; ++v) s[wave][l * VPL + v] = acc[v];
+  __syncthreads();
+  for (int i = threadIdx.x; i < 64 * VPL; i += 256) {
+    if (c0 + i < d) dwg[(size_t)e * d + c0 + i] = ((s[0][i] + s[1][i]) + s[2][i]) + s[3][i];
+  }
+}
+
+// dW_down[e] (d x h) = sum_p dO[eti[p]]^T (w_p y[p]): M = d, N = h, K = rows of e.
+// The score-scaled activation A' = w_p y[p] is formed while staging the B
+// operand and held in the activation dtype, as the SonicMoE analysis page
+// (sec. 3.4.1) defines A' = Broadcast(s) A for the dW2 grouped GEMM.
+template <class C>
+__global__ __launch_bounds__(NTHREADS, 2) void dw_down_kernel(const typename C::T* __restrict__ dout,
+                                                              const typename C::T* __restrict__ y_swi,
+                                                              const int32_t* __restrict__ offsets,
+                                                              const int32_t* __restrict__ eti,
+                                                              const float* __restrict__ w_pos,
+                                                              float* __restrict__ dw_down, int d, int h) {
+  __shared__ __attribute__((aligned(16))) char smem[C::LDS_BYTES];
+  using TIN = typename C::T;
+  const int nmb = d / C::BM, nnb = h / C::BN;
+  const int e = blockIdx.y;
+  const int mb = blockIdx.x / nnb, nb = blockIdx.x % nnb;
+  const int p0 = offsets[e], p1 = offsets[e + 1];
+  const int wave = threadIdx.x >> 6, wm = wave / C::WN, wn = wave % C::WN;
+  (void)nmb;
+  KRowLoader<TIN, SrcRowsGather<TIN>, false> la;
+  la.src.base = (const char*)(dout + mb * C::BM);
+  la.src.ld_bytes = (size_t)d * sizeof(TIN);
+  la.src.p0 = p0;
+  la.src.p1 = p1;
+  la.src.eti = eti;
+  la.src.scale = nullptr;
+  KRowLoader<TIN, SrcRowsContig<TIN>, true> lb;
+  lb.src.base = (const char*)(y_swi + nb * C::BN);
+  lb.src.ld_bytes = (size_t)h * sizeof(TIN);
+  lb.src.p0 = p0;
+  lb.src.p1 = p1;
+  lb.src.scale = w_pos;
+  f32x16_t acc[C::FM][C::FN];
+  gemm_mainloop<C>(la, lb, (p1 - p0 + C::BK - 1) / C::BK, smem, acc, wm, wn);
+  const int l = lane_id();
+  float* o = dw_down + (size_t)e * d * h;
+#pragma unroll
+  for (int fm = 0; fm < C::FM; ++fm)
+#pragma unroll
+    for (int fn = 0; fn < C::FN; ++fn)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int m = mb * C::BM + C::a_row0(wm, fm) + frag_row(r, l);
+        const int n = nb * C::BN + C::b_row0(wn, fn) + frag_col(l);
+        o[(size_t)m * h + n] = acc[fm][fn][r];
+      }
+}
+
+// dW_gate / dW_up [e] (h x d) = sum_p dH[p]^T x[eti[p]]: M = 2h, N = d, K = rows of e
+template <class C>
+__global__ __launch_bounds__(NTHREADS, 2) void dw_gate_up_kernel(const typename C::T* __restrict__ dh,
+                                                                 const typename C::T* __restrict__ x,
+                                                                 const int32_t* __restrict__ offsets,
+                                                                 const int32_t* __restrict__ eti,
+                                                                 float* __restrict__ dw_gate,
+                                                                 float* __restrict__ dw_up, int d, int h) {
+  __shared__ __attribute__((aligned(16))) char smem[C::LDS_BYTES];
+  using TIN = typename C::T;
+  const int nnb = d / C::BN;
+  const int e = blockIdx.y;
+  const int mb = blockIdx.x / nnb, nb = blockIdx.x % nnb;
+  const int p0 = offsets[e], p1 = offsets[e + 1];
+  const int wave = threadIdx.x >> 6, wm = wave / C::WN, wn = wave % C::WN;
+  KRowLoader<TIN, SrcRowsContig<TIN>, false> la;
+  la.src.base = (const char*)(dh + mb * C::BM);
+  la.src.ld_bytes = (size_t)2 * h * sizeof(TIN);
+  la.src.p0 = p0;
+  la.src.p1 = p1;
+  la.src.scale = nullptr;
+  KRowLoader<TIN, SrcRowsGather<TIN>, false> lb;
+  lb.src.base = (const char*)(x + nb * C::BN);
+  lb.src.ld_bytes = (size_t)d * sizeof(TIN);
+  lb.src.p0 = p0;
+  lb.src.p1 = p1;
+  lb.src.eti = eti;
+  lb.src.scale = nullptr;
+  f32x16_t acc[C::FM][C::FN];
+  gemm_mainloop<C>(la, lb, (p1 - p0 + C::BK - 1) / C::BK, smem, acc, wm, wn);
+  const int l = lane_id();
+  const bool up = mb * C::BM >= h;
+  float* o = (up ? dw_up : dw_gate) + (size_t)e * h * d;
+  const int mrow0 = mb * C::BM - (up ? h : 0);
+#pragma unroll
+  for (int fm = 0; fm < C::FM; ++fm)
+#pragma unroll
+    for (int fn = 0; fn < C::FN; ++fn)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int m = mrow0 + C::a_row0(wm, fm) + frag_row(r, l);
+        const int n = nb * C::BN + C::b_row0(wn, fn) + frag_col(l);
+        o[(size_t)m * d + n] = acc[fm][fn][r];
+      }
+}
+
+// dX~ = dH [W_gate; W_up] (M rows of e, N = 128 of d, K = 2h) + ordered fold into dX
+template <class C>
+__global__ __launch_bounds__(NTHREADS, 2) void dx_fold_kernel(
+    const typename C::T* __restrict__ dh, const typename C::T* __restrict__ w_gate,
+    const typename C::T* __restrict__ w_up, const int32_t* __restrict__ offsets, const int32_t* __restrict__ eti,
+    const int32_t* __restrict__ mb_off, const int32_t* __restrict__ rank_pos, int32_t* turn, float* accws,
+    typename C::T* __restrict__ dx, int32_t* counters, int d, int E, int K, int h, int spin_limit) {
+  __shared__ __attribute__((aligned(16))) char smem[C::LDS_BYTES];
+  using TIN = typename C::T;
+  const int NB = d / C::BN;
+  const int tile = claim_ticket(counters, smem);
+  const int g = tile / NB, nb = tile % NB;
+  if (g >= mb_off[E]) return;
+  const RowTile rt = decode_row_tile<C::BM>(mb_off, offsets, E, g);
+  const int wave = threadIdx.x >> 6, wm = wave / C::WN, wn = wave % C::WN;
+  const size_t ldh = (size_t)2 * h * sizeof(TIN);
+  RowLoader<C::BM> la;
+#pragma unroll
+  for (int i = 0; i < RowLoader<C::BM>::CPT; ++i) {
+    const int p = rt.r0 + RowLoader<C::BM>::my_row(i);
+    la.row_ptr[i] = p < rt.r1 ? (const char*)dh + (size_t)p * ldh : nullptr;
+  }
+  KRowLoader<TIN, SrcWeightKN2<TIN>, false> lb;
+  lb.src.b1 = (const char*)(w_gate + (size_t)rt.e * h * d + nb * C::BN);
+  lb.src.b2 = (const char*)(w_up + (size_t)rt.e * h * d + nb * C::BN);
+  lb.src.ld_bytes = (size_t)d * sizeof(TIN);
+  lb.src.h = h;
+  f32x16_t acc[C::FM][C::FN];
+  gemm_mainloop<C>(la, lb, (2 * h) / C::BK, smem, acc, wm, wn);
+  fold_epilogue<C, false>(acc, rt, nb, NB, wm, wn, eti, nullptr, rank_pos, K, d, turn, accws, dx, counters,
+                          spin_limit, smem);
+}
+
+template <typename TIN>
+static hipError_t backward_t(const Shape& s, const void* dout, const void* x, const void* wg, const void* w_gate,
+                             const void* w_up, const void* w_down, const int32_t* ids, const float* topk_w,
+                             const int32_t* offsets, const int32_t* eti, const int32_t* tim, const void* h_ab,
+                             const void* y_swi, void* dx, float* dwg, float* dw_gate, float* dw_up,
+                             float* dw_down, float* ds, const ExpertWs& ws, int spin_limit, hipStream_t st) {
+  using C = Cfg<TIN, 128, 128, 2, 2>;
+  const int nbh = s.h / C::BN;
+  const int nbd = s.d / C::BN;
+  const long long mbmax = max_row_blocks(s);
+  hipError_t err;
+  timing_mark(st, "dh", true);
+  {
+    const long long nblk = (mbmax * nbh + 7) / 8 * 8;
+    dh_kernel<C><<<dim3((unsigned)nblk), dim3(NTHREADS), 0, st>>>(
+        (const TIN*)dout, (const TIN*)w_down, (const TIN*)h_ab, (const TIN*)y_swi, offsets, eti, ws.mb_off,
+        ws.w_pos, (TIN*)ws.dh, ws.ds_part, s.d, s.E, s.h, nbh, (int)nblk);
+  }
+  timing_mark(st, "dh", false);
+  if ((err = hipGetLastError()) != hipSuccess) return err;
+
+  timing_mark(st, "router_bwd", true);
+  router_bwd_kernel<TIN><<<dim3(s.T), dim3(256), 0, st>>>(ids, topk_w, tim, ws.ds_part, nbh, (const TIN*)wg,
+                                                          ws.dz_pos, ds, ws.acc, s.T, s.d, s.K);
+  timing_mark(st, "router_bwd", false);
+  if ((err = hipGetLastError()) != hipSuccess) return err;
+
+  timing_mark(st, "dwg", true);
+  {
+    constexpr int VPL = 16 / sizeof(TIN);
+    const int ncb = (s.d + 64 * VPL - 1) / (64 * VPL);
+    dwg_kernel<TIN><<<dim3(s.E, ncb), dim3(256), 0, st>>>((const TIN*)x, offsets, eti, ws.dz_pos, dwg, s.d);
+  }
+  timing_mark(st, "dwg", false);
+  if ((err = hipGetLastError()) != hipSuccess) return err;
+
+  timing_mark(st, "dw_down", true);
+  dw_down_kernel<C><<<dim3((s.d / C::BM) * (s.h / C::BN), s.E), dim3(NTHREADS), 0, st>>>(
+      (const TIN*)dout, (const TIN*)y_swi, offsets, eti, ws.w_pos, dw_down, s.d, s.h);
+  timing_mark(st, "dw_down", false);
+  if ((err = hipGetLastError()) != hipSuccess) return err;
+
+  timing_mark(st, "dw_gate_up", true);
+  dw_gate_up_kernel<C><<<dim3((2 * s.h / C::BM) * (s.d / C::BN), s.E), dim3(NTHREADS), 0, st>>>(
+      (const TIN*)ws.dh, (const TIN*)x, offsets, eti, dw_gate, dw_up, s.d, s.h);
+  timing_mark(st, "dw_gate_up", false);
+  if ((err = hipGetLastError()) != hipSuccess) return err;
+
+  timing_mark(st, "dx_fold", true);
+  dx_fold_kernel<C><<<dim3((unsigned)(mbmax * nbd)), dim3(NTHREADS), 0, st>>>(
+      (const TIN*)ws.dh, (const TIN*)w_gate, (const TIN*)w_up, offsets, eti, ws.mb_off, ws.rank_pos, ws.turn,
+      ws.acc, (TIN*)dx, ws.counters, s.d, s.E, s.K, s.h, spin_limit);
+  timing_mark(st, "dx_fold", false);
+  return hipGetLastError();
+}
+
+hipError_t launch_backward(const Shape& s, const void* dout, const void* x, const void* wg, const void* w_gate,
+                           const void* w_up, const void* w_down, const int32_t* ids, const float* topk_w,
+                           const int32_t* offsets, const int32_t* eti, const int32_t* tim, const void* h_ab,
+                           const void* y_swi, void* dx, float* dwg, float* dw_gate, float* dw_up, float* dw_down,
+                           float* ds, const ExpertWs& ws, int spin_limit, hipStream_t st) {
+  if (s.bf16)
+    return backward_t<bf16_t>(s, dout, x, wg, w_gate, w_up, w_down, ids, topk_w, offsets, eti, tim, h_ab, y_swi,
+                              dx, dwg, dw_gate, dw_up, dw_down, ds, ws, spin_limit, st);
+  return backward_t<float>(s, dout, x, wg, w_gate, w_up, w_down, ids, topk_w, offsets, eti, tim, h_ab, y_swi, dx,
+                           dwg, dw_gate, dw_up, dw_down, ds, ws, spin_limit, st);
+}
+
+}  // namespace moe

@@ -1,0 +1,107 @@
+// Workspace layouts and launch-side declarations shared by the C-ABI and the
+// kernel translation units.  Every size depends on the shape only, never on
+// the routing, so a workspace sized once serves any routing of that shape.
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace moe {
+
+constexpr int TILE = 128;           // row-block / column-block of every expert GEMM
+constexpr int IDX_CHUNK = 256;      // tokens per index-build workgroup
+constexpr int IDX_WAVES = IDX_CHUNK / 64;
+constexpr int N_COUNTERS = 64;      // [0] error flag, [1] fold ticket, [2..] reserved
+
+struct Shape {
+  int T, d, E, K, h, bf16;
+  long long A() const { return (long long)T * K; }
+  int elem() const { return bf16 ? 2 : 4; }
+};
+
+inline size_t align_up(size_t v, size_t a) { return (v + a - 1) / a * a; }
+
+// Upper bound on the number of TILE-row blocks over all experts.
+inline long long max_row_blocks(const Shape& s) {
+  return (s.A() + (long long)s.E * (TILE - 1)) / TILE;
+}
+
+// ---- index workspace ------------------------------------------------------
+struct IndexWs {
+  uint64_t* masks;     // [nchunks][IDX_WAVES][E] token bitmaps per (chunk, wave, expert)
+  int32_t* base;       // [E][nchunks] counts, scanned in place to absolute bases
+  size_t bytes;
+  int nchunks;
+};
+inline IndexWs index_ws(const Shape& s, void* p) {
+  IndexWs w{};
+  w.nchunks = (s.T + IDX_CHUNK - 1) / IDX_CHUNK;
+  size_t off = 0;
+  w.masks = (uint64_t*)((char*)p + off);
+  off = align_up(off + (size_t)w.nchunks * IDX_WAVES * s.E * 8, 256);
+  w.base = (int32_t*)((char*)p + off);
+  off = align_up(off + (size_t)s.E * w.nchunks * 4, 256);
+  w.bytes = off;
+  return w;
+}
+
+// ---- per-call expert workspace (tile map, per-position data, fold state) --
+struct ExpertWs {
+  int32_t* counters;   // [N_COUNTERS]
+  int32_t* mb_off;     // [E+1] exclusive prefix of ceil(count_e / TILE)
+  float* w_pos;        // [A] combine weight of the assignment at each position
+  int32_t* rank_pos;   // [A] rank of the position's expert among its token's experts
+  int32_t* turn;       // [T][d/TILE] ordered-fold turn counters
+  float* acc;          // [T][d] fp32 fold accumulator
+  float* ds_part;      // [A][h/TILE] router-score partial sums (backward)
+  float* dz_pos;       // [A] router logit gradient per position (backward)
+  void* dh;            // [A][2h] activation-dtype gradient of the pre-activations (backward)
+  size_t bytes;
+};
+enum { WS_EXPERT_FWD = 1, WS_COMBINE = 2, WS_EXPERT_BWD = 3 };
+
+inline ExpertWs expert_ws(const Shape& s, int which, void* p) {
+  ExpertWs w{};
+  const size_t A = (size_t)s.A();
+  size_t off = 0;
+  auto take = [&](size_t bytes) { void* q = (char*)p + off; off = align_up(off + bytes, 256); return q; };
+  w.counters = (int32_t*)take(N_COUNTERS * 4);
+  w.mb_off = (int32_t*)take((size_t)(s.E + 1) * 4);
+  if (which == WS_COMBINE || which == WS_EXPERT_BWD) {
+    w.w_pos = (float*)take(A * 4);
+    w.rank_pos = (int32_t*)take(A * 4);
+    w.turn = (int32_t*)take((size_t)s.T * (s.d / TILE) * 4);
+    w.acc = (float*)take((size_t)s.T * s.d * 4);
+  }
+  if (which == WS_EXPERT_BWD) {
+    w.ds_part = (float*)take(A * (s.h / TILE) * 4);
+    w.dz_pos = (float*)take(A * 4);
+    w.dh = take(A * 2 * (size_t)s.h * s.elem());
+  }
+  w.bytes = off;
+  return w;
+}
+
+// ---- kernel launchers (defined in the kernel translation units) -----------
+hipError_t launch_router_logits(const Shape& s, const void* x, const void* wg, const float* bias, float* logits,
+                                hipStream_t st);
+hipError_t launch_topk(const Shape& s, const float* logits, int32_t* ids, float* w, hipStream_t st);
+hipError_t launch_build_index(const Shape& s, const int32_t* ids, int32_t* offsets, int32_t* eti, int32_t* tim,
+                              const IndexWs& ws, hipStream_t st);
+hipError_t launch_prep(const Shape& s, const ExpertWs& ws, const int32_t* offsets, const int32_t* ids,
+                       const float* topk_w, const int32_t* tim, bool per_position, hipStream_t st);
+hipError_t launch_gate_up(const Shape& s, const void* x, const int32_t* offsets, const int32_t* eti,
+                          const void* w_gate, const void* w_up, void* h_ab, void* y_swi, const ExpertWs& ws,
+                          hipStream_t st);
+hipError_t launch_down_combine(const Shape& s, const void* y_swi, const void* w_down, const int32_t* offsets,
+                               const int32_t* eti, void* out, const ExpertWs& ws, int spin_limit, hipStream_t st);
+hipError_t launch_backward(const Shape& s, const void* dout, const void* x, const void* wg, const void* w_gate,
+                           const void* w_up, const void* w_down, const int32_t* ids, const float* topk_w,
+                           const int32_t* offsets, const int32_t* eti, const int32_t* tim, const void* h_ab,
+                           const void* y_swi, void* dx, float* dwg, float* dw_gate, float* dw_up, float* dw_down,
+                           float* ds, const ExpertWs& ws, int spin_limit, hipStream_t st);
+
+// Optional per-kernel timing hooks (set by the C-ABI timing calls).
+void timing_mark(hipStream_t st, const char* name, bool begin);
+
+}  // namespace moe

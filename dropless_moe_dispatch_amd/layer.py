@@ -1,0 +1,107 @@
+"""Device buffers and the call sequence of one MoE layer through the C-ABI.
+
+torch is used for device memory and the stream only; every computation is a
+library kernel.  ``MoEBuffers`` allocates every output and workspace once for
+a shape (sizes do not depend on the routing); ``forward``/``backward`` enqueue
+the five entry points in order on the current stream with no host sync.
+"""
+from __future__ import annotations
+
+from dataclasses import dataclass
+from typing import Optional
+
+import torch
+
+from . import binding as B
+
+
+def torch_dtype(dtype: str):
+    return torch.bfloat16 if dtype == "bf16" else torch.float32
+
+
+@dataclass
+class MoEBuffers:
+    T: int
+    d: int
+    E: int
+    K: int
+    h: int
+    dtype: str = "bf16"
+    backward: bool = True
+    device: str = "cuda"
+
+    def __post_init__(self):
+        dev, td = self.device, torch_dtype(self.dtype)
+        T, d, E, K, h = self.T, self.d, self.E, self.K, self.h
+        self.shape = B.shape(T, d, E, K, h, self.dtype)
+        A = T * K
+        i32, f32 = torch.int32, torch.float32
+        self.logits = torch.empty(T, E, dtype=f32, device=dev)
+        self.topk_ids = torch.empty(T, K, dtype=i32, device=dev)
+        self.topk_w = torch.empty(T, K, dtype=f32, device=dev)
+        self.offsets = torch.empty(E + 1, dtype=i32, device=dev)
+        self.eti = torch.empty(A, dtype=i32, device=dev)
+        self.tim = torch.empty(A, dtype=i32, device=dev)
+        self.h_ab = torch.empty(A, 2 * h, dtype=td, device=dev)
+        self.y_swi = torch.empty(A, h, dtype=td, device=dev)
+        self.out = torch.empty(T, d, dtype=td, device=dev)
+        self.ws_index = self._ws(B.MOE_WS_INDEX)
+        self.ws_fwd = self._ws(B.MOE_WS_EXPERT_FWD)
+        self.ws_comb = self._ws(B.MOE_WS_COMBINE)
+        if self.backward:
+            self.dx = torch.empty(T, d, dtype=td, device=dev)
+            self.dwg = torch.empty(E, d, dtype=f32, device=dev)
+            self.dw_gate = torch.empty(E, h, d, dtype=f32, device=dev)
+            self.dw_up = torch.empty(E, h, d, dtype=f32, device=dev)
+            self.dw_down = torch.empty(E, d, h, dtype=f32, device=dev)
+            self.ds = torch.empty(T, K, dtype=f32, device=dev)
+            self.ws_bwd = self._ws(B.MOE_WS_EXPERT_BWD)
+
+    def _ws(self, which):
+        n = B.workspace_bytes(self.shape, which)
+        if n == 0:
+            raise B.MoeError("moe_workspace_bytes", B.MOE_ERR_INVALID_ARG)
+        return torch.empty(n, dtype=torch.uint8, device=self.device)
+
+    # -- accounting ---------------------------------------------------------
+    def saved_for_backward_bytes(self) -> int:
+        """Activations kept from the forward for the backward: a|b, y_swi,
+        the top-K ids and weights, and the index arrays."""
+        ts = [self.h_ab, self.y_swi, self.topk_ids, self.topk_w, self.offsets, self.eti, self.tim]
+        return sum(t.numel() * t.element_size() for t in ts)
+
+    def workspace_bytes(self) -> int:
+        ws = [self.ws_index, self.ws_fwd, self.ws_comb] + ([self.ws_bwd] if self.backward else [])
+        return sum(t.numel() for t in ws)
+
+    def device_error_words(self):
+        """Ordered-combine error words (nonzero: a bounded wait ran out)."""
+        w = [self.ws_comb[:4]] + ([self.ws_bwd[:4]] if self.backward else [])
+        return [int(x.view(torch.int32).item()) for x in w]
+
+
+def route(buf: MoEBuffers, x, wg, bias=None, logits_in: bool = False, stream=None):
+    B.moe_route_topk(buf.shape, None if logits_in else x, wg, bias, buf.logits, buf.topk_ids, buf.topk_w, stream)
+
+
+def forward(buf: MoEBuffers, x, wg, bias, w_gate, w_up, w_down, logits_in: bool = False, stream=None):
+    s = buf.shape
+    route(buf, x, wg, bias, logits_in, stream)
+    B.moe_build_index(s, buf.topk_ids, buf.offsets, buf.eti, buf.tim, buf.ws_index, stream)
+    B.moe_expert_fwd(s, x, buf.offsets, buf.eti, w_gate, w_up, buf.h_ab, buf.y_swi, buf.ws_fwd, stream)
+    B.moe_combine(s, buf.y_swi, w_down, buf.offsets, buf.eti, buf.tim, buf.topk_ids, buf.topk_w, buf.out,
+                  buf.ws_comb, stream)
+    return buf.out
+
+
+def backward(buf: MoEBuffers, dy, x, wg, w_gate, w_up, w_down, stream=None, want_ds: bool = True):
+    B.moe_expert_bwd(buf.shape, dy, x, wg, w_gate, w_up, w_down, buf.topk_ids, buf.topk_w, buf.offsets, buf.eti,
+                     buf.tim, buf.h_ab, buf.y_swi, buf.dx, buf.dwg, buf.dw_gate, buf.dw_up, buf.dw_down,
+                     buf.ds if want_ds else None, buf.ws_bwd, stream)
+    return buf.dx
+
+
+def to_device(arr, dtype: str, device="cuda"):
+    """float32 numpy array (already representable in ``dtype``) -> device tensor."""
+    t = torch.from_numpy(arr).to(device)
+    return t.to(torch_dtype(dtype)) if dtype == "bf16" else t

@@ -1,0 +1,187 @@
+/*
+ * moe_dispatch.h -- C ABI of the dropless Mixture-of-Experts layer hot path
+ * for AMD Instinct MI355X (gfx950).
+ *
+ * The layer (token-choice top-K routing, SwiGLU experts):
+ *   z      = x Wg^T (+ b)                          router logits, [T,E]
+ *   S_t    = TopK(z_t), w_t = softmax over z_t[S_t] (renormalised top-K weights)
+ *   a, b   = x_t W_gate[e]^T, x_t W_up[e]^T        per assignment (t, e in S_t)
+ *   y      = SiLU(a) * b,  SiLU(u) = u * sigmoid(u)
+ *   out_t  = sum_k w_{t,k} * y_{t,k} W_down[e_k]^T
+ * with the backward pass of L = <dY, out>, recomputing SiLU from the saved
+ * pre-activations.
+ *
+ * Sources:
+ *   MoEBlaze reading notes (papercache.org), sec. 2.1 (gating network:
+ *     TopK(softmax(W_g x)), W_g in R^{E x d}), sec. 2.3 (weighted output
+ *     aggregation), sec. 4.1 and Figure 2 (the index structures), sec. 5.2
+ *     Algorithm 1 (fused SwiGLU MoE training: forward stores A, B, Y_swi;
+ *     backward recomputes SiLU(A)).
+ *   "MoEBlaze: Breaking the Memory Wall for Efficient MoE Training on Modern
+ *     GPUs" (paper-graph-ui analysis page): "Memory-Efficient Token Routing:
+ *     Forward Pass / Backward Pass", "Dispatch Data Structures:
+ *     Specification and Roles", "Dispatch Data Structure Construction: The
+ *     Atomic-Free Three-Step Algorithm", "Fused SwiGLU Kernel with
+ *     Activation Checkpoint".
+ *   "SonicMoE: Accelerating MoE with IO and Tile-aware Optimizations"
+ *     (paper-graph-ui analysis page), sec. 3.4.1 (dS = <dA', A>, dA = s*dA').
+ *   "Dropless MoE, in depth" (aicassindra.com), "A reference implementation"
+ *     (renormalised top-K weights; counts stay on the device).
+ *
+ * Conventions for every entry point
+ *   - Pointers are DEVICE pointers unless marked "host".  The caller owns all
+ *     memory, including the workspace; the library never allocates, frees or
+ *     keeps a pointer after the call returns.
+ *   - Every call only enqueues work on `stream` (a hipStream_t; NULL = the
+ *     default stream).  No device-to-host copy, no synchronisation, and no
+ *     launch size depends on the routing, so a call sequence can be captured
+ *     into a HIP graph.  Results are valid once the stream has completed.
+ *   - Layouts are row-major.  Activations x, dY, out, dX: [T,d].  Router
+ *     weight Wg: [E,d].  Expert weights in [out,in] layout per expert:
+ *     W_gate, W_up: [E,h,d]; W_down: [E,d,h].  Weight gradients are fp32 in
+ *     the same layouts.  Activations and expert weights use moe_shape.dtype
+ *     (bf16 or fp32); router logits and top-K weights are fp32; index arrays
+ *     are int32.
+ *   - Return value: a moe_status.  Arguments are validated on the host
+ *     before anything is enqueued; on MOE_ERR_INVALID_ARG, _UNSUPPORTED or
+ *     _WORKSPACE nothing has been enqueued.  MOE_ERR_HIP reports a failed
+ *     launch (hipGetLastError after the enqueue).
+ *   - Workspaces hold no state between calls; size them with
+ *     moe_workspace_bytes, which depends on the shape only (never on the
+ *     routing, so skewed routing cannot exhaust it).  The first 4 bytes of a
+ *     MOE_WS_COMBINE / MOE_WS_EXPERT_BWD workspace are a device error word:
+ *     nonzero after the call if a bounded wait of the ordered combine ran out
+ *     (see moe_set_spin_limit); it is cleared at the start of each call.
+ *   - Supported shapes: 1 <= K <= min(E, 32), E <= 1024, T*K < 2^31,
+ *     d and h multiples of 128; device pointers 16-byte aligned.
+ */
+#ifndef MOE_DISPATCH_H
+#define MOE_DISPATCH_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  MOE_OK = 0,
+  MOE_ERR_INVALID_ARG = 1,   /* null required pointer, bad size, K > E, misaligned pointer */
+  MOE_ERR_UNSUPPORTED = 2,   /* shape or dtype outside what the kernels cover */
+  MOE_ERR_WORKSPACE = 3,     /* workspace smaller than moe_workspace_bytes */
+  MOE_ERR_HIP = 4            /* a kernel launch failed */
+} moe_status;
+
+typedef enum { MOE_F32 = 0, MOE_BF16 = 1 } moe_dtype;
+
+/* host struct: T tokens, model dim d, E experts, top-K, expert hidden h */
+typedef struct {
+  int32_t T, d, E, K, h;
+  int32_t dtype; /* moe_dtype of activations and expert weights */
+} moe_shape;
+
+typedef enum {
+  MOE_WS_INDEX = 0,       /* moe_build_index */
+  MOE_WS_EXPERT_FWD = 1,  /* moe_expert_fwd */
+  MOE_WS_COMBINE = 2,     /* moe_combine */
+  MOE_WS_EXPERT_BWD = 3   /* moe_expert_bwd */
+} moe_workspace_kind;
+
+/* Bytes of device workspace the call of kind `which` needs for shape *s
+ * (host pointer).  Returns 0 for an invalid shape or kind. */
+size_t moe_workspace_bytes(const moe_shape* s, int which);
+
+/* Router (MoEBlaze reading notes sec. 2.1; Dropless MoE in depth, "A reference
+ * implementation").
+ *   x != NULL: logits[T,E] (fp32, output) = x Wg^T (+ bias), fp32 accumulation.
+ *   x == NULL: logits[T,E] is an INPUT (routing from given logits); wg and
+ *              bias are ignored.
+ *   topk_ids[T,K] (int32, output): the K largest logits of each token, in
+ *     descending order; ties go to the lower expert id.  This array is the
+ *     token_expert_indices structure of the index.
+ *   topk_w[T,K] (fp32, output): softmax of the chosen K logits, i.e. the
+ *     softmax probabilities renormalised over the chosen experts.
+ *   bias[E] (fp32, nullable): fixed per-expert logit offset. */
+int moe_route_topk(const moe_shape* s, const void* x, const void* wg, const float* bias, float* logits,
+                   int32_t* topk_ids, float* topk_w, void* stream);
+
+/* Routing index by counting sort, without a global sort or atomics
+ * (MoEBlaze analysis page, "Dispatch Data Structures" and "Dispatch Data
+ * Structure Construction"; MoEBlaze reading notes sec. 4.1, Figure 2).
+ *   topk_ids[T*K]: input (token_expert_indices).
+ *   offsets[E+1] (output): expert_token_offsets, offsets[E] = T*K.
+ *   expert_token_indices[T*K] (output): token ids grouped by ascending
+ *     expert, ascending token id within an expert.
+ *   token_index_map[T*K] (output): entry t*K+k is the position of
+ *     (t, topk_ids[t,k]) in expert_token_indices.
+ * Bit-exact and deterministic.  ws: MOE_WS_INDEX workspace. */
+int moe_build_index(const moe_shape* s, const int32_t* topk_ids, int32_t* offsets, int32_t* expert_token_indices,
+                    int32_t* token_index_map, void* ws, size_t ws_bytes, void* stream);
+
+/* Gate/up grouped GEMM with the SwiGLU epilogue, gathering x rows in place
+ * through expert_token_indices (MoEBlaze analysis page, "Fused SwiGLU Kernel
+ * with Activation Checkpoint"; reading notes Algorithm 1 forward).  For each
+ * position p of expert e (offsets[e] <= p < offsets[e+1]), t = eti[p]:
+ *   h_ab[p, 0:h]  = a = x[t] W_gate[e]^T     (rounded to dtype)
+ *   h_ab[p, h:2h] = b = x[t] W_up[e]^T       (rounded to dtype)
+ *   y_swi[p, :]   = SiLU(a) * b, from the unrounded fp32 a and b.
+ * h_ab: [T*K, 2h], y_swi: [T*K, h], both dtype, outputs (saved for the
+ * backward).  No permuted copy of x is made.  ws: MOE_WS_EXPERT_FWD. */
+int moe_expert_fwd(const moe_shape* s, const void* x, const int32_t* offsets, const int32_t* expert_token_indices,
+                   const void* w_gate, const void* w_up, void* h_ab, void* y_swi, void* ws, size_t ws_bytes,
+                   void* stream);
+
+/* Down-projection grouped GEMM whose epilogue does the weighted combine
+ * through the reverse index (MoEBlaze analysis page, "On-the-Fly Output
+ * Aggregation"; reading notes sec. 2.3):
+ *   out[t] = sum_k topk_w[t,k] * y_swi[token_index_map[t*K+k]] W_down[e_k]^T.
+ * No float atomics and no [T*K, d] buffer: each output row block receives its
+ * K contributions in ascending expert order through integer turn counters,
+ * accumulating in an fp32 [T,d] workspace; deterministic.
+ * out: [T,d] dtype, output.  ws: MOE_WS_COMBINE. */
+int moe_combine(const moe_shape* s, const void* y_swi, const void* w_down, const int32_t* offsets,
+                const int32_t* expert_token_indices, const int32_t* token_index_map, const int32_t* topk_ids,
+                const float* topk_w, void* out, void* ws, size_t ws_bytes, void* stream);
+
+/* Backward of L = <dout, out> (reading notes Algorithm 1 backward; MoEBlaze
+ * analysis page "Backward Pass" and "Fused SwiGLU Kernel"; SonicMoE analysis
+ * page sec. 3.4.1).  Per position p (expert e, token t, weight w):
+ *   dA' = dout[t] W_down[e]            dS = <dA', y_swi[p]>
+ *   sigma = sigmoid(a), recomputed from the saved a; dy = w * dA'
+ *   da = dy * b * (sigma + a*sigma*(1-sigma)),   db = dy * a * sigma
+ *   dw_down[e] += (w dout[t])^T y_swi[p];  dw_gate[e] += da^T x[t];
+ *   dw_up[e] += db^T x[t];  dx[t] += da W_gate[e] + db W_up[e]
+ *   router: dz[t,S_k] = w_k (dS_k - sum_j w_j dS_j), zero elsewhere;
+ *           dwg[e] = sum_t dz[t,e] x[t];  dx[t] += sum_k dz[t,S_k] Wg[S_k].
+ * Inputs: dout, x [T,d]; wg [E,d]; weights; routing arrays; h_ab, y_swi from
+ * moe_expert_fwd.  Outputs (every element written; experts with no rows get
+ * exact zeros): dx [T,d] dtype, dwg [E,d] fp32, dw_gate/dw_up [E,h,d] fp32,
+ * dw_down [E,d,h] fp32, ds [T,K] fp32 (nullable: the router score
+ * gradient dL/dw).  The bias, if any, gets no gradient.  dx is assembled by
+ * the same ordered, atomic-free fold as moe_combine.  ws: MOE_WS_EXPERT_BWD. */
+int moe_expert_bwd(const moe_shape* s, const void* dout, const void* x, const void* wg, const void* w_gate,
+                   const void* w_up, const void* w_down, const int32_t* topk_ids, const float* topk_w,
+                   const int32_t* offsets, const int32_t* expert_token_indices, const int32_t* token_index_map,
+                   const void* h_ab, const void* y_swi, void* dx, float* dwg, float* dw_gate, float* dw_up,
+                   float* dw_down, float* ds, void* ws, size_t ws_bytes, void* stream);
+
+/* Static string for a moe_status value (host). */
+const char* moe_status_string(int code);
+
+/* Bound on the polls of one wait in the ordered combine (default 1<<20,
+ * about a second); a wait that runs out sets the workspace error word and
+ * proceeds, so every kernel always finishes.  Returns the previous value. */
+int moe_set_spin_limit(int polls);
+
+/* Per-kernel timing (profiling aid).  While enabled, each internal kernel
+ * launch is bracketed by HIP events on its stream; moe_timing_read
+ * synchronises on those events and returns up to `cap` (name, milliseconds)
+ * records in launch order (host arrays), then clears them.  Off by default. */
+int moe_timing_enable(int on);
+int moe_timing_read(const char** names, float* ms, int cap);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* MOE_DISPATCH_H */

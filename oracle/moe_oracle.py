@@ -39,6 +39,8 @@ design notes of the repository):
     SiLU from the rounded a, b.  ``store=None`` gives the pure float64 layer.
   * the router score gradient dS is taken with respect to the renormalised
     weights w, and dX includes the router path.
+  * dW_down uses the score-scaled activation A' = w * y held in the storage
+    type, as SonicMoE sec. 3.4.1 defines it (dW2 = A'^T dO).
 
 Parity status: every function below is pinned by tests/test_oracle_pins.py
 (worked example, brute force, closed forms, special cases, finite
@@ -202,9 +204,12 @@ def _rows_of(ids, k, e):
     return np.nonzero(ids[:, k] == e)[0]
 
 
-def moe_forward(x, ids, w, w_gate, w_up, w_down, dtype="bf16"):
+def moe_forward(x, ids, w, w_gate, w_up, w_down, dtype="bf16", only_experts=None):
     """Forward pass.  Returns out [T,d] plus the per-assignment tensors
-    a_s, b_s, y_s [T,K,h] (storage-rounded) and ye [T,K,d] (expert output)."""
+    a_s, b_s, y_s [T,K,h] (storage-rounded) and ye [T,K,d] (expert output).
+
+    ``only_experts`` (for sampled checks) evaluates only the assignments of
+    those experts; quantities of the other assignments stay zero."""
     st = storage_rounder(dtype)
     x = _f64(x)
     w = _f64(w)
@@ -217,7 +222,7 @@ def moe_forward(x, ids, w, w_gate, w_up, w_down, dtype="bf16"):
     ye = np.zeros((T, K, d))
     out = np.zeros((T, d))
     for k in range(K):                       # slot order of the weighted sum
-        for e in range(E):
+        for e in range(E) if only_experts is None else only_experts:
             r = _rows_of(ids, k, e)
             if len(r) == 0:
                 continue
@@ -242,8 +247,10 @@ def moe_forward(x, ids, w, w_gate, w_up, w_down, dtype="bf16"):
 # ---------------------------------------------------------------------------
 
 
-def moe_backward(dy, x, wg, ids, w, w_gate, w_up, w_down, fwd, z, dtype="bf16"):
+def moe_backward(dy, x, wg, ids, w, w_gate, w_up, w_down, fwd, z, dtype="bf16", only_experts=None):
     """Backward pass.  ``z`` are the logits the weights were computed from.
+    ``only_experts`` restricts the expert path to those experts (the weight
+    gradients of those experts are then complete; dx, ds, dwg are not).
 
     Returns dx [T,d], dwg [E,d], dw_gate/dw_up [E,h,d], dw_down [E,d,h],
     ds [T,K] (= dL/dw), ds_alt [T,K] (= <dA', y>), dz [T,E] (closed form),
@@ -265,7 +272,7 @@ def moe_backward(dy, x, wg, ids, w, w_gate, w_up, w_down, fwd, z, dtype="bf16"):
     dh_a = np.zeros((T, K, h))
     dh_b = np.zeros((T, K, h))
     for k in range(K):
-        for e in range(E):
+        for e in range(E) if only_experts is None else only_experts:
             r = _rows_of(ids, k, e)
             if len(r) == 0:
                 continue
@@ -281,7 +288,9 @@ def moe_backward(dy, x, wg, ids, w, w_gate, w_up, w_down, fwd, z, dtype="bf16"):
             db = st(dyv * silu(a))
             dh_a[r, k] = da
             dh_b[r, k] = db
-            dw_down[e] += (w[r, k][:, None] * g).T @ fwd["y_s"][r, k]
+            # A' = w * y, held in the storage type (SonicMoE sec. 3.4.1: dW2 = A'^T dO)
+            a_prime = st(w[r, k][:, None] * fwd["y_s"][r, k])
+            dw_down[e] += g.T @ a_prime
             dw_gate[e] += da.T @ x[r]
             dw_up[e] += db.T @ x[r]
             dx[r] += da @ _f64(w_gate[e]) + db @ _f64(w_up[e])

@@ -1,0 +1,90 @@
+"""C-ABI library checks that need no GPU: it loads, exports every declared
+symbol, sizes workspaces from the shape alone and rejects bad arguments on the
+host before anything is enqueued."""
+import ctypes
+import os
+import re
+
+import pytest
+
+from dropless_moe_dispatch_amd import binding as B
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "moe_dispatch.h")
+
+
+def _declared():
+    txt = open(HEADER).read()
+    txt = re.sub(r"/\*.*?\*/", "", txt, flags=re.S)
+    return sorted(set(re.findall(r"\b(moe_[a-z_]+)\s*\(", txt)))
+
+
+def test_library_exports_every_declared_symbol():
+    L = B.lib()
+    names = _declared()
+    assert {"moe_route_topk", "moe_build_index", "moe_expert_fwd", "moe_combine", "moe_expert_bwd"} <= set(names)
+    for n in names:
+        assert hasattr(L, n), n
+
+
+def test_status_strings():
+    assert B.status_string(0) == "ok"
+    assert "workspace" in B.status_string(B.MOE_ERR_WORKSPACE)
+    assert B.status_string(99) == "unknown status"
+
+
+def test_workspace_sizes_depend_on_shape_only():
+    s = B.shape(16384, 2048, 128, 8, 768)
+    sizes = [B.workspace_bytes(s, w) for w in range(4)]
+    assert all(n > 0 for n in sizes)
+    assert B.workspace_bytes(s, 7) == 0
+    # combine workspace holds the fp32 [T,d] fold accumulator, not a [T*K,d] buffer
+    comb = sizes[B.MOE_WS_COMBINE]
+    assert 16384 * 2048 * 4 <= comb < 16384 * 8 * 2048 * 2
+    bad = B.shape(16, 100, 8, 2, 128)           # d not a multiple of 128
+    assert B.workspace_bytes(bad, 0) == 0
+
+
+FAKE = 0x10000  # 16-byte aligned fake device address: never dereferenced
+
+
+@pytest.mark.parametrize("T,d,E,K,h,dt,code", [
+    (0, 128, 8, 2, 128, "bf16", B.MOE_ERR_INVALID_ARG),
+    (16, 128, 4, 5, 128, "bf16", B.MOE_ERR_INVALID_ARG),      # K > E
+    (16, 128, 2000, 2, 128, "bf16", B.MOE_ERR_UNSUPPORTED),   # E > 1024
+    (16, 128, 64, 40, 128, "bf16", B.MOE_ERR_UNSUPPORTED),    # K > 32
+    (16, 96, 8, 2, 128, "bf16", B.MOE_ERR_UNSUPPORTED),       # d % 128
+    (16, 128, 8, 2, 200, "f32", B.MOE_ERR_UNSUPPORTED),       # h % 128
+    (1 << 29, 128, 8, 8, 128, "bf16", B.MOE_ERR_INVALID_ARG),  # T*K >= 2^31
+])
+def test_shape_validation_happens_on_host(T, d, E, K, h, dt, code):
+    s = B.shape(T, d, E, K, h, dt)
+    assert B.moe_route_topk(s, FAKE, FAKE, None, FAKE, FAKE, FAKE, stream=0, check=False) == code
+    assert B.moe_build_index(s, FAKE, FAKE, FAKE, FAKE, FAKE, stream=0, check=False, ws_bytes=1 << 40) == code
+
+
+def test_pointer_and_workspace_validation():
+    s = B.shape(64, 128, 8, 2, 128)
+    L = B.lib()
+    sp = ctypes.byref(s)
+    # null required pointer
+    assert L.moe_route_topk(sp, FAKE, FAKE, None, None, FAKE, FAKE, 0) == B.MOE_ERR_INVALID_ARG
+    # misaligned pointer
+    assert L.moe_build_index(sp, FAKE + 4, FAKE, FAKE, FAKE, FAKE, 1 << 30, 0) == B.MOE_ERR_INVALID_ARG
+    # workspace too small
+    need = B.workspace_bytes(s, B.MOE_WS_INDEX)
+    assert L.moe_build_index(sp, FAKE, FAKE, FAKE, FAKE, FAKE, need - 1, 0) == B.MOE_ERR_WORKSPACE
+    need = B.workspace_bytes(s, B.MOE_WS_COMBINE)
+    assert L.moe_combine(sp, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, need - 1, 0) == B.MOE_ERR_WORKSPACE
+    need = B.workspace_bytes(s, B.MOE_WS_EXPERT_FWD)
+    assert L.moe_expert_fwd(sp, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, need - 1, 0) == B.MOE_ERR_WORKSPACE
+    need = B.workspace_bytes(s, B.MOE_WS_EXPERT_BWD)
+    req = [FAKE] * 18            # dout .. dw_down
+    assert L.moe_expert_bwd(sp, *req, None, FAKE, need - 1, 0) == B.MOE_ERR_WORKSPACE   # ds is optional
+    req[14] = None               # dwg missing
+    assert L.moe_expert_bwd(sp, *req, None, FAKE, need, 0) == B.MOE_ERR_INVALID_ARG
+
+
+def test_spin_limit_setter_roundtrip():
+    prev = B.set_spin_limit(1000)
+    assert B.set_spin_limit(prev) == 1000
