@@ -1,0 +1,178 @@
+"""Benchmark: one dropless MoE layer, forward + backward, on one MI355X.
+
+A step is one pass of the whole hot path over one batch of synthetic input:
+router logits + top-K, counting-sort index, gathered gate/up GEMM with the
+SwiGLU epilogue, down projection with the ordered combine, and the backward
+(dH with SiLU recompute, router backward, dWg, dW_down, dW_gate/up, dX fold).
+Inputs are resident in HBM before the timed region starts.
+
+Prints ONE JSON line (see the keys below).  Per-kernel durations come from
+HIP events recorded by the library around each of its launches, on the
+launch stream, during the timed steps.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+PEAK_BF16_TFLOPS = 2500.0     # MI355X dense bf16 MFMA
+PEAK_F32_MFMA_TFLOPS = 157.3  # MI355X fp32 (MFMA and vector)
+PEAK_HBM_GBS = 8000.0
+
+METRIC = "MoE layer fwd+bwd tokens/s and TFLOP/s at 1 GPU; % bf16 MFMA peak; peak act MB"
+
+
+def kernel_flops(name, T, d, E, K, h):
+    A = T * K
+    return {
+        "router_logits": 2.0 * T * d * E,
+        "gate_up": 4.0 * A * d * h,
+        "down_combine": 2.0 * A * d * h,
+        "dh": 2.0 * A * d * h,
+        "dw_down": 2.0 * A * d * h,
+        "dw_gate_up": 4.0 * A * d * h,
+        "dx_fold": 4.0 * A * d * h,
+    }.get(name)
+
+
+def cpu_baseline(wl, inp, sample_tokens):
+    """The CPU oracle (float64 numpy) on the first ``sample_tokens`` tokens of
+    the same workload, forward + backward."""
+    import numpy as np
+    from oracle import moe_oracle as O
+    try:
+        from threadpoolctl import threadpool_info
+        cores = max([i.get("num_threads", 1) for i in threadpool_info()] + [1])
+    except Exception:  # pragma: no cover
+        cores = os.cpu_count() or 1
+    n = sample_tokens
+    x, dy = inp["x"][:n], inp["dy"][:n]
+    t0 = time.perf_counter()
+    z = O.router_logits(x, inp["wg"], inp["bias"])
+    ids, w = O.route(z.astype(np.float32).astype(np.float64), wl.K)
+    O.build_index(ids, wl.E)
+    f = O.moe_forward(x, ids, w, inp["w_gate"], inp["w_up"], inp["w_down"], dtype=wl.dtype)
+    if wl.backward:
+        O.moe_backward(dy, x, inp["wg"], ids, w, inp["w_gate"], inp["w_up"], inp["w_down"], f, z, dtype=wl.dtype)
+    dt = time.perf_counter() - t0
+    return {"value": n / dt, "unit": "tokens/s", "cores": int(cores), "kind": "oracle",
+            "sample": f"first {n} tokens of the workload, router+index+forward" + ("+backward" if wl.backward else "")
+                      + f", float64 numpy, {dt:.1f} s wall"}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--workload", type=int, default=3, help="1..5 (default 3: fine-grained fwd+bwd)")
+    ap.add_argument("--cpu-sample", type=int, default=64, help="tokens for the CPU oracle baseline (0 = skip)")
+    ap.add_argument("--no-timing", action="store_true", help="do not record per-kernel events")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py runs on one GPU only; --gpus {args.gpus} is not supported "
+              "(the layer is measured on one GPU's share)", file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+    from dropless_moe_dispatch_amd import binding as B
+    from dropless_moe_dispatch_amd import layer as L
+    from dropless_moe_dispatch_amd import synth
+
+    wl = synth.WORKLOADS[args.workload]
+    T, d, E, K, h, dt = wl.T, wl.d, wl.E, wl.K, wl.h, wl.dtype
+    torch.cuda.set_device(0)
+    print(f"[bench] generating workload {wl.name}", file=sys.stderr, flush=True)
+    inp = synth.make_inputs(wl, tensors=("x", "wg", "w_gate", "w_up", "w_down") + (("dy",) if wl.backward else ()))
+    dev = {k: L.to_device(inp[k], dt) for k in ("x", "wg", "w_gate", "w_up", "w_down", "dy") if k in inp}
+    bias = torch.from_numpy(inp["bias"]).cuda() if inp["bias"] is not None else None
+    torch.cuda.synchronize()
+    base_alloc = torch.cuda.memory_allocated()
+    torch.cuda.reset_peak_memory_stats()
+    buf = L.MoEBuffers(T, d, E, K, h, dt, backward=wl.backward)
+
+    def step():
+        L.forward(buf, dev["x"], dev["wg"], bias, dev["w_gate"], dev["w_up"], dev["w_down"])
+        if wl.backward:
+            L.backward(buf, dev["dy"], dev["x"], dev["wg"], dev["w_gate"], dev["w_up"], dev["w_down"])
+
+    print("[bench] warmup", file=sys.stderr, flush=True)
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    if not args.no_timing:
+        B.timing_enable(True)
+        B.timing_read()
+    print("[bench] timed", file=sys.stderr, flush=True)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(args.steps):
+        step()
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    recs = B.timing_read() if not args.no_timing else []
+    B.timing_enable(False)
+    errs = buf.device_error_words()
+    peak_alloc = torch.cuda.max_memory_allocated()
+
+    ms = (t1 - t0) * 1e3 / args.steps
+    flops = (18.0 if wl.backward else 6.0) * T * K * d * h
+    tflops = flops / (ms * 1e-3) / 1e12
+    per = {}
+    for name, t in recs:
+        per.setdefault(name, []).append(t)
+    per_kernel = {k: {"avg_ms": float(np.mean(v)), "launches": len(v)} for k, v in per.items()}
+    roofline = None
+    gemms = {k: v for k, v in per_kernel.items() if kernel_flops(k, T, d, E, K, h) is not None and k != "router_logits"}
+    if gemms:
+        dom = max(gemms, key=lambda k: gemms[k]["avg_ms"] * gemms[k]["launches"])
+        fl = kernel_flops(dom, T, d, E, K, h)
+        ach = fl / (gemms[dom]["avg_ms"] * 1e-3) / 1e12
+        peak = PEAK_BF16_TFLOPS if dt == "bf16" else PEAK_F32_MFMA_TFLOPS
+        roofline = {"bound": "mfma", "kernel": dom, "achieved": round(ach, 2), "peak": peak, "unit": "TFLOP/s",
+                    "frac": round(ach / peak, 4), "traffic": None, "avg_launch_ms": round(gemms[dom]["avg_ms"], 4),
+                    "algorithmic_flop_per_launch": fl}
+    counts = np.diff(buf.offsets.cpu().numpy())
+    cpu = cpu_baseline(wl, inp, args.cpu_sample) if args.cpu_sample > 0 else None
+    out = {
+        "metric": METRIC,
+        "value": round(T / (ms * 1e-3), 1),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": dt,
+        "data": "synthetic (seeded Philox normals, random-init weights)",
+        "config": {"workload": wl.name, "T": T, "d": d, "E": E, "K": K, "h": h,
+                   "backward": wl.backward, "zipf_s": wl.zipf_s, "seed": wl.seed},
+        "tflops": round(tflops, 2),
+        "mfma_peak_frac": round(tflops / (PEAK_BF16_TFLOPS if dt == "bf16" else PEAK_F32_MFMA_TFLOPS), 4),
+        "model_flop_per_step": flops,
+        "roofline": roofline,
+        "cpu_baseline": cpu,
+        "per_kernel_ms": {k: round(v["avg_ms"], 4) for k, v in per_kernel.items()},
+        "act_saved_MB": round(buf.saved_for_backward_bytes() / 1e6, 1),
+        "workspace_MB": round(buf.workspace_bytes() / 1e6, 1),
+        "peak_transient_MB": round((peak_alloc - base_alloc) / 1e6, 1),
+        "avoided_TKd_buffer_MB": round(T * K * d * (2 if dt == "bf16" else 4) / 1e6, 1),
+        "routing": {"max_rows": int(counts.max()), "min_rows": int(counts.min()),
+                    "zero_row_experts": int((counts == 0).sum()),
+                    "padded_row_frac": round(float((np.ceil(counts / 128) * 128).sum() / counts.sum() - 1), 4)},
+        "device_errors": errs,
+    }
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -148,42 +148,51 @@ MOE_DEV void fold_epilogue(const f32x16_t (&acc)[C::FM][C::FN], const RowTile& r
       }
       __builtin_amdgcn_s_sleep(2);
     }
-    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
   }
   __syncthreads();
-  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
+  // one device-scope acquire per tile: the predecessors' accumulator rows
+  // (possibly written through another XCD's L2) become visible to every wave
+  if (tid < 64) __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
+  __syncthreads();
   const int l = lane_id();
+  // issue every accumulator read first, then combine and store
+  float prev[C::FM][C::FN][16];
+#pragma unroll
+  for (int fm = 0; fm < C::FM; ++fm)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      const int row = C::a_row0(wm, fm) + frag_row(r, l);
+      const bool need = row < rows && !(INIT_FIRST && s_rank[row] == 0);
+      const size_t ob = need ? (size_t)s_t[row] * d + nb * C::BN : 0;
+#pragma unroll
+      for (int fn = 0; fn < C::FN; ++fn)
+        prev[fm][fn][r] = need ? accws[ob + C::b_row0(wn, fn) + frag_col(l)] : 0.0f;
+    }
 #pragma unroll
   for (int fm = 0; fm < C::FM; ++fm)
 #pragma unroll
     for (int r = 0; r < 16; ++r) {
       const int row = C::a_row0(wm, fm) + frag_row(r, l);
       if (row >= rows) continue;
-      const int t = s_t[row];
+      const size_t ob = (size_t)s_t[row] * d + nb * C::BN;
       const float w = s_w[row];
-      const int rank = s_rank[row];
+      const bool last = s_rank[row] == K - 1;
 #pragma unroll
       for (int fn = 0; fn < C::FN; ++fn) {
-        const int col = nb * C::BN + C::b_row0(wn, fn) + frag_col(l);
-        const size_t o = (size_t)t * d + col;
-        const float v = w * acc[fm][fn][r];
-        if (rank == K - 1) {
-          const float prev = (INIT_FIRST && rank == 0) ? 0.0f : accws[o];
-          ElemT<typename C::T>::store(out + o, prev + v);
-        } else if (INIT_FIRST && rank == 0) {
-          accws[o] = v;
-        } else {
-          accws[o] = accws[o] + v;
-        }
+        const size_t o = ob + C::b_row0(wn, fn) + frag_col(l);
+        const float v = prev[fm][fn][r] + w * acc[fm][fn][r];
+        if (last) ElemT<typename C::T>::store(out + o, v);
+        else accws[o] = v;
       }
     }
-  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");
+  // all waves' stores complete, then one device-scope release, then the turns
+  __builtin_amdgcn_s_waitcnt(0);
   __syncthreads();
-  if (tid < rows) {
-    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");
+  if (tid < 64) __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");
+  __syncthreads();
+  if (tid < rows)
     __hip_atomic_store(turn + (size_t)s_t[tid] * NB + nb, s_rank[tid] + 1, __ATOMIC_RELAXED,
                        __HIP_MEMORY_SCOPE_AGENT);
-  }
 }
 
 MOE_DEV int claim_ticket(int32_t* counters, char* smem) {

@@ -1,0 +1,125 @@
+"""GPU parity at the five full workload sizes, in the launch configuration the
+benchmark times (router on the GPU, the five entry points in order).
+
+The oracle evaluates sampled outputs one by one: 32 random tokens (out, dx,
+dS, saved a/b/y), the weight gradients of the smallest and the largest
+expert, dWg of the smallest expert; index arrays are checked bit-exact in
+full, and exact zeros for experts without rows.
+"""
+import sys
+
+import numpy as np
+import pytest
+
+torch = pytest.importorskip("torch")
+
+from dropless_moe_dispatch_amd import binding as B
+from dropless_moe_dispatch_amd import layer as Lyr
+from dropless_moe_dispatch_amd import synth
+from oracle import moe_oracle as O
+from tests.gpu_util import assert_close, to_np, topk_margin
+
+pytestmark = pytest.mark.gpu
+
+
+def _say(*a):
+    print("[case]", *a, file=sys.stderr, flush=True)
+
+
+@pytest.mark.timeout(900)
+@pytest.mark.parametrize("idx", [1, 2, 3, 4, 5])
+def test_workload_full_size(idx):
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    wl = synth.WORKLOADS[idx]
+    _say("workload", idx, wl.name, "generate")
+    T, d, E, K, h, dt = wl.T, wl.d, wl.E, wl.K, wl.h, wl.dtype
+    tensors = ("x", "wg", "w_gate", "w_up", "w_down") + (("dy",) if wl.backward else ())
+    inp = synth.make_inputs(wl, tensors=tensors)
+    dev = {k: Lyr.to_device(inp[k], dt) for k in tensors}
+    bias = torch.from_numpy(inp["bias"]).cuda() if inp["bias"] is not None else None
+    buf = Lyr.MoEBuffers(T, d, E, K, h, dt, backward=wl.backward)
+
+    def run():
+        Lyr.forward(buf, dev["x"], dev["wg"], bias, dev["w_gate"], dev["w_up"], dev["w_down"])
+        if wl.backward:
+            Lyr.backward(buf, dev["dy"], dev["x"], dev["wg"], dev["w_gate"], dev["w_up"], dev["w_down"])
+        torch.cuda.synchronize()
+
+    _say("workload", idx, "gpu run 1")
+    run()
+    assert buf.device_error_words() == [0, 0][: 2 if wl.backward else 1] or all(
+        e == 0 for e in buf.device_error_words())
+    keep = {k: getattr(buf, k).clone() for k in ("out",) + (("dx", "dw_gate", "dw_up", "dw_down", "dwg")
+                                                            if wl.backward else ())}
+    _say("workload", idx, "gpu run 2 (repeatability)")
+    run()
+    for k, v in keep.items():
+        assert torch.equal(v, getattr(buf, k)), f"run-to-run difference in {k}"
+    del keep
+
+    _say("workload", idx, "oracle routing")
+    z = O.router_logits(inp["x"], inp["wg"], inp["bias"])
+    zg = to_np(buf.logits)
+    dz = float(np.abs(zg - z).max())
+    assert dz < 1e-4, dz
+    z32 = z.astype(np.float32)
+    ids_ref = O.topk_select(z32, K)
+    ids_gpu = to_np(buf.topk_ids)
+    mism = np.nonzero((ids_gpu != ids_ref).any(axis=1))[0]
+    margin = topk_margin(z32, K)
+    assert np.all(margin[mism] <= 4 * dz), "routing differs away from a near tie"
+    _say("workload", idx, "near-tie tokens:", len(mism), "max |dz|:", dz)
+    w_ref = O.topk_weights(z32.astype(np.float64), ids_ref)
+    counts = np.bincount(ids_ref.reshape(-1), minlength=E)
+    if len(mism) == 0:
+        ix = O.build_index(ids_ref, E)
+        assert np.array_equal(to_np(buf.offsets), ix["offsets"])
+        assert np.array_equal(to_np(buf.eti), ix["expert_token_indices"])
+        assert np.array_equal(to_np(buf.tim), ix["token_index_map"])
+        np.testing.assert_allclose(to_np(buf.topk_w), w_ref, rtol=1e-4, atol=1e-7)
+    if wl.zipf_s:
+        share = counts.max() / counts.sum()
+        # the Zipf(1.2) logit offset puts one expert in nearly every token's set
+        # and leaves the least popular experts with only a few tens of rows
+        assert share > 0.10 and counts.min() < 32, (share, counts.min())
+
+    rng = np.random.default_rng(idx)
+    ok_tokens = np.setdiff1d(np.arange(T), mism)
+    sub = np.sort(rng.choice(ok_tokens, size=min(32, len(ok_tokens)), replace=False))
+    _say("workload", idx, "oracle sampled tokens")
+    f = O.moe_forward(inp["x"][sub], ids_ref[sub], w_ref[sub], inp["w_gate"], inp["w_up"], inp["w_down"], dtype=dt)
+    assert_close("out[sample]", to_np(buf.out[torch.from_numpy(sub).cuda()]), f["out"])
+    pos = to_np(buf.tim).reshape(T, K)[sub]
+    hab = to_np(buf.h_ab[torch.from_numpy(pos.reshape(-1)).cuda()]).reshape(len(sub), K, 2 * h)
+    assert_close("a[sample]", hab[..., :h], f["a_s"])
+    assert_close("b[sample]", hab[..., h:], f["b_s"])
+    if not wl.backward:
+        return
+    b = O.moe_backward(inp["dy"][sub], inp["x"][sub], inp["wg"], ids_ref[sub], w_ref[sub], inp["w_gate"],
+                       inp["w_up"], inp["w_down"], f, z32[sub].astype(np.float64), dtype=dt)
+    assert_close("dx[sample]", to_np(buf.dx[torch.from_numpy(sub).cuda()]), b["dx"])
+    assert_close("ds[sample]", to_np(buf.ds)[sub], b["ds"])
+
+    nz = np.nonzero(counts > 0)[0]
+    e_small = int(nz[np.argmin(counts[nz])])
+    e_big = int(np.argmax(counts))
+    for e in sorted({e_small, e_big}):
+        toks = np.nonzero((ids_ref == e).any(axis=1))[0]
+        if np.isin(toks, mism).any():
+            continue
+        _say("workload", idx, "oracle expert", e, "rows", len(toks))
+        full_k = e == e_small
+        fe = O.moe_forward(inp["x"][toks], ids_ref[toks], w_ref[toks], inp["w_gate"], inp["w_up"], inp["w_down"],
+                           dtype=dt, only_experts=None if full_k else [e])
+        be = O.moe_backward(inp["dy"][toks], inp["x"][toks], inp["wg"], ids_ref[toks], w_ref[toks], inp["w_gate"],
+                            inp["w_up"], inp["w_down"], fe, z32[toks].astype(np.float64), dtype=dt,
+                            only_experts=None if full_k else [e])
+        assert_close(f"dw_gate[{e}]", to_np(buf.dw_gate[e]), be["dw_gate"][e])
+        assert_close(f"dw_up[{e}]", to_np(buf.dw_up[e]), be["dw_up"][e])
+        assert_close(f"dw_down[{e}]", to_np(buf.dw_down[e]), be["dw_down"][e])
+        if full_k:
+            assert_close(f"dwg[{e}]", to_np(buf.dwg[e]), be["dwg"][e])
+    for e in np.nonzero(counts == 0)[0]:
+        for key in ("dw_gate", "dw_up", "dw_down", "dwg"):
+            assert float(getattr(buf, key)[int(e)].abs().max()) == 0.0, (key, e)
