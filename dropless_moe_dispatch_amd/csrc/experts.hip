@@ -12,11 +12,13 @@
 //    store a, b, y  (Algorithm 1 keeps A, B and Y_swi for the backward)
 //    out[t] = sum_k w_{t,k} y_{p(t,k)} W_down^T    (owner-ordered combine)
 //  backward (same pages, "Backward Pass" and Algorithm 1 backward; SonicMoE
-//  analysis page sec. 3.4.1 for dS = <dA', y> and dA = s * dA'):
+//  analysis page sec. 3.4.1 for dS = <dA', y>, dA = s * dA', dW2 = A'^T dO):
 //    dA' = dO W_down;  dS = <dA', y>;  dy = w dA'
 //    sigma, SiLU recomputed from the stored a:  da = dy b SiLU'(a), db = dy SiLU(a)
-//    dW_down[e] = sum_p (w_p dO_p)^T y_p;  dW_gate/up[e] = sum_p da/db_p^T x_p
+//    dW_down[e] = sum_p dO_p^T (w_p y_p);  dW_gate/up[e] = sum_p da/db_p^T x_p
 //    dX[t] = sum_k (da W_gate + db W_up)_{p(t,k)} + router term
+#include <stdlib.h>
+
 #include "gemm.hpp"
 #include "layout.hpp"
 
@@ -25,71 +27,98 @@ namespace moe {
 template <typename T> MOE_DEV float ld_f(const T* p) { return ElemT<T>::load(p); }
 template <typename T> MOE_DEV void st_f(T* p, float v) { ElemT<T>::store(p, v); }
 
+// Two tile shapes: 128 x 128 (64 x 64 per wave, two workgroups per CU) and
+// 256 x 256 (128 x 128 per wave, one workgroup per CU, accumulators in
+// AGPRs).  The host picks one per kernel from the shape: the large tile
+// halves the LDS traffic per MFMA and pays off when the reduction is long;
+// the small one keeps two workgroups per CU, which hides epilogues and the
+// ordered combine's waits.
+template <typename TIN, int B> using GCfg = Cfg<TIN, B, B, 2, 2>;
+template <typename TIN, int B> using PCfg = Cfg<TIN, B, B, 2, 2, true>;
+
+// MOE_DISPATCH_TILE=128|256 forces one tile for every expert GEMM (tuning aid).
+static int forced_tile() {
+  static int v = [] {
+    const char* e = getenv("MOE_DISPATCH_TILE");
+    if (!e) return 0;
+    const int t = atoi(e);
+    return (t == TILE_S || t == TILE_L) ? t : 0;
+  }();
+  return v;
+}
+static bool pick_large(bool auto_choice) {
+  const int f = forced_tile();
+  return f ? f == TILE_L : auto_choice;
+}
+
 // ===========================================================================
-// Forward gate/up: M = rows of expert e, N = 64 gate + 64 up columns, K = d.
+// Forward gate/up: M = rows of expert e, N = 128 gate + 128 up columns, K = d.
 // ===========================================================================
 template <class C>
-__global__ __launch_bounds__(NTHREADS, 2) void gate_up_kernel(const typename C::T* __restrict__ x,
-                                                              const int32_t* __restrict__ offsets,
-                                                              const int32_t* __restrict__ eti,
-                                                              const int32_t* __restrict__ mb_off,
-                                                              const typename C::T* __restrict__ w_gate,
-                                                              const typename C::T* __restrict__ w_up,
-                                                              typename C::T* __restrict__ h_ab,
-                                                              typename C::T* __restrict__ y_swi, int d, int E,
-                                                              int h, int nbn, int nblk) {
+__global__ __launch_bounds__(NTHREADS, C::WAVES_PER_EU) void gate_up_kernel(
+    const typename C::T* __restrict__ x, const int32_t* __restrict__ offsets, const int32_t* __restrict__ eti,
+    const int32_t* __restrict__ mb_off, const typename C::T* __restrict__ w_gate,
+    const typename C::T* __restrict__ w_up, typename C::T* __restrict__ h_ab, typename C::T* __restrict__ y_swi,
+    int T, int d, int E, int h, int nbn, int nblk) {
   __shared__ __attribute__((aligned(16))) char smem[C::LDS_BYTES];
   using TIN = typename C::T;
+  constexpr int HB = C::BN / 2;     // gate (= up) columns per tile
+  constexpr int HF = C::FN / 2;     // gate fragments per wave
   const int id = xcd_swizzle(blockIdx.x, nblk);
   const int g = id / nbn, nb = id % nbn;
   if (g >= mb_off[E]) return;
   const RowTile rt = decode_row_tile<C::BM>(mb_off, offsets, E, g);
   const int wave = threadIdx.x >> 6, wm = wave / C::WN, wn = wave % C::WN;
-  const size_t ldx = (size_t)d * sizeof(TIN);
-  const int j0 = nb * (C::BN / 2);  // first gate/up column of this tile
+  const uint32_t ldx = (uint32_t)d * sizeof(TIN);
+  const int j0 = nb * HB;  // first gate/up column of this tile
   RowLoader<C::BM> la;
-  RowLoader<C::BN> lb;
+  RowLoader<C::BN, true> lb;   // rows [0,HB) gate, [HB,BN) up
+  la.rs[0] = make_rsrc(x, (size_t)T * ldx);
 #pragma unroll
   for (int i = 0; i < RowLoader<C::BM>::CPT; ++i) {
     const int p = rt.r0 + RowLoader<C::BM>::my_row(i);
-    la.row_ptr[i] = p < rt.r1 ? (const char*)x + (size_t)eti[p] * ldx : nullptr;
+    la.roff[i] = p < rt.r1 ? (uint32_t)eti[p] * ldx : OOB_OFF;
   }
+  lb.rs[0] = make_rsrc(w_gate + (size_t)rt.e * h * d, (size_t)h * ldx);
+  lb.rs[1] = make_rsrc(w_up + (size_t)rt.e * h * d, (size_t)h * ldx);
 #pragma unroll
   for (int i = 0; i < RowLoader<C::BN>::CPT; ++i) {
-    const int r = RowLoader<C::BN>::my_row(i);
-    const TIN* w = r < C::BN / 2 ? w_gate : w_up;
-    const int j = j0 + (r % (C::BN / 2));
-    lb.row_ptr[i] = (const char*)(w + ((size_t)rt.e * h + j) * d);
+    const int j = j0 + (RowLoader<C::BN>::my_row(i) % HB);
+    lb.roff[i] = j < h ? (uint32_t)j * ldx : OOB_OFF;
   }
   f32x16_t acc[C::FM][C::FN];
   gemm_mainloop<C>(la, lb, d / C::BK, smem, acc, wm, wn);
   const int l = lane_id();
-  const int j = j0 + wn * 32 + frag_col(l);
 #pragma unroll
-  for (int fm = 0; fm < C::FM; ++fm)
+  for (int f = 0; f < HF; ++f) {
+    const int j = j0 + C::b_row0(wn, f) + frag_col(l);
+    if (j >= h) continue;
 #pragma unroll
-    for (int r = 0; r < 16; ++r) {
-      const int p = rt.r0 + C::a_row0(wm, fm) + frag_row(r, l);
-      if (p >= rt.r1) continue;
-      const float a = acc[fm][0][r];
-      const float b = acc[fm][1][r];
-      st_f(h_ab + (size_t)p * 2 * h + j, a);
-      st_f(h_ab + (size_t)p * 2 * h + h + j, b);
-      st_f(y_swi + (size_t)p * h + j, a * sigmoidf_(a) * b);
-    }
+    for (int fm = 0; fm < C::FM; ++fm)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int p = rt.r0 + C::a_row0(wm, fm) + frag_row(r, l);
+        if (p >= rt.r1) continue;
+        const float a = acc[fm][f][r];
+        const float b = acc[fm][f + HF][r];
+        st_f(h_ab + (size_t)p * 2 * h + j, a);
+        st_f(h_ab + (size_t)p * 2 * h + h + j, b);
+        st_f(y_swi + (size_t)p * h + j, a * sigmoidf_(a) * b);
+      }
+  }
 }
 
-template <typename TIN>
+template <typename TIN, int B>
 static hipError_t gate_up_t(const Shape& s, const void* x, const int32_t* offsets, const int32_t* eti,
                             const void* w_gate, const void* w_up, void* h_ab, void* y_swi, const ExpertWs& ws,
                             hipStream_t st) {
-  using C = Cfg<TIN, 128, 128, 2, 2, true>;
-  const int nbn = s.h / (C::BN / 2);
-  long long nblk = max_row_blocks(s) * nbn;
+  using C = PCfg<TIN, B>;
+  const int nbn = col_blocks(s.h, C::BN / 2);
+  long long nblk = max_row_blocks(s, B) * nbn;
   nblk = (nblk + 7) / 8 * 8;
   gate_up_kernel<C><<<dim3((unsigned)nblk), dim3(NTHREADS), 0, st>>>(
-      (const TIN*)x, offsets, eti, ws.mb_off, (const TIN*)w_gate, (const TIN*)w_up, (TIN*)h_ab, (TIN*)y_swi, s.d,
-      s.E, s.h, nbn, (int)nblk);
+      (const TIN*)x, offsets, eti, ws.tile_map(B), (const TIN*)w_gate, (const TIN*)w_up, (TIN*)h_ab, (TIN*)y_swi,
+      s.T, s.d, s.E, s.h, nbn, (int)nblk);
   return hipGetLastError();
 }
 
@@ -97,8 +126,15 @@ hipError_t launch_gate_up(const Shape& s, const void* x, const int32_t* offsets,
                           const void* w_gate, const void* w_up, void* h_ab, void* y_swi, const ExpertWs& ws,
                           hipStream_t st) {
   timing_mark(st, "gate_up", true);
-  hipError_t e = s.bf16 ? gate_up_t<bf16_t>(s, x, offsets, eti, w_gate, w_up, h_ab, y_swi, ws, st)
-                        : gate_up_t<float>(s, x, offsets, eti, w_gate, w_up, h_ab, y_swi, ws, st);
+  // measured on MI355X: the large tile wins only for the longest reductions
+  const bool big = pick_large(s.d >= 6144);
+  hipError_t e;
+  if (s.bf16)
+    e = big ? gate_up_t<bf16_t, TILE_L>(s, x, offsets, eti, w_gate, w_up, h_ab, y_swi, ws, st)
+            : gate_up_t<bf16_t, TILE_S>(s, x, offsets, eti, w_gate, w_up, h_ab, y_swi, ws, st);
+  else
+    e = big ? gate_up_t<float, TILE_L>(s, x, offsets, eti, w_gate, w_up, h_ab, y_swi, ws, st)
+            : gate_up_t<float, TILE_S>(s, x, offsets, eti, w_gate, w_up, h_ab, y_swi, ws, st);
   timing_mark(st, "gate_up", false);
   return e;
 }
@@ -106,7 +142,7 @@ hipError_t launch_gate_up(const Shape& s, const void* x, const int32_t* offsets,
 // ===========================================================================
 // Ordered fold: the owner-computes weighted combine through the reverse index.
 //
-// Every output row out[t] (per 128-column block) receives K contributions
+// Every output row out[t] (per BN-column block) receives K contributions
 // from K different expert tiles.  Tiles are claimed through a ticket counter
 // in ascending (expert, row-block, column-block) order, and a contribution of
 // rank r (the position of its expert among the token's experts, ascending)
@@ -115,6 +151,9 @@ hipError_t launch_gate_up(const Shape& s, const void* x, const int32_t* offsets,
 // running workgroups, so the waits always drain.  The fp32 accumulator sees
 // the K contributions in ascending expert order: deterministic, with integer
 // flags only (no float atomics).  The last rank writes the output row.
+//
+// Visibility across XCDs: one device-scope acquire per tile after the waits
+// and one device-scope release per tile before the turns are published.
 //
 // INIT_FIRST: rank 0 writes the accumulator (forward); otherwise the
 // accumulator is pre-initialised and every rank adds (backward dX, where the
@@ -132,13 +171,13 @@ MOE_DEV void fold_epilogue(const f32x16_t (&acc)[C::FM][C::FN], const RowTile& r
   const int tid = threadIdx.x;
   const int rows = rt.r1 - rt.r0;
   __syncthreads();  // LDS stages are reused below
-  if (tid < rows) {
-    const int p = rt.r0 + tid;
+  for (int i = tid; i < rows; i += NTHREADS) {
+    const int p = rt.r0 + i;
     const int t = eti[p];
     const int rank = rank_pos[p];
-    s_t[tid] = t;
-    s_w[tid] = w_pos ? w_pos[p] : 1.0f;
-    s_rank[tid] = rank;
+    s_t[i] = t;
+    s_w[i] = w_pos ? w_pos[p] : 1.0f;
+    s_rank[i] = rank;
     int32_t* f = turn + (size_t)t * NB + nb;
     int spins = 0;
     while (__hip_atomic_load(f, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) < rank) {
@@ -150,49 +189,49 @@ MOE_DEV void fold_epilogue(const f32x16_t (&acc)[C::FM][C::FN], const RowTile& r
     }
   }
   __syncthreads();
-  // one device-scope acquire per tile: the predecessors' accumulator rows
-  // (possibly written through another XCD's L2) become visible to every wave
   if (tid < 64) __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
   __syncthreads();
   const int l = lane_id();
-  // issue every accumulator read first, then combine and store
-  float prev[C::FM][C::FN][16];
+  const int cbase = nb * C::BN;
 #pragma unroll
-  for (int fm = 0; fm < C::FM; ++fm)
+  for (int fm = 0; fm < C::FM; ++fm) {
+    // issue this fragment row's accumulator reads first, then combine and store
+    float prev[C::FN][16];
 #pragma unroll
     for (int r = 0; r < 16; ++r) {
       const int row = C::a_row0(wm, fm) + frag_row(r, l);
       const bool need = row < rows && !(INIT_FIRST && s_rank[row] == 0);
-      const size_t ob = need ? (size_t)s_t[row] * d + nb * C::BN : 0;
+      const size_t ob = need ? (size_t)s_t[row] * d : 0;
 #pragma unroll
-      for (int fn = 0; fn < C::FN; ++fn)
-        prev[fm][fn][r] = need ? accws[ob + C::b_row0(wn, fn) + frag_col(l)] : 0.0f;
+      for (int fn = 0; fn < C::FN; ++fn) {
+        const int col = cbase + C::b_row0(wn, fn) + frag_col(l);
+        prev[fn][r] = (need && col < d) ? accws[ob + col] : 0.0f;
+      }
     }
-#pragma unroll
-  for (int fm = 0; fm < C::FM; ++fm)
 #pragma unroll
     for (int r = 0; r < 16; ++r) {
       const int row = C::a_row0(wm, fm) + frag_row(r, l);
       if (row >= rows) continue;
-      const size_t ob = (size_t)s_t[row] * d + nb * C::BN;
+      const size_t ob = (size_t)s_t[row] * d;
       const float w = s_w[row];
       const bool last = s_rank[row] == K - 1;
 #pragma unroll
       for (int fn = 0; fn < C::FN; ++fn) {
-        const size_t o = ob + C::b_row0(wn, fn) + frag_col(l);
-        const float v = prev[fm][fn][r] + w * acc[fm][fn][r];
-        if (last) ElemT<typename C::T>::store(out + o, v);
-        else accws[o] = v;
+        const int col = cbase + C::b_row0(wn, fn) + frag_col(l);
+        if (col >= d) continue;
+        const float v = prev[fn][r] + w * acc[fm][fn][r];
+        if (last) ElemT<typename C::T>::store(out + ob + col, v);
+        else accws[ob + col] = v;
       }
     }
+  }
   // all waves' stores complete, then one device-scope release, then the turns
   __builtin_amdgcn_s_waitcnt(0);
   __syncthreads();
   if (tid < 64) __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");
   __syncthreads();
-  if (tid < rows)
-    __hip_atomic_store(turn + (size_t)s_t[tid] * NB + nb, s_rank[tid] + 1, __ATOMIC_RELAXED,
-                       __HIP_MEMORY_SCOPE_AGENT);
+  for (int i = tid; i < rows; i += NTHREADS)
+    __hip_atomic_store(turn + (size_t)s_t[i] * NB + nb, s_rank[i] + 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
 MOE_DEV int claim_ticket(int32_t* counters, char* smem) {
@@ -205,34 +244,36 @@ MOE_DEV int claim_ticket(int32_t* counters, char* smem) {
 }
 
 // ===========================================================================
-// Down projection + combine: M = rows of expert e, N = 128 output columns, K = h.
+// Down projection + combine: M = rows of expert e, N = TILE output columns, K = h.
 // ===========================================================================
 template <class C>
-__global__ __launch_bounds__(NTHREADS, 2) void down_combine_kernel(
+__global__ __launch_bounds__(NTHREADS, C::WAVES_PER_EU) void down_combine_kernel(
     const typename C::T* __restrict__ y_swi, const typename C::T* __restrict__ w_down,
     const int32_t* __restrict__ offsets, const int32_t* __restrict__ eti, const int32_t* __restrict__ mb_off,
     const float* __restrict__ w_pos, const int32_t* __restrict__ rank_pos, int32_t* turn, float* accws,
     typename C::T* __restrict__ out, int32_t* counters, int d, int E, int K, int h, int spin_limit) {
   __shared__ __attribute__((aligned(16))) char smem[C::LDS_BYTES];
   using TIN = typename C::T;
-  const int NB = d / C::BN;
+  const int NB = col_blocks(d, C::BN);
   const int tile = claim_ticket(counters, smem);
   const int g = tile / NB, nb = tile % NB;
   if (g >= mb_off[E]) return;
   const RowTile rt = decode_row_tile<C::BM>(mb_off, offsets, E, g);
   const int wave = threadIdx.x >> 6, wm = wave / C::WN, wn = wave % C::WN;
-  const size_t ldy = (size_t)h * sizeof(TIN);
+  const uint32_t ldy = (uint32_t)h * sizeof(TIN);
   RowLoader<C::BM> la;
   RowLoader<C::BN> lb;
+  la.rs[0] = make_rsrc(y_swi + (size_t)rt.r0 * h, (size_t)(rt.r1 - rt.r0) * ldy);
 #pragma unroll
   for (int i = 0; i < RowLoader<C::BM>::CPT; ++i) {
-    const int p = rt.r0 + RowLoader<C::BM>::my_row(i);
-    la.row_ptr[i] = p < rt.r1 ? (const char*)y_swi + (size_t)p * ldy : nullptr;
+    const int r = RowLoader<C::BM>::my_row(i);
+    la.roff[i] = rt.r0 + r < rt.r1 ? (uint32_t)r * ldy : OOB_OFF;
   }
+  lb.rs[0] = make_rsrc(w_down + (size_t)rt.e * d * h, (size_t)d * ldy);
 #pragma unroll
   for (int i = 0; i < RowLoader<C::BN>::CPT; ++i) {
     const int n = nb * C::BN + RowLoader<C::BN>::my_row(i);
-    lb.row_ptr[i] = (const char*)(w_down + ((size_t)rt.e * d + n) * h);
+    lb.roff[i] = n < d ? (uint32_t)n * ldy : OOB_OFF;
   }
   f32x16_t acc[C::FM][C::FN];
   gemm_mainloop<C>(la, lb, h / C::BK, smem, acc, wm, wn);
@@ -240,13 +281,13 @@ __global__ __launch_bounds__(NTHREADS, 2) void down_combine_kernel(
                          spin_limit, smem);
 }
 
-template <typename TIN>
+template <typename TIN, int B>
 static hipError_t down_combine_t(const Shape& s, const void* y_swi, const void* w_down, const int32_t* offsets,
                                  const int32_t* eti, void* out, const ExpertWs& ws, int spin_limit, hipStream_t st) {
-  using C = Cfg<TIN, 128, 128, 2, 2>;
-  const long long nblk = max_row_blocks(s) * (s.d / C::BN);
+  using C = GCfg<TIN, B>;
+  const long long nblk = max_row_blocks(s, B) * col_blocks(s.d, B);
   down_combine_kernel<C><<<dim3((unsigned)nblk), dim3(NTHREADS), 0, st>>>(
-      (const TIN*)y_swi, (const TIN*)w_down, offsets, eti, ws.mb_off, ws.w_pos, ws.rank_pos, ws.turn, ws.acc,
+      (const TIN*)y_swi, (const TIN*)w_down, offsets, eti, ws.tile_map(B), ws.w_pos, ws.rank_pos, ws.turn, ws.acc,
       (TIN*)out, ws.counters, s.d, s.E, s.K, s.h, spin_limit);
   return hipGetLastError();
 }
@@ -254,8 +295,14 @@ static hipError_t down_combine_t(const Shape& s, const void* y_swi, const void* 
 hipError_t launch_down_combine(const Shape& s, const void* y_swi, const void* w_down, const int32_t* offsets,
                                const int32_t* eti, void* out, const ExpertWs& ws, int spin_limit, hipStream_t st) {
   timing_mark(st, "down_combine", true);
-  hipError_t e = s.bf16 ? down_combine_t<bf16_t>(s, y_swi, w_down, offsets, eti, out, ws, spin_limit, st)
-                        : down_combine_t<float>(s, y_swi, w_down, offsets, eti, out, ws, spin_limit, st);
+  const bool big = pick_large(s.h >= 2048);
+  hipError_t e;
+  if (s.bf16)
+    e = big ? down_combine_t<bf16_t, TILE_L>(s, y_swi, w_down, offsets, eti, out, ws, spin_limit, st)
+            : down_combine_t<bf16_t, TILE_S>(s, y_swi, w_down, offsets, eti, out, ws, spin_limit, st);
+  else
+    e = big ? down_combine_t<float, TILE_L>(s, y_swi, w_down, offsets, eti, out, ws, spin_limit, st)
+            : down_combine_t<float, TILE_S>(s, y_swi, w_down, offsets, eti, out, ws, spin_limit, st);
   timing_mark(st, "down_combine", false);
   return e;
 }
@@ -264,59 +311,60 @@ hipError_t launch_down_combine(const Shape& s, const void* y_swi, const void* w_
 // Backward
 // ===========================================================================
 
-// k-row sources for the transposed loaders -----------------------------------
+// Each source gives the buffer resource of a k-tile (rsrc), the byte offset
+// of k-row k at the tile's first column (row_off, OOB_OFF outside the
+// problem) and optionally a per-k-row scale.
 template <typename T>
-struct SrcWeightKN {   // B[k][n] = W[k * ld + n0 + n]
-  const char* base;    // &W[0][n0]
-  size_t ld_bytes;
-  MOE_DEV const char* ptr(int k, float&) const { return base + (size_t)k * ld_bytes; }
+struct SrcWeightKN {   // B[k][n] = W[k][n0 + n], W one expert's [K, ld] matrix
+  rsrc_t rs;
+  uint32_t ld_bytes, col0;
+  MOE_DEV rsrc_t rsrc(int) const { return rs; }
+  MOE_DEV uint32_t row_off(int k) const { return (uint32_t)k * ld_bytes + col0; }
+  MOE_DEV float scale(int) const { return 1.0f; }
 };
 template <typename T>
-struct SrcWeightKN2 {  // k < h: W1[k][n0+n], else W2[k-h][n0+n]
-  const char* b1;
-  const char* b2;
-  size_t ld_bytes;
-  int h;
-  MOE_DEV const char* ptr(int k, float&) const {
-    return k < h ? b1 + (size_t)k * ld_bytes : b2 + (size_t)(k - h) * ld_bytes;
-  }
+struct SrcWeightKN2 {  // k < h: W1[k][n0+n], else W2[k-h][n0+n]; a k-tile never straddles h
+  rsrc_t rs1, rs2;
+  uint32_t ld_bytes, col0;
+  int h, kpt;
+  MOE_DEV rsrc_t rsrc(int kt) const { return kt * kpt < h ? rs1 : rs2; }
+  MOE_DEV uint32_t row_off(int k) const { return (uint32_t)(k < h ? k : k - h) * ld_bytes + col0; }
+  MOE_DEV float scale(int) const { return 1.0f; }
 };
 template <typename T>
-struct SrcRowsContig {  // rows p = p0 + k < p1 of a [rows, ld] array, columns from col0
-  const char* base;     // &A[0][col0]
-  size_t ld_bytes;
-  int p0, p1;
-  const float* scale;   // optional per-row scale
-  MOE_DEV const char* ptr(int k, float& s) const {
-    const int p = p0 + k;
-    if (p >= p1) return nullptr;
-    if (scale) s = scale[p];
-    return base + (size_t)p * ld_bytes;
-  }
+struct SrcRowsContig {  // rows p0 + k < p1 of a [rows, ld] array (resource based at row p0)
+  rsrc_t rs;
+  uint32_t ld_bytes, col0;
+  int n;                // p1 - p0
+  int p0;
+  const float* scl;     // optional per-row scale, indexed by p
+  MOE_DEV rsrc_t rsrc(int) const { return rs; }
+  MOE_DEV uint32_t row_off(int k) const { return k < n ? (uint32_t)k * ld_bytes + col0 : OOB_OFF; }
+  MOE_DEV float scale(int k) const { return scl[p0 + k]; }
 };
 template <typename T>
-struct SrcRowsGather {  // rows eti[p], p = p0 + k < p1, optional scale w_pos[p]
-  const char* base;     // &X[0][col0]
-  size_t ld_bytes;
+struct SrcRowsGather {  // rows eti[p], p = p0 + k < p1
+  rsrc_t rs;
+  uint32_t ld_bytes, col0;
   int p0, p1;
   const int32_t* eti;
-  const float* scale;
-  MOE_DEV const char* ptr(int k, float& s) const {
-    const int p = p0 + k;
-    if (p >= p1) return nullptr;
-    if (scale) s = scale[p];
-    return base + (size_t)eti[p] * ld_bytes;
+  MOE_DEV rsrc_t rsrc(int) const { return rs; }
+  MOE_DEV uint32_t row_off(int k) const {
+    return p0 + k < p1 ? (uint32_t)eti[p0 + k] * ld_bytes + col0 : OOB_OFF;
   }
+  MOE_DEV float scale(int) const { return 1.0f; }
 };
 
-// dH kernel: dA' = dO W_down (M rows of e, N = 128 of h, K = d) + SwiGLU backward
+MOE_DEV int min_i(int a, int b) { return a < b ? a : b; }
+
+// dH kernel: dA' = dO W_down (M rows of e, N = TILE of h, K = d) + SwiGLU backward
 template <class C>
-__global__ __launch_bounds__(NTHREADS, 2) void dh_kernel(
+__global__ __launch_bounds__(NTHREADS, C::WAVES_PER_EU) void dh_kernel(
     const typename C::T* __restrict__ dout, const typename C::T* __restrict__ w_down,
     const typename C::T* __restrict__ h_ab, const typename C::T* __restrict__ y_swi,
     const int32_t* __restrict__ offsets, const int32_t* __restrict__ eti, const int32_t* __restrict__ mb_off,
-    const float* __restrict__ w_pos, typename C::T* __restrict__ dh, float* __restrict__ ds_part, int d, int E,
-    int h, int nbn, int nblk) {
+    const float* __restrict__ w_pos, typename C::T* __restrict__ dh, float* __restrict__ ds_part, int T, int d,
+    int E, int h, int nbn, int nblk) {
   __shared__ __attribute__((aligned(16))) char smem[C::LDS_BYTES];
   using TIN = typename C::T;
   const int id = xcd_swizzle(blockIdx.x, nblk);
@@ -324,73 +372,75 @@ __global__ __launch_bounds__(NTHREADS, 2) void dh_kernel(
   if (g >= mb_off[E]) return;
   const RowTile rt = decode_row_tile<C::BM>(mb_off, offsets, E, g);
   const int wave = threadIdx.x >> 6, wm = wave / C::WN, wn = wave % C::WN;
-  const size_t ldd = (size_t)d * sizeof(TIN);
+  const uint32_t ldd = (uint32_t)d * sizeof(TIN);
   RowLoader<C::BM> la;
+  la.rs[0] = make_rsrc(dout, (size_t)T * ldd);
 #pragma unroll
   for (int i = 0; i < RowLoader<C::BM>::CPT; ++i) {
     const int p = rt.r0 + RowLoader<C::BM>::my_row(i);
-    la.row_ptr[i] = p < rt.r1 ? (const char*)dout + (size_t)eti[p] * ldd : nullptr;
+    la.roff[i] = p < rt.r1 ? (uint32_t)eti[p] * ldd : OOB_OFF;
   }
-  KRowLoader<TIN, SrcWeightKN<TIN>, false> lb;
-  lb.src.base = (const char*)(w_down + (size_t)rt.e * d * h + nb * C::BN);
-  lb.src.ld_bytes = (size_t)h * sizeof(TIN);
+  KRowLoader<TIN, C::BN, SrcWeightKN<TIN>, false> lb;
+  lb.src.rs = make_rsrc(w_down + (size_t)rt.e * d * h, (size_t)d * h * sizeof(TIN));
+  lb.src.ld_bytes = (uint32_t)h * sizeof(TIN);
+  lb.src.col0 = (uint32_t)(nb * C::BN) * sizeof(TIN);
+  lb.ncols = min_i(C::BN, h - nb * C::BN);
   f32x16_t acc[C::FM][C::FN];
   gemm_mainloop<C>(la, lb, d / C::BK, smem, acc, wm, wn);
 
   const int l = lane_id();
   float* s_ds = (float*)smem;  // [WN][BM]
-  float rs[C::FM][16];
-#pragma unroll
-  for (int fm = 0; fm < C::FM; ++fm)
-#pragma unroll
-    for (int r = 0; r < 16; ++r) {
-      const int p = rt.r0 + C::a_row0(wm, fm) + frag_row(r, l);
-      float dsum = 0.0f;
-      if (p < rt.r1) {
-        const float w = w_pos[p];
-#pragma unroll
-        for (int fn = 0; fn < C::FN; ++fn) {
-          const int j = nb * C::BN + C::b_row0(wn, fn) + frag_col(l);
-          const float dap = acc[fm][fn][r];
-          const float a = ld_f(h_ab + (size_t)p * 2 * h + j);
-          const float b = ld_f(h_ab + (size_t)p * 2 * h + h + j);
-          const float y = ld_f(y_swi + (size_t)p * h + j);
-          dsum += dap * y;
-          const float dy = w * dap;
-          const float sg = sigmoidf_(a);
-          st_f(dh + (size_t)p * 2 * h + j, dy * b * sg * (1.0f + a * (1.0f - sg)));
-          st_f(dh + (size_t)p * 2 * h + h + j, dy * a * sg);
-        }
-      }
-      rs[fm][r] = dsum;
-    }
-  // reduce each row's partial over the 32 columns of the half-wave, fixed order
-#pragma unroll
-  for (int fm = 0; fm < C::FM; ++fm)
-#pragma unroll
-    for (int r = 0; r < 16; ++r) {
-      float v = rs[fm][r];
-      v += __shfl_xor(v, 16, 32);
-      v += __shfl_xor(v, 8, 32);
-      v += __shfl_xor(v, 4, 32);
-      v += __shfl_xor(v, 2, 32);
-      v += __shfl_xor(v, 1, 32);
-      rs[fm][r] = v;
-    }
   __syncthreads();
-  if ((l & 31) == 0) {
 #pragma unroll
-    for (int fm = 0; fm < C::FM; ++fm)
+  for (int fm = 0; fm < C::FM; ++fm) {
 #pragma unroll
-      for (int r = 0; r < 16; ++r) s_ds[wn * C::BM + C::a_row0(wm, fm) + frag_row(r, l)] = rs[fm][r];
+    for (int rq = 0; rq < 16; rq += 4) {
+      // four accumulator rows at a time: their a, b, y loads are in flight
+      // together without holding the whole fragment's operands in registers
+      float rs[4];
+#pragma unroll
+      for (int ri = 0; ri < 4; ++ri) {
+        const int r = rq + ri;
+        const int p = rt.r0 + C::a_row0(wm, fm) + frag_row(r, l);
+        float dsum = 0.0f;
+        if (p < rt.r1) {
+          const float w = w_pos[p];
+#pragma unroll
+          for (int fn = 0; fn < C::FN; ++fn) {
+            const int j = nb * C::BN + C::b_row0(wn, fn) + frag_col(l);
+            if (j >= h) continue;
+            const float dap = acc[fm][fn][r];
+            const float a = ld_f(h_ab + (size_t)p * 2 * h + j);
+            const float b = ld_f(h_ab + (size_t)p * 2 * h + h + j);
+            const float y = ld_f(y_swi + (size_t)p * h + j);
+            dsum += dap * y;
+            const float dy = w * dap;
+            const float sg = sigmoidf_(a);
+            st_f(dh + (size_t)p * 2 * h + j, dy * b * sg * (1.0f + a * (1.0f - sg)));
+            st_f(dh + (size_t)p * 2 * h + h + j, dy * a * sg);
+          }
+        }
+        // reduce the row's partial over the 32 columns of the half-wave, fixed order
+        dsum += __shfl_xor(dsum, 16, 32);
+        dsum += __shfl_xor(dsum, 8, 32);
+        dsum += __shfl_xor(dsum, 4, 32);
+        dsum += __shfl_xor(dsum, 2, 32);
+        dsum += __shfl_xor(dsum, 1, 32);
+        rs[ri] = dsum;
+      }
+      if ((l & 31) == 0) {
+#pragma unroll
+        for (int ri = 0; ri < 4; ++ri) s_ds[wn * C::BM + C::a_row0(wm, fm) + frag_row(rq + ri, l)] = rs[ri];
+      }
+      __builtin_amdgcn_sched_barrier(0);
+    }
   }
   __syncthreads();
-  const int tid = threadIdx.x;
-  if (tid < rt.r1 - rt.r0) {
+  for (int i = threadIdx.x; i < rt.r1 - rt.r0; i += NTHREADS) {
     float v = 0.0f;
 #pragma unroll
-    for (int w = 0; w < C::WN; ++w) v += s_ds[w * C::BM + tid];
-    ds_part[(size_t)(rt.r0 + tid) * nbn + nb] = v;
+    for (int w = 0; w < C::WN; ++w) v += s_ds[w * C::BM + i];
+    ds_part[(size_t)(rt.r0 + i) * nbn + nb] = v;
   }
 }
 
@@ -436,7 +486,7 @@ __global__ __launch_bounds__(256) void router_bwd_kernel(const int32_t* __restri
   }
 }
 
-// dWg[e] = sum_{p in e} dz_p x[eti[p]]: one workgroup per (expert, 512 columns);
+// dWg[e] = sum_{p in e} dz_p x[eti[p]]: one workgroup per (expert, column block);
 // each wave strides over rows, fixed-order reduction across the 4 waves.
 template <typename TIN>
 __global__ __launch_bounds__(256) void dwg_kernel(const TIN* __restrict__ x, const int32_t* __restrict__ offsets,
@@ -473,33 +523,33 @@ __global__ __launch_bounds__(256) void dwg_kernel(const TIN* __restrict__ x, con
 // operand and held in the activation dtype, as the SonicMoE analysis page
 // (sec. 3.4.1) defines A' = Broadcast(s) A for the dW2 grouped GEMM.
 template <class C>
-__global__ __launch_bounds__(NTHREADS, 2) void dw_down_kernel(const typename C::T* __restrict__ dout,
-                                                              const typename C::T* __restrict__ y_swi,
-                                                              const int32_t* __restrict__ offsets,
-                                                              const int32_t* __restrict__ eti,
-                                                              const float* __restrict__ w_pos,
-                                                              float* __restrict__ dw_down, int d, int h) {
+__global__ __launch_bounds__(NTHREADS, C::WAVES_PER_EU) void dw_down_kernel(
+    const typename C::T* __restrict__ dout, const typename C::T* __restrict__ y_swi,
+    const int32_t* __restrict__ offsets, const int32_t* __restrict__ eti, const float* __restrict__ w_pos,
+    float* __restrict__ dw_down, int T, int d, int h) {
   __shared__ __attribute__((aligned(16))) char smem[C::LDS_BYTES];
   using TIN = typename C::T;
-  const int nmb = d / C::BM, nnb = h / C::BN;
+  const int nnb = col_blocks(h, C::BN);
   const int e = blockIdx.y;
   const int mb = blockIdx.x / nnb, nb = blockIdx.x % nnb;
   const int p0 = offsets[e], p1 = offsets[e + 1];
   const int wave = threadIdx.x >> 6, wm = wave / C::WN, wn = wave % C::WN;
-  (void)nmb;
-  KRowLoader<TIN, SrcRowsGather<TIN>, false> la;
-  la.src.base = (const char*)(dout + mb * C::BM);
-  la.src.ld_bytes = (size_t)d * sizeof(TIN);
+  KRowLoader<TIN, C::BM, SrcRowsGather<TIN>, false> la;
+  la.src.rs = make_rsrc(dout, (size_t)T * d * sizeof(TIN));
+  la.src.ld_bytes = (uint32_t)d * sizeof(TIN);
+  la.src.col0 = (uint32_t)(mb * C::BM) * sizeof(TIN);
   la.src.p0 = p0;
   la.src.p1 = p1;
   la.src.eti = eti;
-  la.src.scale = nullptr;
-  KRowLoader<TIN, SrcRowsContig<TIN>, true> lb;
-  lb.src.base = (const char*)(y_swi + nb * C::BN);
-  lb.src.ld_bytes = (size_t)h * sizeof(TIN);
+  la.ncols = min_i(C::BM, d - mb * C::BM);
+  KRowLoader<TIN, C::BN, SrcRowsContig<TIN>, true> lb;
+  lb.src.rs = make_rsrc(y_swi + (size_t)p0 * h, (size_t)(p1 - p0) * h * sizeof(TIN));
+  lb.src.ld_bytes = (uint32_t)h * sizeof(TIN);
+  lb.src.col0 = (uint32_t)(nb * C::BN) * sizeof(TIN);
+  lb.src.n = p1 - p0;
   lb.src.p0 = p0;
-  lb.src.p1 = p1;
-  lb.src.scale = w_pos;
+  lb.src.scl = w_pos;
+  lb.ncols = min_i(C::BN, h - nb * C::BN);
   f32x16_t acc[C::FM][C::FN];
   gemm_mainloop<C>(la, lb, (p1 - p0 + C::BK - 1) / C::BK, smem, acc, wm, wn);
   const int l = lane_id();
@@ -507,92 +557,119 @@ __global__ __launch_bounds__(NTHREADS, 2) void dw_down_kernel(const typename C::
 #pragma unroll
   for (int fm = 0; fm < C::FM; ++fm)
 #pragma unroll
-    for (int fn = 0; fn < C::FN; ++fn)
+    for (int fn = 0; fn < C::FN; ++fn) {
+      const int n = nb * C::BN + C::b_row0(wn, fn) + frag_col(l);
+      if (n >= h) continue;
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
         const int m = mb * C::BM + C::a_row0(wm, fm) + frag_row(r, l);
-        const int n = nb * C::BN + C::b_row0(wn, fn) + frag_col(l);
-        o[(size_t)m * h + n] = acc[fm][fn][r];
+        if (m < d) o[(size_t)m * h + n] = acc[fm][fn][r];
       }
+    }
 }
 
 // dW_gate / dW_up [e] (h x d) = sum_p dH[p]^T x[eti[p]]: M = 2h, N = d, K = rows of e
 template <class C>
-__global__ __launch_bounds__(NTHREADS, 2) void dw_gate_up_kernel(const typename C::T* __restrict__ dh,
-                                                                 const typename C::T* __restrict__ x,
-                                                                 const int32_t* __restrict__ offsets,
-                                                                 const int32_t* __restrict__ eti,
-                                                                 float* __restrict__ dw_gate,
-                                                                 float* __restrict__ dw_up, int d, int h) {
+__global__ __launch_bounds__(NTHREADS, C::WAVES_PER_EU) void dw_gate_up_kernel(
+    const typename C::T* __restrict__ dh, const typename C::T* __restrict__ x, const int32_t* __restrict__ offsets,
+    const int32_t* __restrict__ eti, float* __restrict__ dw_gate, float* __restrict__ dw_up, int T, int d, int h) {
   __shared__ __attribute__((aligned(16))) char smem[C::LDS_BYTES];
   using TIN = typename C::T;
-  const int nnb = d / C::BN;
+  const int nnb = col_blocks(d, C::BN);
   const int e = blockIdx.y;
   const int mb = blockIdx.x / nnb, nb = blockIdx.x % nnb;
   const int p0 = offsets[e], p1 = offsets[e + 1];
   const int wave = threadIdx.x >> 6, wm = wave / C::WN, wn = wave % C::WN;
-  KRowLoader<TIN, SrcRowsContig<TIN>, false> la;
-  la.src.base = (const char*)(dh + mb * C::BM);
-  la.src.ld_bytes = (size_t)2 * h * sizeof(TIN);
+  KRowLoader<TIN, C::BM, SrcRowsContig<TIN>, false> la;
+  la.src.rs = make_rsrc(dh + (size_t)p0 * 2 * h, (size_t)(p1 - p0) * 2 * h * sizeof(TIN));
+  la.src.ld_bytes = (uint32_t)(2 * h) * sizeof(TIN);
+  la.src.col0 = (uint32_t)(mb * C::BM) * sizeof(TIN);
+  la.src.n = p1 - p0;
   la.src.p0 = p0;
-  la.src.p1 = p1;
-  la.src.scale = nullptr;
-  KRowLoader<TIN, SrcRowsGather<TIN>, false> lb;
-  lb.src.base = (const char*)(x + nb * C::BN);
-  lb.src.ld_bytes = (size_t)d * sizeof(TIN);
+  la.src.scl = nullptr;
+  la.ncols = min_i(C::BM, 2 * h - mb * C::BM);
+  KRowLoader<TIN, C::BN, SrcRowsGather<TIN>, false> lb;
+  lb.src.rs = make_rsrc(x, (size_t)T * d * sizeof(TIN));
+  lb.src.ld_bytes = (uint32_t)d * sizeof(TIN);
+  lb.src.col0 = (uint32_t)(nb * C::BN) * sizeof(TIN);
   lb.src.p0 = p0;
   lb.src.p1 = p1;
   lb.src.eti = eti;
-  lb.src.scale = nullptr;
+  lb.ncols = min_i(C::BN, d - nb * C::BN);
   f32x16_t acc[C::FM][C::FN];
   gemm_mainloop<C>(la, lb, (p1 - p0 + C::BK - 1) / C::BK, smem, acc, wm, wn);
   const int l = lane_id();
-  const bool up = mb * C::BM >= h;
-  float* o = (up ? dw_up : dw_gate) + (size_t)e * h * d;
-  const int mrow0 = mb * C::BM - (up ? h : 0);
 #pragma unroll
   for (int fm = 0; fm < C::FM; ++fm)
 #pragma unroll
-    for (int fn = 0; fn < C::FN; ++fn)
+    for (int r = 0; r < 16; ++r) {
+      const int m = mb * C::BM + C::a_row0(wm, fm) + frag_row(r, l);
+      if (m >= 2 * h) continue;
+      float* o = m < h ? dw_gate + ((size_t)e * h + m) * d : dw_up + ((size_t)e * h + (m - h)) * d;
 #pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const int m = mrow0 + C::a_row0(wm, fm) + frag_row(r, l);
+      for (int fn = 0; fn < C::FN; ++fn) {
         const int n = nb * C::BN + C::b_row0(wn, fn) + frag_col(l);
-        o[(size_t)m * d + n] = acc[fm][fn][r];
+        if (n < d) o[n] = acc[fm][fn][r];
       }
+    }
 }
 
-// dX~ = dH [W_gate; W_up] (M rows of e, N = 128 of d, K = 2h) + ordered fold into dX
+// dX~ = dH [W_gate; W_up] (M rows of e, N = TILE of d, K = 2h) + ordered fold into dX
 template <class C>
-__global__ __launch_bounds__(NTHREADS, 2) void dx_fold_kernel(
+__global__ __launch_bounds__(NTHREADS, C::WAVES_PER_EU) void dx_fold_kernel(
     const typename C::T* __restrict__ dh, const typename C::T* __restrict__ w_gate,
     const typename C::T* __restrict__ w_up, const int32_t* __restrict__ offsets, const int32_t* __restrict__ eti,
     const int32_t* __restrict__ mb_off, const int32_t* __restrict__ rank_pos, int32_t* turn, float* accws,
     typename C::T* __restrict__ dx, int32_t* counters, int d, int E, int K, int h, int spin_limit) {
   __shared__ __attribute__((aligned(16))) char smem[C::LDS_BYTES];
   using TIN = typename C::T;
-  const int NB = d / C::BN;
+  const int NB = col_blocks(d, C::BN);
   const int tile = claim_ticket(counters, smem);
   const int g = tile / NB, nb = tile % NB;
   if (g >= mb_off[E]) return;
   const RowTile rt = decode_row_tile<C::BM>(mb_off, offsets, E, g);
   const int wave = threadIdx.x >> 6, wm = wave / C::WN, wn = wave % C::WN;
-  const size_t ldh = (size_t)2 * h * sizeof(TIN);
+  const uint32_t ldh = (uint32_t)(2 * h) * sizeof(TIN);
   RowLoader<C::BM> la;
+  la.rs[0] = make_rsrc(dh + (size_t)rt.r0 * 2 * h, (size_t)(rt.r1 - rt.r0) * ldh);
 #pragma unroll
   for (int i = 0; i < RowLoader<C::BM>::CPT; ++i) {
-    const int p = rt.r0 + RowLoader<C::BM>::my_row(i);
-    la.row_ptr[i] = p < rt.r1 ? (const char*)dh + (size_t)p * ldh : nullptr;
+    const int r = RowLoader<C::BM>::my_row(i);
+    la.roff[i] = rt.r0 + r < rt.r1 ? (uint32_t)r * ldh : OOB_OFF;
   }
-  KRowLoader<TIN, SrcWeightKN2<TIN>, false> lb;
-  lb.src.b1 = (const char*)(w_gate + (size_t)rt.e * h * d + nb * C::BN);
-  lb.src.b2 = (const char*)(w_up + (size_t)rt.e * h * d + nb * C::BN);
-  lb.src.ld_bytes = (size_t)d * sizeof(TIN);
+  KRowLoader<TIN, C::BN, SrcWeightKN2<TIN>, false> lb;
+  lb.src.rs1 = make_rsrc(w_gate + (size_t)rt.e * h * d, (size_t)h * d * sizeof(TIN));
+  lb.src.rs2 = make_rsrc(w_up + (size_t)rt.e * h * d, (size_t)h * d * sizeof(TIN));
+  lb.src.ld_bytes = (uint32_t)d * sizeof(TIN);
+  lb.src.col0 = (uint32_t)(nb * C::BN) * sizeof(TIN);
   lb.src.h = h;
+  lb.src.kpt = C::BK;
+  lb.ncols = min_i(C::BN, d - nb * C::BN);
   f32x16_t acc[C::FM][C::FN];
   gemm_mainloop<C>(la, lb, (2 * h) / C::BK, smem, acc, wm, wn);
   fold_epilogue<C, false>(acc, rt, nb, NB, wm, wn, eti, nullptr, rank_pos, K, d, turn, accws, dx, counters,
                           spin_limit, smem);
+}
+
+template <typename TIN, int B>
+static void launch_dh(const Shape& s, const void* dout, const void* w_down, const void* h_ab, const void* y_swi,
+                      const int32_t* offsets, const int32_t* eti, const ExpertWs& ws, hipStream_t st) {
+  using C = GCfg<TIN, B>;
+  const int nbn = col_blocks(s.h, B);
+  const long long nblk = (max_row_blocks(s, B) * nbn + 7) / 8 * 8;
+  dh_kernel<C><<<dim3((unsigned)nblk), dim3(NTHREADS), 0, st>>>(
+      (const TIN*)dout, (const TIN*)w_down, (const TIN*)h_ab, (const TIN*)y_swi, offsets, eti, ws.tile_map(B),
+      ws.w_pos, (TIN*)ws.dh, ws.ds_part, s.T, s.d, s.E, s.h, nbn, (int)nblk);
+}
+
+template <typename TIN, int B>
+static void launch_dx_fold(const Shape& s, const void* w_gate, const void* w_up, const int32_t* offsets,
+                           const int32_t* eti, void* dx, const ExpertWs& ws, int spin_limit, hipStream_t st) {
+  using C = GCfg<TIN, B>;
+  const long long nblk = max_row_blocks(s, B) * col_blocks(s.d, B);
+  dx_fold_kernel<C><<<dim3((unsigned)nblk), dim3(NTHREADS), 0, st>>>(
+      (const TIN*)ws.dh, (const TIN*)w_gate, (const TIN*)w_up, offsets, eti, ws.tile_map(B), ws.rank_pos, ws.turn,
+      ws.acc, (TIN*)dx, ws.counters, s.d, s.E, s.K, s.h, spin_limit);
 }
 
 template <typename TIN>
@@ -601,18 +678,14 @@ static hipError_t backward_t(const Shape& s, const void* dout, const void* x, co
                              const int32_t* offsets, const int32_t* eti, const int32_t* tim, const void* h_ab,
                              const void* y_swi, void* dx, float* dwg, float* dw_gate, float* dw_up,
                              float* dw_down, float* ds, const ExpertWs& ws, int spin_limit, hipStream_t st) {
-  using C = Cfg<TIN, 128, 128, 2, 2>;
-  const int nbh = s.h / C::BN;
-  const int nbd = s.d / C::BN;
-  const long long mbmax = max_row_blocks(s);
+  using CL = GCfg<TIN, TILE_L>;
+  // the large-tile dH epilogue spills; the small tile is used for every shape
+  const bool dh_big = forced_tile() == TILE_L;
+  const int nbh = col_blocks(s.h, dh_big ? TILE_L : TILE_S);
   hipError_t err;
   timing_mark(st, "dh", true);
-  {
-    const long long nblk = (mbmax * nbh + 7) / 8 * 8;
-    dh_kernel<C><<<dim3((unsigned)nblk), dim3(NTHREADS), 0, st>>>(
-        (const TIN*)dout, (const TIN*)w_down, (const TIN*)h_ab, (const TIN*)y_swi, offsets, eti, ws.mb_off,
-        ws.w_pos, (TIN*)ws.dh, ws.ds_part, s.d, s.E, s.h, nbh, (int)nblk);
-  }
+  if (dh_big) launch_dh<TIN, TILE_L>(s, dout, w_down, h_ab, y_swi, offsets, eti, ws, st);
+  else launch_dh<TIN, TILE_S>(s, dout, w_down, h_ab, y_swi, offsets, eti, ws, st);
   timing_mark(st, "dh", false);
   if ((err = hipGetLastError()) != hipSuccess) return err;
 
@@ -632,21 +705,20 @@ static hipError_t backward_t(const Shape& s, const void* dout, const void* x, co
   if ((err = hipGetLastError()) != hipSuccess) return err;
 
   timing_mark(st, "dw_down", true);
-  dw_down_kernel<C><<<dim3((s.d / C::BM) * (s.h / C::BN), s.E), dim3(NTHREADS), 0, st>>>(
-      (const TIN*)dout, (const TIN*)y_swi, offsets, eti, ws.w_pos, dw_down, s.d, s.h);
+  dw_down_kernel<CL><<<dim3(col_blocks(s.d, TILE_L) * col_blocks(s.h, TILE_L), s.E), dim3(NTHREADS), 0, st>>>(
+      (const TIN*)dout, (const TIN*)y_swi, offsets, eti, ws.w_pos, dw_down, s.T, s.d, s.h);
   timing_mark(st, "dw_down", false);
   if ((err = hipGetLastError()) != hipSuccess) return err;
 
   timing_mark(st, "dw_gate_up", true);
-  dw_gate_up_kernel<C><<<dim3((2 * s.h / C::BM) * (s.d / C::BN), s.E), dim3(NTHREADS), 0, st>>>(
-      (const TIN*)ws.dh, (const TIN*)x, offsets, eti, dw_gate, dw_up, s.d, s.h);
+  dw_gate_up_kernel<CL><<<dim3(col_blocks(2 * s.h, TILE_L) * col_blocks(s.d, TILE_L), s.E), dim3(NTHREADS), 0,
+                          st>>>((const TIN*)ws.dh, (const TIN*)x, offsets, eti, dw_gate, dw_up, s.T, s.d, s.h);
   timing_mark(st, "dw_gate_up", false);
   if ((err = hipGetLastError()) != hipSuccess) return err;
 
   timing_mark(st, "dx_fold", true);
-  dx_fold_kernel<C><<<dim3((unsigned)(mbmax * nbd)), dim3(NTHREADS), 0, st>>>(
-      (const TIN*)ws.dh, (const TIN*)w_gate, (const TIN*)w_up, offsets, eti, ws.mb_off, ws.rank_pos, ws.turn,
-      ws.acc, (TIN*)dx, ws.counters, s.d, s.E, s.K, s.h, spin_limit);
+  if (pick_large(2 * s.h >= 3072)) launch_dx_fold<TIN, TILE_L>(s, w_gate, w_up, offsets, eti, dx, ws, spin_limit, st);
+  else launch_dx_fold<TIN, TILE_S>(s, w_gate, w_up, offsets, eti, dx, ws, spin_limit, st);
   timing_mark(st, "dx_fold", false);
   return hipGetLastError();
 }

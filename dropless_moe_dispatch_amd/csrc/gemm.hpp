@@ -1,12 +1,18 @@
 // Generic grouped-GEMM core for the expert projections (gfx950 MFMA).
 //
-// One workgroup = 256 threads = 4 wave64s, computing a BM x BN fp32 tile of
-// C = A * B^T where both operands are staged in LDS as [row][k] (k
-// contiguous), 128 bytes of k per row per stage (64 bf16 or 32 fp32), rows
-// padded to 144 bytes so that the 16-byte MFMA operand reads of 8 lanes hit
-// distinct banks.  Two LDS stages: the global loads of k-tile t+1 are issued
-// before the MFMAs of tile t and written to the other stage afterwards, one
-// barrier per k-tile.
+// One workgroup = 256 threads = 4 wave64s computing a BM x BN fp32 tile of
+// C = A * B^T.  Both operands are staged in LDS as [row][k] (k contiguous),
+// 128 bytes of k per row per stage (64 bf16 or 32 fp32), rows padded to 144
+// bytes so that the 16-byte MFMA operand reads of 8 lanes hit distinct banks.
+// The expert GEMMs use 256 x 256 tiles with a 128 x 128 tile per wave: 16
+// MFMA 32x32x16 per 8 operand fragments read from LDS, accumulators in the
+// AGPR half of the register file, one workgroup per CU.
+//
+// Pipeline: two LDS stages.  The global loads of k-tile t+1 are issued
+// before the MFMAs of tile t and written to the other LDS stage after them;
+// one barrier per k-tile.  Loaders whose rows come through an index (gathered
+// token rows) fetch the indices of k-tile t+2 at the same time, so the data
+// loads never wait on an index load.
 //
 // Operand sources:
 //   RowLoader  - rows that are contiguous in k in global memory (activations
@@ -14,7 +20,7 @@
 //                8 consecutive threads fetch one row's 128-byte slice.
 //   KRowLoader - sources whose rows are k (activations [rows, m] reduced over
 //                rows, or weights [k, n]).  Each thread fetches four k-rows of
-//                one 16-byte column chunk and transposes them in registers so
+//                16-byte column chunks and transposes them in registers so
 //                that LDS still holds [m][k].
 #pragma once
 #include "common.hpp"
@@ -29,7 +35,9 @@ template <typename TIN, int BM_, int BN_, int WM_, int WN_, bool PAIRED_ = false
 struct Cfg {
   using T = TIN;
   static constexpr int BM = BM_, BN = BN_, WM = WM_, WN = WN_;
-  static constexpr bool PAIRED = PAIRED_;   // B rows [0,BN/2) and [BN/2,BN) pair up column-wise
+  // PAIRED: B rows [0,BN/2) and [BN/2,BN) pair up column by column, and each
+  // wave holds both halves of its columns (fragments fn and fn + FN/2).
+  static constexpr bool PAIRED = PAIRED_;
   static constexpr int EB = (int)sizeof(TIN);
   static constexpr int BK = KBYTES / EB;
   static constexpr int FM = BM / WM / 32;
@@ -38,40 +46,62 @@ struct Cfg {
   static constexpr int B_BYTES = BN * LDS_ROW;
   static constexpr int STAGE = A_BYTES + B_BYTES;
   static constexpr int LDS_BYTES = 2 * STAGE;
+  static constexpr int WAVES_PER_EU = (BM * BN >= 256 * 256) ? 1 : 2;
   static_assert(WM * WN == 4, "four waves per workgroup");
   static_assert(FM >= 1 && FN >= 1 && FM * WM * 32 == BM && FN * WN * 32 == BN, "tile shape");
-  static_assert(!PAIRED || (FN == 2 && WN * 32 * 2 == BN), "paired layout");
+  static_assert(!PAIRED || (FN % 2 == 0), "paired layout");
 
   // tile-local row of A fragment fm for this wave
   static MOE_DEV int a_row0(int wm, int fm) { return wm * (BM / WM) + fm * 32; }
   // tile-local column (B row) of fragment fn for this wave
   static MOE_DEV int b_row0(int wn, int fn) {
-    if constexpr (PAIRED) return fn * (BN / 2) + wn * 32;
-    else return wn * (BN / WN) + fn * 32;
+    if constexpr (PAIRED) {
+      constexpr int H = FN / 2;
+      return (fn >= H ? BN / 2 : 0) + wn * (BN / 2 / WN) + (fn % H) * 32;
+    } else {
+      return wn * (BN / WN) + fn * 32;
+    }
   }
 };
 
 // ---------------------------------------------------------------------------
-// RowLoader<ROWS>: ROWS tile rows, each a 128-byte k-slice per stage.
-// The caller sets row_ptr[i] (byte pointer to the row's first element, or
-// nullptr for a row outside the problem -> zeros) for the rows this thread
-// owns: row = (tid >> 3) + 32*i, i < ROWS/32.
+// Buffer-resource loads.  Every operand fetch is a 16-byte buffer load from a
+// resource descriptor held in SGPRs with a 32-bit byte offset; an offset at or
+// beyond the descriptor's size returns zeros, which is how rows and columns
+// outside the problem are masked (OOB_OFF), without branches around loads.
 // ---------------------------------------------------------------------------
-template <int ROWS>
+typedef __amdgpu_buffer_rsrc_t rsrc_t;
+constexpr uint32_t OOB_OFF = 0x80000000u;
+
+MOE_DEV rsrc_t make_rsrc(const void* base, size_t bytes) {
+  const int n = bytes > 0x7ffffff0ull ? 0x7ffffff0 : (int)bytes;
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, n, 0x00020000);
+}
+MOE_DEV u32x4_t buf_load16(rsrc_t r, uint32_t off) {
+  return __builtin_bit_cast(u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(r, (int)off, 0, 0));
+}
+
+// ---------------------------------------------------------------------------
+// RowLoader<ROWS, SPLIT>: ROWS tile rows, each a 128-byte k-slice per stage.
+// The caller sets rs[0] (and rs[1] for the second half of the rows when
+// SPLIT) and roff[i], the byte offset of the row's first element, or OOB_OFF
+// for a row outside the problem, for the rows this thread owns:
+// row = (tid >> 3) + 32*i, i < ROWS/32.
+// ---------------------------------------------------------------------------
+template <int ROWS, bool SPLIT = false>
 struct RowLoader {
   static constexpr int CPT = ROWS / 32;
-  const char* row_ptr[CPT];
+  rsrc_t rs[2];
+  uint32_t roff[CPT];
   u32x4_t reg[CPT];
 
   static MOE_DEV int my_row(int i) { return (int)(threadIdx.x >> 3) + 32 * i; }
 
+  MOE_DEV void prefetch(int) {}
   MOE_DEV void load(int kt) {
-    const int off = kt * KBYTES + (int)(threadIdx.x & 7) * 16;
+    const uint32_t off = (uint32_t)(kt * KBYTES) + (threadIdx.x & 7) * 16;
 #pragma unroll
-    for (int i = 0; i < CPT; ++i) {
-      if (row_ptr[i]) reg[i] = *(const u32x4_t*)(row_ptr[i] + off);
-      else reg[i] = u32x4_t{0u, 0u, 0u, 0u};
-    }
+    for (int i = 0; i < CPT; ++i) reg[i] = buf_load16(rs[(SPLIT && i >= CPT / 2) ? 1 : 0], roff[i] + off);
   }
   MOE_DEV void store(char* lds) const {
 #pragma unroll
@@ -81,91 +111,109 @@ struct RowLoader {
 };
 
 // ---------------------------------------------------------------------------
-// KRowLoader<T, Src>: 128 tile rows (m), k-rows from a source functor.
-//   Src::ptr(krow, scale&) -> byte pointer to element (krow, col0) or nullptr,
-//   with an optional per-k-row scale (1.0f when unused).
-// bf16: thread owns k-rows 4*(tid&15)+0..3, columns 8*(tid>>4)+0..7.
-// fp32: thread owns k-rows 4*(tid&7)+0..3,  columns 4*(tid>>3)+0..3.
+// KRowLoader<T, ROWS, Src, SCALED>: ROWS tile rows (m), k-rows from a source:
+//   Src::rsrc(kt)   -> buffer resource of k-tile kt (uniform);
+//   Src::row_off(k) -> byte offset of element (k-row k, tile column 0), or
+//                      OOB_OFF outside the problem (may read an index);
+//   Src::scale(k)   -> per-k-row scale (SCALED only).
+// ncols: valid tile columns (multiple of the chunk width); others read 0.
+// prefetch(kt) fetches the row offsets (and scales) of k-tile kt; load(kt)
+// issues the data loads with them, after which the next prefetch may reuse
+// the registers.
+// bf16: thread owns k-rows 4*(tid&15)+0..3, columns c*128 + 8*(tid>>4)+0..7.
+// fp32: thread owns k-rows 4*(tid&7)+0..3,  columns c*128 + 4*(tid>>3)+0..3.
 // ---------------------------------------------------------------------------
-template <typename T, class Src, bool SCALED>
-struct KRowLoader;
-
-template <class Src, bool SCALED>
-struct KRowLoader<bf16_t, Src, SCALED> {
-  Src src;
-  u32x4_t reg[4];
-  float scl[4];
-  MOE_DEV int kg() const { return (int)(threadIdx.x & 15); }
-  MOE_DEV int mc() const { return (int)(threadIdx.x >> 4); }
-
-  MOE_DEV void load(int kt) {
-    const int kbase = kt * 64 + 4 * kg();
-#pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      float s = 1.0f;
-      const char* p = src.ptr(kbase + j, s);
-      scl[j] = s;
-      if (p) reg[j] = *(const u32x4_t*)(p + mc() * 16);
-      else reg[j] = u32x4_t{0u, 0u, 0u, 0u};
-    }
-  }
-  MOE_DEV void store(char* lds) const {
-    u32x4_t r[4];
-#pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      r[j] = reg[j];
-      if constexpr (SCALED) {
-#pragma unroll
-        for (int q = 0; q < 4; ++q) {
-          const uint32_t v = r[j][q];
-          const uint32_t lo = f32_to_bf16(bf16_to_f32(v & 0xffffu) * scl[j]);
-          const uint32_t hi = f32_to_bf16(bf16_to_f32(v >> 16) * scl[j]);
-          r[j][q] = lo | (hi << 16);
-        }
-      }
-    }
-    char* base = lds + (mc() * 8) * LDS_ROW + kg() * 8;
-#pragma unroll
-    for (int q = 0; q < 4; ++q) {
-      // columns 2q (low halves) and 2q+1 (high halves)
-      u32x2_t e, o;
-      e[0] = (r[0][q] & 0xffffu) | (r[1][q] << 16);
-      e[1] = (r[2][q] & 0xffffu) | (r[3][q] << 16);
-      o[0] = (r[0][q] >> 16) | (r[1][q] & 0xffff0000u);
-      o[1] = (r[2][q] >> 16) | (r[3][q] & 0xffff0000u);
-      *(u32x2_t*)(base + (2 * q) * LDS_ROW) = e;
-      *(u32x2_t*)(base + (2 * q + 1) * LDS_ROW) = o;
-    }
-  }
+template <typename T> struct KRowGeom;
+template <> struct KRowGeom<bf16_t> {
+  static MOE_DEV int kg() { return (int)(threadIdx.x & 15); }
+  static MOE_DEV int mc() { return (int)(threadIdx.x >> 4); }
+  static constexpr int KPT = 64;  // k-rows per stage
+  static constexpr int CW = 8;    // columns per chunk
+};
+template <> struct KRowGeom<float> {
+  static MOE_DEV int kg() { return (int)(threadIdx.x & 7); }
+  static MOE_DEV int mc() { return (int)(threadIdx.x >> 3); }
+  static constexpr int KPT = 32;
+  static constexpr int CW = 4;
 };
 
-template <class Src, bool SCALED>
-struct KRowLoader<float, Src, SCALED> {
+template <typename T, int ROWS, class Src, bool SCALED>
+struct KRowLoader {
+  using G = KRowGeom<T>;
+  static constexpr int NC = ROWS / 128;  // column chunks per thread
   Src src;
-  f32x4_t reg[4];
-  MOE_DEV int kg() const { return (int)(threadIdx.x & 7); }
-  MOE_DEV int mc() const { return (int)(threadIdx.x >> 3); }
+  int ncols;
+  uint32_t offs[4];
+  float spre[4];      // scales fetched with the offsets
+  float sdat[4];      // scales of the loaded data
+  u32x4_t reg[NC][4];
 
-  MOE_DEV void load(int kt) {
-    const int kbase = kt * 32 + 4 * kg();
+  MOE_DEV int col(int c) const { return c * 128 + G::mc() * G::CW; }
+
+  MOE_DEV void prefetch(int kt) {
+    const int kbase = kt * G::KPT + 4 * G::kg();
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
-      float s = 1.0f;
-      const char* p = src.ptr(kbase + j, s);
-      if (p) {
-        reg[j] = *(const f32x4_t*)(p + mc() * 16);
-        if constexpr (SCALED) reg[j] *= s;
-      } else {
-        reg[j] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+      offs[j] = src.row_off(kbase + j);
+      if constexpr (SCALED) spre[j] = offs[j] != OOB_OFF ? src.scale(kbase + j) : 0.0f;
+    }
+  }
+  MOE_DEV void load(int kt) {
+    const rsrc_t r = src.rsrc(kt);
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      if constexpr (SCALED) sdat[j] = spre[j];
+#pragma unroll
+      for (int c = 0; c < NC; ++c) {
+        const uint32_t o = col(c) < ncols ? offs[j] + (uint32_t)(col(c) * (int)sizeof(T)) : OOB_OFF;
+        reg[c][j] = buf_load16(r, o);
       }
     }
   }
   MOE_DEV void store(char* lds) const {
-    char* base = lds + (mc() * 4) * LDS_ROW + kg() * 16;
 #pragma unroll
-    for (int q = 0; q < 4; ++q) {
-      f32x4_t v{reg[0][q], reg[1][q], reg[2][q], reg[3][q]};
-      *(f32x4_t*)(base + q * LDS_ROW) = v;
+    for (int c = 0; c < NC; ++c) {
+      if constexpr (sizeof(T) == 2) {
+        u32x4_t r[4];
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          r[j] = reg[c][j];
+          if constexpr (SCALED) {
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+              const uint32_t v = r[j][q];
+              const uint32_t lo = f32_to_bf16(bf16_to_f32(v & 0xffffu) * sdat[j]);
+              const uint32_t hi = f32_to_bf16(bf16_to_f32(v >> 16) * sdat[j]);
+              r[j][q] = lo | (hi << 16);
+            }
+          }
+        }
+        char* base = lds + col(c) * LDS_ROW + G::kg() * 8;
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          // columns 2q (low halves) and 2q+1 (high halves)
+          u32x2_t e, o;
+          e[0] = (r[0][q] & 0xffffu) | (r[1][q] << 16);
+          e[1] = (r[2][q] & 0xffffu) | (r[3][q] << 16);
+          o[0] = (r[0][q] >> 16) | (r[1][q] & 0xffff0000u);
+          o[1] = (r[2][q] >> 16) | (r[3][q] & 0xffff0000u);
+          *(u32x2_t*)(base + (2 * q) * LDS_ROW) = e;
+          *(u32x2_t*)(base + (2 * q + 1) * LDS_ROW) = o;
+        }
+      } else {
+        f32x4_t r[4];
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          r[j] = __builtin_bit_cast(f32x4_t, reg[c][j]);
+          if constexpr (SCALED) r[j] *= sdat[j];
+        }
+        char* base = lds + col(c) * LDS_ROW + G::kg() * 16;
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          f32x4_t v{r[0][q], r[1][q], r[2][q], r[3][q]};
+          *(f32x4_t*)(base + q * LDS_ROW) = v;
+        }
+      }
     }
   }
 };
@@ -181,17 +229,30 @@ MOE_DEV void mma_stage(const char* stage, f32x16_t (&acc)[C::FM][C::FN], int wm,
   constexpr int NSTEP = KBYTES / STEP;
   const char* a_base = stage + (l & 31) * LDS_ROW + (l >> 5) * (8 * C::EB);
   const char* b_base = stage + C::A_BYTES + (l & 31) * LDS_ROW + (l >> 5) * (8 * C::EB);
+  // operand fragments are read one k-step ahead of the MFMAs that use them;
+  // the scheduling barrier keeps the compiler from hoisting every step's
+  // reads (and their registers) to the top of the stage
+  typename M::Frag a[2][C::FM], b[2][C::FN];
+#pragma unroll
+  for (int fm = 0; fm < C::FM; ++fm) a[0][fm] = M::lds_read(a_base + C::a_row0(wm, fm) * LDS_ROW);
+#pragma unroll
+  for (int fn = 0; fn < C::FN; ++fn) b[0][fn] = M::lds_read(b_base + C::b_row0(wn, fn) * LDS_ROW);
 #pragma unroll
   for (int s = 0; s < NSTEP; ++s) {
-    typename M::Frag a[C::FM], b[C::FN];
+    const int cur = s & 1;
+    if (s + 1 < NSTEP) {
 #pragma unroll
-    for (int fm = 0; fm < C::FM; ++fm) a[fm] = M::lds_read(a_base + C::a_row0(wm, fm) * LDS_ROW + s * STEP);
+      for (int fm = 0; fm < C::FM; ++fm)
+        a[cur ^ 1][fm] = M::lds_read(a_base + C::a_row0(wm, fm) * LDS_ROW + (s + 1) * STEP);
 #pragma unroll
-    for (int fn = 0; fn < C::FN; ++fn) b[fn] = M::lds_read(b_base + C::b_row0(wn, fn) * LDS_ROW + s * STEP);
+      for (int fn = 0; fn < C::FN; ++fn)
+        b[cur ^ 1][fn] = M::lds_read(b_base + C::b_row0(wn, fn) * LDS_ROW + (s + 1) * STEP);
+    }
 #pragma unroll
     for (int fm = 0; fm < C::FM; ++fm)
 #pragma unroll
-      for (int fn = 0; fn < C::FN; ++fn) M::mma(acc[fm][fn], a[fm], b[fn]);
+      for (int fn = 0; fn < C::FN; ++fn) M::mma(acc[fm][fn], a[cur][fm], b[cur][fn]);
+    __builtin_amdgcn_sched_barrier(0);
   }
 }
 
@@ -204,23 +265,33 @@ MOE_DEV void gemm_mainloop(LA& la, LB& lb, int nk, char* smem, f32x16_t (&acc)[C
 #pragma unroll
       for (int r = 0; r < 16; ++r) acc[fm][fn][r] = 0.0f;
   if (nk <= 0) return;
+  // prologue: tile 0 into stage 0, indices of tile 1 fetched
+  la.prefetch(0);
+  lb.prefetch(0);
   la.load(0);
   lb.load(0);
+  if (nk > 1) {
+    la.prefetch(1);
+    lb.prefetch(1);
+  }
   la.store(smem);
   lb.store(smem + C::A_BYTES);
   __syncthreads();
   for (int kt = 0; kt < nk; ++kt) {
-    char* cur = smem + (kt & 1) * C::STAGE;
-    char* nxt = smem + ((kt + 1) & 1) * C::STAGE;
-    const bool more = kt + 1 < nk;
-    if (more) {
+    const int cur = kt & 1;
+    // loads of k-tile kt+1 (and indices of kt+2) overlap the MFMAs of kt
+    if (kt + 1 < nk) {
       la.load(kt + 1);
       lb.load(kt + 1);
     }
-    mma_stage<C>(cur, acc, wm, wn);
-    if (more) {
-      la.store(nxt);
-      lb.store(nxt + C::A_BYTES);
+    if (kt + 2 < nk) {
+      la.prefetch(kt + 2);
+      lb.prefetch(kt + 2);
+    }
+    mma_stage<C>(smem + cur * C::STAGE, acc, wm, wn);
+    if (kt + 1 < nk) {
+      la.store(smem + (cur ^ 1) * C::STAGE);
+      lb.store(smem + (cur ^ 1) * C::STAGE + C::A_BYTES);
     }
     __syncthreads();
   }

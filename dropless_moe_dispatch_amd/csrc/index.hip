@@ -119,7 +119,8 @@ hipError_t launch_build_index(const Shape& s, const int32_t* ids, int32_t* offse
 
 // ---------------------------------------------------------------------------
 // Per-call preparation for the expert GEMMs:
-//   block 0: mb_off[e] = sum_{e' < e} ceil(count_e' / TILE)  (tile map);
+//   block 0: mb_off[b][e] = sum_{e' < e} ceil(count_e' / bm_b), bm = 128, 256
+//            (tile maps of the two row blockings);
 //   all blocks: per position p = token_index_map[t*K+k]:
 //     w_pos[p] = topk_w[t,k], rank_pos[p] = #{j : ids[t,j] < ids[t,k]};
 //   zero the fold turn counters and the counters block.
@@ -134,29 +135,34 @@ __global__ __launch_bounds__(256) void prep_kernel(int T, int E, int K, const in
   if (blockIdx.x == 0) {
     __shared__ int sh[256];
     const int per = (E + 255) / 256;
-    int loc[4];
-    int sum = 0;
-    for (int i = 0; i < per; ++i) {
-      const int e = tid * per + i;
-      const int c = e < E ? offsets[e + 1] - offsets[e] : 0;
-      loc[i] = (c + TILE - 1) / TILE;
-      sum += loc[i];
-    }
-    sh[tid] = sum;
-    __syncthreads();
-    for (int off = 1; off < 256; off <<= 1) {
-      const int v = tid >= off ? sh[tid - off] : 0;
+    for (int b = 0; b < 2; ++b) {
+      const int bm = b ? TILE_L : TILE_S;
+      int32_t* mo = mb_off + b * (E + 1);
+      int loc[4];
+      int sum = 0;
+      for (int i = 0; i < per; ++i) {
+        const int e = tid * per + i;
+        const int c = e < E ? offsets[e + 1] - offsets[e] : 0;
+        loc[i] = (c + bm - 1) / bm;
+        sum += loc[i];
+      }
       __syncthreads();
-      sh[tid] += v;
+      sh[tid] = sum;
       __syncthreads();
+      for (int off = 1; off < 256; off <<= 1) {
+        const int v = tid >= off ? sh[tid - off] : 0;
+        __syncthreads();
+        sh[tid] += v;
+        __syncthreads();
+      }
+      int run = sh[tid] - sum;
+      for (int i = 0; i < per; ++i) {
+        const int e = tid * per + i;
+        if (e < E) mo[e] = run;
+        run += loc[i];
+      }
+      if (tid == 255) mo[E] = sh[255];
     }
-    int run = sh[tid] - sum;
-    for (int i = 0; i < per; ++i) {
-      const int e = tid * per + i;
-      if (e < E) mb_off[e] = run;
-      run += loc[i];
-    }
-    if (tid == 255) mb_off[E] = sh[255];
     if (tid < N_COUNTERS) counters[tid] = 0;
   }
   const long long gsz = (long long)gridDim.x * 256;
@@ -181,7 +187,7 @@ __global__ __launch_bounds__(256) void prep_kernel(int T, int E, int K, const in
 hipError_t launch_prep(const Shape& s, const ExpertWs& ws, const int32_t* offsets, const int32_t* ids,
                        const float* topk_w, const int32_t* tim, bool per_position, hipStream_t st) {
   timing_mark(st, "prep", true);
-  const long long n_turn = per_position ? (long long)s.T * (s.d / TILE) : 0;
+  const long long n_turn = per_position ? (long long)s.T * col_blocks(s.d, TILE_S) : 0;
   long long work = per_position ? (n_turn > s.T ? n_turn : s.T) : 1;
   int blocks = (int)((work + 255) / 256);
   if (blocks > 2048) blocks = 2048;

@@ -8,7 +8,10 @@
 
 namespace moe {
 
-constexpr int TILE = 128;           // row-block / column-block of every expert GEMM
+// Expert GEMM tiles are 128 or 256 rows/columns (chosen per kernel and shape
+// on the host); per-call state is sized for the finer 128 blocking.
+constexpr int TILE_S = 128;
+constexpr int TILE_L = 256;
 constexpr int IDX_CHUNK = 256;      // tokens per index-build workgroup
 constexpr int IDX_WAVES = IDX_CHUNK / 64;
 constexpr int N_COUNTERS = 64;      // [0] error flag, [1] fold ticket, [2..] reserved
@@ -20,10 +23,12 @@ struct Shape {
 };
 
 inline size_t align_up(size_t v, size_t a) { return (v + a - 1) / a * a; }
+// column blocks of width bn covering n columns (the last may be partial)
+__host__ __device__ inline int col_blocks(int n, int bn) { return (n + bn - 1) / bn; }
 
-// Upper bound on the number of TILE-row blocks over all experts.
-inline long long max_row_blocks(const Shape& s) {
-  return (s.A() + (long long)s.E * (TILE - 1)) / TILE;
+// Upper bound on the number of bm-row blocks over all experts.
+inline long long max_row_blocks(const Shape& s, int bm) {
+  return (s.A() + (long long)s.E * (bm - 1)) / bm;
 }
 
 // ---- index workspace ------------------------------------------------------
@@ -48,33 +53,36 @@ inline IndexWs index_ws(const Shape& s, void* p) {
 // ---- per-call expert workspace (tile map, per-position data, fold state) --
 struct ExpertWs {
   int32_t* counters;   // [N_COUNTERS]
-  int32_t* mb_off;     // [E+1] exclusive prefix of ceil(count_e / TILE)
+  int32_t* mb_off;     // [2][E+1] exclusive prefix of ceil(count_e / bm), bm = 128 then 256
   float* w_pos;        // [A] combine weight of the assignment at each position
   int32_t* rank_pos;   // [A] rank of the position's expert among its token's experts
-  int32_t* turn;       // [T][d/TILE] ordered-fold turn counters
+  int32_t* turn;       // [T][d/128] ordered-fold turn counters
   float* acc;          // [T][d] fp32 fold accumulator
-  float* ds_part;      // [A][h/TILE] router-score partial sums (backward)
+  float* ds_part;      // [A][h/128] router-score partial sums (backward)
   float* dz_pos;       // [A] router logit gradient per position (backward)
   void* dh;            // [A][2h] activation-dtype gradient of the pre-activations (backward)
   size_t bytes;
+  int E;
+  const int32_t* tile_map(int bm) const { return mb_off + (bm == TILE_L ? E + 1 : 0); }
 };
 enum { WS_EXPERT_FWD = 1, WS_COMBINE = 2, WS_EXPERT_BWD = 3 };
 
 inline ExpertWs expert_ws(const Shape& s, int which, void* p) {
   ExpertWs w{};
+  w.E = s.E;
   const size_t A = (size_t)s.A();
   size_t off = 0;
   auto take = [&](size_t bytes) { void* q = (char*)p + off; off = align_up(off + bytes, 256); return q; };
   w.counters = (int32_t*)take(N_COUNTERS * 4);
-  w.mb_off = (int32_t*)take((size_t)(s.E + 1) * 4);
+  w.mb_off = (int32_t*)take((size_t)2 * (s.E + 1) * 4);
   if (which == WS_COMBINE || which == WS_EXPERT_BWD) {
     w.w_pos = (float*)take(A * 4);
     w.rank_pos = (int32_t*)take(A * 4);
-    w.turn = (int32_t*)take((size_t)s.T * (s.d / TILE) * 4);
+    w.turn = (int32_t*)take((size_t)s.T * col_blocks(s.d, TILE_S) * 4);
     w.acc = (float*)take((size_t)s.T * s.d * 4);
   }
   if (which == WS_EXPERT_BWD) {
-    w.ds_part = (float*)take(A * (s.h / TILE) * 4);
+    w.ds_part = (float*)take(A * col_blocks(s.h, TILE_S) * 4);
     w.dz_pos = (float*)take(A * 4);
     w.dh = take(A * 2 * (size_t)s.h * s.elem());
   }

@@ -26,18 +26,20 @@ __global__ __launch_bounds__(NTHREADS, 2) void router_logits_kernel(const typena
   const int m0 = blockIdx.x * C::BM;
   const int n0 = blockIdx.y * C::BN;
   const int wave = threadIdx.x >> 6, wm = wave / C::WN, wn = wave % C::WN;
-  const size_t ld = (size_t)d * sizeof(TIN);
+  const uint32_t ld = (uint32_t)d * sizeof(TIN);
   RowLoader<C::BM> la;
   RowLoader<C::BN> lb;
+  la.rs[0] = make_rsrc(x + (size_t)m0 * d, (size_t)(T - m0) * ld);
 #pragma unroll
   for (int i = 0; i < RowLoader<C::BM>::CPT; ++i) {
-    const int t = m0 + RowLoader<C::BM>::my_row(i);
-    la.row_ptr[i] = t < T ? (const char*)x + (size_t)t * ld : nullptr;
+    const int r = RowLoader<C::BM>::my_row(i);
+    la.roff[i] = m0 + r < T ? (uint32_t)r * ld : OOB_OFF;
   }
+  lb.rs[0] = make_rsrc(wg, (size_t)E * ld);
 #pragma unroll
   for (int i = 0; i < RowLoader<C::BN>::CPT; ++i) {
     const int e = n0 + RowLoader<C::BN>::my_row(i);
-    lb.row_ptr[i] = e < E ? (const char*)wg + (size_t)e * ld : nullptr;
+    lb.roff[i] = e < E ? (uint32_t)e * ld : OOB_OFF;
   }
   f32x16_t acc[C::FM][C::FN];
   gemm_mainloop<C>(la, lb, d / C::BK, smem, acc, wm, wn);
