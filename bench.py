@@ -28,6 +28,30 @@ PEAK_HBM_GBS = 8000.0
 METRIC = "MoE layer fwd+bwd tokens/s and TFLOP/s at 1 GPU; % bf16 MFMA peak; peak act MB"
 
 
+def kernel_source_hash():
+    """Hash of the HIP sources; counter data taken with other sources is stale."""
+    import hashlib
+    h = hashlib.sha256()
+    csrc = os.path.join(ROOT, "dropless_moe_dispatch_amd", "csrc")
+    for f in sorted(os.listdir(csrc)):
+        if f.endswith((".hip", ".hpp")):
+            h.update(open(os.path.join(csrc, f), "rb").read())
+    return h.hexdigest()[:16]
+
+
+def committed_traffic(workload, kernel):
+    """HBM bytes per launch of ``kernel`` from the committed counter summary
+    (profiles/traffic_<workload>.json), if it was taken with these sources."""
+    path = os.path.join(ROOT, "profiles", f"traffic_{workload}.json")
+    if not os.path.exists(path):
+        return None
+    rec = json.load(open(path))
+    if rec.get("src_sha") != kernel_source_hash():
+        return None
+    k = rec.get("kernels", {}).get(kernel)
+    return None if k is None else k.get("hbm_bytes_per_launch")
+
+
 def kernel_flops(name, T, d, E, K, h):
     A = T * K
     return {
@@ -74,6 +98,9 @@ def main():
     ap.add_argument("--workload", type=int, default=3, help="1..5 (default 3: fine-grained fwd+bwd)")
     ap.add_argument("--cpu-sample", type=int, default=64, help="tokens for the CPU oracle baseline (0 = skip)")
     ap.add_argument("--no-timing", action="store_true", help="do not record per-kernel events")
+    ap.add_argument("--calib-copy-mb", type=int, default=0,
+                    help="after the timed steps, run one plain device copy of this many MB "
+                         "(reference kernel for scaling the HBM byte counters)")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py runs on one GPU only; --gpus {args.gpus} is not supported "
@@ -119,6 +146,14 @@ def main():
     t1 = time.perf_counter()
     recs = B.timing_read() if not args.no_timing else []
     B.timing_enable(False)
+    if args.calib_copy_mb > 0:
+        n = args.calib_copy_mb * (1 << 20)
+        src = torch.ones(n // 4, dtype=torch.float32, device="cuda")
+        dst = torch.empty_like(src)
+        torch.cuda.synchronize()
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
     errs = buf.device_error_words()
     peak_alloc = torch.cuda.max_memory_allocated()
 
@@ -137,8 +172,9 @@ def main():
         ach = fl / (gemms[dom]["avg_ms"] * 1e-3) / 1e12
         peak = PEAK_BF16_TFLOPS if dt == "bf16" else PEAK_F32_MFMA_TFLOPS
         roofline = {"bound": "mfma", "kernel": dom, "achieved": round(ach, 2), "peak": peak, "unit": "TFLOP/s",
-                    "frac": round(ach / peak, 4), "traffic": None, "avg_launch_ms": round(gemms[dom]["avg_ms"], 4),
-                    "algorithmic_flop_per_launch": fl}
+                    "frac": round(ach / peak, 4), "traffic": committed_traffic(wl.name, dom),
+                    "avg_launch_ms": round(gemms[dom]["avg_ms"], 4), "algorithmic_flop_per_launch": fl,
+                    "src_sha": kernel_source_hash()}
     counts = np.diff(buf.offsets.cpu().numpy())
     cpu = cpu_baseline(wl, inp, args.cpu_sample) if args.cpu_sample > 0 else None
     out = {
