@@ -18,10 +18,9 @@ typedef uint32_t u32x2_t __attribute__((ext_vector_type(2)));
 MOE_DEV float bf16_to_f32(uint32_t v) { return __uint_as_float(v << 16); }
 
 MOE_DEV uint32_t f32_to_bf16(float f) {
-  uint32_t u = __float_as_uint(f);
-  if ((u & 0x7fffffffu) > 0x7f800000u) return (u >> 16) | 0x40u;  // quiet NaN
-  u += 0x7fffu + ((u >> 16) & 1u);
-  return u >> 16;
+  const uint32_t u = __float_as_uint(f);
+  const uint32_t rounded = (u + 0x7fffu + ((u >> 16) & 1u)) >> 16;
+  return (u & 0x7fffffffu) > 0x7f800000u ? (u >> 16) | 0x40u : rounded;  // NaN stays a quiet NaN
 }
 
 template <typename T> struct ElemT;

@@ -142,96 +142,141 @@ hipError_t launch_gate_up(const Shape& s, const void* x, const int32_t* offsets,
 // ===========================================================================
 // Ordered fold: the owner-computes weighted combine through the reverse index.
 //
-// Every output row out[t] (per BN-column block) receives K contributions
+// Every output row out[t] (per 128-column block) receives K contributions
 // from K different expert tiles.  Tiles are claimed through a ticket counter
 // in ascending (expert, row-block, column-block) order, and a contribution of
 // rank r (the position of its expert among the token's experts, ascending)
-// is applied only after turn[t][block] == r; it then bumps the turn.  All
-// predecessors of a contribution live in tiles with smaller tickets, held by
-// running workgroups, so the waits always drain.  The fp32 accumulator sees
-// the K contributions in ascending expert order: deterministic, with integer
-// flags only (no float atomics).  The last rank writes the output row.
+// is applied only after turn[t][block] == r; it then bumps the turn.  The
+// fp32 accumulator sees the K contributions in ascending expert order:
+// deterministic, with integer flags only (no float atomics).  The last rank
+// writes the output row.
 //
-// Visibility across XCDs: one device-scope acquire per tile after the waits
-// and one device-scope release per tile before the turns are published.
+// Row-granular waits.  The tile's result is parked in LDS and each wave
+// folds its 32 rows in whatever order their turns arrive, publishing each
+// row's turn as soon as that row is stored.  A row therefore waits only on
+// its own token's lower-ranked contributions (at most K - 1 of them), never
+// on the other rows of the tile; a tile-wide wait would chain every expert's
+// tiles behind the previous expert's slowest row.  Every predecessor of a
+// contribution lives in a tile with a smaller ticket, held by a running
+// workgroup, so the waits drain (bounded by the spin limit all the same).
+//
+// Visibility across XCDs without cache-wide fences: every accumulator load
+// and store is a device-coherent access (the cache policy the compiler gives
+// a relaxed device-scope atomic), so no XCD's L2 holds a stale or dirty
+// accumulator line.  A wave waits for its accumulator stores to complete
+// before it publishes their turns, and issues accumulator loads only for rows
+// whose turns it has seen.  A device-scope release/acquire fence pair would
+// instead write back and invalidate the whole L2 of the XCD on every tile,
+// evicting the weight tiles the other workgroups are reusing.
 //
 // INIT_FIRST: rank 0 writes the accumulator (forward); otherwise the
 // accumulator is pre-initialised and every rank adds (backward dX, where the
 // router term is the initial value).
 // ===========================================================================
+MOE_DEV u32x2_t coherent_load2(const float* p) {
+  const uint64_t v = __hip_atomic_load((const uint64_t*)p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  return __builtin_bit_cast(u32x2_t, v);
+}
+MOE_DEV void coherent_store2(float* p, float a, float b) {
+  const uint64_t v = (uint64_t)__float_as_uint(a) | ((uint64_t)__float_as_uint(b) << 32);
+  __hip_atomic_store((uint64_t*)p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+MOE_DEV void store2(float* p, float a, float b) { *(float2*)p = make_float2(a, b); }
+MOE_DEV void store2(bf16_t* p, float a, float b) { *(uint32_t*)p = f32_to_bf16(a) | (f32_to_bf16(b) << 16); }
+
+constexpr int FOLD_LD = 136;  // floats per parked row (128 + 8: the two half-waves' rows land on disjoint banks)
+constexpr int FOLD_ROWS_PER_WAVE = 32;
+constexpr int FOLD_BATCH = 16;
+
 template <class C, bool INIT_FIRST>
 MOE_DEV void fold_epilogue(const f32x16_t (&acc)[C::FM][C::FN], const RowTile& rt, int nb, int NB, int wm, int wn,
                            const int32_t* __restrict__ eti, const float* __restrict__ w_pos,
                            const int32_t* __restrict__ rank_pos, int K, int d, int32_t* turn,
                            float* __restrict__ accws, typename C::T* __restrict__ out, int32_t* counters,
                            int spin_limit, char* smem) {
-  int* s_t = (int*)smem;
-  float* s_w = (float*)(smem + 4 * C::BM);
-  int* s_rank = (int*)(smem + 8 * C::BM);
+  static_assert(C::BM == 128 && C::BN == 128, "the fold parks a 128 x 128 tile");
+  static_assert(C::BM * FOLD_LD * 4 + 3 * C::BM * 4 <= C::LDS_BYTES, "parked tile fits the LDS stages");
+  float* s_c = (float*)smem;
+  int* s_t = (int*)(smem + C::BM * FOLD_LD * 4);
+  float* s_w = (float*)(s_t + C::BM);
+  int* s_rank = (int*)(s_w + C::BM);
   const int tid = threadIdx.x;
+  const int l = lane_id();
   const int rows = rt.r1 - rt.r0;
-  __syncthreads();  // LDS stages are reused below
-  for (int i = tid; i < rows; i += NTHREADS) {
+  __syncthreads();  // the LDS stages are reused below
+  for (int i = tid; i < C::BM; i += NTHREADS) {  // rows past the tile read token 0 and are never stored
     const int p = rt.r0 + i;
-    const int t = eti[p];
-    const int rank = rank_pos[p];
-    s_t[i] = t;
-    s_w[i] = w_pos ? w_pos[p] : 1.0f;
-    s_rank[i] = rank;
-    int32_t* f = turn + (size_t)t * NB + nb;
-    int spins = 0;
-    while (__hip_atomic_load(f, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) < rank) {
+    const bool in = i < rows;
+    s_t[i] = in ? eti[p] : 0;
+    s_w[i] = in && w_pos ? w_pos[p] : 1.0f;
+    s_rank[i] = in ? rank_pos[p] : 0;
+  }
+#pragma unroll
+  for (int fm = 0; fm < C::FM; ++fm)
+#pragma unroll
+    for (int fn = 0; fn < C::FN; ++fn)
+#pragma unroll
+      for (int r = 0; r < 16; ++r)
+        s_c[(C::a_row0(wm, fm) + frag_row(r, l)) * FOLD_LD + C::b_row0(wn, fn) + frag_col(l)] = acc[fm][fn][r];
+  __syncthreads();
+
+  // wave w folds tile rows w, w + 4, ..., w + 124; lane j < 32 watches row w + 4j
+  const int wave = tid >> 6;
+  const int j = l & 31;
+  const int my_row = wave + 4 * j;
+  const bool mine = l < 32 && my_row < rows;
+  const int my_t = mine ? s_t[my_row] : 0;
+  const int my_rank = mine ? s_rank[my_row] : 0;
+  int32_t* my_turn = turn + (size_t)my_t * NB + nb;
+  const int col = 2 * l;  // each lane folds two adjacent columns of a row
+  const size_t cofs = (size_t)nb * C::BN + col;
+  uint64_t pending = __builtin_amdgcn_ballot_w64(mine);
+  int spins = 0;
+  while (pending) {
+    const bool ready = ((pending >> j) & 1) && l < 32 &&
+                       __hip_atomic_load(my_turn, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) >= my_rank;
+    const uint64_t m = __builtin_amdgcn_ballot_w64(ready) & pending;
+    if (m == 0) {
       if (++spins > spin_limit) {
         __hip_atomic_store(counters, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
         break;
       }
       __builtin_amdgcn_s_sleep(2);
+      continue;
     }
-  }
-  __syncthreads();
-  if (tid < 64) __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
-  __syncthreads();
-  const int l = lane_id();
-  const int cbase = nb * C::BN;
+    spins = 0;
+    // In batches of 16 rows: read the accumulator of every row of the batch
+    // without branches (a row that is not ready yet, or past the tile, reads
+    // a value that is never stored), combine, then store the ready rows, so
+    // that no store waits on a load.
 #pragma unroll
-  for (int fm = 0; fm < C::FM; ++fm) {
-    // issue this fragment row's accumulator reads first, then combine and store
-    float prev[C::FN][16];
+    for (int b0 = 0; b0 < FOLD_ROWS_PER_WAVE; b0 += FOLD_BATCH) {
+      if (((m >> b0) & ((1ull << FOLD_BATCH) - 1)) == 0) continue;
+      u32x2_t prev[FOLD_BATCH];
 #pragma unroll
-    for (int r = 0; r < 16; ++r) {
-      const int row = C::a_row0(wm, fm) + frag_row(r, l);
-      const bool need = row < rows && !(INIT_FIRST && s_rank[row] == 0);
-      const size_t ob = need ? (size_t)s_t[row] * d : 0;
+      for (int i = 0; i < FOLD_BATCH; ++i)
+        prev[i] = coherent_load2(accws + (size_t)s_t[wave + 4 * (b0 + i)] * d + cofs);
 #pragma unroll
-      for (int fn = 0; fn < C::FN; ++fn) {
-        const int col = cbase + C::b_row0(wn, fn) + frag_col(l);
-        prev[fn][r] = (need && col < d) ? accws[ob + col] : 0.0f;
+      for (int i = 0; i < FOLD_BATCH; ++i) {
+        const int row = wave + 4 * (b0 + i);
+        const float w = s_w[row];
+        const float2 c = *(const float2*)(s_c + row * FOLD_LD + col);
+        const bool fresh = INIT_FIRST && s_rank[row] == 0;  // rank 0 starts the sum (forward)
+        const float a = (fresh ? 0.0f : __uint_as_float(prev[i][0])) + w * c.x;
+        const float b = (fresh ? 0.0f : __uint_as_float(prev[i][1])) + w * c.y;
+        if ((m >> (b0 + i)) & 1) {
+          const size_t o = (size_t)s_t[row] * d + cofs;
+          if (s_rank[row] == K - 1) store2(out + o, a, b);
+          else coherent_store2(accws + o, a, b);
+        }
       }
     }
-#pragma unroll
-    for (int r = 0; r < 16; ++r) {
-      const int row = C::a_row0(wm, fm) + frag_row(r, l);
-      if (row >= rows) continue;
-      const size_t ob = (size_t)s_t[row] * d;
-      const float w = s_w[row];
-      const bool last = s_rank[row] == K - 1;
-#pragma unroll
-      for (int fn = 0; fn < C::FN; ++fn) {
-        const int col = cbase + C::b_row0(wn, fn) + frag_col(l);
-        if (col >= d) continue;
-        const float v = prev[fn][r] + w * acc[fm][fn][r];
-        if (last) ElemT<typename C::T>::store(out + ob + col, v);
-        else accws[ob + col] = v;
-      }
-    }
+    // this wave's stores have completed before the turns of its rows move on
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    if ((m >> j) & 1 && l < 32)
+      __hip_atomic_store(my_turn, my_rank + 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    pending &= ~m;
   }
-  // all waves' stores complete, then one device-scope release, then the turns
-  __builtin_amdgcn_s_waitcnt(0);
-  __syncthreads();
-  if (tid < 64) __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");
-  __syncthreads();
-  for (int i = tid; i < rows; i += NTHREADS)
-    __hip_atomic_store(turn + (size_t)s_t[i] * NB + nb, s_rank[i] + 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
 MOE_DEV int claim_ticket(int32_t* counters, char* smem) {
@@ -295,14 +340,9 @@ static hipError_t down_combine_t(const Shape& s, const void* y_swi, const void* 
 hipError_t launch_down_combine(const Shape& s, const void* y_swi, const void* w_down, const int32_t* offsets,
                                const int32_t* eti, void* out, const ExpertWs& ws, int spin_limit, hipStream_t st) {
   timing_mark(st, "down_combine", true);
-  const bool big = pick_large(s.h >= 2048);
-  hipError_t e;
-  if (s.bf16)
-    e = big ? down_combine_t<bf16_t, TILE_L>(s, y_swi, w_down, offsets, eti, out, ws, spin_limit, st)
-            : down_combine_t<bf16_t, TILE_S>(s, y_swi, w_down, offsets, eti, out, ws, spin_limit, st);
-  else
-    e = big ? down_combine_t<float, TILE_L>(s, y_swi, w_down, offsets, eti, out, ws, spin_limit, st)
-            : down_combine_t<float, TILE_S>(s, y_swi, w_down, offsets, eti, out, ws, spin_limit, st);
+  // the fold parks 128 x 128 tiles (also the faster tile for every measured shape)
+  const hipError_t e = s.bf16 ? down_combine_t<bf16_t, TILE_S>(s, y_swi, w_down, offsets, eti, out, ws, spin_limit, st)
+                              : down_combine_t<float, TILE_S>(s, y_swi, w_down, offsets, eti, out, ws, spin_limit, st);
   timing_mark(st, "down_combine", false);
   return e;
 }
@@ -717,8 +757,7 @@ static hipError_t backward_t(const Shape& s, const void* dout, const void* x, co
   if ((err = hipGetLastError()) != hipSuccess) return err;
 
   timing_mark(st, "dx_fold", true);
-  if (pick_large(2 * s.h >= 3072)) launch_dx_fold<TIN, TILE_L>(s, w_gate, w_up, offsets, eti, dx, ws, spin_limit, st);
-  else launch_dx_fold<TIN, TILE_S>(s, w_gate, w_up, offsets, eti, dx, ws, spin_limit, st);
+  launch_dx_fold<TIN, TILE_S>(s, w_gate, w_up, offsets, eti, dx, ws, spin_limit, st);
   timing_mark(st, "dx_fold", false);
   return hipGetLastError();
 }
