@@ -19,6 +19,8 @@
 //    dX[t] = sum_k (da W_gate + db W_up)_{p(t,k)} + router term
 #include <stdlib.h>
 
+#include <type_traits>
+
 #include "gemm.hpp"
 #include "layout.hpp"
 
@@ -35,6 +37,14 @@ template <typename T> MOE_DEV void st_f(T* p, float v) { ElemT<T>::store(p, v); 
 // ordered combine's waits.
 template <typename TIN, int B> using GCfg = Cfg<TIN, B, B, 2, 2>;
 template <typename TIN, int B> using PCfg = Cfg<TIN, B, B, 2, 2, true>;
+// Operands whose source is k-major (weights read as [k][n], activations
+// reduced over rows) are staged k-major and read with the LDS transpose in
+// bf16; fp32 operands are transposed in registers (KRowLoader).
+template <typename TIN> constexpr bool kTr = sizeof(TIN) == 2;
+template <typename TIN, int B, bool AK, bool BK>
+using KCfg = Cfg<TIN, B, B, 2, 2, false, AK && kTr<TIN>, BK && kTr<TIN>>;
+template <class C, bool KM, int ROWS, class Src, bool SCALED>
+using KSrcLoader = std::conditional_t<KM, KLoader<ROWS, Src, SCALED>, KRowLoader<typename C::T, ROWS, Src, SCALED>>;
 
 // MOE_DISPATCH_TILE=128|256 forces one tile for every expert GEMM (tuning aid).
 static int forced_tile() {
@@ -420,7 +430,7 @@ __global__ __launch_bounds__(NTHREADS, C::WAVES_PER_EU) void dh_kernel(
     const int p = rt.r0 + RowLoader<C::BM>::my_row(i);
     la.roff[i] = p < rt.r1 ? (uint32_t)eti[p] * ldd : OOB_OFF;
   }
-  KRowLoader<TIN, C::BN, SrcWeightKN<TIN>, false> lb;
+  KSrcLoader<C, C::BKM, C::BN, SrcWeightKN<TIN>, false> lb;
   lb.src.rs = make_rsrc(w_down + (size_t)rt.e * d * h, (size_t)d * h * sizeof(TIN));
   lb.src.ld_bytes = (uint32_t)h * sizeof(TIN);
   lb.src.col0 = (uint32_t)(nb * C::BN) * sizeof(TIN);
@@ -574,7 +584,7 @@ __global__ __launch_bounds__(NTHREADS, C::WAVES_PER_EU) void dw_down_kernel(
   const int mb = blockIdx.x / nnb, nb = blockIdx.x % nnb;
   const int p0 = offsets[e], p1 = offsets[e + 1];
   const int wave = threadIdx.x >> 6, wm = wave / C::WN, wn = wave % C::WN;
-  KRowLoader<TIN, C::BM, SrcRowsGather<TIN>, false> la;
+  KSrcLoader<C, C::AKM, C::BM, SrcRowsGather<TIN>, false> la;
   la.src.rs = make_rsrc(dout, (size_t)T * d * sizeof(TIN));
   la.src.ld_bytes = (uint32_t)d * sizeof(TIN);
   la.src.col0 = (uint32_t)(mb * C::BM) * sizeof(TIN);
@@ -582,7 +592,7 @@ __global__ __launch_bounds__(NTHREADS, C::WAVES_PER_EU) void dw_down_kernel(
   la.src.p1 = p1;
   la.src.eti = eti;
   la.ncols = min_i(C::BM, d - mb * C::BM);
-  KRowLoader<TIN, C::BN, SrcRowsContig<TIN>, true> lb;
+  KSrcLoader<C, C::BKM, C::BN, SrcRowsContig<TIN>, true> lb;
   lb.src.rs = make_rsrc(y_swi + (size_t)p0 * h, (size_t)(p1 - p0) * h * sizeof(TIN));
   lb.src.ld_bytes = (uint32_t)h * sizeof(TIN);
   lb.src.col0 = (uint32_t)(nb * C::BN) * sizeof(TIN);
@@ -620,7 +630,7 @@ __global__ __launch_bounds__(NTHREADS, C::WAVES_PER_EU) void dw_gate_up_kernel(
   const int mb = blockIdx.x / nnb, nb = blockIdx.x % nnb;
   const int p0 = offsets[e], p1 = offsets[e + 1];
   const int wave = threadIdx.x >> 6, wm = wave / C::WN, wn = wave % C::WN;
-  KRowLoader<TIN, C::BM, SrcRowsContig<TIN>, false> la;
+  KSrcLoader<C, C::AKM, C::BM, SrcRowsContig<TIN>, false> la;
   la.src.rs = make_rsrc(dh + (size_t)p0 * 2 * h, (size_t)(p1 - p0) * 2 * h * sizeof(TIN));
   la.src.ld_bytes = (uint32_t)(2 * h) * sizeof(TIN);
   la.src.col0 = (uint32_t)(mb * C::BM) * sizeof(TIN);
@@ -628,7 +638,7 @@ __global__ __launch_bounds__(NTHREADS, C::WAVES_PER_EU) void dw_gate_up_kernel(
   la.src.p0 = p0;
   la.src.scl = nullptr;
   la.ncols = min_i(C::BM, 2 * h - mb * C::BM);
-  KRowLoader<TIN, C::BN, SrcRowsGather<TIN>, false> lb;
+  KSrcLoader<C, C::BKM, C::BN, SrcRowsGather<TIN>, false> lb;
   lb.src.rs = make_rsrc(x, (size_t)T * d * sizeof(TIN));
   lb.src.ld_bytes = (uint32_t)d * sizeof(TIN);
   lb.src.col0 = (uint32_t)(nb * C::BN) * sizeof(TIN);
@@ -677,7 +687,7 @@ __global__ __launch_bounds__(NTHREADS, C::WAVES_PER_EU) void dx_fold_kernel(
     const int r = RowLoader<C::BM>::my_row(i);
     la.roff[i] = rt.r0 + r < rt.r1 ? (uint32_t)r * ldh : OOB_OFF;
   }
-  KRowLoader<TIN, C::BN, SrcWeightKN2<TIN>, false> lb;
+  KSrcLoader<C, C::BKM, C::BN, SrcWeightKN2<TIN>, false> lb;
   lb.src.rs1 = make_rsrc(w_gate + (size_t)rt.e * h * d, (size_t)h * d * sizeof(TIN));
   lb.src.rs2 = make_rsrc(w_up + (size_t)rt.e * h * d, (size_t)h * d * sizeof(TIN));
   lb.src.ld_bytes = (uint32_t)d * sizeof(TIN);
@@ -694,7 +704,7 @@ __global__ __launch_bounds__(NTHREADS, C::WAVES_PER_EU) void dx_fold_kernel(
 template <typename TIN, int B>
 static void launch_dh(const Shape& s, const void* dout, const void* w_down, const void* h_ab, const void* y_swi,
                       const int32_t* offsets, const int32_t* eti, const ExpertWs& ws, hipStream_t st) {
-  using C = GCfg<TIN, B>;
+  using C = KCfg<TIN, B, false, true>;
   const int nbn = col_blocks(s.h, B);
   const long long nblk = (max_row_blocks(s, B) * nbn + 7) / 8 * 8;
   dh_kernel<C><<<dim3((unsigned)nblk), dim3(NTHREADS), 0, st>>>(
@@ -705,7 +715,7 @@ static void launch_dh(const Shape& s, const void* dout, const void* w_down, cons
 template <typename TIN, int B>
 static void launch_dx_fold(const Shape& s, const void* w_gate, const void* w_up, const int32_t* offsets,
                            const int32_t* eti, void* dx, const ExpertWs& ws, int spin_limit, hipStream_t st) {
-  using C = GCfg<TIN, B>;
+  using C = KCfg<TIN, B, false, true>;
   const long long nblk = max_row_blocks(s, B) * col_blocks(s.d, B);
   dx_fold_kernel<C><<<dim3((unsigned)nblk), dim3(NTHREADS), 0, st>>>(
       (const TIN*)ws.dh, (const TIN*)w_gate, (const TIN*)w_up, offsets, eti, ws.tile_map(B), ws.rank_pos, ws.turn,
@@ -718,7 +728,7 @@ static hipError_t backward_t(const Shape& s, const void* dout, const void* x, co
                              const int32_t* offsets, const int32_t* eti, const int32_t* tim, const void* h_ab,
                              const void* y_swi, void* dx, float* dwg, float* dw_gate, float* dw_up,
                              float* dw_down, float* ds, const ExpertWs& ws, int spin_limit, hipStream_t st) {
-  using CL = GCfg<TIN, TILE_L>;
+  using CL = KCfg<TIN, TILE_L, true, true>;
   // the large-tile dH epilogue spills; the small tile is used for every shape
   const bool dh_big = forced_tile() == TILE_L;
   const int nbh = col_blocks(s.h, dh_big ? TILE_L : TILE_S);
@@ -745,13 +755,13 @@ static hipError_t backward_t(const Shape& s, const void* dout, const void* x, co
   if ((err = hipGetLastError()) != hipSuccess) return err;
 
   timing_mark(st, "dw_down", true);
-  dw_down_kernel<CL><<<dim3(col_blocks(s.d, TILE_L) * col_blocks(s.h, TILE_L), s.E), dim3(NTHREADS), 0, st>>>(
+  dw_down_kernel<CL><<<dim3(col_blocks(s.d, CL::BM) * col_blocks(s.h, CL::BN), s.E), dim3(NTHREADS), 0, st>>>(
       (const TIN*)dout, (const TIN*)y_swi, offsets, eti, ws.w_pos, dw_down, s.T, s.d, s.h);
   timing_mark(st, "dw_down", false);
   if ((err = hipGetLastError()) != hipSuccess) return err;
 
   timing_mark(st, "dw_gate_up", true);
-  dw_gate_up_kernel<CL><<<dim3(col_blocks(2 * s.h, TILE_L) * col_blocks(s.d, TILE_L), s.E), dim3(NTHREADS), 0,
+  dw_gate_up_kernel<CL><<<dim3(col_blocks(2 * s.h, CL::BM) * col_blocks(s.d, CL::BN), s.E), dim3(NTHREADS), 0,
                           st>>>((const TIN*)ws.dh, (const TIN*)x, offsets, eti, dw_gate, dw_up, s.T, s.d, s.h);
   timing_mark(st, "dw_gate_up", false);
   if ((err = hipGetLastError()) != hipSuccess) return err;

@@ -23,6 +23,8 @@
 //                16-byte column chunks and transposes them in registers so
 //                that LDS still holds [m][k].
 #pragma once
+#include <type_traits>
+
 #include "common.hpp"
 
 namespace moe {
@@ -31,22 +33,41 @@ constexpr int NTHREADS = 256;
 constexpr int LDS_ROW = 144;
 constexpr int KBYTES = 128;
 
-template <typename TIN, int BM_, int BN_, int WM_, int WN_, bool PAIRED_ = false>
+// k-major LDS layout (bf16 only): the stage holds 64 k-rows of ROWS
+// elements, each k-row padded to PITCH bytes; MFMA operands are read from it
+// with the LDS transpose read (ds_read_b64_tr_b16).
+constexpr int KM_PAD = 64;  // 64 banks: the four k-rows of a transpose read land on disjoint banks
+template <int ROWS>
+struct KmGeom {
+  static constexpr int PITCH = ROWS * 2 + KM_PAD;
+  static constexpr int BYTES = 64 * PITCH;
+  static constexpr int CPR = ROWS / 8;          // 16-byte chunks per k-row
+  static constexpr int RPP = NTHREADS / CPR;    // k-rows per pass of the workgroup
+  static constexpr int NPASS = 64 / RPP;        // chunks per thread per stage
+};
+
+template <typename TIN, int BM_, int BN_, int WM_, int WN_, bool PAIRED_ = false, bool AKM_ = false,
+          bool BKM_ = false>
 struct Cfg {
   using T = TIN;
   static constexpr int BM = BM_, BN = BN_, WM = WM_, WN = WN_;
   // PAIRED: B rows [0,BN/2) and [BN/2,BN) pair up column by column, and each
   // wave holds both halves of its columns (fragments fn and fn + FN/2).
   static constexpr bool PAIRED = PAIRED_;
+  // AKM / BKM: the operand is staged k-major (see KmGeom) instead of [row][k]
+  static constexpr bool AKM = AKM_, BKM = BKM_;
   static constexpr int EB = (int)sizeof(TIN);
+  static_assert(!(AKM || BKM) || EB == 2, "k-major staging is bf16 only");
   static constexpr int BK = KBYTES / EB;
   static constexpr int FM = BM / WM / 32;
   static constexpr int FN = BN / WN / 32;
-  static constexpr int A_BYTES = BM * LDS_ROW;
-  static constexpr int B_BYTES = BN * LDS_ROW;
+  static constexpr int A_BYTES = AKM ? KmGeom<BM>::BYTES : BM * LDS_ROW;
+  static constexpr int B_BYTES = BKM ? KmGeom<BN>::BYTES : BN * LDS_ROW;
   static constexpr int STAGE = A_BYTES + B_BYTES;
   static constexpr int LDS_BYTES = 2 * STAGE;
   static constexpr int WAVES_PER_EU = (BM * BN >= 256 * 256) ? 1 : 2;
+  // register sets for staging global loads (the 256 x 256 tile has no room for two)
+  static constexpr int NSETS = (BM * BN >= 256 * 256) ? 1 : 2;
   static_assert(WM * WN == 4, "four waves per workgroup");
   static_assert(FM >= 1 && FN >= 1 && FM * WM * 32 == BM && FN * WN * 32 == BN, "tile shape");
   static_assert(!PAIRED || (FN % 2 == 0), "paired layout");
@@ -93,20 +114,23 @@ struct RowLoader {
   static constexpr int CPT = ROWS / 32;
   rsrc_t rs[2];
   uint32_t roff[CPT];
-  u32x4_t reg[CPT];
+  u32x4_t reg[2][CPT];  // two register sets: k-tile j lives in set j % 2
 
   static MOE_DEV int my_row(int i) { return (int)(threadIdx.x >> 3) + 32 * i; }
 
   MOE_DEV void prefetch(int) {}
+  template <int SET>
   MOE_DEV void load(int kt) {
     const uint32_t off = (uint32_t)(kt * KBYTES) + (threadIdx.x & 7) * 16;
 #pragma unroll
-    for (int i = 0; i < CPT; ++i) reg[i] = buf_load16(rs[(SPLIT && i >= CPT / 2) ? 1 : 0], roff[i] + off);
+    for (int i = 0; i < CPT; ++i) reg[SET][i] = buf_load16(rs[(SPLIT && i >= CPT / 2) ? 1 : 0], roff[i] + off);
   }
+  // chunks i with i % NPART == PART
+  template <int SET, int PART, int NPART>
   MOE_DEV void store(char* lds) const {
 #pragma unroll
-    for (int i = 0; i < CPT; ++i)
-      *(u32x4_t*)(lds + my_row(i) * LDS_ROW + (threadIdx.x & 7) * 16) = reg[i];
+    for (int i = PART; i < CPT; i += NPART)
+      *(u32x4_t*)(lds + my_row(i) * LDS_ROW + (threadIdx.x & 7) * 16) = reg[SET][i];
   }
 };
 
@@ -144,9 +168,9 @@ struct KRowLoader {
   Src src;
   int ncols;
   uint32_t offs[4];
-  float spre[4];      // scales fetched with the offsets
-  float sdat[4];      // scales of the loaded data
-  u32x4_t reg[NC][4];
+  float spre[4];         // scales fetched with the offsets
+  float sdat[2][4];      // scales of the loaded data, per register set
+  u32x4_t reg[2][NC][4];
 
   MOE_DEV int col(int c) const { return c * 128 + G::mc() * G::CW; }
 
@@ -158,32 +182,36 @@ struct KRowLoader {
       if constexpr (SCALED) spre[j] = offs[j] != OOB_OFF ? src.scale(kbase + j) : 0.0f;
     }
   }
+  template <int SET>
   MOE_DEV void load(int kt) {
     const rsrc_t r = src.rsrc(kt);
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
-      if constexpr (SCALED) sdat[j] = spre[j];
+      if constexpr (SCALED) sdat[SET][j] = spre[j];
 #pragma unroll
       for (int c = 0; c < NC; ++c) {
         const uint32_t o = col(c) < ncols ? offs[j] + (uint32_t)(col(c) * (int)sizeof(T)) : OOB_OFF;
-        reg[c][j] = buf_load16(r, o);
+        reg[SET][c][j] = buf_load16(r, o);
       }
     }
   }
+  // the register transpose writes a whole chunk column at once: all in part 0
+  template <int SET, int PART, int NPART>
   MOE_DEV void store(char* lds) const {
+    if constexpr (PART != 0) return;
 #pragma unroll
     for (int c = 0; c < NC; ++c) {
       if constexpr (sizeof(T) == 2) {
         u32x4_t r[4];
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
-          r[j] = reg[c][j];
+          r[j] = reg[SET][c][j];
           if constexpr (SCALED) {
 #pragma unroll
             for (int q = 0; q < 4; ++q) {
               const uint32_t v = r[j][q];
-              const uint32_t lo = f32_to_bf16(bf16_to_f32(v & 0xffffu) * sdat[j]);
-              const uint32_t hi = f32_to_bf16(bf16_to_f32(v >> 16) * sdat[j]);
+              const uint32_t lo = f32_to_bf16(bf16_to_f32(v & 0xffffu) * sdat[SET][j]);
+              const uint32_t hi = f32_to_bf16(bf16_to_f32(v >> 16) * sdat[SET][j]);
               r[j][q] = lo | (hi << 16);
             }
           }
@@ -204,8 +232,8 @@ struct KRowLoader {
         f32x4_t r[4];
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
-          r[j] = __builtin_bit_cast(f32x4_t, reg[c][j]);
-          if constexpr (SCALED) r[j] *= sdat[j];
+          r[j] = __builtin_bit_cast(f32x4_t, reg[SET][c][j]);
+          if constexpr (SCALED) r[j] *= sdat[SET][j];
         }
         char* base = lds + col(c) * LDS_ROW + G::kg() * 16;
 #pragma unroll
@@ -219,43 +247,169 @@ struct KRowLoader {
 };
 
 // ---------------------------------------------------------------------------
-// MFMA over one LDS stage.
+// KLoader<ROWS, Src, SCALED> (bf16): the same sources as KRowLoader, staged
+// k-major without any transpose: thread t copies the 16-byte chunk
+// (t % CPR) of k-rows t / CPR + RPP * i into LDS as is.  The transpose
+// happens in the LDS read that forms the MFMA operand.
 // ---------------------------------------------------------------------------
-template <class C>
-MOE_DEV void mma_stage(const char* stage, f32x16_t (&acc)[C::FM][C::FN], int wm, int wn) {
+template <int ROWS, class Src, bool SCALED>
+struct KLoader {
+  using G = KmGeom<ROWS>;
+  Src src;
+  int ncols;
+  uint32_t offs[G::NPASS];
+  float spre[G::NPASS];
+  float sdat[2][G::NPASS];
+  u32x4_t reg[2][G::NPASS];
+
+  static MOE_DEV int cc() { return (int)threadIdx.x % G::CPR; }
+  static MOE_DEV int kr(int i) { return (int)threadIdx.x / G::CPR + G::RPP * i; }
+
+  MOE_DEV void prefetch(int kt) {
+#pragma unroll
+    for (int i = 0; i < G::NPASS; ++i) {
+      offs[i] = src.row_off(kt * 64 + kr(i));
+      if constexpr (SCALED) spre[i] = offs[i] != OOB_OFF ? src.scale(kt * 64 + kr(i)) : 0.0f;
+    }
+  }
+  template <int SET>
+  MOE_DEV void load(int kt) {
+    const rsrc_t r = src.rsrc(kt);
+    const uint32_t co = cc() * 8 < ncols ? (uint32_t)cc() * 16 : OOB_OFF;
+#pragma unroll
+    for (int i = 0; i < G::NPASS; ++i) {
+      if constexpr (SCALED) sdat[SET][i] = spre[i];
+      reg[SET][i] = buf_load16(r, offs[i] + co);  // OOB_OFF plus a chunk offset stays out of range
+    }
+  }
+  template <int SET, int PART, int NPART>
+  MOE_DEV void store(char* lds) const {
+#pragma unroll
+    for (int i = PART; i < G::NPASS; i += NPART) {
+      u32x4_t v = reg[SET][i];
+      if constexpr (SCALED) {
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          const uint32_t lo = f32_to_bf16(bf16_to_f32(v[q] & 0xffffu) * sdat[SET][i]);
+          const uint32_t hi = f32_to_bf16(bf16_to_f32(v[q] >> 16) * sdat[SET][i]);
+          v[q] = lo | (hi << 16);
+        }
+      }
+      *(u32x4_t*)(lds + kr(i) * G::PITCH + cc() * 16) = v;
+    }
+  }
+};
+
+// ---------------------------------------------------------------------------
+// MFMA over one LDS stage.
+//
+// k-major operands: ds_read_b64_tr_b16 works on groups of 16 lanes; lane
+// 4q + s of a group receives element s of the 8-byte chunks addressed by
+// lanes q, q + 4, q + 8 and q + 12 of the group.  Lane j therefore points at
+// k-row kb + j / 4, columns mb + 4 (j % 4) .. + 3, and every lane ends up with
+// four consecutive k of one row: lanes 0-15 rows 0-15 and lanes 16-31 rows
+// 16-31 (k 0-3 of the step, then k 4-7 from the next four k-rows), lanes
+// 32-63 the same rows for k 8-15 -- the 32x32x16 operand layout.
+// ---------------------------------------------------------------------------
+typedef short s16x4_t __attribute__((ext_vector_type(4)));
+
+MOE_DEV int km_lane_off(int pitch) {
+  const int l = lane_id(), g = l >> 4, j = l & 15;
+  return (8 * (g >> 1) + (j >> 2)) * pitch + (16 * (g & 1) + 4 * (j & 3)) * 2;
+}
+MOE_DEV u32x4_t km_read(const char* p, int pitch) {
+  typedef __attribute__((address_space(3))) s16x4_t lds_s4;
+  const s16x4_t lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s4*)p);
+  const s16x4_t hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s4*)(p + 4 * pitch));
+  const u32x2_t a = __builtin_bit_cast(u32x2_t, lo), b = __builtin_bit_cast(u32x2_t, hi);
+  return u32x4_t{a[0], a[1], b[0], b[1]};
+}
+
+template <bool KM, int ROWS, class M>
+struct OperandReader {
+  // lane base for [row][k] staging: row l % 32, k-group l / 32
+  static MOE_DEV const char* base(const char* op, int eb) {
+    if constexpr (KM) return op + km_lane_off(KmGeom<ROWS>::PITCH);
+    else return op + (lane_id() & 31) * LDS_ROW + (lane_id() >> 5) * (8 * eb);
+  }
+  // fragment of tile rows row0 .. row0+31, k-step s (16 k)
+  static MOE_DEV typename M::Frag read(const char* b, int row0, int s, int step_bytes) {
+    if constexpr (KM) {
+      typename M::Frag f;
+      f.v = km_read(b + s * 16 * KmGeom<ROWS>::PITCH + row0 * 2, KmGeom<ROWS>::PITCH);
+      return f;
+    } else {
+      return M::lds_read(b + row0 * LDS_ROW + s * step_bytes);
+    }
+  }
+};
+// compile-time loop: f(std::integral_constant<int, I>) for I = 0 .. N-1
+template <int N, int I = 0, class F>
+MOE_DEV void static_for(F&& f) {
+  if constexpr (I < N) {
+    f(std::integral_constant<int, I>{});
+    static_for<N, I + 1>(static_cast<F&&>(f));
+  }
+}
+
+// MFMAs of one LDS stage; after the MFMAs of k-step s >= FIRST, share
+// s - FIRST of the next k-tile (register set SET of the loaders) is written
+// to the other stage.
+template <class C, int SET, int FIRST, class LA, class LB>
+MOE_DEV void mma_stage(const char* stage, f32x16_t (&acc)[C::FM][C::FN], int wm, int wn, const LA& la,
+                       const LB& lb, char* next) {
   using M = Mfma<typename C::T>;
-  const int l = lane_id();
-  constexpr int STEP = 16 * C::EB;            // bytes of k per MFMA step
+  using RA = OperandReader<C::AKM, C::BM, M>;
+  using RB = OperandReader<C::BKM, C::BN, M>;
+  constexpr int STEP = 16 * C::EB;            // bytes of k per MFMA step ([row][k] staging)
   constexpr int NSTEP = KBYTES / STEP;
-  const char* a_base = stage + (l & 31) * LDS_ROW + (l >> 5) * (8 * C::EB);
-  const char* b_base = stage + C::A_BYTES + (l & 31) * LDS_ROW + (l >> 5) * (8 * C::EB);
+  const char* a_base = RA::base(stage, C::EB);
+  const char* b_base = RB::base(stage + C::A_BYTES, C::EB);
   // operand fragments are read one k-step ahead of the MFMAs that use them;
   // the scheduling barrier keeps the compiler from hoisting every step's
   // reads (and their registers) to the top of the stage
   typename M::Frag a[2][C::FM], b[2][C::FN];
 #pragma unroll
-  for (int fm = 0; fm < C::FM; ++fm) a[0][fm] = M::lds_read(a_base + C::a_row0(wm, fm) * LDS_ROW);
+  for (int fm = 0; fm < C::FM; ++fm) a[0][fm] = RA::read(a_base, C::a_row0(wm, fm), 0, STEP);
 #pragma unroll
-  for (int fn = 0; fn < C::FN; ++fn) b[0][fn] = M::lds_read(b_base + C::b_row0(wn, fn) * LDS_ROW);
+  for (int fn = 0; fn < C::FN; ++fn) b[0][fn] = RB::read(b_base, C::b_row0(wn, fn), 0, STEP);
+  static_for<NSTEP>([&](auto sc) {
+    constexpr int s = decltype(sc)::value;
+    constexpr int cur = s & 1;
+    if constexpr (s + 1 < NSTEP) {
 #pragma unroll
-  for (int s = 0; s < NSTEP; ++s) {
-    const int cur = s & 1;
-    if (s + 1 < NSTEP) {
+      for (int fm = 0; fm < C::FM; ++fm) a[cur ^ 1][fm] = RA::read(a_base, C::a_row0(wm, fm), s + 1, STEP);
 #pragma unroll
-      for (int fm = 0; fm < C::FM; ++fm)
-        a[cur ^ 1][fm] = M::lds_read(a_base + C::a_row0(wm, fm) * LDS_ROW + (s + 1) * STEP);
-#pragma unroll
-      for (int fn = 0; fn < C::FN; ++fn)
-        b[cur ^ 1][fn] = M::lds_read(b_base + C::b_row0(wn, fn) * LDS_ROW + (s + 1) * STEP);
+      for (int fn = 0; fn < C::FN; ++fn) b[cur ^ 1][fn] = RB::read(b_base, C::b_row0(wn, fn), s + 1, STEP);
     }
 #pragma unroll
     for (int fm = 0; fm < C::FM; ++fm)
 #pragma unroll
       for (int fn = 0; fn < C::FN; ++fn) M::mma(acc[fm][fn], a[cur][fm], b[cur][fn]);
+    if constexpr (s >= FIRST) {
+      la.template store<SET, s - FIRST, NSTEP - FIRST>(next);
+      lb.template store<SET, s - FIRST, NSTEP - FIRST>(next + C::A_BYTES);
+    }
     __builtin_amdgcn_sched_barrier(0);
-  }
+  });
 }
 
+// Main loop.  LDS holds two stages, one barrier per k-tile.
+//
+// Two register sets (NSETS = 2): at the top of iteration kt, k-tile kt sits
+// in stage kt % 2 and k-tile kt + 1 in register set (kt + 1) % 2; k-tile
+// kt + 2 is loaded into the free set, and k-tile kt + 1 goes to the other
+// stage piecewise between the MFMAs of kt.  The global loads have a whole
+// iteration to land.
+//
+// One register set (NSETS = 1): k-tile kt + 1 is loaded at the top of
+// iteration kt and written to the other stage between the MFMAs of the
+// second half of kt's k-steps.
+//
+// Loads and index fetches run past the last k-tile unconditionally
+// (out-of-range rows, columns and k read zeros or unused in-range data, never
+// consumed), so every iteration has the same loads in flight and the
+// compiler's waits stay exact.
 template <class C, class LA, class LB>
 MOE_DEV void gemm_mainloop(LA& la, LB& lb, int nk, char* smem, f32x16_t (&acc)[C::FM][C::FN], int wm, int wn) {
 #pragma unroll
@@ -265,35 +419,54 @@ MOE_DEV void gemm_mainloop(LA& la, LB& lb, int nk, char* smem, f32x16_t (&acc)[C
 #pragma unroll
       for (int r = 0; r < 16; ++r) acc[fm][fn][r] = 0.0f;
   if (nk <= 0) return;
-  // prologue: tile 0 into stage 0, indices of tile 1 fetched
+  constexpr int NSTEP = KBYTES / (16 * C::EB);
   la.prefetch(0);
   lb.prefetch(0);
-  la.load(0);
-  lb.load(0);
-  if (nk > 1) {
-    la.prefetch(1);
-    lb.prefetch(1);
+  la.template load<0>(0);
+  lb.template load<0>(0);
+  la.prefetch(1);
+  lb.prefetch(1);
+  if constexpr (C::NSETS == 2) {
+    la.template load<1>(1);
+    lb.template load<1>(1);
+    la.prefetch(2);
+    lb.prefetch(2);
   }
-  la.store(smem);
-  lb.store(smem + C::A_BYTES);
+  la.template store<0, 0, 1>(smem);
+  lb.template store<0, 0, 1>(smem + C::A_BYTES);
   __syncthreads();
-  for (int kt = 0; kt < nk; ++kt) {
-    const int cur = kt & 1;
-    // loads of k-tile kt+1 (and indices of kt+2) overlap the MFMAs of kt
-    if (kt + 1 < nk) {
-      la.load(kt + 1);
-      lb.load(kt + 1);
+  if constexpr (C::NSETS == 2) {
+    // two k-tiles per iteration, the odd last one after the loop: a loop
+    // without an exit in the middle keeps the accumulators in place
+    int kt = 0;
+    for (; kt + 1 < nk; kt += 2) {
+      la.template load<0>(kt + 2);
+      lb.template load<0>(kt + 2);
+      la.prefetch(kt + 3);
+      lb.prefetch(kt + 3);
+      mma_stage<C, 1, 0>(smem, acc, wm, wn, la, lb, smem + C::STAGE);
+      __syncthreads();
+      la.template load<1>(kt + 3);
+      lb.template load<1>(kt + 3);
+      la.prefetch(kt + 4);
+      lb.prefetch(kt + 4);
+      mma_stage<C, 0, 0>(smem + C::STAGE, acc, wm, wn, la, lb, smem);
+      __syncthreads();
     }
-    if (kt + 2 < nk) {
+    if (kt < nk) {
+      mma_stage<C, 1, 0>(smem, acc, wm, wn, la, lb, smem + C::STAGE);
+      __syncthreads();
+    }
+  } else {
+    for (int kt = 0; kt < nk; ++kt) {
+      const int cur = kt & 1;
+      la.template load<0>(kt + 1);
+      lb.template load<0>(kt + 1);
       la.prefetch(kt + 2);
       lb.prefetch(kt + 2);
+      mma_stage<C, 0, NSTEP / 2>(smem + cur * C::STAGE, acc, wm, wn, la, lb, smem + (cur ^ 1) * C::STAGE);
+      __syncthreads();
     }
-    mma_stage<C>(smem + cur * C::STAGE, acc, wm, wn);
-    if (kt + 1 < nk) {
-      la.store(smem + (cur ^ 1) * C::STAGE);
-      lb.store(smem + (cur ^ 1) * C::STAGE + C::A_BYTES);
-    }
-    __syncthreads();
   }
 }
 
