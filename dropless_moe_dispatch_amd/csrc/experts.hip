@@ -29,22 +29,28 @@ namespace moe {
 template <typename T> MOE_DEV float ld_f(const T* p) { return ElemT<T>::load(p); }
 template <typename T> MOE_DEV void st_f(T* p, float v) { ElemT<T>::store(p, v); }
 
-// Two tile shapes: 128 x 128 (64 x 64 per wave, two workgroups per CU) and
-// 256 x 256 (128 x 128 per wave, one workgroup per CU, accumulators in
-// AGPRs).  The host picks one per kernel from the shape: the large tile
-// halves the LDS traffic per MFMA and pays off when the reduction is long;
-// the small one keeps two workgroups per CU, which hides epilogues and the
-// ordered combine's waits.
+// The host picks a tile per kernel and shape (128 x 128 or 256 x 256, see
+// XCfg below); the folds always use 128 x 128.
 template <typename TIN, int B> using GCfg = Cfg<TIN, B, B, 2, 2>;
-template <typename TIN, int B> using PCfg = Cfg<TIN, B, B, 2, 2, true>;
 // Operands whose source is k-major (weights read as [k][n], activations
 // reduced over rows) are staged k-major and read with the LDS transpose in
 // bf16; fp32 operands are transposed in registers (KRowLoader).
 template <typename TIN> constexpr bool kTr = sizeof(TIN) == 2;
-template <typename TIN, int B, bool AK, bool BK>
-using KCfg = Cfg<TIN, B, B, 2, 2, false, AK && kTr<TIN>, BK && kTr<TIN>>;
+// Tile configurations.  128 x 128: four waves of 64 x 64, two workgroups per
+// CU.  256 x 256 in bf16: eight waves of 64 x 128, one workgroup per CU and
+// two waves per SIMD (half the operand traffic per MFMA of the small tile,
+// with a second wave per SIMD to cover latencies); in fp32 four waves of
+// 128 x 128.  AK / BK: operand staged k-major (bf16 only).
+template <typename TIN, int B, bool PAIRED, bool AK, bool BK>
+using XCfg = Cfg<TIN, B, B, (B == TILE_L && kTr<TIN>) ? 4 : 2, 2, PAIRED, AK && kTr<TIN>, BK && kTr<TIN>>;
+template <typename TIN, int B, bool AK, bool BK> using KCfg = XCfg<TIN, B, false, AK, BK>;
 template <class C, bool KM, int ROWS, class Src, bool SCALED>
-using KSrcLoader = std::conditional_t<KM, KLoader<ROWS, Src, SCALED>, KRowLoader<typename C::T, ROWS, Src, SCALED>>;
+struct KSrcSel {
+  static_assert(KM || C::NT == NTHREADS, "the register transpose assumes four waves");
+  using type = std::conditional_t<KM, KLoader<ROWS, Src, SCALED, C::NT>, KRowLoader<typename C::T, ROWS, Src, SCALED>>;
+};
+template <class C, bool KM, int ROWS, class Src, bool SCALED>
+using KSrcLoader = typename KSrcSel<C, KM, ROWS, Src, SCALED>::type;
 
 // MOE_DISPATCH_TILE=128|256 forces one tile for every expert GEMM (tuning aid).
 static int forced_tile() {
@@ -65,7 +71,7 @@ static bool pick_large(bool auto_choice) {
 // Forward gate/up: M = rows of expert e, N = 128 gate + 128 up columns, K = d.
 // ===========================================================================
 template <class C>
-__global__ __launch_bounds__(NTHREADS, C::WAVES_PER_EU) void gate_up_kernel(
+__global__ __launch_bounds__(C::NT, C::WAVES_PER_EU) void gate_up_kernel(
     const typename C::T* __restrict__ x, const int32_t* __restrict__ offsets, const int32_t* __restrict__ eti,
     const int32_t* __restrict__ mb_off, const typename C::T* __restrict__ w_gate,
     const typename C::T* __restrict__ w_up, typename C::T* __restrict__ h_ab, typename C::T* __restrict__ y_swi,
@@ -81,19 +87,21 @@ __global__ __launch_bounds__(NTHREADS, C::WAVES_PER_EU) void gate_up_kernel(
   const int wave = threadIdx.x >> 6, wm = wave / C::WN, wn = wave % C::WN;
   const uint32_t ldx = (uint32_t)d * sizeof(TIN);
   const int j0 = nb * HB;  // first gate/up column of this tile
-  RowLoader<C::BM> la;
-  RowLoader<C::BN, true> lb;   // rows [0,HB) gate, [HB,BN) up
+  using LA = RowLoader<C::BM, false, C::NT>;
+  using LB = RowLoader<C::BN, true, C::NT>;  // rows [0,HB) gate, [HB,BN) up
+  LA la;
+  LB lb;
   la.rs[0] = make_rsrc(x, (size_t)T * ldx);
 #pragma unroll
-  for (int i = 0; i < RowLoader<C::BM>::CPT; ++i) {
-    const int p = rt.r0 + RowLoader<C::BM>::my_row(i);
+  for (int i = 0; i < LA::CPT; ++i) {
+    const int p = rt.r0 + LA::my_row(i);
     la.roff[i] = p < rt.r1 ? (uint32_t)eti[p] * ldx : OOB_OFF;
   }
   lb.rs[0] = make_rsrc(w_gate + (size_t)rt.e * h * d, (size_t)h * ldx);
   lb.rs[1] = make_rsrc(w_up + (size_t)rt.e * h * d, (size_t)h * ldx);
 #pragma unroll
-  for (int i = 0; i < RowLoader<C::BN>::CPT; ++i) {
-    const int j = j0 + (RowLoader<C::BN>::my_row(i) % HB);
+  for (int i = 0; i < LB::CPT; ++i) {
+    const int j = j0 + (LB::my_row(i) % HB);
     lb.roff[i] = j < h ? (uint32_t)j * ldx : OOB_OFF;
   }
   f32x16_t acc[C::FM][C::FN];
@@ -122,11 +130,11 @@ template <typename TIN, int B>
 static hipError_t gate_up_t(const Shape& s, const void* x, const int32_t* offsets, const int32_t* eti,
                             const void* w_gate, const void* w_up, void* h_ab, void* y_swi, const ExpertWs& ws,
                             hipStream_t st) {
-  using C = PCfg<TIN, B>;
+  using C = XCfg<TIN, B, true, false, false>;
   const int nbn = col_blocks(s.h, C::BN / 2);
   long long nblk = max_row_blocks(s, B) * nbn;
   nblk = (nblk + 7) / 8 * 8;
-  gate_up_kernel<C><<<dim3((unsigned)nblk), dim3(NTHREADS), 0, st>>>(
+  gate_up_kernel<C><<<dim3((unsigned)nblk), dim3(C::NT), 0, st>>>(
       (const TIN*)x, offsets, eti, ws.tile_map(B), (const TIN*)w_gate, (const TIN*)w_up, (TIN*)h_ab, (TIN*)y_swi,
       s.T, s.d, s.E, s.h, nbn, (int)nblk);
   return hipGetLastError();
@@ -136,8 +144,9 @@ hipError_t launch_gate_up(const Shape& s, const void* x, const int32_t* offsets,
                           const void* w_gate, const void* w_up, void* h_ab, void* y_swi, const ExpertWs& ws,
                           hipStream_t st) {
   timing_mark(st, "gate_up", true);
-  // measured on MI355X: the large tile wins only for the longest reductions
-  const bool big = pick_large(s.d >= 6144);
+  // measured on MI355X: the large tile wins from d = 4096 on (the small one
+  // wastes less on partial row tiles for short reductions)
+  const bool big = pick_large(s.d >= 4096);
   hipError_t e;
   if (s.bf16)
     e = big ? gate_up_t<bf16_t, TILE_L>(s, x, offsets, eti, w_gate, w_up, h_ab, y_swi, ws, st)
@@ -204,7 +213,7 @@ MOE_DEV void fold_epilogue(const f32x16_t (&acc)[C::FM][C::FN], const RowTile& r
                            const int32_t* __restrict__ rank_pos, int K, int d, int32_t* turn,
                            float* __restrict__ accws, typename C::T* __restrict__ out, int32_t* counters,
                            int spin_limit, char* smem) {
-  static_assert(C::BM == 128 && C::BN == 128, "the fold parks a 128 x 128 tile");
+  static_assert(C::BM == 128 && C::BN == 128 && C::NT == NTHREADS, "the fold parks a 128 x 128 tile, four waves");
   static_assert(C::BM * FOLD_LD * 4 + 3 * C::BM * 4 <= C::LDS_BYTES, "parked tile fits the LDS stages");
   float* s_c = (float*)smem;
   int* s_t = (int*)(smem + C::BM * FOLD_LD * 4);
@@ -302,7 +311,7 @@ MOE_DEV int claim_ticket(int32_t* counters, char* smem) {
 // Down projection + combine: M = rows of expert e, N = TILE output columns, K = h.
 // ===========================================================================
 template <class C>
-__global__ __launch_bounds__(NTHREADS, C::WAVES_PER_EU) void down_combine_kernel(
+__global__ __launch_bounds__(C::NT, C::WAVES_PER_EU) void down_combine_kernel(
     const typename C::T* __restrict__ y_swi, const typename C::T* __restrict__ w_down,
     const int32_t* __restrict__ offsets, const int32_t* __restrict__ eti, const int32_t* __restrict__ mb_off,
     const float* __restrict__ w_pos, const int32_t* __restrict__ rank_pos, int32_t* turn, float* accws,
@@ -316,18 +325,20 @@ __global__ __launch_bounds__(NTHREADS, C::WAVES_PER_EU) void down_combine_kernel
   const RowTile rt = decode_row_tile<C::BM>(mb_off, offsets, E, g);
   const int wave = threadIdx.x >> 6, wm = wave / C::WN, wn = wave % C::WN;
   const uint32_t ldy = (uint32_t)h * sizeof(TIN);
-  RowLoader<C::BM> la;
-  RowLoader<C::BN> lb;
+  using LA = RowLoader<C::BM, false, C::NT>;
+  using LB = RowLoader<C::BN, false, C::NT>;
+  LA la;
+  LB lb;
   la.rs[0] = make_rsrc(y_swi + (size_t)rt.r0 * h, (size_t)(rt.r1 - rt.r0) * ldy);
 #pragma unroll
-  for (int i = 0; i < RowLoader<C::BM>::CPT; ++i) {
-    const int r = RowLoader<C::BM>::my_row(i);
+  for (int i = 0; i < LA::CPT; ++i) {
+    const int r = LA::my_row(i);
     la.roff[i] = rt.r0 + r < rt.r1 ? (uint32_t)r * ldy : OOB_OFF;
   }
   lb.rs[0] = make_rsrc(w_down + (size_t)rt.e * d * h, (size_t)d * ldy);
 #pragma unroll
-  for (int i = 0; i < RowLoader<C::BN>::CPT; ++i) {
-    const int n = nb * C::BN + RowLoader<C::BN>::my_row(i);
+  for (int i = 0; i < LB::CPT; ++i) {
+    const int n = nb * C::BN + LB::my_row(i);
     lb.roff[i] = n < d ? (uint32_t)n * ldy : OOB_OFF;
   }
   f32x16_t acc[C::FM][C::FN];
@@ -341,7 +352,7 @@ static hipError_t down_combine_t(const Shape& s, const void* y_swi, const void* 
                                  const int32_t* eti, void* out, const ExpertWs& ws, int spin_limit, hipStream_t st) {
   using C = GCfg<TIN, B>;
   const long long nblk = max_row_blocks(s, B) * col_blocks(s.d, B);
-  down_combine_kernel<C><<<dim3((unsigned)nblk), dim3(NTHREADS), 0, st>>>(
+  down_combine_kernel<C><<<dim3((unsigned)nblk), dim3(C::NT), 0, st>>>(
       (const TIN*)y_swi, (const TIN*)w_down, offsets, eti, ws.tile_map(B), ws.w_pos, ws.rank_pos, ws.turn, ws.acc,
       (TIN*)out, ws.counters, s.d, s.E, s.K, s.h, spin_limit);
   return hipGetLastError();
@@ -409,7 +420,7 @@ MOE_DEV int min_i(int a, int b) { return a < b ? a : b; }
 
 // dH kernel: dA' = dO W_down (M rows of e, N = TILE of h, K = d) + SwiGLU backward
 template <class C>
-__global__ __launch_bounds__(NTHREADS, C::WAVES_PER_EU) void dh_kernel(
+__global__ __launch_bounds__(C::NT, C::WAVES_PER_EU) void dh_kernel(
     const typename C::T* __restrict__ dout, const typename C::T* __restrict__ w_down,
     const typename C::T* __restrict__ h_ab, const typename C::T* __restrict__ y_swi,
     const int32_t* __restrict__ offsets, const int32_t* __restrict__ eti, const int32_t* __restrict__ mb_off,
@@ -423,11 +434,12 @@ __global__ __launch_bounds__(NTHREADS, C::WAVES_PER_EU) void dh_kernel(
   const RowTile rt = decode_row_tile<C::BM>(mb_off, offsets, E, g);
   const int wave = threadIdx.x >> 6, wm = wave / C::WN, wn = wave % C::WN;
   const uint32_t ldd = (uint32_t)d * sizeof(TIN);
-  RowLoader<C::BM> la;
+  using LA = RowLoader<C::BM, false, C::NT>;
+  LA la;
   la.rs[0] = make_rsrc(dout, (size_t)T * ldd);
 #pragma unroll
-  for (int i = 0; i < RowLoader<C::BM>::CPT; ++i) {
-    const int p = rt.r0 + RowLoader<C::BM>::my_row(i);
+  for (int i = 0; i < LA::CPT; ++i) {
+    const int p = rt.r0 + LA::my_row(i);
     la.roff[i] = p < rt.r1 ? (uint32_t)eti[p] * ldd : OOB_OFF;
   }
   KSrcLoader<C, C::BKM, C::BN, SrcWeightKN<TIN>, false> lb;
@@ -486,7 +498,7 @@ __global__ __launch_bounds__(NTHREADS, C::WAVES_PER_EU) void dh_kernel(
     }
   }
   __syncthreads();
-  for (int i = threadIdx.x; i < rt.r1 - rt.r0; i += NTHREADS) {
+  for (int i = threadIdx.x; i < rt.r1 - rt.r0; i += C::NT) {
     float v = 0.0f;
 #pragma unroll
     for (int w = 0; w < C::WN; ++w) v += s_ds[w * C::BM + i];
@@ -573,7 +585,7 @@ __global__ __launch_bounds__(256) void dwg_kernel(const TIN* __restrict__ x, con
 // operand and held in the activation dtype, as the SonicMoE analysis page
 // (sec. 3.4.1) defines A' = Broadcast(s) A for the dW2 grouped GEMM.
 template <class C>
-__global__ __launch_bounds__(NTHREADS, C::WAVES_PER_EU) void dw_down_kernel(
+__global__ __launch_bounds__(C::NT, C::WAVES_PER_EU) void dw_down_kernel(
     const typename C::T* __restrict__ dout, const typename C::T* __restrict__ y_swi,
     const int32_t* __restrict__ offsets, const int32_t* __restrict__ eti, const float* __restrict__ w_pos,
     float* __restrict__ dw_down, int T, int d, int h) {
@@ -620,7 +632,7 @@ __global__ __launch_bounds__(NTHREADS, C::WAVES_PER_EU) void dw_down_kernel(
 
 // dW_gate / dW_up [e] (h x d) = sum_p dH[p]^T x[eti[p]]: M = 2h, N = d, K = rows of e
 template <class C>
-__global__ __launch_bounds__(NTHREADS, C::WAVES_PER_EU) void dw_gate_up_kernel(
+__global__ __launch_bounds__(C::NT, C::WAVES_PER_EU) void dw_gate_up_kernel(
     const typename C::T* __restrict__ dh, const typename C::T* __restrict__ x, const int32_t* __restrict__ offsets,
     const int32_t* __restrict__ eti, float* __restrict__ dw_gate, float* __restrict__ dw_up, int T, int d, int h) {
   __shared__ __attribute__((aligned(16))) char smem[C::LDS_BYTES];
@@ -666,7 +678,7 @@ __global__ __launch_bounds__(NTHREADS, C::WAVES_PER_EU) void dw_gate_up_kernel(
 
 // dX~ = dH [W_gate; W_up] (M rows of e, N = TILE of d, K = 2h) + ordered fold into dX
 template <class C>
-__global__ __launch_bounds__(NTHREADS, C::WAVES_PER_EU) void dx_fold_kernel(
+__global__ __launch_bounds__(C::NT, C::WAVES_PER_EU) void dx_fold_kernel(
     const typename C::T* __restrict__ dh, const typename C::T* __restrict__ w_gate,
     const typename C::T* __restrict__ w_up, const int32_t* __restrict__ offsets, const int32_t* __restrict__ eti,
     const int32_t* __restrict__ mb_off, const int32_t* __restrict__ rank_pos, int32_t* turn, float* accws,
@@ -680,11 +692,12 @@ __global__ __launch_bounds__(NTHREADS, C::WAVES_PER_EU) void dx_fold_kernel(
   const RowTile rt = decode_row_tile<C::BM>(mb_off, offsets, E, g);
   const int wave = threadIdx.x >> 6, wm = wave / C::WN, wn = wave % C::WN;
   const uint32_t ldh = (uint32_t)(2 * h) * sizeof(TIN);
-  RowLoader<C::BM> la;
+  using LA = RowLoader<C::BM, false, C::NT>;
+  LA la;
   la.rs[0] = make_rsrc(dh + (size_t)rt.r0 * 2 * h, (size_t)(rt.r1 - rt.r0) * ldh);
 #pragma unroll
-  for (int i = 0; i < RowLoader<C::BM>::CPT; ++i) {
-    const int r = RowLoader<C::BM>::my_row(i);
+  for (int i = 0; i < LA::CPT; ++i) {
+    const int r = LA::my_row(i);
     la.roff[i] = rt.r0 + r < rt.r1 ? (uint32_t)r * ldh : OOB_OFF;
   }
   KSrcLoader<C, C::BKM, C::BN, SrcWeightKN2<TIN>, false> lb;
@@ -707,7 +720,7 @@ static void launch_dh(const Shape& s, const void* dout, const void* w_down, cons
   using C = KCfg<TIN, B, false, true>;
   const int nbn = col_blocks(s.h, B);
   const long long nblk = (max_row_blocks(s, B) * nbn + 7) / 8 * 8;
-  dh_kernel<C><<<dim3((unsigned)nblk), dim3(NTHREADS), 0, st>>>(
+  dh_kernel<C><<<dim3((unsigned)nblk), dim3(C::NT), 0, st>>>(
       (const TIN*)dout, (const TIN*)w_down, (const TIN*)h_ab, (const TIN*)y_swi, offsets, eti, ws.tile_map(B),
       ws.w_pos, (TIN*)ws.dh, ws.ds_part, s.T, s.d, s.E, s.h, nbn, (int)nblk);
 }
@@ -717,7 +730,7 @@ static void launch_dx_fold(const Shape& s, const void* w_gate, const void* w_up,
                            const int32_t* eti, void* dx, const ExpertWs& ws, int spin_limit, hipStream_t st) {
   using C = KCfg<TIN, B, false, true>;
   const long long nblk = max_row_blocks(s, B) * col_blocks(s.d, B);
-  dx_fold_kernel<C><<<dim3((unsigned)nblk), dim3(NTHREADS), 0, st>>>(
+  dx_fold_kernel<C><<<dim3((unsigned)nblk), dim3(C::NT), 0, st>>>(
       (const TIN*)ws.dh, (const TIN*)w_gate, (const TIN*)w_up, offsets, eti, ws.tile_map(B), ws.rank_pos, ws.turn,
       ws.acc, (TIN*)dx, ws.counters, s.d, s.E, s.K, s.h, spin_limit);
 }
@@ -755,13 +768,13 @@ static hipError_t backward_t(const Shape& s, const void* dout, const void* x, co
   if ((err = hipGetLastError()) != hipSuccess) return err;
 
   timing_mark(st, "dw_down", true);
-  dw_down_kernel<CL><<<dim3(col_blocks(s.d, CL::BM) * col_blocks(s.h, CL::BN), s.E), dim3(NTHREADS), 0, st>>>(
+  dw_down_kernel<CL><<<dim3(col_blocks(s.d, CL::BM) * col_blocks(s.h, CL::BN), s.E), dim3(CL::NT), 0, st>>>(
       (const TIN*)dout, (const TIN*)y_swi, offsets, eti, ws.w_pos, dw_down, s.T, s.d, s.h);
   timing_mark(st, "dw_down", false);
   if ((err = hipGetLastError()) != hipSuccess) return err;
 
   timing_mark(st, "dw_gate_up", true);
-  dw_gate_up_kernel<CL><<<dim3(col_blocks(2 * s.h, CL::BM) * col_blocks(s.d, CL::BN), s.E), dim3(NTHREADS), 0,
+  dw_gate_up_kernel<CL><<<dim3(col_blocks(2 * s.h, CL::BM) * col_blocks(s.d, CL::BN), s.E), dim3(CL::NT), 0,
                           st>>>((const TIN*)ws.dh, (const TIN*)x, offsets, eti, dw_gate, dw_up, s.T, s.d, s.h);
   timing_mark(st, "dw_gate_up", false);
   if ((err = hipGetLastError()) != hipSuccess) return err;

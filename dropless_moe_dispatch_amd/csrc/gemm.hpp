@@ -37,17 +37,17 @@ constexpr int KBYTES = 128;
 // elements, each k-row padded to PITCH bytes; MFMA operands are read from it
 // with the LDS transpose read (ds_read_b64_tr_b16).
 constexpr int KM_PAD = 64;  // 64 banks: the four k-rows of a transpose read land on disjoint banks
-template <int ROWS>
+template <int ROWS, int NT = NTHREADS>
 struct KmGeom {
   static constexpr int PITCH = ROWS * 2 + KM_PAD;
   static constexpr int BYTES = 64 * PITCH;
   static constexpr int CPR = ROWS / 8;          // 16-byte chunks per k-row
-  static constexpr int RPP = NTHREADS / CPR;    // k-rows per pass of the workgroup
+  static constexpr int RPP = NT / CPR;          // k-rows per pass of the workgroup
   static constexpr int NPASS = 64 / RPP;        // chunks per thread per stage
 };
 
 template <typename TIN, int BM_, int BN_, int WM_, int WN_, bool PAIRED_ = false, bool AKM_ = false,
-          bool BKM_ = false>
+          bool BKM_ = false, int NSETS_ = 0>
 struct Cfg {
   using T = TIN;
   static constexpr int BM = BM_, BN = BN_, WM = WM_, WN = WN_;
@@ -65,10 +65,13 @@ struct Cfg {
   static constexpr int B_BYTES = BKM ? KmGeom<BN>::BYTES : BN * LDS_ROW;
   static constexpr int STAGE = A_BYTES + B_BYTES;
   static constexpr int LDS_BYTES = 2 * STAGE;
-  static constexpr int WAVES_PER_EU = (BM * BN >= 256 * 256) ? 1 : 2;
+  // workgroup size follows the wave grid: 4 waves, or 8 for a 256 x 256 tile
+  // with 128 x 64 (or 64 x 128) per wave and two waves per SIMD
+  static constexpr int NT = WM * WN * 64;
+  static constexpr int WAVES_PER_EU = (BM * BN >= 256 * 256) ? NT / 256 : 2;
   // register sets for staging global loads (the 256 x 256 tile has no room for two)
-  static constexpr int NSETS = (BM * BN >= 256 * 256) ? 1 : 2;
-  static_assert(WM * WN == 4, "four waves per workgroup");
+  static constexpr int NSETS = NSETS_ ? NSETS_ : (BM * BN >= 256 * 256) ? 1 : 2;
+  static_assert(WM * WN == 4 || (WM * WN == 8 && BM * BN >= 256 * 256), "four or eight waves per workgroup");
   static_assert(FM >= 1 && FN >= 1 && FM * WM * 32 == BM && FN * WN * 32 == BN, "tile shape");
   static_assert(!PAIRED || (FN % 2 == 0), "paired layout");
 
@@ -107,16 +110,17 @@ MOE_DEV u32x4_t buf_load16(rsrc_t r, uint32_t off) {
 // The caller sets rs[0] (and rs[1] for the second half of the rows when
 // SPLIT) and roff[i], the byte offset of the row's first element, or OOB_OFF
 // for a row outside the problem, for the rows this thread owns:
-// row = (tid >> 3) + 32*i, i < ROWS/32.
+// row = (tid >> 3) + (NT/8)*i, i < CPT.
 // ---------------------------------------------------------------------------
-template <int ROWS, bool SPLIT = false>
+template <int ROWS, bool SPLIT = false, int NT = NTHREADS>
 struct RowLoader {
-  static constexpr int CPT = ROWS / 32;
+  static constexpr int RPP = NT / 8;     // rows per pass of the workgroup
+  static constexpr int CPT = ROWS / RPP;
   rsrc_t rs[2];
   uint32_t roff[CPT];
   u32x4_t reg[2][CPT];  // two register sets: k-tile j lives in set j % 2
 
-  static MOE_DEV int my_row(int i) { return (int)(threadIdx.x >> 3) + 32 * i; }
+  static MOE_DEV int my_row(int i) { return (int)(threadIdx.x >> 3) + RPP * i; }
 
   MOE_DEV void prefetch(int) {}
   template <int SET>
@@ -252,9 +256,9 @@ struct KRowLoader {
 // (t % CPR) of k-rows t / CPR + RPP * i into LDS as is.  The transpose
 // happens in the LDS read that forms the MFMA operand.
 // ---------------------------------------------------------------------------
-template <int ROWS, class Src, bool SCALED>
+template <int ROWS, class Src, bool SCALED, int NT = NTHREADS>
 struct KLoader {
-  using G = KmGeom<ROWS>;
+  using G = KmGeom<ROWS, NT>;
   Src src;
   int ncols;
   uint32_t offs[G::NPASS];
