@@ -247,15 +247,25 @@ def moe_forward(x, ids, w, w_gate, w_up, w_down, dtype="bf16", only_experts=None
 # ---------------------------------------------------------------------------
 
 
-def moe_backward(dy, x, wg, ids, w, w_gate, w_up, w_down, fwd, z, dtype="bf16", only_experts=None):
+def moe_backward(dy, x, wg, ids, w, w_gate, w_up, w_down, fwd, z, dtype="bf16", only_experts=None,
+                 saved="aby"):
     """Backward pass.  ``z`` are the logits the weights were computed from.
     ``only_experts`` restricts the expert path to those experts (the weight
     gradients of those experts are then complete; dx, ds, dwg are not).
+
+    ``saved`` names what the forward kept for the backward:
+      "aby" -- a, b and y (MoEBlaze Algorithm 1 stores A, B and Y_swi);
+      "ab"  -- only the pre-activations H = [a | b] (SonicMoE sec. 3.4.1,
+               minimal cached set): the backward recomputes
+               y = SiLU(a_s) * b_s from the stored a, b and uses it for
+               <dA', y> and for A' = w * y.
 
     Returns dx [T,d], dwg [E,d], dw_gate/dw_up [E,h,d], dw_down [E,d,h],
     ds [T,K] (= dL/dw), ds_alt [T,K] (= <dA', y>), dz [T,E] (closed form),
     dz_long [T,E] (through the full softmax), dh_a/dh_b [T,K,h].
     """
+    if saved not in ("aby", "ab"):
+        raise ValueError(f"saved must be 'aby' or 'ab', not {saved!r}")
     st = storage_rounder(dtype)
     g_all = _f64(dy)
     x = _f64(x)
@@ -279,17 +289,19 @@ def moe_backward(dy, x, wg, ids, w, w_gate, w_up, w_down, fwd, z, dtype="bf16", 
             g = g_all[r]                               # dO rows of these tokens
             wd = _f64(w_down[e])
             da_p = g @ wd                              # dA' = dO W_down   (length h)
-            ds[r, k] = np.einsum("rd,rd->r", g, fwd["ye"][r, k])      # <dO, Y>
-            ds_alt[r, k] = np.einsum("rh,rh->r", da_p, fwd["y_s"][r, k])  # <dA', y>
-            dyv = w[r, k][:, None] * da_p              # gradient reaching y
             a = fwd["a_s"][r, k]
             b = fwd["b_s"][r, k]
+            # the y the backward sees: the stored one, or recomputed from H
+            y_b = fwd["y_s"][r, k] if saved == "aby" else silu(a) * b
+            ds[r, k] = np.einsum("rd,rd->r", g, fwd["ye"][r, k])      # <dO, Y>
+            ds_alt[r, k] = np.einsum("rh,rh->r", da_p, y_b)           # <dA', y>
+            dyv = w[r, k][:, None] * da_p              # gradient reaching y
             da = st(dyv * b * silu_grad(a))            # SiLU recomputed from stored a
             db = st(dyv * silu(a))
             dh_a[r, k] = da
             dh_b[r, k] = db
             # A' = w * y, held in the storage type (SonicMoE sec. 3.4.1: dW2 = A'^T dO)
-            a_prime = st(w[r, k][:, None] * fwd["y_s"][r, k])
+            a_prime = st(w[r, k][:, None] * y_b)
             dw_down[e] += g.T @ a_prime
             dw_gate[e] += da.T @ x[r]
             dw_up[e] += db.T @ x[r]

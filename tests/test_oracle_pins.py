@@ -313,3 +313,56 @@ def test_backward_matches_explicit_per_token_loop():
         np.testing.assert_allclose(b["ds"][t, k], dy[t] @ (wdn[e] @ y), rtol=1e-12)
     dx_t += b["dz"][t] @ wg
     np.testing.assert_allclose(b["dx"][t], dx_t, rtol=1e-11, atol=1e-12)
+
+
+# --------------------------------------------------------------------------
+# H-only saved activations (SonicMoE sec. 3.4.1): y recomputed from a, b
+# --------------------------------------------------------------------------
+
+def test_h_only_backward_equals_stored_y_in_float64():
+    """With no storage rounding the recomputed y is the forward's y, so the
+    H-only backward must equal the stored-y backward -- which the finite
+    difference test pins to the true gradient.  A wrong recompute (SiLU on
+    the up branch, a missing factor) fails here."""
+    x, wg, wgt, wup, wdn, dy = _small_layer(T=24, E=5, K=2, seed=11)
+    z, ids, w, f, b = O.layer_grads(x, wg, None, wgt, wup, wdn, dy, 2)
+    bh = O.moe_backward(dy, x, wg, ids, w, wgt, wup, wdn, f, z, dtype=None, saved="ab")
+    for key in ("dx_f64", "dwg", "dw_gate", "dw_up", "dw_down", "ds_alt"):
+        np.testing.assert_allclose(bh[key], b[key], rtol=1e-12, atol=1e-13, err_msg=key)
+
+
+def test_h_only_backward_finite_differences_on_w_down():
+    """dW_down of the H-only path against central differences directly (the
+    one gradient that goes through A' = w * recomputed y)."""
+    T, d, E, K, h = 12, 8, 4, 2, 8
+    x, wg, wgt, wup, wdn, dy = _small_layer(T=T, d=d, E=E, K=K, h=h, seed=21, scale_router=3.0)
+    z = O.router_logits(x, wg, None)
+    ids, w = O.route(z, K)
+    f = O.moe_forward(x, ids, w, wgt, wup, wdn, dtype=None)
+    bh = O.moe_backward(dy, x, wg, ids, w, wgt, wup, wdn, f, z, dtype=None, saved="ab")
+    eps = 1e-6
+    V = np.random.default_rng(5).standard_normal(wdn.shape)
+    lp = O.layer_loss(x, wg, None, wgt, wup, wdn + eps * V, dy, ids)
+    lm = O.layer_loss(x, wg, None, wgt, wup, wdn - eps * V, dy, ids)
+    fd = (lp - lm) / (2 * eps)
+    an = float((bh["dw_down"] * V).sum())
+    assert abs(fd - an) <= 1e-6 * max(1.0, abs(an))
+
+
+def test_h_only_differs_from_stored_y_by_y_rounding_only():
+    """In bf16 storage the two readings differ only through the rounding of
+    y: every gradient agrees to a few bf16 ulps of y, and the pieces that do
+    not touch y (dH, dW_gate, dW_up, dX) are identical."""
+    x, wg, wgt, wup, wdn, dy = _small_layer(T=32, E=4, K=2, seed=13)
+    x, wg, wgt, wup, wdn, dy = (O.round_bf16(v) for v in (x, wg, wgt, wup, wdn, dy))
+    z = O.router_logits(x, wg, None)
+    ids, w = O.route(z.astype(np.float32).astype(np.float64), 2)
+    f = O.moe_forward(x, ids, w, wgt, wup, wdn, dtype="bf16")
+    b = O.moe_backward(dy, x, wg, ids, w, wgt, wup, wdn, f, z, dtype="bf16")
+    bh = O.moe_backward(dy, x, wg, ids, w, wgt, wup, wdn, f, z, dtype="bf16", saved="ab")
+    for key in ("dh_a", "dh_b", "dw_gate", "dw_up"):
+        np.testing.assert_array_equal(bh[key], b[key], err_msg=key)
+    rel = np.abs(bh["dw_down"] - b["dw_down"]).max() / np.abs(b["dw_down"]).max()
+    assert 0 < rel < 2 ** -6, rel
+    rel = np.abs(bh["ds_alt"] - b["ds_alt"]).max() / np.abs(b["ds_alt"]).max()
+    assert rel < 2 ** -6, rel
