@@ -306,14 +306,18 @@ def moe_backward(dy, x, wg, ids, w, w_gate, w_up, w_down, fwd, z, dtype="bf16", 
             dw_gate[e] += da.T @ x[r]
             dw_up[e] += db.T @ x[r]
             dx[r] += da @ _f64(w_gate[e]) + db @ _f64(w_up[e])
+    # the router gradient takes the dS the backward has: the plain <dO, Y>
+    # with the stored y, or <dA', y> with y recomputed from H (H-only: the
+    # forward's y is gone, SonicMoE sec. 3.4.1 forms dS from the recomputed y)
+    ds_r = ds if saved == "aby" else ds_alt
     # the closed form is exact zero off the chosen set; it is pinned to the
     # long way (full softmax + renormalisation) by the oracle's own tests
-    dz = router_backward_closed(w, ids, ds, E)
+    dz = router_backward_closed(w, ids, ds_r, E)
     dwg = dz.T @ x
     dx = dx + dz @ _f64(wg)
     return dict(dx=st(dx), dx_f64=dx, dwg=dwg, dw_gate=dw_gate, dw_up=dw_up,
-                dw_down=dw_down, ds=ds, ds_alt=ds_alt, dz=dz,
-                dz_long=router_backward_long(z, ids, ds), dh_a=dh_a, dh_b=dh_b)
+                dw_down=dw_down, ds=ds, ds_alt=ds_alt, ds_router=ds_r, dz=dz,
+                dz_long=router_backward_long(z, ids, ds_r), dh_a=dh_a, dh_b=dh_b)
 
 
 def router_backward_long(z, ids, ds) -> np.ndarray:
