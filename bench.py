@@ -65,6 +65,33 @@ def kernel_flops(name, T, d, E, K, h):
     }.get(name)
 
 
+def kernel_bytes(name, T, d, E, K, h, eb):
+    """Algorithmic HBM bytes of the memory-bound stages (operands once, outputs once)."""
+    A = T * K
+    return {
+        "router_logits": eb * T * d + eb * E * d + 4 * T * E,
+        "topk": 4 * T * E + 8 * A,
+        "index": 4 * A + 8 * A + 8 * E * ((T + 63) // 64),
+        "router_bwd": 4 * T * d + eb * E * d + 16 * A,
+        "dwg": eb * A * d + 4 * E * d + 8 * A,
+    }.get(name)
+
+
+def device_info():
+    import torch
+    info = {"rocm": getattr(torch.version, "hip", None)}
+    try:
+        p = torch.cuda.get_device_properties(0)
+        info["gpu"] = getattr(p, "gcnArchName", None) or p.name
+        info["cus"] = p.multi_processor_count
+        clk = getattr(p, "clock_rate", None)
+        if clk:
+            info["max_clock_mhz"] = clk / 1000.0
+    except Exception:  # pragma: no cover
+        pass
+    return info
+
+
 def cpu_baseline(wl, inp, sample_tokens):
     """The CPU oracle (float64 numpy) on the first ``sample_tokens`` tokens of
     the same workload, forward + backward."""
@@ -97,6 +124,8 @@ def main():
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--workload", type=int, default=3, help="1..5 (default 3: fine-grained fwd+bwd)")
     ap.add_argument("--cpu-sample", type=int, default=64, help="tokens for the CPU oracle baseline (0 = skip)")
+    ap.add_argument("--saved", default="aby", choices=("aby", "ab"),
+                    help="saved for backward: a, b and y (default) or H-only (y recomputed)")
     ap.add_argument("--no-timing", action="store_true", help="do not record per-kernel events")
     ap.add_argument("--calib-copy-mb", type=int, default=0,
                     help="after the timed steps, run one plain device copy of this many MB "
@@ -123,7 +152,7 @@ def main():
     torch.cuda.synchronize()
     base_alloc = torch.cuda.memory_allocated()
     torch.cuda.reset_peak_memory_stats()
-    buf = L.MoEBuffers(T, d, E, K, h, dt, backward=wl.backward)
+    buf = L.MoEBuffers(T, d, E, K, h, dt, backward=wl.backward, saved=args.saved)
 
     def step():
         L.forward(buf, dev["x"], dev["wg"], bias, dev["w_gate"], dev["w_up"], dev["w_down"])
@@ -146,6 +175,7 @@ def main():
     t1 = time.perf_counter()
     recs = B.timing_read() if not args.no_timing else []
     B.timing_enable(False)
+    peak_alloc = torch.cuda.max_memory_allocated()
     if args.calib_copy_mb > 0:
         n = args.calib_copy_mb * (1 << 20)
         src = torch.ones(n // 4, dtype=torch.float32, device="cuda")
@@ -155,7 +185,6 @@ def main():
         torch.cuda.synchronize()
         del src, dst
     errs = buf.device_error_words()
-    peak_alloc = torch.cuda.max_memory_allocated()
 
     ms = (t1 - t0) * 1e3 / args.steps
     flops = (18.0 if wl.backward else 6.0) * T * K * d * h
@@ -175,6 +204,20 @@ def main():
                     "frac": round(ach / peak, 4), "traffic": committed_traffic(wl.name, dom),
                     "avg_launch_ms": round(gemms[dom]["avg_ms"], 4), "algorithmic_flop_per_launch": fl,
                     "src_sha": kernel_source_hash()}
+    peak = PEAK_BF16_TFLOPS if dt == "bf16" else PEAK_F32_MFMA_TFLOPS
+    eb = 2 if dt == "bf16" else 4
+    kernels = {}
+    for k, v in per_kernel.items():
+        rec = {"avg_ms": round(v["avg_ms"], 4)}
+        fl = kernel_flops(k, T, d, E, K, h)
+        if fl is not None:
+            rec["tflops"] = round(fl / (v["avg_ms"] * 1e-3) / 1e12, 1)
+            rec["mfma_peak_frac"] = round(rec["tflops"] / peak, 4)
+        by = kernel_bytes(k, T, d, E, K, h, eb)
+        if by is not None:
+            rec["gbs"] = round(by / (v["avg_ms"] * 1e-3) / 1e9, 1)
+            rec["hbm_peak_frac"] = round(rec["gbs"] / PEAK_HBM_GBS, 4)
+        kernels[k] = rec
     counts = np.diff(buf.offsets.cpu().numpy())
     cpu = cpu_baseline(wl, inp, args.cpu_sample) if args.cpu_sample > 0 else None
     out = {
@@ -191,21 +234,24 @@ def main():
         "dtype": dt,
         "data": "synthetic (seeded Philox normals, random-init weights)",
         "config": {"workload": wl.name, "T": T, "d": d, "E": E, "K": K, "h": h,
-                   "backward": wl.backward, "zipf_s": wl.zipf_s, "seed": wl.seed},
+                   "backward": wl.backward, "zipf_s": wl.zipf_s, "seed": wl.seed, "saved": args.saved},
         "tflops": round(tflops, 2),
         "mfma_peak_frac": round(tflops / (PEAK_BF16_TFLOPS if dt == "bf16" else PEAK_F32_MFMA_TFLOPS), 4),
         "model_flop_per_step": flops,
         "roofline": roofline,
         "cpu_baseline": cpu,
         "per_kernel_ms": {k: round(v["avg_ms"], 4) for k, v in per_kernel.items()},
+        "kernels": kernels,
         "act_saved_MB": round(buf.saved_for_backward_bytes() / 1e6, 1),
         "workspace_MB": round(buf.workspace_bytes() / 1e6, 1),
-        "peak_transient_MB": round((peak_alloc - base_alloc) / 1e6, 1),
+        # device bytes at the peak beyond inputs, weights and weight gradients
+        "peak_transient_MB": round((peak_alloc - base_alloc - buf.weight_grad_bytes()) / 1e6, 1),
         "avoided_TKd_buffer_MB": round(T * K * d * (2 if dt == "bf16" else 4) / 1e6, 1),
         "routing": {"max_rows": int(counts.max()), "min_rows": int(counts.min()),
                     "zero_row_experts": int((counts == 0).sum()),
                     "padded_row_frac": round(float((np.ceil(counts / 128) * 128).sum() / counts.sum() - 1), 4)},
         "device_errors": errs,
+        "device": device_info(),
     }
     print(json.dumps(out), flush=True)
 

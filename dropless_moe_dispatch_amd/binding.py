@@ -15,7 +15,7 @@ LIB_PATH = os.path.join(HERE, "lib", "libmoe_dispatch.so")
 
 MOE_OK, MOE_ERR_INVALID_ARG, MOE_ERR_UNSUPPORTED, MOE_ERR_WORKSPACE, MOE_ERR_HIP = 0, 1, 2, 3, 4
 MOE_F32, MOE_BF16 = 0, 1
-MOE_WS_INDEX, MOE_WS_EXPERT_FWD, MOE_WS_COMBINE, MOE_WS_EXPERT_BWD = 0, 1, 2, 3
+MOE_WS_INDEX, MOE_WS_EXPERT_FWD, MOE_WS_COMBINE, MOE_WS_EXPERT_BWD, MOE_WS_EXPERT_BWD_H = 0, 1, 2, 3, 4
 
 
 class MoeShape(ctypes.Structure):

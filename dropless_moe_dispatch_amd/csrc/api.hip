@@ -101,6 +101,7 @@ size_t moe_workspace_bytes(const moe_shape* s, int which) {
     case MOE_WS_EXPERT_FWD: return expert_ws(sh, WS_EXPERT_FWD, nullptr).bytes;
     case MOE_WS_COMBINE: return expert_ws(sh, WS_COMBINE, nullptr).bytes;
     case MOE_WS_EXPERT_BWD: return expert_ws(sh, WS_EXPERT_BWD, nullptr).bytes;
+    case MOE_WS_EXPERT_BWD_H: return expert_ws(sh, WS_EXPERT_BWD_H, nullptr).bytes;
     default: return 0;
   }
 }
@@ -223,7 +224,7 @@ int moe_expert_bwd(const moe_shape* s, const void* dout, const void* x, const vo
   REQ(expert_token_indices);
   REQ(token_index_map);
   REQ(h_ab);
-  REQ(y_swi);
+  OPT(y_swi);  // NULL: H-only saving, y recomputed from h_ab
   REQ(dx);
   REQ(dwg);
   REQ(dw_gate);
@@ -231,7 +232,7 @@ int moe_expert_bwd(const moe_shape* s, const void* dout, const void* x, const vo
   REQ(dw_down);
   OPT(ds);
   REQ(ws);
-  const ExpertWs w = expert_ws(sh, WS_EXPERT_BWD, ws);
+  const ExpertWs w = expert_ws(sh, y_swi ? WS_EXPERT_BWD : WS_EXPERT_BWD_H, ws);
   if (ws_bytes < w.bytes) return MOE_ERR_WORKSPACE;
   hipStream_t st = (hipStream_t)stream;
   rc = hip_status(launch_prep(sh, w, offsets, topk_ids, topk_w, token_index_map, true, st));

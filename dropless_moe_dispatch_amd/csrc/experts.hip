@@ -418,14 +418,17 @@ struct SrcRowsGather {  // rows eti[p], p = p0 + k < p1
 
 MOE_DEV int min_i(int a, int b) { return a < b ? a : b; }
 
-// dH kernel: dA' = dO W_down (M rows of e, N = TILE of h, K = d) + SwiGLU backward
-template <class C>
+// dH kernel: dA' = dO W_down (M rows of e, N = TILE of h, K = d) + SwiGLU backward.
+// HONLY (H-only saving, SonicMoE analysis page sec. 3.4.1): y is recomputed
+// as SiLU(a) * b from the saved a, b instead of read from y_swi, and the
+// kernel also writes A' = w * y for the dW_down GEMM.
+template <class C, bool HONLY>
 __global__ __launch_bounds__(C::NT, C::WAVES_PER_EU) void dh_kernel(
     const typename C::T* __restrict__ dout, const typename C::T* __restrict__ w_down,
     const typename C::T* __restrict__ h_ab, const typename C::T* __restrict__ y_swi,
     const int32_t* __restrict__ offsets, const int32_t* __restrict__ eti, const int32_t* __restrict__ mb_off,
-    const float* __restrict__ w_pos, typename C::T* __restrict__ dh, float* __restrict__ ds_part, int T, int d,
-    int E, int h, int nbn, int nblk) {
+    const float* __restrict__ w_pos, typename C::T* __restrict__ dh, float* __restrict__ ds_part,
+    typename C::T* __restrict__ a_prime, int T, int d, int E, int h, int nbn, int nblk) {
   __shared__ __attribute__((aligned(16))) char smem[C::LDS_BYTES];
   using TIN = typename C::T;
   const int id = xcd_swizzle(blockIdx.x, nblk);
@@ -474,10 +477,16 @@ __global__ __launch_bounds__(C::NT, C::WAVES_PER_EU) void dh_kernel(
             const float dap = acc[fm][fn][r];
             const float a = ld_f(h_ab + (size_t)p * 2 * h + j);
             const float b = ld_f(h_ab + (size_t)p * 2 * h + h + j);
-            const float y = ld_f(y_swi + (size_t)p * h + j);
+            const float sg = sigmoidf_(a);
+            float y;
+            if constexpr (HONLY) {
+              y = a * sg * b;
+              st_f(a_prime + (size_t)p * h + j, w * y);
+            } else {
+              y = ld_f(y_swi + (size_t)p * h + j);
+            }
             dsum += dap * y;
             const float dy = w * dap;
-            const float sg = sigmoidf_(a);
             st_f(dh + (size_t)p * 2 * h + j, dy * b * sg * (1.0f + a * (1.0f - sg)));
             st_f(dh + (size_t)p * 2 * h + h + j, dy * a * sg);
           }
@@ -584,7 +593,9 @@ __global__ __launch_bounds__(256) void dwg_kernel(const TIN* __restrict__ x, con
 // The score-scaled activation A' = w_p y[p] is formed while staging the B
 // operand and held in the activation dtype, as the SonicMoE analysis page
 // (sec. 3.4.1) defines A' = Broadcast(s) A for the dW2 grouped GEMM.
-template <class C>
+// SCALE: the right-hand rows are y_swi and get the score here; otherwise
+// they are A' written by the H-only dH kernel.
+template <class C, bool SCALE>
 __global__ __launch_bounds__(C::NT, C::WAVES_PER_EU) void dw_down_kernel(
     const typename C::T* __restrict__ dout, const typename C::T* __restrict__ y_swi,
     const int32_t* __restrict__ offsets, const int32_t* __restrict__ eti, const float* __restrict__ w_pos,
@@ -604,7 +615,7 @@ __global__ __launch_bounds__(C::NT, C::WAVES_PER_EU) void dw_down_kernel(
   la.src.p1 = p1;
   la.src.eti = eti;
   la.ncols = min_i(C::BM, d - mb * C::BM);
-  KSrcLoader<C, C::BKM, C::BN, SrcRowsContig<TIN>, true> lb;
+  KSrcLoader<C, C::BKM, C::BN, SrcRowsContig<TIN>, SCALE> lb;
   lb.src.rs = make_rsrc(y_swi + (size_t)p0 * h, (size_t)(p1 - p0) * h * sizeof(TIN));
   lb.src.ld_bytes = (uint32_t)h * sizeof(TIN);
   lb.src.col0 = (uint32_t)(nb * C::BN) * sizeof(TIN);
@@ -714,15 +725,15 @@ __global__ __launch_bounds__(C::NT, C::WAVES_PER_EU) void dx_fold_kernel(
                           spin_limit, smem);
 }
 
-template <typename TIN, int B>
+template <typename TIN, int B, bool HONLY>
 static void launch_dh(const Shape& s, const void* dout, const void* w_down, const void* h_ab, const void* y_swi,
                       const int32_t* offsets, const int32_t* eti, const ExpertWs& ws, hipStream_t st) {
   using C = KCfg<TIN, B, false, true>;
   const int nbn = col_blocks(s.h, B);
   const long long nblk = (max_row_blocks(s, B) * nbn + 7) / 8 * 8;
-  dh_kernel<C><<<dim3((unsigned)nblk), dim3(C::NT), 0, st>>>(
+  dh_kernel<C, HONLY><<<dim3((unsigned)nblk), dim3(C::NT), 0, st>>>(
       (const TIN*)dout, (const TIN*)w_down, (const TIN*)h_ab, (const TIN*)y_swi, offsets, eti, ws.tile_map(B),
-      ws.w_pos, (TIN*)ws.dh, ws.ds_part, s.T, s.d, s.E, s.h, nbn, (int)nblk);
+      ws.w_pos, (TIN*)ws.dh, ws.ds_part, (TIN*)ws.a_prime, s.T, s.d, s.E, s.h, nbn, (int)nblk);
 }
 
 template <typename TIN, int B>
@@ -747,8 +758,14 @@ static hipError_t backward_t(const Shape& s, const void* dout, const void* x, co
   const int nbh = col_blocks(s.h, dh_big ? TILE_L : TILE_S);
   hipError_t err;
   timing_mark(st, "dh", true);
-  if (dh_big) launch_dh<TIN, TILE_L>(s, dout, w_down, h_ab, y_swi, offsets, eti, ws, st);
-  else launch_dh<TIN, TILE_S>(s, dout, w_down, h_ab, y_swi, offsets, eti, ws, st);
+  const bool honly = y_swi == nullptr;
+  if (dh_big) {
+    if (honly) launch_dh<TIN, TILE_L, true>(s, dout, w_down, h_ab, y_swi, offsets, eti, ws, st);
+    else launch_dh<TIN, TILE_L, false>(s, dout, w_down, h_ab, y_swi, offsets, eti, ws, st);
+  } else {
+    if (honly) launch_dh<TIN, TILE_S, true>(s, dout, w_down, h_ab, y_swi, offsets, eti, ws, st);
+    else launch_dh<TIN, TILE_S, false>(s, dout, w_down, h_ab, y_swi, offsets, eti, ws, st);
+  }
   timing_mark(st, "dh", false);
   if ((err = hipGetLastError()) != hipSuccess) return err;
 
@@ -768,8 +785,15 @@ static hipError_t backward_t(const Shape& s, const void* dout, const void* x, co
   if ((err = hipGetLastError()) != hipSuccess) return err;
 
   timing_mark(st, "dw_down", true);
-  dw_down_kernel<CL><<<dim3(col_blocks(s.d, CL::BM) * col_blocks(s.h, CL::BN), s.E), dim3(CL::NT), 0, st>>>(
-      (const TIN*)dout, (const TIN*)y_swi, offsets, eti, ws.w_pos, dw_down, s.T, s.d, s.h);
+  {
+    const dim3 grid(col_blocks(s.d, CL::BM) * col_blocks(s.h, CL::BN), s.E);
+    if (honly)
+      dw_down_kernel<CL, false><<<grid, dim3(CL::NT), 0, st>>>((const TIN*)dout, (const TIN*)ws.a_prime, offsets,
+                                                               eti, ws.w_pos, dw_down, s.T, s.d, s.h);
+    else
+      dw_down_kernel<CL, true><<<grid, dim3(CL::NT), 0, st>>>((const TIN*)dout, (const TIN*)y_swi, offsets, eti,
+                                                              ws.w_pos, dw_down, s.T, s.d, s.h);
+  }
   timing_mark(st, "dw_down", false);
   if ((err = hipGetLastError()) != hipSuccess) return err;
 

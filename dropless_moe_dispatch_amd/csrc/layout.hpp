@@ -61,11 +61,12 @@ struct ExpertWs {
   float* ds_part;      // [A][h/128] router-score partial sums (backward)
   float* dz_pos;       // [A] router logit gradient per position (backward)
   void* dh;            // [A][2h] activation-dtype gradient of the pre-activations (backward)
+  void* a_prime;       // [A][h] activation-dtype A' = w * y recomputed from a, b (H-only backward)
   size_t bytes;
   int E;
   const int32_t* tile_map(int bm) const { return mb_off + (bm == TILE_L ? E + 1 : 0); }
 };
-enum { WS_EXPERT_FWD = 1, WS_COMBINE = 2, WS_EXPERT_BWD = 3 };
+enum { WS_EXPERT_FWD = 1, WS_COMBINE = 2, WS_EXPERT_BWD = 3, WS_EXPERT_BWD_H = 4 };
 
 inline ExpertWs expert_ws(const Shape& s, int which, void* p) {
   ExpertWs w{};
@@ -75,17 +76,19 @@ inline ExpertWs expert_ws(const Shape& s, int which, void* p) {
   auto take = [&](size_t bytes) { void* q = (char*)p + off; off = align_up(off + bytes, 256); return q; };
   w.counters = (int32_t*)take(N_COUNTERS * 4);
   w.mb_off = (int32_t*)take((size_t)2 * (s.E + 1) * 4);
-  if (which == WS_COMBINE || which == WS_EXPERT_BWD) {
+  const bool bwd = which == WS_EXPERT_BWD || which == WS_EXPERT_BWD_H;
+  if (which == WS_COMBINE || bwd) {
     w.w_pos = (float*)take(A * 4);
     w.rank_pos = (int32_t*)take(A * 4);
     w.turn = (int32_t*)take((size_t)s.T * col_blocks(s.d, TILE_S) * 4);
     w.acc = (float*)take((size_t)s.T * s.d * 4);
   }
-  if (which == WS_EXPERT_BWD) {
+  if (bwd) {
     w.ds_part = (float*)take(A * col_blocks(s.h, TILE_S) * 4);
     w.dz_pos = (float*)take(A * 4);
     w.dh = take(A * 2 * (size_t)s.h * s.elem());
   }
+  if (which == WS_EXPERT_BWD_H) w.a_prime = take(A * (size_t)s.h * s.elem());
   w.bytes = off;
   return w;
 }

@@ -29,6 +29,10 @@ class MoEBuffers:
     dtype: str = "bf16"
     backward: bool = True
     device: str = "cuda"
+    # what the forward keeps for the backward: "aby" = a, b and y (MoEBlaze
+    # Algorithm 1); "ab" = only H = [a | b] (SonicMoE's minimal cached set):
+    # y_swi is then a forward transient and the backward recomputes y
+    saved: str = "aby"
 
     def __post_init__(self):
         dev, td = self.device, torch_dtype(self.dtype)
@@ -55,7 +59,9 @@ class MoEBuffers:
             self.dw_up = torch.empty(E, h, d, dtype=f32, device=dev)
             self.dw_down = torch.empty(E, d, h, dtype=f32, device=dev)
             self.ds = torch.empty(T, K, dtype=f32, device=dev)
-            self.ws_bwd = self._ws(B.MOE_WS_EXPERT_BWD)
+            if self.saved not in ("aby", "ab"):
+                raise ValueError(f"saved must be 'aby' or 'ab', not {self.saved!r}")
+            self.ws_bwd = self._ws(B.MOE_WS_EXPERT_BWD if self.saved == "aby" else B.MOE_WS_EXPERT_BWD_H)
 
     def _ws(self, which):
         n = B.workspace_bytes(self.shape, which)
@@ -65,10 +71,18 @@ class MoEBuffers:
 
     # -- accounting ---------------------------------------------------------
     def saved_for_backward_bytes(self) -> int:
-        """Activations kept from the forward for the backward: a|b, y_swi,
-        the top-K ids and weights, and the index arrays."""
-        ts = [self.h_ab, self.y_swi, self.topk_ids, self.topk_w, self.offsets, self.eti, self.tim]
+        """Activations kept from the forward for the backward: a|b, y_swi
+        (unless H-only), the top-K ids and weights, and the index arrays."""
+        ts = [self.h_ab, self.topk_ids, self.topk_w, self.offsets, self.eti, self.tim]
+        if self.saved == "aby":
+            ts.append(self.y_swi)
         return sum(t.numel() * t.element_size() for t in ts)
+
+    def weight_grad_bytes(self) -> int:
+        """The fp32 weight gradients (dWg, dW_gate, dW_up, dW_down)."""
+        if not self.backward:
+            return 0
+        return sum(t.numel() * t.element_size() for t in (self.dwg, self.dw_gate, self.dw_up, self.dw_down))
 
     def workspace_bytes(self) -> int:
         ws = [self.ws_index, self.ws_fwd, self.ws_comb] + ([self.ws_bwd] if self.backward else [])
@@ -96,7 +110,8 @@ def forward(buf: MoEBuffers, x, wg, bias, w_gate, w_up, w_down, logits_in: bool 
 
 def backward(buf: MoEBuffers, dy, x, wg, w_gate, w_up, w_down, stream=None, want_ds: bool = True):
     B.moe_expert_bwd(buf.shape, dy, x, wg, w_gate, w_up, w_down, buf.topk_ids, buf.topk_w, buf.offsets, buf.eti,
-                     buf.tim, buf.h_ab, buf.y_swi, buf.dx, buf.dwg, buf.dw_gate, buf.dw_up, buf.dw_down,
+                     buf.tim, buf.h_ab, buf.y_swi if buf.saved == "aby" else None, buf.dx, buf.dwg, buf.dw_gate,
+                     buf.dw_up, buf.dw_down,
                      buf.ds if want_ds else None, buf.ws_bwd, stream)
     return buf.dx
 

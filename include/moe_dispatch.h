@@ -85,7 +85,9 @@ typedef enum {
   MOE_WS_INDEX = 0,       /* moe_build_index */
   MOE_WS_EXPERT_FWD = 1,  /* moe_expert_fwd */
   MOE_WS_COMBINE = 2,     /* moe_combine */
-  MOE_WS_EXPERT_BWD = 3   /* moe_expert_bwd */
+  MOE_WS_EXPERT_BWD = 3,  /* moe_expert_bwd with the saved y_swi */
+  MOE_WS_EXPERT_BWD_H = 4 /* moe_expert_bwd with y_swi == NULL (H-only saving):
+                             MOE_WS_EXPERT_BWD plus a [T*K, h] dtype buffer */
 } moe_workspace_kind;
 
 /* Bytes of device workspace the call of kind `which` needs for shape *s
@@ -159,7 +161,16 @@ int moe_combine(const moe_shape* s, const void* y_swi, const void* w_down, const
  * exact zeros): dx [T,d] dtype, dwg [E,d] fp32, dw_gate/dw_up [E,h,d] fp32,
  * dw_down [E,d,h] fp32, ds [T,K] fp32 (nullable: the router score
  * gradient dL/dw).  The bias, if any, gets no gradient.  dx is assembled by
- * the same ordered, atomic-free fold as moe_combine.  ws: MOE_WS_EXPERT_BWD. */
+ * the same ordered, atomic-free fold as moe_combine.  ws: MOE_WS_EXPERT_BWD.
+ *
+ * H-only saving (SonicMoE analysis page sec. 3.4.1, the minimal cached set
+ * of the memory-efficient backward): y_swi == NULL.  The forward's y_swi is
+ * then only a forward transient (moe_combine reads it; the caller may free
+ * it before the backward).  The dH kernel recomputes y = SiLU(a) * b from the
+ * saved bf16 a and b, uses it for dS = <dA', y>, and writes A' = w * y in
+ * the activation dtype into the workspace, where dW_down reads it as its
+ * right-hand operand (dw_down[e] += dout[t]^T A'[p]).  ws:
+ * MOE_WS_EXPERT_BWD_H (MOE_ERR_WORKSPACE if smaller). */
 int moe_expert_bwd(const moe_shape* s, const void* dout, const void* x, const void* wg, const void* w_gate,
                    const void* w_up, const void* w_down, const int32_t* topk_ids, const float* topk_w,
                    const int32_t* offsets, const int32_t* expert_token_indices, const int32_t* token_index_map,

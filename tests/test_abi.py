@@ -35,9 +35,12 @@ def test_status_strings():
 
 def test_workspace_sizes_depend_on_shape_only():
     s = B.shape(16384, 2048, 128, 8, 768)
-    sizes = [B.workspace_bytes(s, w) for w in range(4)]
+    sizes = [B.workspace_bytes(s, w) for w in range(5)]
     assert all(n > 0 for n in sizes)
     assert B.workspace_bytes(s, 7) == 0
+    # the H-only backward workspace adds exactly the [T*K, h] A' buffer (256-byte aligned)
+    extra = sizes[B.MOE_WS_EXPERT_BWD_H] - sizes[B.MOE_WS_EXPERT_BWD]
+    assert 16384 * 8 * 768 * 2 <= extra < 16384 * 8 * 768 * 2 + 256
     # combine workspace holds the fp32 [T,d] fold accumulator, not a [T*K,d] buffer
     comb = sizes[B.MOE_WS_COMBINE]
     assert 16384 * 2048 * 4 <= comb < 16384 * 8 * 2048 * 2
@@ -83,6 +86,14 @@ def test_pointer_and_workspace_validation():
     assert L.moe_expert_bwd(sp, *req, None, FAKE, need - 1, 0) == B.MOE_ERR_WORKSPACE   # ds is optional
     req[14] = None               # dwg missing
     assert L.moe_expert_bwd(sp, *req, None, FAKE, need, 0) == B.MOE_ERR_INVALID_ARG
+    # y_swi == NULL (H-only saving) needs the larger MOE_WS_EXPERT_BWD_H workspace
+    req = [FAKE] * 18
+    req[12] = None               # y_swi
+    need_h = B.workspace_bytes(s, B.MOE_WS_EXPERT_BWD_H)
+    assert need_h > need
+    assert L.moe_expert_bwd(sp, *req, None, FAKE, need, 0) == B.MOE_ERR_WORKSPACE
+    req[11] = None               # h_ab is still required
+    assert L.moe_expert_bwd(sp, *req, None, FAKE, need_h, 0) == B.MOE_ERR_INVALID_ARG
 
 
 def test_spin_limit_setter_roundtrip():

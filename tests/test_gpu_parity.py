@@ -118,9 +118,9 @@ LAYER_CASES = [
 ]
 
 
-def _gpu_layer(inp, wl, logits32=None, backward=True):
+def _gpu_layer(inp, wl, logits32=None, backward=True, saved="aby"):
     dt = wl.dtype
-    buf = Lyr.MoEBuffers(wl.T, wl.d, wl.E, wl.K, wl.h, dt, backward=backward)
+    buf = Lyr.MoEBuffers(wl.T, wl.d, wl.E, wl.K, wl.h, dt, backward=backward, saved=saved)
     dev = {k: Lyr.to_device(inp[k], dt) for k in ("x", "wg", "w_gate", "w_up", "w_down", "dy") if k in inp}
     bias = torch.from_numpy(inp["bias"]).cuda() if inp.get("bias") is not None else None
     if logits32 is not None:
@@ -133,7 +133,7 @@ def _gpu_layer(inp, wl, logits32=None, backward=True):
     return buf, dev
 
 
-def _compare_layer(buf, inp, wl, z32, backward=True, report=None, w_rtol=2e-6):
+def _compare_layer(buf, inp, wl, z32, backward=True, report=None, w_rtol=2e-6, saved="aby"):
     T, K, E, h = wl.T, wl.K, wl.E, wl.h
     zz = z32.astype(np.float64)
     ids, w = O.route(zz, K)
@@ -153,8 +153,9 @@ def _compare_layer(buf, inp, wl, z32, backward=True, report=None, w_rtol=2e-6):
     if not backward:
         return
     bw = O.moe_backward(inp["dy"], inp["x"], inp["wg"], ids, w, inp["w_gate"], inp["w_up"], inp["w_down"], f, zz,
-                        dtype=wl.dtype)
-    assert_close("ds", to_np(buf.ds), bw["ds"], report=report)
+                        dtype=wl.dtype, saved=saved)
+    # the kernels form dS = <dA', y> with the y the backward sees
+    assert_close("ds", to_np(buf.ds), bw["ds_alt"] if saved == "ab" else bw["ds"], report=report)
     assert_close("dx", to_np(buf.dx), bw["dx"], report=report)
     assert_close("dwg", to_np(buf.dwg), bw["dwg"], report=report)
     assert_close("dw_gate", to_np(buf.dw_gate), bw["dw_gate"], report=report)
@@ -176,6 +177,36 @@ def test_layer_parity_from_logits(case):
     buf, _ = _gpu_layer(inp, wl, logits32=z32)
     assert buf.device_error_words() == [0, 0]
     _compare_layer(buf, inp, wl, z32)
+
+
+H_ONLY_CASES = [c for c in LAYER_CASES if c[0] in ("ragged", "multi_tile", "skewed", "t1", "f32_bwd")]
+
+
+@pytest.mark.parametrize("case", H_ONLY_CASES, ids=[c[0] for c in H_ONLY_CASES])
+def test_layer_parity_h_only(case):
+    """H-only saving: the backward recomputes y from a, b (y_swi not passed)."""
+    name, T, d, E, K, h, dtype, zipf = case
+    _say("layer_h_only", case)
+    wl = synth.small_workload(T, d, E, K, h, dtype=dtype, seed=sum(map(ord, name)) + 7, zipf_s=zipf)
+    inp = synth.make_inputs(wl)
+    z32 = O.router_logits(inp["x"], inp["wg"], inp["bias"]).astype(np.float32)
+    buf, _ = _gpu_layer(inp, wl, logits32=z32, saved="ab")
+    assert buf.device_error_words() == [0, 0]
+    _compare_layer(buf, inp, wl, z32, saved="ab")
+
+
+def test_h_only_leaves_y_independent_gradients_unchanged():
+    """dW_gate and dW_up do not depend on y: the two savings give them bit for bit."""
+    T, d, E, K, h = 700, 256, 16, 4, 256
+    _say("h_only_vs_aby", T, d, E, K, h)
+    wl = synth.small_workload(T, d, E, K, h, seed=31)
+    inp = synth.make_inputs(wl)
+    z32 = O.router_logits(inp["x"], inp["wg"], inp["bias"]).astype(np.float32)
+    b1, _ = _gpu_layer(inp, wl, logits32=z32, saved="aby")
+    b2, _ = _gpu_layer(inp, wl, logits32=z32, saved="ab")
+    for key in ("out", "dw_gate", "dw_up"):
+        assert torch.equal(getattr(b1, key), getattr(b2, key)), key
+    assert not torch.equal(b1.dw_down, b2.dw_down)  # A' comes from a different y rounding
 
 
 @pytest.mark.parametrize("kind", ["one_expert_set", "zero_rows", "hot_expert"])
