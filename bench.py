@@ -58,6 +58,7 @@ def kernel_flops(name, T, d, E, K, h):
         "router_logits": 2.0 * T * d * E,
         "gate_up": 4.0 * A * d * h,
         "down_combine": 2.0 * A * d * h,
+        "down_staged": 2.0 * A * d * h,
         "dh": 2.0 * A * d * h,
         "dw_down": 2.0 * A * d * h,
         "dw_gate_up": 4.0 * A * d * h,
@@ -74,6 +75,7 @@ def kernel_bytes(name, T, d, E, K, h, eb):
         "index": 4 * A + 8 * A + 8 * E * ((T + 63) // 64),
         "router_bwd": 4 * T * d + eb * E * d + 16 * A,
         "dwg": eb * A * d + 4 * E * d + 8 * A,
+        "gather_sum": eb * A * d + eb * T * d + 8 * A,
     }.get(name)
 
 
@@ -126,6 +128,8 @@ def main():
     ap.add_argument("--cpu-sample", type=int, default=64, help="tokens for the CPU oracle baseline (0 = skip)")
     ap.add_argument("--saved", default="aby", choices=("aby", "ab"),
                     help="saved for backward: a, b and y (default) or H-only (y recomputed)")
+    ap.add_argument("--combine", default="fold", choices=("fold", "staged"),
+                    help="forward combine: the ordered fold (default) or the staged-Y ablation")
     ap.add_argument("--no-timing", action="store_true", help="do not record per-kernel events")
     ap.add_argument("--calib-copy-mb", type=int, default=0,
                     help="after the timed steps, run one plain device copy of this many MB "
@@ -152,7 +156,7 @@ def main():
     torch.cuda.synchronize()
     base_alloc = torch.cuda.memory_allocated()
     torch.cuda.reset_peak_memory_stats()
-    buf = L.MoEBuffers(T, d, E, K, h, dt, backward=wl.backward, saved=args.saved)
+    buf = L.MoEBuffers(T, d, E, K, h, dt, backward=wl.backward, saved=args.saved, combine=args.combine)
 
     def step():
         L.forward(buf, dev["x"], dev["wg"], bias, dev["w_gate"], dev["w_up"], dev["w_down"])
@@ -234,7 +238,8 @@ def main():
         "dtype": dt,
         "data": "synthetic (seeded Philox normals, random-init weights)",
         "config": {"workload": wl.name, "T": T, "d": d, "E": E, "K": K, "h": h,
-                   "backward": wl.backward, "zipf_s": wl.zipf_s, "seed": wl.seed, "saved": args.saved},
+                   "backward": wl.backward, "zipf_s": wl.zipf_s, "seed": wl.seed, "saved": args.saved,
+                   "combine": args.combine},
         "tflops": round(tflops, 2),
         "mfma_peak_frac": round(tflops / (PEAK_BF16_TFLOPS if dt == "bf16" else PEAK_F32_MFMA_TFLOPS), 4),
         "model_flop_per_step": flops,

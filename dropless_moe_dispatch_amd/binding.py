@@ -16,6 +16,7 @@ LIB_PATH = os.path.join(HERE, "lib", "libmoe_dispatch.so")
 MOE_OK, MOE_ERR_INVALID_ARG, MOE_ERR_UNSUPPORTED, MOE_ERR_WORKSPACE, MOE_ERR_HIP = 0, 1, 2, 3, 4
 MOE_F32, MOE_BF16 = 0, 1
 MOE_WS_INDEX, MOE_WS_EXPERT_FWD, MOE_WS_COMBINE, MOE_WS_EXPERT_BWD, MOE_WS_EXPERT_BWD_H = 0, 1, 2, 3, 4
+MOE_WS_COMBINE_STAGED = 5
 
 
 class MoeShape(ctypes.Structure):
@@ -47,8 +48,9 @@ def lib():
         L.moe_build_index.argtypes = [sp, _P, _P, _P, _P, _P, ctypes.c_size_t, _P]
         L.moe_expert_fwd.argtypes = [sp, _P, _P, _P, _P, _P, _P, _P, _P, ctypes.c_size_t, _P]
         L.moe_combine.argtypes = [sp, _P, _P, _P, _P, _P, _P, _P, _P, _P, ctypes.c_size_t, _P]
+        L.moe_combine_staged.argtypes = [sp, _P, _P, _P, _P, _P, _P, _P, _P, _P, ctypes.c_size_t, _P]
         L.moe_expert_bwd.argtypes = [sp] + [_P] * 20 + [ctypes.c_size_t, _P]
-        for f in ("moe_route_topk", "moe_build_index", "moe_expert_fwd", "moe_combine", "moe_expert_bwd"):
+        for f in ("moe_route_topk", "moe_build_index", "moe_expert_fwd", "moe_combine", "moe_combine_staged", "moe_expert_bwd"):
             getattr(L, f).restype = ctypes.c_int
         L.moe_status_string.argtypes = [ctypes.c_int]
         L.moe_status_string.restype = ctypes.c_char_p
@@ -127,6 +129,15 @@ def moe_combine(s, y_swi, w_down, offsets, eti, tim, topk_ids, topk_w, out, ws, 
                            _ptr(topk_ids), _ptr(topk_w), _ptr(out), _ptr(ws), _nbytes(ws), _stream(stream))
     if check:
         _check("moe_combine", rc)
+    return rc
+
+
+def moe_combine_staged(s, y_swi, w_down, offsets, eti, tim, topk_ids, topk_w, out, ws, stream=None, check=True):
+    """Staged-Y combine (ablation of moe_combine; materialises a [T*K, d] buffer)."""
+    rc = lib().moe_combine_staged(ctypes.byref(s), _ptr(y_swi), _ptr(w_down), _ptr(offsets), _ptr(eti), _ptr(tim),
+                                  _ptr(topk_ids), _ptr(topk_w), _ptr(out), _ptr(ws), _nbytes(ws), _stream(stream))
+    if check:
+        _check("moe_combine_staged", rc)
     return rc
 
 

@@ -102,6 +102,7 @@ size_t moe_workspace_bytes(const moe_shape* s, int which) {
     case MOE_WS_COMBINE: return expert_ws(sh, WS_COMBINE, nullptr).bytes;
     case MOE_WS_EXPERT_BWD: return expert_ws(sh, WS_EXPERT_BWD, nullptr).bytes;
     case MOE_WS_EXPERT_BWD_H: return expert_ws(sh, WS_EXPERT_BWD_H, nullptr).bytes;
+    case MOE_WS_COMBINE_STAGED: return expert_ws(sh, WS_COMBINE_STAGED, nullptr).bytes;
     default: return 0;
   }
 }
@@ -202,6 +203,29 @@ int moe_combine(const moe_shape* s, const void* y_swi, const void* w_down, const
   rc = hip_status(launch_prep(sh, w, offsets, topk_ids, topk_w, token_index_map, true, st));
   if (rc) return rc;
   return hip_status(launch_down_combine(sh, y_swi, w_down, offsets, expert_token_indices, out, w, g_spin_limit, st));
+}
+
+int moe_combine_staged(const moe_shape* s, const void* y_swi, const void* w_down, const int32_t* offsets,
+                       const int32_t* expert_token_indices, const int32_t* token_index_map, const int32_t* topk_ids,
+                       const float* topk_w, void* out, void* ws, size_t ws_bytes, void* stream) {
+  Shape sh;
+  int rc = check_shape(s, &sh);
+  if (rc) return rc;
+  REQ(y_swi);
+  REQ(w_down);
+  REQ(offsets);
+  REQ(expert_token_indices);
+  REQ(token_index_map);
+  REQ(topk_ids);
+  REQ(topk_w);
+  REQ(out);
+  REQ(ws);
+  const ExpertWs w = expert_ws(sh, WS_COMBINE_STAGED, ws);
+  if (ws_bytes < w.bytes) return MOE_ERR_WORKSPACE;
+  hipStream_t st = (hipStream_t)stream;
+  rc = hip_status(launch_prep(sh, w, offsets, nullptr, nullptr, nullptr, false, st));
+  if (rc) return rc;
+  return hip_status(launch_combine_staged(sh, y_swi, w_down, offsets, token_index_map, topk_w, out, w, st));
 }
 
 int moe_expert_bwd(const moe_shape* s, const void* dout, const void* x, const void* wg, const void* w_gate,

@@ -369,6 +369,154 @@ hipError_t launch_down_combine(const Shape& s, const void* y_swi, const void* w_
 }
 
 // ===========================================================================
+// Staged-Y combine (ablation of the ordered fold, never the product path):
+// the down projection writes Y[p] = y_swi[p] W_down[e]^T for every position
+// (a T*K x d buffer, in the activation dtype), then a gather-and-sum kernel
+// forms out[t] = sum_k w[t,k] Y[token_index_map[t*K+k]] in slot order --
+// the SonicMoE analysis page's temporary Y (sec. 3.4.1) and gather-and-sum
+// aggregation ("O") kernel (sec. 3.4.2, Figure 17 left).
+// ===========================================================================
+template <class C>
+__global__ __launch_bounds__(C::NT, C::WAVES_PER_EU) void down_staged_kernel(
+    const typename C::T* __restrict__ y_swi, const typename C::T* __restrict__ w_down,
+    const int32_t* __restrict__ offsets, const int32_t* __restrict__ mb_off, typename C::T* __restrict__ ystage,
+    int d, int E, int h, int nbn, int nblk) {
+  static_assert(C::BM == 128 && C::BN == 128 && C::NT == NTHREADS, "128 x 128 tile, four waves");
+  __shared__ __attribute__((aligned(16))) char smem[C::LDS_BYTES];
+  using TIN = typename C::T;
+  const int id = xcd_swizzle(blockIdx.x, nblk);
+  const int g = id / nbn, nb = id % nbn;
+  if (g >= mb_off[E]) return;
+  const RowTile rt = decode_row_tile<C::BM>(mb_off, offsets, E, g);
+  const int wave = threadIdx.x >> 6, wm = wave / C::WN, wn = wave % C::WN;
+  const uint32_t ldy = (uint32_t)h * sizeof(TIN);
+  using LA = RowLoader<C::BM, false, C::NT>;
+  using LB = RowLoader<C::BN, false, C::NT>;
+  LA la;
+  LB lb;
+  la.rs[0] = make_rsrc(y_swi + (size_t)rt.r0 * h, (size_t)(rt.r1 - rt.r0) * ldy);
+#pragma unroll
+  for (int i = 0; i < LA::CPT; ++i) {
+    const int r = LA::my_row(i);
+    la.roff[i] = rt.r0 + r < rt.r1 ? (uint32_t)r * ldy : OOB_OFF;
+  }
+  lb.rs[0] = make_rsrc(w_down + (size_t)rt.e * d * h, (size_t)d * ldy);
+#pragma unroll
+  for (int i = 0; i < LB::CPT; ++i) {
+    const int n = nb * C::BN + LB::my_row(i);
+    lb.roff[i] = n < d ? (uint32_t)n * ldy : OOB_OFF;
+  }
+  f32x16_t acc[C::FM][C::FN];
+  gemm_mainloop<C>(la, lb, h / C::BK, smem, acc, wm, wn);
+  // park the tile in LDS, then write whole 16-byte row chunks
+  float* s_c = (float*)smem;
+  const int l = lane_id();
+  __syncthreads();
+#pragma unroll
+  for (int fm = 0; fm < C::FM; ++fm)
+#pragma unroll
+    for (int fn = 0; fn < C::FN; ++fn)
+#pragma unroll
+      for (int r = 0; r < 16; ++r)
+        s_c[(C::a_row0(wm, fm) + frag_row(r, l)) * FOLD_LD + C::b_row0(wn, fn) + frag_col(l)] = acc[fm][fn][r];
+  __syncthreads();
+  constexpr int VPC = 16 / sizeof(TIN);          // values per 16-byte chunk
+  constexpr int CPR = C::BN / VPC;               // chunks per tile row
+  const int rows = rt.r1 - rt.r0;
+  for (int c = threadIdx.x; c < C::BM * CPR; c += C::NT) {
+    const int row = c / CPR, cc = c % CPR;
+    if (row >= rows) break;
+    const float* src = s_c + row * FOLD_LD + cc * VPC;
+    TIN* dst = ystage + (size_t)(rt.r0 + row) * d + nb * C::BN + cc * VPC;
+    if constexpr (sizeof(TIN) == 2) {
+      u32x4_t v;
+#pragma unroll
+      for (int q = 0; q < 4; ++q) v[q] = f32_to_bf16(src[2 * q]) | (f32_to_bf16(src[2 * q + 1]) << 16);
+      *(u32x4_t*)dst = v;
+    } else {
+      *(f32x4_t*)dst = *(const f32x4_t*)src;
+    }
+  }
+}
+
+// out[t] = sum_k w[t,k] Y[tim[t*K+k]] (slot order, fp32), 8 columns per thread
+template <typename TIN>
+__global__ __launch_bounds__(256) void gather_sum_kernel(const TIN* __restrict__ ystage,
+                                                         const int32_t* __restrict__ tim,
+                                                         const float* __restrict__ topk_w, TIN* __restrict__ out,
+                                                         int d, int K) {
+  const int t = blockIdx.x;
+  __shared__ int s_p[32];
+  __shared__ float s_w[32];
+  if (threadIdx.x < K) {
+    s_p[threadIdx.x] = tim[(size_t)t * K + threadIdx.x];
+    s_w[threadIdx.x] = topk_w[(size_t)t * K + threadIdx.x];
+  }
+  __syncthreads();
+  for (int c0 = threadIdx.x * 8; c0 < d; c0 += 256 * 8) {
+    float acc[8];
+#pragma unroll
+    for (int v = 0; v < 8; ++v) acc[v] = 0.0f;
+    for (int k = 0; k < K; ++k) {
+      const TIN* row = ystage + (size_t)s_p[k] * d + c0;
+      const float w = s_w[k];
+      if constexpr (sizeof(TIN) == 2) {
+        const u32x4_t q = *(const u32x4_t*)row;
+#pragma unroll
+        for (int v = 0; v < 4; ++v) {
+          acc[2 * v] += w * bf16_to_f32(q[v] & 0xffffu);
+          acc[2 * v + 1] += w * bf16_to_f32(q[v] >> 16);
+        }
+      } else {
+        const f32x4_t q0 = *(const f32x4_t*)row, q1 = *(const f32x4_t*)(row + 4);
+#pragma unroll
+        for (int v = 0; v < 4; ++v) {
+          acc[v] += w * q0[v];
+          acc[4 + v] += w * q1[v];
+        }
+      }
+    }
+    TIN* o = out + (size_t)t * d + c0;
+    if constexpr (sizeof(TIN) == 2) {
+      u32x4_t q;
+#pragma unroll
+      for (int v = 0; v < 4; ++v) q[v] = f32_to_bf16(acc[2 * v]) | (f32_to_bf16(acc[2 * v + 1]) << 16);
+      *(u32x4_t*)o = q;
+    } else {
+      *(f32x4_t*)o = f32x4_t{acc[0], acc[1], acc[2], acc[3]};
+      *(f32x4_t*)(o + 4) = f32x4_t{acc[4], acc[5], acc[6], acc[7]};
+    }
+  }
+}
+
+template <typename TIN>
+static hipError_t combine_staged_t(const Shape& s, const void* y_swi, const void* w_down, const int32_t* offsets,
+                                   const int32_t* tim, const float* topk_w, void* out, const ExpertWs& ws,
+                                   hipStream_t st) {
+  using C = GCfg<TIN, TILE_S>;
+  const int nbn = col_blocks(s.d, TILE_S);
+  const long long nblk = (max_row_blocks(s, TILE_S) * nbn + 7) / 8 * 8;
+  timing_mark(st, "down_staged", true);
+  down_staged_kernel<C><<<dim3((unsigned)nblk), dim3(C::NT), 0, st>>>(
+      (const TIN*)y_swi, (const TIN*)w_down, offsets, ws.tile_map(TILE_S), (TIN*)ws.ystage, s.d, s.E, s.h, nbn,
+      (int)nblk);
+  timing_mark(st, "down_staged", false);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  timing_mark(st, "gather_sum", true);
+  gather_sum_kernel<TIN><<<dim3(s.T), dim3(256), 0, st>>>((const TIN*)ws.ystage, tim, topk_w, (TIN*)out, s.d, s.K);
+  timing_mark(st, "gather_sum", false);
+  return hipGetLastError();
+}
+
+hipError_t launch_combine_staged(const Shape& s, const void* y_swi, const void* w_down, const int32_t* offsets,
+                                 const int32_t* tim, const float* topk_w, void* out, const ExpertWs& ws,
+                                 hipStream_t st) {
+  return s.bf16 ? combine_staged_t<bf16_t>(s, y_swi, w_down, offsets, tim, topk_w, out, ws, st)
+                : combine_staged_t<float>(s, y_swi, w_down, offsets, tim, topk_w, out, ws, st);
+}
+
+// ===========================================================================
 // Backward
 // ===========================================================================
 

@@ -62,11 +62,12 @@ struct ExpertWs {
   float* dz_pos;       // [A] router logit gradient per position (backward)
   void* dh;            // [A][2h] activation-dtype gradient of the pre-activations (backward)
   void* a_prime;       // [A][h] activation-dtype A' = w * y recomputed from a, b (H-only backward)
+  void* ystage;        // [A][d] activation-dtype staged expert outputs (staged-Y combine ablation)
   size_t bytes;
   int E;
   const int32_t* tile_map(int bm) const { return mb_off + (bm == TILE_L ? E + 1 : 0); }
 };
-enum { WS_EXPERT_FWD = 1, WS_COMBINE = 2, WS_EXPERT_BWD = 3, WS_EXPERT_BWD_H = 4 };
+enum { WS_EXPERT_FWD = 1, WS_COMBINE = 2, WS_EXPERT_BWD = 3, WS_EXPERT_BWD_H = 4, WS_COMBINE_STAGED = 5 };
 
 inline ExpertWs expert_ws(const Shape& s, int which, void* p) {
   ExpertWs w{};
@@ -89,6 +90,7 @@ inline ExpertWs expert_ws(const Shape& s, int which, void* p) {
     w.dh = take(A * 2 * (size_t)s.h * s.elem());
   }
   if (which == WS_EXPERT_BWD_H) w.a_prime = take(A * (size_t)s.h * s.elem());
+  if (which == WS_COMBINE_STAGED) w.ystage = take(A * (size_t)s.d * s.elem());
   w.bytes = off;
   return w;
 }
@@ -106,6 +108,9 @@ hipError_t launch_gate_up(const Shape& s, const void* x, const int32_t* offsets,
                           hipStream_t st);
 hipError_t launch_down_combine(const Shape& s, const void* y_swi, const void* w_down, const int32_t* offsets,
                                const int32_t* eti, void* out, const ExpertWs& ws, int spin_limit, hipStream_t st);
+hipError_t launch_combine_staged(const Shape& s, const void* y_swi, const void* w_down, const int32_t* offsets,
+                                 const int32_t* tim, const float* topk_w, void* out, const ExpertWs& ws,
+                                 hipStream_t st);
 hipError_t launch_backward(const Shape& s, const void* dout, const void* x, const void* wg, const void* w_gate,
                            const void* w_up, const void* w_down, const int32_t* ids, const float* topk_w,
                            const int32_t* offsets, const int32_t* eti, const int32_t* tim, const void* h_ab,

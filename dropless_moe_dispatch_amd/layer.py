@@ -33,6 +33,9 @@ class MoEBuffers:
     # Algorithm 1); "ab" = only H = [a | b] (SonicMoE's minimal cached set):
     # y_swi is then a forward transient and the backward recomputes y
     saved: str = "aby"
+    # forward combine: "fold" (the ordered, buffer-free combine) or "staged"
+    # (the staged-Y ablation, which holds a [T*K, d] buffer in its workspace)
+    combine: str = "fold"
 
     def __post_init__(self):
         dev, td = self.device, torch_dtype(self.dtype)
@@ -51,7 +54,9 @@ class MoEBuffers:
         self.out = torch.empty(T, d, dtype=td, device=dev)
         self.ws_index = self._ws(B.MOE_WS_INDEX)
         self.ws_fwd = self._ws(B.MOE_WS_EXPERT_FWD)
-        self.ws_comb = self._ws(B.MOE_WS_COMBINE)
+        if self.combine not in ("fold", "staged"):
+            raise ValueError(f"combine must be 'fold' or 'staged', not {self.combine!r}")
+        self.ws_comb = self._ws(B.MOE_WS_COMBINE if self.combine == "fold" else B.MOE_WS_COMBINE_STAGED)
         if self.backward:
             self.dx = torch.empty(T, d, dtype=td, device=dev)
             self.dwg = torch.empty(E, d, dtype=f32, device=dev)
@@ -90,7 +95,7 @@ class MoEBuffers:
 
     def device_error_words(self):
         """Ordered-combine error words (nonzero: a bounded wait ran out)."""
-        w = [self.ws_comb[:4]] + ([self.ws_bwd[:4]] if self.backward else [])
+        w = ([self.ws_comb[:4]] if self.combine == "fold" else []) + ([self.ws_bwd[:4]] if self.backward else [])
         return [int(x.view(torch.int32).item()) for x in w]
 
 
@@ -103,8 +108,8 @@ def forward(buf: MoEBuffers, x, wg, bias, w_gate, w_up, w_down, logits_in: bool 
     route(buf, x, wg, bias, logits_in, stream)
     B.moe_build_index(s, buf.topk_ids, buf.offsets, buf.eti, buf.tim, buf.ws_index, stream)
     B.moe_expert_fwd(s, x, buf.offsets, buf.eti, w_gate, w_up, buf.h_ab, buf.y_swi, buf.ws_fwd, stream)
-    B.moe_combine(s, buf.y_swi, w_down, buf.offsets, buf.eti, buf.tim, buf.topk_ids, buf.topk_w, buf.out,
-                  buf.ws_comb, stream)
+    comb = B.moe_combine if buf.combine == "fold" else B.moe_combine_staged
+    comb(s, buf.y_swi, w_down, buf.offsets, buf.eti, buf.tim, buf.topk_ids, buf.topk_w, buf.out, buf.ws_comb, stream)
     return buf.out
 
 

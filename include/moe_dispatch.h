@@ -86,8 +86,9 @@ typedef enum {
   MOE_WS_EXPERT_FWD = 1,  /* moe_expert_fwd */
   MOE_WS_COMBINE = 2,     /* moe_combine */
   MOE_WS_EXPERT_BWD = 3,  /* moe_expert_bwd with the saved y_swi */
-  MOE_WS_EXPERT_BWD_H = 4 /* moe_expert_bwd with y_swi == NULL (H-only saving):
-                             MOE_WS_EXPERT_BWD plus a [T*K, h] dtype buffer */
+  MOE_WS_EXPERT_BWD_H = 4, /* moe_expert_bwd with y_swi == NULL (H-only saving):
+                              MOE_WS_EXPERT_BWD plus a [T*K, h] dtype buffer */
+  MOE_WS_COMBINE_STAGED = 5 /* moe_combine_staged: holds a [T*K, d] dtype buffer */
 } moe_workspace_kind;
 
 /* Bytes of device workspace the call of kind `which` needs for shape *s
@@ -145,6 +146,22 @@ int moe_expert_fwd(const moe_shape* s, const void* x, const int32_t* offsets, co
 int moe_combine(const moe_shape* s, const void* y_swi, const void* w_down, const int32_t* offsets,
                 const int32_t* expert_token_indices, const int32_t* token_index_map, const int32_t* topk_ids,
                 const float* topk_w, void* out, void* ws, size_t ws_bytes, void* stream);
+
+/* Staged-Y combine: an ABLATION of moe_combine, not part of the product path
+ * (SonicMoE analysis page, sec. 3.4.1 on the temporary Y, sec. 3.4.2
+ * "Expert aggregation kernels: gather-and-sum", Figure 17 left: the down
+ * projection stores Y = y_swi W_down^T for every assignment contiguously,
+ * then an aggregation kernel gathers each token's K rows and sums).  It
+ * computes the same out[t] = sum_k topk_w[t,k] * Y[token_index_map[t*K+k]]
+ * as moe_combine, but materialises Y: a [T*K, d] buffer in the activation
+ * dtype inside the workspace (MOE_WS_COMBINE_STAGED).  The sum runs in slot
+ * order k = 0..K-1 in fp32; Y is rounded to the activation dtype before it,
+ * so results differ from moe_combine by that rounding.  Deterministic, no
+ * atomics.  Same arguments and errors as moe_combine. */
+int moe_combine_staged(const moe_shape* s, const void* y_swi, const void* w_down, const int32_t* offsets,
+                       const int32_t* expert_token_indices, const int32_t* token_index_map,
+                       const int32_t* topk_ids, const float* topk_w, void* out, void* ws, size_t ws_bytes,
+                       void* stream);
 
 /* Backward of L = <dout, out> (reading notes Algorithm 1 backward; MoEBlaze
  * analysis page "Backward Pass" and "Fused SwiGLU Kernel"; SonicMoE analysis

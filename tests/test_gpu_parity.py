@@ -118,9 +118,9 @@ LAYER_CASES = [
 ]
 
 
-def _gpu_layer(inp, wl, logits32=None, backward=True, saved="aby"):
+def _gpu_layer(inp, wl, logits32=None, backward=True, saved="aby", combine="fold"):
     dt = wl.dtype
-    buf = Lyr.MoEBuffers(wl.T, wl.d, wl.E, wl.K, wl.h, dt, backward=backward, saved=saved)
+    buf = Lyr.MoEBuffers(wl.T, wl.d, wl.E, wl.K, wl.h, dt, backward=backward, saved=saved, combine=combine)
     dev = {k: Lyr.to_device(inp[k], dt) for k in ("x", "wg", "w_gate", "w_up", "w_down", "dy") if k in inp}
     bias = torch.from_numpy(inp["bias"]).cuda() if inp.get("bias") is not None else None
     if logits32 is not None:
@@ -207,6 +207,34 @@ def test_h_only_leaves_y_independent_gradients_unchanged():
     for key in ("out", "dw_gate", "dw_up"):
         assert torch.equal(getattr(b1, key), getattr(b2, key)), key
     assert not torch.equal(b1.dw_down, b2.dw_down)  # A' comes from a different y rounding
+
+
+STAGED_CASES = [c for c in LAYER_CASES if c[0] in ("ragged", "multi_tile", "skewed", "t1", "tiny_f32", "k_eq_e")]
+
+
+@pytest.mark.parametrize("case", STAGED_CASES, ids=[c[0] for c in STAGED_CASES])
+def test_staged_combine_parity(case):
+    """Staged-Y combine (ablation): same forward outputs within tolerance."""
+    name, T, d, E, K, h, dtype, zipf = case
+    _say("staged_combine", case)
+    wl = synth.small_workload(T, d, E, K, h, dtype=dtype, seed=sum(map(ord, name)) + 3, zipf_s=zipf)
+    inp = synth.make_inputs(wl)
+    z32 = O.router_logits(inp["x"], inp["wg"], inp["bias"]).astype(np.float32)
+    buf, _ = _gpu_layer(inp, wl, logits32=z32, backward=False, combine="staged")
+    _compare_layer(buf, inp, wl, z32, backward=False)
+
+
+def test_staged_combine_repeatable_and_close_to_fold():
+    T, d, E, K, h = 900, 256, 16, 4, 256
+    _say("staged_vs_fold", T, d, E, K, h)
+    wl = synth.small_workload(T, d, E, K, h, seed=41)
+    inp = synth.make_inputs(wl)
+    z32 = O.router_logits(inp["x"], inp["wg"], inp["bias"]).astype(np.float32)
+    a, _ = _gpu_layer(inp, wl, logits32=z32, backward=False, combine="staged")
+    b, _ = _gpu_layer(inp, wl, logits32=z32, backward=False, combine="staged")
+    c, _ = _gpu_layer(inp, wl, logits32=z32, backward=False, combine="fold")
+    assert torch.equal(a.out, b.out)
+    assert_close("staged_vs_fold", to_np(a.out), to_np(c.out))
 
 
 @pytest.mark.parametrize("kind", ["one_expert_set", "zero_rows", "hot_expert"])
