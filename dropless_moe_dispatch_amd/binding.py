@@ -17,6 +17,7 @@ MOE_OK, MOE_ERR_INVALID_ARG, MOE_ERR_UNSUPPORTED, MOE_ERR_WORKSPACE, MOE_ERR_HIP
 MOE_F32, MOE_BF16 = 0, 1
 MOE_WS_INDEX, MOE_WS_EXPERT_FWD, MOE_WS_COMBINE, MOE_WS_EXPERT_BWD, MOE_WS_EXPERT_BWD_H = 0, 1, 2, 3, 4
 MOE_WS_COMBINE_STAGED = 5
+MOE_WS_INDEX_DENSE = 6
 
 
 class MoeShape(ctypes.Structure):
@@ -46,11 +47,12 @@ def lib():
         L.moe_workspace_bytes.restype = ctypes.c_size_t
         L.moe_route_topk.argtypes = [sp, _P, _P, _P, _P, _P, _P, _P]
         L.moe_build_index.argtypes = [sp, _P, _P, _P, _P, _P, ctypes.c_size_t, _P]
+        L.moe_build_index_dense.argtypes = [sp, _P, _P, _P, _P, _P, ctypes.c_size_t, _P]
         L.moe_expert_fwd.argtypes = [sp, _P, _P, _P, _P, _P, _P, _P, _P, ctypes.c_size_t, _P]
         L.moe_combine.argtypes = [sp, _P, _P, _P, _P, _P, _P, _P, _P, _P, ctypes.c_size_t, _P]
         L.moe_combine_staged.argtypes = [sp, _P, _P, _P, _P, _P, _P, _P, _P, _P, ctypes.c_size_t, _P]
         L.moe_expert_bwd.argtypes = [sp] + [_P] * 20 + [ctypes.c_size_t, _P]
-        for f in ("moe_route_topk", "moe_build_index", "moe_expert_fwd", "moe_combine", "moe_combine_staged", "moe_expert_bwd"):
+        for f in ("moe_route_topk", "moe_build_index", "moe_build_index_dense", "moe_expert_fwd", "moe_combine", "moe_combine_staged", "moe_expert_bwd"):
             getattr(L, f).restype = ctypes.c_int
         L.moe_status_string.argtypes = [ctypes.c_int]
         L.moe_status_string.restype = ctypes.c_char_p
@@ -113,6 +115,15 @@ def moe_build_index(s, topk_ids, offsets, eti, tim, ws, stream=None, check=True,
                                _nbytes(ws) if ws_bytes is None else ws_bytes, _stream(stream))
     if check:
         _check("moe_build_index", rc)
+    return rc
+
+
+def moe_build_index_dense(s, topk_ids, offsets, eti, tim, ws, stream=None, check=True, ws_bytes=None):
+    """The same index through MoEBlaze's literal three steps (dense [E][T] map)."""
+    rc = lib().moe_build_index_dense(ctypes.byref(s), _ptr(topk_ids), _ptr(offsets), _ptr(eti), _ptr(tim), _ptr(ws),
+                                     _nbytes(ws) if ws_bytes is None else ws_bytes, _stream(stream))
+    if check:
+        _check("moe_build_index_dense", rc)
     return rc
 
 

@@ -13,7 +13,7 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(HERE, "csrc")
 OUT_DIR = os.path.join(HERE, "lib")
 LIB = os.path.join(OUT_DIR, "libmoe_dispatch.so")
-SOURCES = ["api.hip", "route.hip", "index.hip", "experts.hip"]
+SOURCES = ["api.hip", "route.hip", "index.hip", "index_dense.hip", "experts.hip"]
 ARCH = "gfx950"
 
 

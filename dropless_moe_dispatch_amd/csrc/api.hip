@@ -103,6 +103,7 @@ size_t moe_workspace_bytes(const moe_shape* s, int which) {
     case MOE_WS_EXPERT_BWD: return expert_ws(sh, WS_EXPERT_BWD, nullptr).bytes;
     case MOE_WS_EXPERT_BWD_H: return expert_ws(sh, WS_EXPERT_BWD_H, nullptr).bytes;
     case MOE_WS_COMBINE_STAGED: return expert_ws(sh, WS_COMBINE_STAGED, nullptr).bytes;
+    case MOE_WS_INDEX_DENSE: return dense_index_ws(sh, nullptr).bytes;
     default: return 0;
   }
 }
@@ -158,6 +159,23 @@ int moe_build_index(const moe_shape* s, const int32_t* topk_ids, int32_t* offset
   if (ws_bytes < w.bytes) return MOE_ERR_WORKSPACE;
   return hip_status(launch_build_index(sh, topk_ids, offsets, expert_token_indices, token_index_map, w,
                                        (hipStream_t)stream));
+}
+
+int moe_build_index_dense(const moe_shape* s, const int32_t* topk_ids, int32_t* offsets,
+                          int32_t* expert_token_indices, int32_t* token_index_map, void* ws, size_t ws_bytes,
+                          void* stream) {
+  Shape sh;
+  int rc = check_shape(s, &sh);
+  if (rc) return rc;
+  REQ(topk_ids);
+  REQ(offsets);
+  REQ(expert_token_indices);
+  REQ(token_index_map);
+  REQ(ws);
+  const DenseIndexWs w = dense_index_ws(sh, ws);
+  if (ws_bytes < w.bytes) return MOE_ERR_WORKSPACE;
+  return hip_status(launch_build_index_dense(sh, topk_ids, offsets, expert_token_indices, token_index_map, w,
+                                             (hipStream_t)stream));
 }
 
 int moe_expert_fwd(const moe_shape* s, const void* x, const int32_t* offsets, const int32_t* expert_token_indices,

@@ -50,6 +50,24 @@ inline IndexWs index_ws(const Shape& s, void* p) {
   return w;
 }
 
+// ---- dense-map index workspace (the literal three-step backend) -----------
+struct DenseIndexWs {
+  int32_t* d5;         // [E][T] token id or -1
+  int32_t* loc;        // [E][T] position in expert_token_indices (where d5 >= 0)
+  int32_t* lengths;    // [E]
+  size_t bytes;
+};
+inline DenseIndexWs dense_index_ws(const Shape& s, void* p) {
+  DenseIndexWs w{};
+  size_t off = 0;
+  auto take = [&](size_t bytes) { void* q = (char*)p + off; off = align_up(off + bytes, 256); return q; };
+  w.d5 = (int32_t*)take((size_t)s.E * s.T * 4);
+  w.loc = (int32_t*)take((size_t)s.E * s.T * 4);
+  w.lengths = (int32_t*)take((size_t)s.E * 4);
+  w.bytes = off;
+  return w;
+}
+
 // ---- per-call expert workspace (tile map, per-position data, fold state) --
 struct ExpertWs {
   int32_t* counters;   // [N_COUNTERS]
@@ -101,6 +119,8 @@ hipError_t launch_router_logits(const Shape& s, const void* x, const void* wg, c
 hipError_t launch_topk(const Shape& s, const float* logits, int32_t* ids, float* w, hipStream_t st);
 hipError_t launch_build_index(const Shape& s, const int32_t* ids, int32_t* offsets, int32_t* eti, int32_t* tim,
                               const IndexWs& ws, hipStream_t st);
+hipError_t launch_build_index_dense(const Shape& s, const int32_t* ids, int32_t* offsets, int32_t* eti, int32_t* tim,
+                                    const DenseIndexWs& ws, hipStream_t st);
 hipError_t launch_prep(const Shape& s, const ExpertWs& ws, const int32_t* offsets, const int32_t* ids,
                        const float* topk_w, const int32_t* tim, bool per_position, hipStream_t st);
 hipError_t launch_gate_up(const Shape& s, const void* x, const int32_t* offsets, const int32_t* eti,

@@ -88,7 +88,8 @@ typedef enum {
   MOE_WS_EXPERT_BWD = 3,  /* moe_expert_bwd with the saved y_swi */
   MOE_WS_EXPERT_BWD_H = 4, /* moe_expert_bwd with y_swi == NULL (H-only saving):
                               MOE_WS_EXPERT_BWD plus a [T*K, h] dtype buffer */
-  MOE_WS_COMBINE_STAGED = 5 /* moe_combine_staged: holds a [T*K, d] dtype buffer */
+  MOE_WS_COMBINE_STAGED = 5, /* moe_combine_staged: holds a [T*K, d] dtype buffer */
+  MOE_WS_INDEX_DENSE = 6     /* moe_build_index_dense: two [E, T] int32 maps */
 } moe_workspace_kind;
 
 /* Bytes of device workspace the call of kind `which` needs for shape *s
@@ -121,6 +122,19 @@ int moe_route_topk(const moe_shape* s, const void* x, const void* wg, const floa
  * Bit-exact and deterministic.  ws: MOE_WS_INDEX workspace. */
 int moe_build_index(const moe_shape* s, const int32_t* topk_ids, int32_t* offsets, int32_t* expert_token_indices,
                     int32_t* token_index_map, void* ws, size_t ws_bytes, void* stream);
+
+/* The same routing index, built by MoEBlaze's three steps taken literally
+ * (MoEBlaze analysis page, "Dispatch Data Structure Construction: The
+ * Atomic-Free Three-Step Algorithm"): a dense token-expert map [E][T]
+ * (token id or -1), one workgroup per expert to count its column, an
+ * exclusive scan of the lengths, one workgroup per expert for the tile-level
+ * scan that gives each entry its position (the location map), and a final
+ * conflict-free scatter.  Same arguments, outputs and errors as
+ * moe_build_index, and the same arrays bit for bit; the workspace
+ * (MOE_WS_INDEX_DENSE) grows as T*E.  An alternate backend for comparison. */
+int moe_build_index_dense(const moe_shape* s, const int32_t* topk_ids, int32_t* offsets,
+                          int32_t* expert_token_indices, int32_t* token_index_map, void* ws, size_t ws_bytes,
+                          void* stream);
 
 /* Gate/up grouped GEMM with the SwiGLU epilogue, gathering x rows in place
  * through expert_token_indices (MoEBlaze analysis page, "Fused SwiGLU Kernel

@@ -35,7 +35,7 @@ def test_status_strings():
 
 def test_workspace_sizes_depend_on_shape_only():
     s = B.shape(16384, 2048, 128, 8, 768)
-    sizes = [B.workspace_bytes(s, w) for w in range(6)]
+    sizes = [B.workspace_bytes(s, w) for w in range(7)]
     assert all(n > 0 for n in sizes)
     assert B.workspace_bytes(s, 7) == 0
     # the H-only backward workspace adds exactly the [T*K, h] A' buffer (256-byte aligned)
@@ -43,6 +43,8 @@ def test_workspace_sizes_depend_on_shape_only():
     assert 16384 * 8 * 768 * 2 <= extra < 16384 * 8 * 768 * 2 + 256
     # the staged-Y ablation's workspace is the one that holds a T*K*d buffer
     assert sizes[B.MOE_WS_COMBINE_STAGED] >= 16384 * 8 * 2048 * 2
+    # the dense-map index backend holds two [E][T] int32 maps
+    assert 2 * 128 * 16384 * 4 <= sizes[B.MOE_WS_INDEX_DENSE] < 2 * 128 * 16384 * 4 + 1024
     # combine workspace holds the fp32 [T,d] fold accumulator, not a [T*K,d] buffer
     comb = sizes[B.MOE_WS_COMBINE]
     assert 16384 * 2048 * 4 <= comb < 16384 * 8 * 2048 * 2

@@ -66,14 +66,21 @@ INDEX_CASES = [
 ]
 
 
+@pytest.mark.parametrize("backend", ["ballot", "dense"])
 @pytest.mark.parametrize("T,E,K,kind", INDEX_CASES)
-def test_index_bitexact(T, E, K, kind):
-    _say("index", T, E, K, kind)
+def test_index_bitexact(T, E, K, kind, backend):
+    """Both index backends: the wave-ballot counting sort and MoEBlaze's
+    literal three steps with a dense [E][T] map."""
+    _say("index", backend, T, E, K, kind)
     z = synth.structured_logits(T, E, K, kind, seed=2 * T + E)
     ids_np = O.topk_select(z, K)
     buf = Lyr.MoEBuffers(T, 128, E, K, 128, "bf16", backward=False)
     buf.topk_ids.copy_(torch.from_numpy(ids_np))
-    B.moe_build_index(buf.shape, buf.topk_ids, buf.offsets, buf.eti, buf.tim, buf.ws_index)
+    if backend == "ballot":
+        B.moe_build_index(buf.shape, buf.topk_ids, buf.offsets, buf.eti, buf.tim, buf.ws_index)
+    else:
+        ws = torch.empty(B.workspace_bytes(buf.shape, B.MOE_WS_INDEX_DENSE), dtype=torch.uint8, device="cuda")
+        B.moe_build_index_dense(buf.shape, buf.topk_ids, buf.offsets, buf.eti, buf.tim, ws)
     torch.cuda.synchronize()
     ix = O.build_index(ids_np, E)
     assert np.array_equal(to_np(buf.offsets), ix["offsets"])
