@@ -96,6 +96,23 @@ def silu_grad(u):
     return s + u * s * (1.0 - s)
 
 
+def relu(u):
+    return np.maximum(u, 0.0)
+
+
+def relu_grad(u):
+    """d ReLU / du: 1 where u > 0, else 0 (0 at the kink)."""
+    return (np.asarray(u) > 0.0).astype(np.float64)
+
+
+# Expert feed-forward kinds.  "swiglu": y = SiLU(x W_gate^T) * (x W_up^T), the
+# gated expert of MoEBlaze sec. 5 (Algorithm 1).  "silu" / "relu": the plain
+# two-layer expert E_i(x) = W_2 sigma(W_1 x) of the MoEBlaze reading notes
+# (sec. 2.2, expert FFNs) with sigma = SiLU or ReLU; W_1 is passed as w_gate
+# and there is no w_up.
+ACTS = {"silu": (silu, silu_grad), "relu": (relu, relu_grad)}
+
+
 # ---------------------------------------------------------------------------
 # a1: router logits   topk experts = TopK(softmax(W_g x)), W_g in R^{E x d}  [MBn sec. 2.1]
 # ---------------------------------------------------------------------------
@@ -204,12 +221,16 @@ def _rows_of(ids, k, e):
     return np.nonzero(ids[:, k] == e)[0]
 
 
-def moe_forward(x, ids, w, w_gate, w_up, w_down, dtype="bf16", only_experts=None):
+def moe_forward(x, ids, w, w_gate, w_up, w_down, dtype="bf16", only_experts=None, act="swiglu"):
     """Forward pass.  Returns out [T,d] plus the per-assignment tensors
     a_s, b_s, y_s [T,K,h] (storage-rounded) and ye [T,K,d] (expert output).
 
     ``only_experts`` (for sampled checks) evaluates only the assignments of
-    those experts; quantities of the other assignments stay zero."""
+    those experts; quantities of the other assignments stay zero.
+    ``act``: "swiglu" (gated), or "silu" / "relu" (two-layer expert with
+    W_1 = w_gate; w_up is unused and b_s stays zero)."""
+    if act not in ("swiglu", *ACTS):
+        raise ValueError(f"unknown activation {act!r}")
     st = storage_rounder(dtype)
     x = _f64(x)
     w = _f64(w)
@@ -227,12 +248,15 @@ def moe_forward(x, ids, w, w_gate, w_up, w_down, dtype="bf16", only_experts=None
             if len(r) == 0:
                 continue
             xe = x[r]
-            a = xe @ _f64(w_gate[e]).T       # gate projection
-            b = xe @ _f64(w_up[e]).T         # up projection
-            y = st(silu(a) * b)              # SiLU(a) * b from the unrounded a, b
+            a = xe @ _f64(w_gate[e]).T       # gate projection (W_1 of a plain expert)
+            if act == "swiglu":
+                b = xe @ _f64(w_up[e]).T     # up projection
+                y = st(silu(a) * b)          # SiLU(a) * b from the unrounded a, b
+                b_s[r, k] = st(b)
+            else:
+                y = st(ACTS[act][0](a))      # sigma(a) from the unrounded a
             yo = y @ _f64(w_down[e]).T       # down projection
             a_s[r, k] = st(a)
-            b_s[r, k] = st(b)
             y_s[r, k] = y
             ye[r, k] = yo
             out[r] += w[r, k][:, None] * yo
@@ -248,7 +272,7 @@ def moe_forward(x, ids, w, w_gate, w_up, w_down, dtype="bf16", only_experts=None
 
 
 def moe_backward(dy, x, wg, ids, w, w_gate, w_up, w_down, fwd, z, dtype="bf16", only_experts=None,
-                 saved="aby"):
+                 saved="aby", act="swiglu"):
     """Backward pass.  ``z`` are the logits the weights were computed from.
     ``only_experts`` restricts the expert path to those experts (the weight
     gradients of those experts are then complete; dx, ds, dwg are not).
@@ -292,20 +316,29 @@ def moe_backward(dy, x, wg, ids, w, w_gate, w_up, w_down, fwd, z, dtype="bf16", 
             a = fwd["a_s"][r, k]
             b = fwd["b_s"][r, k]
             # the y the backward sees: the stored one, or recomputed from H
-            y_b = fwd["y_s"][r, k] if saved == "aby" else silu(a) * b
+            if saved == "aby":
+                y_b = fwd["y_s"][r, k]
+            else:
+                y_b = silu(a) * b if act == "swiglu" else ACTS[act][0](a)
             ds[r, k] = np.einsum("rd,rd->r", g, fwd["ye"][r, k])      # <dO, Y>
             ds_alt[r, k] = np.einsum("rh,rh->r", da_p, y_b)           # <dA', y>
             dyv = w[r, k][:, None] * da_p              # gradient reaching y
-            da = st(dyv * b * silu_grad(a))            # SiLU recomputed from stored a
-            db = st(dyv * silu(a))
+            if act == "swiglu":
+                da = st(dyv * b * silu_grad(a))        # SiLU recomputed from stored a
+                db = st(dyv * silu(a))
+                dh_b[r, k] = db
+            else:
+                da = st(dyv * ACTS[act][1](a))         # sigma' recomputed from stored a
+                db = None
             dh_a[r, k] = da
-            dh_b[r, k] = db
             # A' = w * y, held in the storage type (SonicMoE sec. 3.4.1: dW2 = A'^T dO)
             a_prime = st(w[r, k][:, None] * y_b)
             dw_down[e] += g.T @ a_prime
             dw_gate[e] += da.T @ x[r]
-            dw_up[e] += db.T @ x[r]
-            dx[r] += da @ _f64(w_gate[e]) + db @ _f64(w_up[e])
+            dx[r] += da @ _f64(w_gate[e])
+            if db is not None:
+                dw_up[e] += db.T @ x[r]
+                dx[r] += db @ _f64(w_up[e])
     # the router gradient takes the dS the backward has: the plain <dO, Y>
     # with the stored y, or <dA', y> with y recomputed from H (H-only: the
     # forward's y is gone, SonicMoE sec. 3.4.1 forms dS from the recomputed y)
@@ -355,19 +388,19 @@ def router_backward_closed(w, ids, ds, E: int) -> np.ndarray:
 # ---------------------------------------------------------------------------
 
 
-def layer_loss(x, wg, bias, w_gate, w_up, w_down, dy, ids):
+def layer_loss(x, wg, bias, w_gate, w_up, w_down, dy, ids, act="swiglu"):
     """L = <dY, out> of the pure float64 layer with the routing set ``ids``
     held fixed (the weights w still depend on the logits)."""
     z = router_logits(x, wg, bias)
     w = topk_weights(z, ids)
-    f = moe_forward(x, ids, w, w_gate, w_up, w_down, dtype=None)
+    f = moe_forward(x, ids, w, w_gate, w_up, w_down, dtype=None, act=act)
     return float((_f64(dy) * f["out_f64"]).sum())
 
 
-def layer_grads(x, wg, bias, w_gate, w_up, w_down, dy, K):
+def layer_grads(x, wg, bias, w_gate, w_up, w_down, dy, K, act="swiglu"):
     """Pure float64 forward + backward of the whole layer."""
     z = router_logits(x, wg, bias)
     ids, w = route(z, K)
-    f = moe_forward(x, ids, w, w_gate, w_up, w_down, dtype=None)
-    b = moe_backward(dy, x, wg, ids, w, w_gate, w_up, w_down, f, z, dtype=None)
+    f = moe_forward(x, ids, w, w_gate, w_up, w_down, dtype=None, act=act)
+    b = moe_backward(dy, x, wg, ids, w, w_gate, w_up, w_down, f, z, dtype=None, act=act)
     return z, ids, w, f, b

@@ -370,3 +370,60 @@ def test_h_only_differs_from_stored_y_by_y_rounding_only():
     assert 0 < rel < 2 ** -6, rel
     rel = np.abs(bh["ds_alt"] - b["ds_alt"]).max() / np.abs(b["ds_alt"]).max()
     assert rel < 2 ** -6, rel
+
+
+# --------------------------------------------------------------------------
+# non-gated experts: E_i(x) = W_2 sigma(W_1 x), sigma = SiLU or ReLU
+# --------------------------------------------------------------------------
+
+@pytest.mark.parametrize("act", ["silu", "relu"])
+def test_non_gated_forward_reduces_to_dense_mlp_when_single_expert(act):
+    x, wg, w1, _, w2, dy = _small_layer(E=1, K=1, seed=2)
+    z = O.router_logits(x, wg)
+    ids, w = O.route(z, 1)
+    f = O.moe_forward(x, ids, w, w1, None, w2, dtype=None, act=act)
+    a = x @ w1[0].T
+    hid = a / (1 + np.exp(-a)) if act == "silu" else np.where(a > 0, a, 0.0)
+    np.testing.assert_allclose(f["out"], hid @ w2[0].T, rtol=1e-12, atol=1e-12)
+    assert np.all(f["b_s"] == 0.0)
+
+
+@pytest.mark.parametrize("act", ["silu", "relu"])
+@pytest.mark.parametrize("E,K", [(4, 2), (3, 3)])
+def test_non_gated_backward_finite_differences(act, E, K):
+    T, d, h = 16, 8, 8
+    x, wg, w1, _, w2, dy = _small_layer(T=T, d=d, E=E, K=K, h=h, seed=E * 7 + K, scale_router=3.0)
+    z, ids, w, f, b = O.layer_grads(x, wg, None, w1, None, w2, dy, K, act=act)
+    assert _margin(z, K) > 1e-3
+    if act == "relu":   # stay off the kink: every pre-activation clear of zero by >> eps
+        assert np.abs(f["a_s"][f["a_s"] != 0]).min() > 1e-4
+    eps = 1e-6
+    rng = np.random.default_rng(7)
+    params = dict(x=x, wg=wg, w1=w1, w2=w2)
+    grads = dict(x=b["dx"], wg=b["dwg"], w1=b["dw_gate"], w2=b["dw_down"])
+    for name, P in params.items():
+        for _ in range(2):
+            V = rng.standard_normal(P.shape)
+            args = dict(params)
+            args[name] = P + eps * V
+            lp = O.layer_loss(args["x"], args["wg"], None, args["w1"], None, args["w2"], dy, ids, act=act)
+            args[name] = P - eps * V
+            lm = O.layer_loss(args["x"], args["wg"], None, args["w1"], None, args["w2"], dy, ids, act=act)
+            fd = (lp - lm) / (2 * eps)
+            an = float((grads[name] * V).sum())
+            assert abs(fd - an) <= 1e-6 * max(1.0, abs(an)), (act, name, fd, an)
+    assert np.all(b["dw_up"] == 0.0)
+
+
+def test_relu_expert_rows_with_negative_preactivation_are_inert():
+    """ReLU: an assignment whose pre-activations are all negative adds
+    nothing to out and passes no gradient to W_1 or x (only the router
+    term remains)."""
+    x, wg, w1, _, w2, dy = _small_layer(T=10, E=2, K=1, seed=9)
+    w1 = np.abs(w1)
+    x[3] = -np.abs(x[3])                      # token 3: a = x W1^T < 0 for both experts
+    z, ids, w, f, b = O.layer_grads(x, wg, None, w1, None, w2, dy, 1, act="relu")
+    assert np.all(f["a_s"][3] < 0)
+    np.testing.assert_array_equal(f["out"][3], 0.0)
+    np.testing.assert_array_equal(b["dh_a"][3], 0.0)
+    np.testing.assert_allclose(b["dx"][3], b["dz"][3] @ wg, rtol=1e-12, atol=1e-14)
