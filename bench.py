@@ -52,17 +52,20 @@ def committed_traffic(workload, kernel):
     return None if k is None else k.get("hbm_bytes_per_launch")
 
 
-def kernel_flops(name, T, d, E, K, h):
+def kernel_flops(name, T, d, E, K, h, gated=True):
+    """Model FLOP of one launch; a plain two-layer expert has one first-layer
+    projection where the gated one has two (gate and up)."""
     A = T * K
+    g = 2.0 if gated else 1.0
     return {
         "router_logits": 2.0 * T * d * E,
-        "gate_up": 4.0 * A * d * h,
+        "gate_up": 2.0 * g * A * d * h,
         "down_combine": 2.0 * A * d * h,
         "down_staged": 2.0 * A * d * h,
         "dh": 2.0 * A * d * h,
         "dw_down": 2.0 * A * d * h,
-        "dw_gate_up": 4.0 * A * d * h,
-        "dx_fold": 4.0 * A * d * h,
+        "dw_gate_up": 2.0 * g * A * d * h,
+        "dx_fold": 2.0 * g * A * d * h,
     }.get(name)
 
 
@@ -110,9 +113,10 @@ def cpu_baseline(wl, inp, sample_tokens):
     z = O.router_logits(x, inp["wg"], inp["bias"])
     ids, w = O.route(z.astype(np.float32).astype(np.float64), wl.K)
     O.build_index(ids, wl.E)
-    f = O.moe_forward(x, ids, w, inp["w_gate"], inp["w_up"], inp["w_down"], dtype=wl.dtype)
+    f = O.moe_forward(x, ids, w, inp["w_gate"], inp["w_up"], inp["w_down"], dtype=wl.dtype, act=wl.act)
     if wl.backward:
-        O.moe_backward(dy, x, inp["wg"], ids, w, inp["w_gate"], inp["w_up"], inp["w_down"], f, z, dtype=wl.dtype)
+        O.moe_backward(dy, x, inp["wg"], ids, w, inp["w_gate"], inp["w_up"], inp["w_down"], f, z, dtype=wl.dtype,
+                       act=wl.act)
     dt = time.perf_counter() - t0
     return {"value": n / dt, "unit": "tokens/s", "cores": int(cores), "kind": "oracle",
             "sample": f"first {n} tokens of the workload, router+index+forward" + ("+backward" if wl.backward else "")
@@ -124,7 +128,7 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=3)
-    ap.add_argument("--workload", type=int, default=3, help="1..5 (default 3: fine-grained fwd+bwd)")
+    ap.add_argument("--workload", type=int, default=3, help="1..9 (default 3: fine-grained fwd+bwd; 6..9: MoEBlaze's shapes, SiLU experts)")
     ap.add_argument("--cpu-sample", type=int, default=64, help="tokens for the CPU oracle baseline (0 = skip)")
     ap.add_argument("--saved", default="aby", choices=("aby", "ab"),
                     help="saved for backward: a, b and y (default) or H-only (y recomputed)")
@@ -151,12 +155,14 @@ def main():
     torch.cuda.set_device(0)
     print(f"[bench] generating workload {wl.name}", file=sys.stderr, flush=True)
     inp = synth.make_inputs(wl, tensors=("x", "wg", "w_gate", "w_up", "w_down") + (("dy",) if wl.backward else ()))
-    dev = {k: L.to_device(inp[k], dt) for k in ("x", "wg", "w_gate", "w_up", "w_down", "dy") if k in inp}
+    dev = {k: (L.to_device(inp[k], dt) if inp[k] is not None else None)
+           for k in ("x", "wg", "w_gate", "w_up", "w_down", "dy") if k in inp}
     bias = torch.from_numpy(inp["bias"]).cuda() if inp["bias"] is not None else None
     torch.cuda.synchronize()
     base_alloc = torch.cuda.memory_allocated()
     torch.cuda.reset_peak_memory_stats()
-    buf = L.MoEBuffers(T, d, E, K, h, dt, backward=wl.backward, saved=args.saved, combine=args.combine)
+    buf = L.MoEBuffers(T, d, E, K, h, dt, backward=wl.backward, saved=args.saved, combine=args.combine,
+                       act=wl.act)
 
     def step():
         L.forward(buf, dev["x"], dev["wg"], bias, dev["w_gate"], dev["w_up"], dev["w_down"])
@@ -191,17 +197,20 @@ def main():
     errs = buf.device_error_words()
 
     ms = (t1 - t0) * 1e3 / args.steps
-    flops = (18.0 if wl.backward else 6.0) * T * K * d * h
+    gated = wl.act == "swiglu"
+    # model FLOP (SonicMoE convention): gated 6 A d h forward + 12 backward;
+    # a plain two-layer expert 4 + 8
+    flops = ((18.0 if wl.backward else 6.0) if gated else (12.0 if wl.backward else 4.0)) * T * K * d * h
     tflops = flops / (ms * 1e-3) / 1e12
     per = {}
     for name, t in recs:
         per.setdefault(name, []).append(t)
     per_kernel = {k: {"avg_ms": float(np.mean(v)), "launches": len(v)} for k, v in per.items()}
     roofline = None
-    gemms = {k: v for k, v in per_kernel.items() if kernel_flops(k, T, d, E, K, h) is not None and k != "router_logits"}
+    gemms = {k: v for k, v in per_kernel.items() if kernel_flops(k, T, d, E, K, h, gated) is not None and k != "router_logits"}
     if gemms:
         dom = max(gemms, key=lambda k: gemms[k]["avg_ms"] * gemms[k]["launches"])
-        fl = kernel_flops(dom, T, d, E, K, h)
+        fl = kernel_flops(dom, T, d, E, K, h, gated)
         ach = fl / (gemms[dom]["avg_ms"] * 1e-3) / 1e12
         peak = PEAK_BF16_TFLOPS if dt == "bf16" else PEAK_F32_MFMA_TFLOPS
         roofline = {"bound": "mfma", "kernel": dom, "achieved": round(ach, 2), "peak": peak, "unit": "TFLOP/s",
@@ -213,7 +222,7 @@ def main():
     kernels = {}
     for k, v in per_kernel.items():
         rec = {"avg_ms": round(v["avg_ms"], 4)}
-        fl = kernel_flops(k, T, d, E, K, h)
+        fl = kernel_flops(k, T, d, E, K, h, gated)
         if fl is not None:
             rec["tflops"] = round(fl / (v["avg_ms"] * 1e-3) / 1e12, 1)
             rec["mfma_peak_frac"] = round(rec["tflops"] / peak, 4)
@@ -238,7 +247,7 @@ def main():
         "dtype": dt,
         "data": "synthetic (seeded Philox normals, random-init weights)",
         "config": {"workload": wl.name, "T": T, "d": d, "E": E, "K": K, "h": h,
-                   "backward": wl.backward, "zipf_s": wl.zipf_s, "seed": wl.seed, "saved": args.saved,
+                   "backward": wl.backward, "zipf_s": wl.zipf_s, "seed": wl.seed, "act": wl.act, "saved": args.saved,
                    "combine": args.combine},
         "tflops": round(tflops, 2),
         "mfma_peak_frac": round(tflops / (PEAK_BF16_TFLOPS if dt == "bf16" else PEAK_F32_MFMA_TFLOPS), 4),

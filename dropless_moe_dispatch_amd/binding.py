@@ -20,9 +20,13 @@ MOE_WS_COMBINE_STAGED = 5
 MOE_WS_INDEX_DENSE = 6
 
 
+MOE_ACT_SWIGLU, MOE_ACT_SILU, MOE_ACT_RELU = 0, 1, 2
+ACTS = {"swiglu": MOE_ACT_SWIGLU, "silu": MOE_ACT_SILU, "relu": MOE_ACT_RELU}
+
+
 class MoeShape(ctypes.Structure):
     _fields_ = [("T", ctypes.c_int32), ("d", ctypes.c_int32), ("E", ctypes.c_int32), ("K", ctypes.c_int32),
-                ("h", ctypes.c_int32), ("dtype", ctypes.c_int32)]
+                ("h", ctypes.c_int32), ("dtype", ctypes.c_int32), ("act", ctypes.c_int32)]
 
 
 class MoeError(RuntimeError):
@@ -70,8 +74,9 @@ def status_string(code: int) -> str:
     return lib().moe_status_string(code).decode()
 
 
-def shape(T, d, E, K, h, dtype="bf16") -> MoeShape:
-    return MoeShape(T, d, E, K, h, MOE_BF16 if dtype == "bf16" else MOE_F32)
+def shape(T, d, E, K, h, dtype="bf16", act="swiglu") -> MoeShape:
+    """act: "swiglu" (gated expert), "silu" or "relu" (plain two-layer expert)."""
+    return MoeShape(T, d, E, K, h, MOE_BF16 if dtype == "bf16" else MOE_F32, ACTS[act])
 
 
 def workspace_bytes(s: MoeShape, which: int) -> int:

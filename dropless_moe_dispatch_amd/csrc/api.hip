@@ -69,7 +69,9 @@ int check_shape(const moe_shape* s, Shape* out) {
   if ((long long)s->T * s->d >= (1LL << 40)) return MOE_ERR_INVALID_ARG;
   if (s->E > 1024 || s->K > 32) return MOE_ERR_UNSUPPORTED;
   if (s->d % 128 != 0 || s->h % 128 != 0) return MOE_ERR_UNSUPPORTED;
+  if (s->act != MOE_ACT_SWIGLU && s->act != MOE_ACT_SILU && s->act != MOE_ACT_RELU) return MOE_ERR_INVALID_ARG;
   out->T = s->T;
+  out->act = s->act;
   out->d = s->d;
   out->E = s->E;
   out->K = s->K;
@@ -188,7 +190,8 @@ int moe_expert_fwd(const moe_shape* s, const void* x, const int32_t* offsets, co
   REQ(offsets);
   REQ(expert_token_indices);
   REQ(w_gate);
-  REQ(w_up);
+  if (sh.gated()) REQ(w_up);
+  else OPT(w_up);  // plain two-layer expert: no up projection
   REQ(h_ab);
   REQ(y_swi);
   REQ(ws);
@@ -258,7 +261,8 @@ int moe_expert_bwd(const moe_shape* s, const void* dout, const void* x, const vo
   REQ(x);
   REQ(wg);
   REQ(w_gate);
-  REQ(w_up);
+  if (sh.gated()) REQ(w_up);
+  else OPT(w_up);  // plain two-layer expert: no up projection
   REQ(w_down);
   REQ(topk_ids);
   REQ(topk_w);
@@ -270,7 +274,8 @@ int moe_expert_bwd(const moe_shape* s, const void* dout, const void* x, const vo
   REQ(dx);
   REQ(dwg);
   REQ(dw_gate);
-  REQ(dw_up);
+  if (sh.gated()) REQ(dw_up);
+  else OPT(dw_up);
   REQ(dw_down);
   OPT(ds);
   REQ(ws);

@@ -37,6 +37,15 @@ template <> struct ElemT<bf16_t> {
 
 MOE_DEV float sigmoidf_(float u) { return 1.0f / (1.0f + expf(-u)); }
 
+// Activation of a plain two-layer expert (act: 1 = SiLU, 2 = ReLU) and its
+// derivative (ReLU: 0 at the kink).
+MOE_DEV float act_fwd(float a, int act) { return act == 2 ? (a > 0.0f ? a : 0.0f) : a * sigmoidf_(a); }
+MOE_DEV float act_grad(float a, int act) {
+  if (act == 2) return a > 0.0f ? 1.0f : 0.0f;
+  const float s = sigmoidf_(a);
+  return s * (1.0f + a * (1.0f - s));
+}
+
 MOE_DEV int lane_id() { return (int)(threadIdx.x & 63); }
 
 // ---------------------------------------------------------------------------

@@ -140,6 +140,71 @@ static hipError_t gate_up_t(const Shape& s, const void* x, const int32_t* offset
   return hipGetLastError();
 }
 
+// Forward first layer of a plain two-layer expert: a = x W_1^T (W_1 in the
+// w_gate slot), y = sigma(a) (SiLU or ReLU) from the fp32 a; stores a (the
+// saved pre-activation, [A][h]) and y.
+template <class C>
+__global__ __launch_bounds__(C::NT, C::WAVES_PER_EU) void up_act_kernel(
+    const typename C::T* __restrict__ x, const int32_t* __restrict__ offsets, const int32_t* __restrict__ eti,
+    const int32_t* __restrict__ mb_off, const typename C::T* __restrict__ w1, typename C::T* __restrict__ h_a,
+    typename C::T* __restrict__ y_swi, int T, int d, int E, int h, int act, int nbn, int nblk) {
+  __shared__ __attribute__((aligned(16))) char smem[C::LDS_BYTES];
+  using TIN = typename C::T;
+  const int id = xcd_swizzle(blockIdx.x, nblk);
+  const int g = id / nbn, nb = id % nbn;
+  if (g >= mb_off[E]) return;
+  const RowTile rt = decode_row_tile<C::BM>(mb_off, offsets, E, g);
+  const int wave = threadIdx.x >> 6, wm = wave / C::WN, wn = wave % C::WN;
+  const uint32_t ldx = (uint32_t)d * sizeof(TIN);
+  using LA = RowLoader<C::BM, false, C::NT>;
+  using LB = RowLoader<C::BN, false, C::NT>;
+  LA la;
+  LB lb;
+  la.rs[0] = make_rsrc(x, (size_t)T * ldx);
+#pragma unroll
+  for (int i = 0; i < LA::CPT; ++i) {
+    const int p = rt.r0 + LA::my_row(i);
+    la.roff[i] = p < rt.r1 ? (uint32_t)eti[p] * ldx : OOB_OFF;
+  }
+  lb.rs[0] = make_rsrc(w1 + (size_t)rt.e * h * d, (size_t)h * ldx);
+#pragma unroll
+  for (int i = 0; i < LB::CPT; ++i) {
+    const int j = nb * C::BN + LB::my_row(i);
+    lb.roff[i] = j < h ? (uint32_t)j * ldx : OOB_OFF;
+  }
+  f32x16_t acc[C::FM][C::FN];
+  gemm_mainloop<C>(la, lb, d / C::BK, smem, acc, wm, wn);
+  const int l = lane_id();
+#pragma unroll
+  for (int fn = 0; fn < C::FN; ++fn) {
+    const int j = nb * C::BN + C::b_row0(wn, fn) + frag_col(l);
+    if (j >= h) continue;
+#pragma unroll
+    for (int fm = 0; fm < C::FM; ++fm)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int p = rt.r0 + C::a_row0(wm, fm) + frag_row(r, l);
+        if (p >= rt.r1) continue;
+        const float a = acc[fm][fn][r];
+        st_f(h_a + (size_t)p * h + j, a);
+        st_f(y_swi + (size_t)p * h + j, act_fwd(a, act));
+      }
+  }
+}
+
+template <typename TIN, int B>
+static hipError_t up_act_t(const Shape& s, const void* x, const int32_t* offsets, const int32_t* eti,
+                           const void* w1, void* h_a, void* y_swi, const ExpertWs& ws, hipStream_t st) {
+  using C = XCfg<TIN, B, false, false, false>;
+  const int nbn = col_blocks(s.h, C::BN);
+  long long nblk = max_row_blocks(s, B) * nbn;
+  nblk = (nblk + 7) / 8 * 8;
+  up_act_kernel<C><<<dim3((unsigned)nblk), dim3(C::NT), 0, st>>>(
+      (const TIN*)x, offsets, eti, ws.tile_map(B), (const TIN*)w1, (TIN*)h_a, (TIN*)y_swi, s.T, s.d, s.E, s.h,
+      s.act, nbn, (int)nblk);
+  return hipGetLastError();
+}
+
 hipError_t launch_gate_up(const Shape& s, const void* x, const int32_t* offsets, const int32_t* eti,
                           const void* w_gate, const void* w_up, void* h_ab, void* y_swi, const ExpertWs& ws,
                           hipStream_t st) {
@@ -148,7 +213,14 @@ hipError_t launch_gate_up(const Shape& s, const void* x, const int32_t* offsets,
   // wastes less on partial row tiles for short reductions)
   const bool big = pick_large(s.d >= 4096);
   hipError_t e;
-  if (s.bf16)
+  if (!s.gated()) {
+    if (s.bf16)
+      e = big ? up_act_t<bf16_t, TILE_L>(s, x, offsets, eti, w_gate, h_ab, y_swi, ws, st)
+              : up_act_t<bf16_t, TILE_S>(s, x, offsets, eti, w_gate, h_ab, y_swi, ws, st);
+    else
+      e = big ? up_act_t<float, TILE_L>(s, x, offsets, eti, w_gate, h_ab, y_swi, ws, st)
+              : up_act_t<float, TILE_S>(s, x, offsets, eti, w_gate, h_ab, y_swi, ws, st);
+  } else if (s.bf16)
     e = big ? gate_up_t<bf16_t, TILE_L>(s, x, offsets, eti, w_gate, w_up, h_ab, y_swi, ws, st)
             : gate_up_t<bf16_t, TILE_S>(s, x, offsets, eti, w_gate, w_up, h_ab, y_swi, ws, st);
   else
@@ -566,7 +638,8 @@ struct SrcRowsGather {  // rows eti[p], p = p0 + k < p1
 
 MOE_DEV int min_i(int a, int b) { return a < b ? a : b; }
 
-// dH kernel: dA' = dO W_down (M rows of e, N = TILE of h, K = d) + SwiGLU backward.
+// dH kernel: dA' = dO W_down (M rows of e, N = TILE of h, K = d) + SwiGLU backward
+// (or, for a plain two-layer expert, dA = w dA' * sigma'(a), dH = [dA]).
 // HONLY (H-only saving, SonicMoE analysis page sec. 3.4.1): y is recomputed
 // as SiLU(a) * b from the saved a, b instead of read from y_swi, and the
 // kernel also writes A' = w * y for the dW_down GEMM.
@@ -576,7 +649,7 @@ __global__ __launch_bounds__(C::NT, C::WAVES_PER_EU) void dh_kernel(
     const typename C::T* __restrict__ h_ab, const typename C::T* __restrict__ y_swi,
     const int32_t* __restrict__ offsets, const int32_t* __restrict__ eti, const int32_t* __restrict__ mb_off,
     const float* __restrict__ w_pos, typename C::T* __restrict__ dh, float* __restrict__ ds_part,
-    typename C::T* __restrict__ a_prime, int T, int d, int E, int h, int nbn, int nblk) {
+    typename C::T* __restrict__ a_prime, int T, int d, int E, int h, int act, int nbn, int nblk) {
   __shared__ __attribute__((aligned(16))) char smem[C::LDS_BYTES];
   using TIN = typename C::T;
   const int id = xcd_swizzle(blockIdx.x, nblk);
@@ -623,20 +696,31 @@ __global__ __launch_bounds__(C::NT, C::WAVES_PER_EU) void dh_kernel(
             const int j = nb * C::BN + C::b_row0(wn, fn) + frag_col(l);
             if (j >= h) continue;
             const float dap = acc[fm][fn][r];
-            const float a = ld_f(h_ab + (size_t)p * 2 * h + j);
-            const float b = ld_f(h_ab + (size_t)p * 2 * h + h + j);
-            const float sg = sigmoidf_(a);
+            const float dy = w * dap;
             float y;
-            if constexpr (HONLY) {
-              y = a * sg * b;
-              st_f(a_prime + (size_t)p * h + j, w * y);
-            } else {
-              y = ld_f(y_swi + (size_t)p * h + j);
+            if (act == ACT_SWIGLU) {
+              const float a = ld_f(h_ab + (size_t)p * 2 * h + j);
+              const float b = ld_f(h_ab + (size_t)p * 2 * h + h + j);
+              const float sg = sigmoidf_(a);
+              if constexpr (HONLY) {
+                y = a * sg * b;
+                st_f(a_prime + (size_t)p * h + j, w * y);
+              } else {
+                y = ld_f(y_swi + (size_t)p * h + j);
+              }
+              st_f(dh + (size_t)p * 2 * h + j, dy * b * sg * (1.0f + a * (1.0f - sg)));
+              st_f(dh + (size_t)p * 2 * h + h + j, dy * a * sg);
+            } else {  // plain expert: dA = dy * sigma'(a), a recomputed from the saved pre-activation
+              const float a = ld_f(h_ab + (size_t)p * h + j);
+              if constexpr (HONLY) {
+                y = act_fwd(a, act);
+                st_f(a_prime + (size_t)p * h + j, w * y);
+              } else {
+                y = ld_f(y_swi + (size_t)p * h + j);
+              }
+              st_f(dh + (size_t)p * h + j, dy * act_grad(a, act));
             }
             dsum += dap * y;
-            const float dy = w * dap;
-            st_f(dh + (size_t)p * 2 * h + j, dy * b * sg * (1.0f + a * (1.0f - sg)));
-            st_f(dh + (size_t)p * 2 * h + h + j, dy * a * sg);
           }
         }
         // reduce the row's partial over the 32 columns of the half-wave, fixed order
@@ -789,11 +873,12 @@ __global__ __launch_bounds__(C::NT, C::WAVES_PER_EU) void dw_down_kernel(
     }
 }
 
-// dW_gate / dW_up [e] (h x d) = sum_p dH[p]^T x[eti[p]]: M = 2h, N = d, K = rows of e
+// dW_gate / dW_up [e] (h x d) = sum_p dH[p]^T x[eti[p]]: M = hw (2h gated, h for a
+// plain expert, whose W_1 gradient goes to dw_gate), N = d, K = rows of e
 template <class C>
 __global__ __launch_bounds__(C::NT, C::WAVES_PER_EU) void dw_gate_up_kernel(
     const typename C::T* __restrict__ dh, const typename C::T* __restrict__ x, const int32_t* __restrict__ offsets,
-    const int32_t* __restrict__ eti, float* __restrict__ dw_gate, float* __restrict__ dw_up, int T, int d, int h) {
+    const int32_t* __restrict__ eti, float* __restrict__ dw_gate, float* __restrict__ dw_up, int T, int d, int h, int hw) {
   __shared__ __attribute__((aligned(16))) char smem[C::LDS_BYTES];
   using TIN = typename C::T;
   const int nnb = col_blocks(d, C::BN);
@@ -802,13 +887,13 @@ __global__ __launch_bounds__(C::NT, C::WAVES_PER_EU) void dw_gate_up_kernel(
   const int p0 = offsets[e], p1 = offsets[e + 1];
   const int wave = threadIdx.x >> 6, wm = wave / C::WN, wn = wave % C::WN;
   KSrcLoader<C, C::AKM, C::BM, SrcRowsContig<TIN>, false> la;
-  la.src.rs = make_rsrc(dh + (size_t)p0 * 2 * h, (size_t)(p1 - p0) * 2 * h * sizeof(TIN));
-  la.src.ld_bytes = (uint32_t)(2 * h) * sizeof(TIN);
+  la.src.rs = make_rsrc(dh + (size_t)p0 * hw, (size_t)(p1 - p0) * hw * sizeof(TIN));
+  la.src.ld_bytes = (uint32_t)hw * sizeof(TIN);
   la.src.col0 = (uint32_t)(mb * C::BM) * sizeof(TIN);
   la.src.n = p1 - p0;
   la.src.p0 = p0;
   la.src.scl = nullptr;
-  la.ncols = min_i(C::BM, 2 * h - mb * C::BM);
+  la.ncols = min_i(C::BM, hw - mb * C::BM);
   KSrcLoader<C, C::BKM, C::BN, SrcRowsGather<TIN>, false> lb;
   lb.src.rs = make_rsrc(x, (size_t)T * d * sizeof(TIN));
   lb.src.ld_bytes = (uint32_t)d * sizeof(TIN);
@@ -825,7 +910,7 @@ __global__ __launch_bounds__(C::NT, C::WAVES_PER_EU) void dw_gate_up_kernel(
 #pragma unroll
     for (int r = 0; r < 16; ++r) {
       const int m = mb * C::BM + C::a_row0(wm, fm) + frag_row(r, l);
-      if (m >= 2 * h) continue;
+      if (m >= hw) continue;
       float* o = m < h ? dw_gate + ((size_t)e * h + m) * d : dw_up + ((size_t)e * h + (m - h)) * d;
 #pragma unroll
       for (int fn = 0; fn < C::FN; ++fn) {
@@ -835,13 +920,14 @@ __global__ __launch_bounds__(C::NT, C::WAVES_PER_EU) void dw_gate_up_kernel(
     }
 }
 
-// dX~ = dH [W_gate; W_up] (M rows of e, N = TILE of d, K = 2h) + ordered fold into dX
+// dX~ = dH [W_gate; W_up] (M rows of e, N = TILE of d, K = hw: 2h, or h with W_1
+// only for a plain expert) + ordered fold into dX
 template <class C>
 __global__ __launch_bounds__(C::NT, C::WAVES_PER_EU) void dx_fold_kernel(
     const typename C::T* __restrict__ dh, const typename C::T* __restrict__ w_gate,
     const typename C::T* __restrict__ w_up, const int32_t* __restrict__ offsets, const int32_t* __restrict__ eti,
     const int32_t* __restrict__ mb_off, const int32_t* __restrict__ rank_pos, int32_t* turn, float* accws,
-    typename C::T* __restrict__ dx, int32_t* counters, int d, int E, int K, int h, int spin_limit) {
+    typename C::T* __restrict__ dx, int32_t* counters, int d, int E, int K, int h, int hw, int spin_limit) {
   __shared__ __attribute__((aligned(16))) char smem[C::LDS_BYTES];
   using TIN = typename C::T;
   const int NB = col_blocks(d, C::BN);
@@ -850,10 +936,10 @@ __global__ __launch_bounds__(C::NT, C::WAVES_PER_EU) void dx_fold_kernel(
   if (g >= mb_off[E]) return;
   const RowTile rt = decode_row_tile<C::BM>(mb_off, offsets, E, g);
   const int wave = threadIdx.x >> 6, wm = wave / C::WN, wn = wave % C::WN;
-  const uint32_t ldh = (uint32_t)(2 * h) * sizeof(TIN);
+  const uint32_t ldh = (uint32_t)hw * sizeof(TIN);
   using LA = RowLoader<C::BM, false, C::NT>;
   LA la;
-  la.rs[0] = make_rsrc(dh + (size_t)rt.r0 * 2 * h, (size_t)(rt.r1 - rt.r0) * ldh);
+  la.rs[0] = make_rsrc(dh + (size_t)rt.r0 * hw, (size_t)(rt.r1 - rt.r0) * ldh);
 #pragma unroll
   for (int i = 0; i < LA::CPT; ++i) {
     const int r = LA::my_row(i);
@@ -868,7 +954,7 @@ __global__ __launch_bounds__(C::NT, C::WAVES_PER_EU) void dx_fold_kernel(
   lb.src.kpt = C::BK;
   lb.ncols = min_i(C::BN, d - nb * C::BN);
   f32x16_t acc[C::FM][C::FN];
-  gemm_mainloop<C>(la, lb, (2 * h) / C::BK, smem, acc, wm, wn);
+  gemm_mainloop<C>(la, lb, hw / C::BK, smem, acc, wm, wn);
   fold_epilogue<C, false>(acc, rt, nb, NB, wm, wn, eti, nullptr, rank_pos, K, d, turn, accws, dx, counters,
                           spin_limit, smem);
 }
@@ -881,7 +967,7 @@ static void launch_dh(const Shape& s, const void* dout, const void* w_down, cons
   const long long nblk = (max_row_blocks(s, B) * nbn + 7) / 8 * 8;
   dh_kernel<C, HONLY><<<dim3((unsigned)nblk), dim3(C::NT), 0, st>>>(
       (const TIN*)dout, (const TIN*)w_down, (const TIN*)h_ab, (const TIN*)y_swi, offsets, eti, ws.tile_map(B),
-      ws.w_pos, (TIN*)ws.dh, ws.ds_part, (TIN*)ws.a_prime, s.T, s.d, s.E, s.h, nbn, (int)nblk);
+      ws.w_pos, (TIN*)ws.dh, ws.ds_part, (TIN*)ws.a_prime, s.T, s.d, s.E, s.h, s.act, nbn, (int)nblk);
 }
 
 template <typename TIN, int B>
@@ -891,7 +977,7 @@ static void launch_dx_fold(const Shape& s, const void* w_gate, const void* w_up,
   const long long nblk = max_row_blocks(s, B) * col_blocks(s.d, B);
   dx_fold_kernel<C><<<dim3((unsigned)nblk), dim3(C::NT), 0, st>>>(
       (const TIN*)ws.dh, (const TIN*)w_gate, (const TIN*)w_up, offsets, eti, ws.tile_map(B), ws.rank_pos, ws.turn,
-      ws.acc, (TIN*)dx, ws.counters, s.d, s.E, s.K, s.h, spin_limit);
+      ws.acc, (TIN*)dx, ws.counters, s.d, s.E, s.K, s.h, s.hw(), spin_limit);
 }
 
 template <typename TIN>
@@ -946,13 +1032,16 @@ static hipError_t backward_t(const Shape& s, const void* dout, const void* x, co
   if ((err = hipGetLastError()) != hipSuccess) return err;
 
   timing_mark(st, "dw_gate_up", true);
-  dw_gate_up_kernel<CL><<<dim3(col_blocks(2 * s.h, CL::BM) * col_blocks(s.d, CL::BN), s.E), dim3(CL::NT), 0,
-                          st>>>((const TIN*)ws.dh, (const TIN*)x, offsets, eti, dw_gate, dw_up, s.T, s.d, s.h);
+  dw_gate_up_kernel<CL><<<dim3(col_blocks(s.hw(), CL::BM) * col_blocks(s.d, CL::BN), s.E), dim3(CL::NT), 0,
+                          st>>>((const TIN*)ws.dh, (const TIN*)x, offsets, eti, dw_gate, dw_up, s.T, s.d, s.h,
+                                s.hw());
   timing_mark(st, "dw_gate_up", false);
   if ((err = hipGetLastError()) != hipSuccess) return err;
 
   timing_mark(st, "dx_fold", true);
-  launch_dx_fold<TIN, TILE_S>(s, w_gate, w_up, offsets, eti, dx, ws, spin_limit, st);
+  // a plain expert has no up projection: its k never reaches h, so the second
+  // weight slot is never read
+  launch_dx_fold<TIN, TILE_S>(s, w_gate, s.gated() ? w_up : w_gate, offsets, eti, dx, ws, spin_limit, st);
   timing_mark(st, "dx_fold", false);
   return hipGetLastError();
 }

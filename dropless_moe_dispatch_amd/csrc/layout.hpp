@@ -16,10 +16,15 @@ constexpr int IDX_CHUNK = 256;      // tokens per index-build workgroup
 constexpr int IDX_WAVES = IDX_CHUNK / 64;
 constexpr int N_COUNTERS = 64;      // [0] error flag, [1] fold ticket, [2..] reserved
 
+enum { ACT_SWIGLU = 0, ACT_SILU = 1, ACT_RELU = 2 };
+
 struct Shape {
   int T, d, E, K, h, bf16;
+  int act;  // ACT_*: SwiGLU (gated) or a plain two-layer expert
   long long A() const { return (long long)T * K; }
   int elem() const { return bf16 ? 2 : 4; }
+  bool gated() const { return act == ACT_SWIGLU; }
+  int hw() const { return gated() ? 2 * h : h; }  // columns of the saved pre-activations and of dH
 };
 
 inline size_t align_up(size_t v, size_t a) { return (v + a - 1) / a * a; }
@@ -78,7 +83,7 @@ struct ExpertWs {
   float* acc;          // [T][d] fp32 fold accumulator
   float* ds_part;      // [A][h/128] router-score partial sums (backward)
   float* dz_pos;       // [A] router logit gradient per position (backward)
-  void* dh;            // [A][2h] activation-dtype gradient of the pre-activations (backward)
+  void* dh;            // [A][hw] activation-dtype gradient of the pre-activations (backward)
   void* a_prime;       // [A][h] activation-dtype A' = w * y recomputed from a, b (H-only backward)
   void* ystage;        // [A][d] activation-dtype staged expert outputs (staged-Y combine ablation)
   size_t bytes;
@@ -105,7 +110,7 @@ inline ExpertWs expert_ws(const Shape& s, int which, void* p) {
   if (bwd) {
     w.ds_part = (float*)take(A * col_blocks(s.h, TILE_S) * 4);
     w.dz_pos = (float*)take(A * 4);
-    w.dh = take(A * 2 * (size_t)s.h * s.elem());
+    w.dh = take(A * (size_t)s.hw() * s.elem());
   }
   if (which == WS_EXPERT_BWD_H) w.a_prime = take(A * (size_t)s.h * s.elem());
   if (which == WS_COMBINE_STAGED) w.ystage = take(A * (size_t)s.d * s.elem());

@@ -36,11 +36,15 @@ class MoEBuffers:
     # forward combine: "fold" (the ordered, buffer-free combine) or "staged"
     # (the staged-Y ablation, which holds a [T*K, d] buffer in its workspace)
     combine: str = "fold"
+    # expert kind: "swiglu" (gated) or "silu" / "relu" (plain two-layer
+    # expert: W_1 in the w_gate slot, no w_up, h_ab holds a only)
+    act: str = "swiglu"
 
     def __post_init__(self):
         dev, td = self.device, torch_dtype(self.dtype)
         T, d, E, K, h = self.T, self.d, self.E, self.K, self.h
-        self.shape = B.shape(T, d, E, K, h, self.dtype)
+        self.shape = B.shape(T, d, E, K, h, self.dtype, self.act)
+        hw = 2 * h if self.act == "swiglu" else h
         A = T * K
         i32, f32 = torch.int32, torch.float32
         self.logits = torch.empty(T, E, dtype=f32, device=dev)
@@ -49,7 +53,7 @@ class MoEBuffers:
         self.offsets = torch.empty(E + 1, dtype=i32, device=dev)
         self.eti = torch.empty(A, dtype=i32, device=dev)
         self.tim = torch.empty(A, dtype=i32, device=dev)
-        self.h_ab = torch.empty(A, 2 * h, dtype=td, device=dev)
+        self.h_ab = torch.empty(A, hw, dtype=td, device=dev)
         self.y_swi = torch.empty(A, h, dtype=td, device=dev)
         self.out = torch.empty(T, d, dtype=td, device=dev)
         self.ws_index = self._ws(B.MOE_WS_INDEX)
@@ -61,7 +65,7 @@ class MoEBuffers:
             self.dx = torch.empty(T, d, dtype=td, device=dev)
             self.dwg = torch.empty(E, d, dtype=f32, device=dev)
             self.dw_gate = torch.empty(E, h, d, dtype=f32, device=dev)
-            self.dw_up = torch.empty(E, h, d, dtype=f32, device=dev)
+            self.dw_up = torch.empty(E, h, d, dtype=f32, device=dev) if self.act == "swiglu" else None
             self.dw_down = torch.empty(E, d, h, dtype=f32, device=dev)
             self.ds = torch.empty(T, K, dtype=f32, device=dev)
             if self.saved not in ("aby", "ab"):
@@ -87,7 +91,8 @@ class MoEBuffers:
         """The fp32 weight gradients (dWg, dW_gate, dW_up, dW_down)."""
         if not self.backward:
             return 0
-        return sum(t.numel() * t.element_size() for t in (self.dwg, self.dw_gate, self.dw_up, self.dw_down))
+        return sum(t.numel() * t.element_size() for t in (self.dwg, self.dw_gate, self.dw_up, self.dw_down)
+                   if t is not None)
 
     def workspace_bytes(self) -> int:
         ws = [self.ws_index, self.ws_fwd, self.ws_comb] + ([self.ws_bwd] if self.backward else [])

@@ -38,6 +38,7 @@ class Workload:
     zipf_s: Optional[float] = None
     seed: int = 0
     note: str = field(default="", compare=False)
+    act: str = "swiglu"   # "swiglu" (gated expert) or "silu" / "relu" (plain two-layer expert)
 
 
 # The five evaluation workloads.  Index i (1-based) uses seed 1000 + i.
@@ -52,6 +53,17 @@ WORKLOADS = {
                 note="large model dimension, forward + backward"),
     5: Workload("skewed_fwdbwd_bf16", 16384, 4096, 64, 6, 1536, "bf16", True, zipf_s=1.2,
                 seed=1005, note="Zipf(1.2) per-expert logit offset, forward + backward"),
+    # MoEBlaze's own evaluation shapes (reading notes, Table 1: the printed
+    # conf1, conf3, conf4 and conf7; T = batch x sequence, h = 4d) with the
+    # plain two-layer SiLU expert of its Figure 3 comparison.
+    6: Workload("moeblaze_conf1_silu", 32 * 2048, 512, 4, 1, 2048, "bf16", True, seed=1006, act="silu",
+                note="MoEBlaze conf1: d=512, E=4, K=1, B=32, L=2048"),
+    7: Workload("moeblaze_conf3_silu", 32 * 2048, 1024, 16, 4, 4096, "bf16", True, seed=1007, act="silu",
+                note="MoEBlaze conf3: d=1024, E=16, K=4, B=32, L=2048"),
+    8: Workload("moeblaze_conf4_silu", 32 * 1024, 2048, 16, 4, 8192, "bf16", True, seed=1008, act="silu",
+                note="MoEBlaze conf4: d=2048, E=16, K=4, B=32, L=1024"),
+    9: Workload("moeblaze_conf7_silu", 16 * 512, 2048, 8, 4, 8192, "bf16", True, seed=1009, act="silu",
+                note="MoEBlaze conf7: d=2048, E=8, K=4, B=16, L=512"),
 }
 
 _TENSOR_KEYS = {"x": 1, "wg": 2, "w_gate": 3, "w_up": 4, "w_down": 5, "dy": 6,
@@ -123,8 +135,9 @@ def make_inputs(wl: Workload, tensors=("x", "wg", "w_gate", "w_up", "w_down", "d
             out[name] = normal(wl.seed, "wg", (wl.E, wl.d), 1.0 / np.sqrt(wl.d), wl.dtype)
         elif name == "w_gate":
             out[name] = normal(wl.seed, "w_gate", (wl.E, wl.h, wl.d), 1.0 / np.sqrt(wl.d), wl.dtype)
-        elif name == "w_up":
-            out[name] = normal(wl.seed, "w_up", (wl.E, wl.h, wl.d), 1.0 / np.sqrt(wl.d), wl.dtype)
+        elif name == "w_up":   # a plain two-layer expert has no up projection
+            out[name] = normal(wl.seed, "w_up", (wl.E, wl.h, wl.d), 1.0 / np.sqrt(wl.d), wl.dtype) \
+                if wl.act == "swiglu" else None
         elif name == "w_down":
             out[name] = normal(wl.seed, "w_down", (wl.E, wl.d, wl.h), 1.0 / np.sqrt(wl.h), wl.dtype)
         else:
@@ -133,8 +146,8 @@ def make_inputs(wl: Workload, tensors=("x", "wg", "w_gate", "w_up", "w_down", "d
     return out
 
 
-def small_workload(T, d, E, K, h, dtype="bf16", seed=7, zipf_s=None, backward=True, name="small"):
-    return Workload(name, T, d, E, K, h, dtype, backward, zipf_s=zipf_s, seed=seed)
+def small_workload(T, d, E, K, h, dtype="bf16", seed=7, zipf_s=None, backward=True, name="small", act="swiglu"):
+    return Workload(name, T, d, E, K, h, dtype, backward, zipf_s=zipf_s, seed=seed, act=act)
 
 
 # ---------------------------------------------------------------------------

@@ -75,10 +75,21 @@ typedef enum {
 
 typedef enum { MOE_F32 = 0, MOE_BF16 = 1 } moe_dtype;
 
+/* Expert feed-forward kind.
+ *   MOE_ACT_SWIGLU: gated, y = SiLU(x W_gate^T) * (x W_up^T) (MoEBlaze
+ *     analysis page, "Fused SwiGLU Kernel with Activation Checkpoint").
+ *   MOE_ACT_SILU / MOE_ACT_RELU: the plain two-layer expert
+ *     E_i(x) = W_2 sigma(W_1 x) of the MoEBlaze reading notes (sec. 2.2),
+ *     sigma = SiLU or ReLU.  W_1 is passed as w_gate; there is no w_up (pass
+ *     NULL) and no dw_up; the saved pre-activation h_ab holds a = x W_1^T
+ *     only ([T*K, h] instead of [T*K, 2h]). */
+typedef enum { MOE_ACT_SWIGLU = 0, MOE_ACT_SILU = 1, MOE_ACT_RELU = 2 } moe_act;
+
 /* host struct: T tokens, model dim d, E experts, top-K, expert hidden h */
 typedef struct {
   int32_t T, d, E, K, h;
   int32_t dtype; /* moe_dtype of activations and expert weights */
+  int32_t act;   /* moe_act; 0 (SwiGLU) for a zero-initialised struct */
 } moe_shape;
 
 typedef enum {

@@ -100,6 +100,29 @@ def test_pointer_and_workspace_validation():
     assert L.moe_expert_bwd(sp, *req, None, FAKE, need_h, 0) == B.MOE_ERR_INVALID_ARG
 
 
+def test_activation_kind_validation():
+    L = B.lib()
+    s = B.shape(64, 128, 8, 2, 128, act="relu")
+    assert B.workspace_bytes(s, B.MOE_WS_EXPERT_FWD) > 0
+    # a plain expert's backward workspace holds dH of width h, not 2h
+    g = B.shape(4096, 128, 8, 2, 1024)
+    p = B.shape(4096, 128, 8, 2, 1024, act="silu")
+    diff = B.workspace_bytes(g, B.MOE_WS_EXPERT_BWD) - B.workspace_bytes(p, B.MOE_WS_EXPERT_BWD)
+    assert 4096 * 2 * 1024 * 2 <= diff < 4096 * 2 * 1024 * 2 + 512
+    bad = B.shape(64, 128, 8, 2, 128)
+    bad.act = 7
+    assert B.workspace_bytes(bad, B.MOE_WS_INDEX) == 0
+    assert L.moe_build_index(ctypes.byref(bad), FAKE, FAKE, FAKE, FAKE, FAKE, 1 << 30, 0) == B.MOE_ERR_INVALID_ARG
+    # w_up is optional for a plain expert and required for SwiGLU
+    need = B.workspace_bytes(s, B.MOE_WS_EXPERT_FWD)
+    assert L.moe_expert_fwd(ctypes.byref(s), FAKE, FAKE, FAKE, FAKE, None, FAKE, FAKE, FAKE, need - 1, 0) \
+        == B.MOE_ERR_WORKSPACE
+    sg = B.shape(64, 128, 8, 2, 128)
+    need = B.workspace_bytes(sg, B.MOE_WS_EXPERT_FWD)
+    assert L.moe_expert_fwd(ctypes.byref(sg), FAKE, FAKE, FAKE, FAKE, None, FAKE, FAKE, FAKE, need, 0) \
+        == B.MOE_ERR_INVALID_ARG
+
+
 def test_spin_limit_setter_roundtrip():
     prev = B.set_spin_limit(1000)
     assert B.set_spin_limit(prev) == 1000

@@ -127,8 +127,10 @@ LAYER_CASES = [
 
 def _gpu_layer(inp, wl, logits32=None, backward=True, saved="aby", combine="fold"):
     dt = wl.dtype
-    buf = Lyr.MoEBuffers(wl.T, wl.d, wl.E, wl.K, wl.h, dt, backward=backward, saved=saved, combine=combine)
-    dev = {k: Lyr.to_device(inp[k], dt) for k in ("x", "wg", "w_gate", "w_up", "w_down", "dy") if k in inp}
+    buf = Lyr.MoEBuffers(wl.T, wl.d, wl.E, wl.K, wl.h, dt, backward=backward, saved=saved, combine=combine,
+                         act=wl.act)
+    dev = {k: (Lyr.to_device(inp[k], dt) if inp[k] is not None else None)
+           for k in ("x", "wg", "w_gate", "w_up", "w_down", "dy") if k in inp}
     bias = torch.from_numpy(inp["bias"]).cuda() if inp.get("bias") is not None else None
     if logits32 is not None:
         buf.logits.copy_(torch.from_numpy(logits32))
@@ -150,27 +152,30 @@ def _compare_layer(buf, inp, wl, z32, backward=True, report=None, w_rtol=2e-6, s
     assert np.array_equal(to_np(buf.offsets), ix["offsets"])
     assert np.array_equal(to_np(buf.eti), ix["expert_token_indices"])
     assert np.array_equal(to_np(buf.tim), ix["token_index_map"])
-    f = O.moe_forward(inp["x"], ids, w, inp["w_gate"], inp["w_up"], inp["w_down"], dtype=wl.dtype)
+    gated = wl.act == "swiglu"
+    f = O.moe_forward(inp["x"], ids, w, inp["w_gate"], inp["w_up"], inp["w_down"], dtype=wl.dtype, act=wl.act)
     pos = ix["token_index_map"].reshape(T, K)
-    hab = to_np(buf.h_ab)[pos]          # [T,K,2h]
+    hab = to_np(buf.h_ab)[pos]          # [T,K,2h] (gated) or [T,K,h]
     assert_close("a", hab[..., :h], f["a_s"], report=report)
-    assert_close("b", hab[..., h:], f["b_s"], report=report)
+    if gated:
+        assert_close("b", hab[..., h:], f["b_s"], report=report)
     assert_close("y_swi", to_np(buf.y_swi)[pos], f["y_s"], report=report)
     assert_close("out", to_np(buf.out), f["out"], report=report)
     if not backward:
         return
     bw = O.moe_backward(inp["dy"], inp["x"], inp["wg"], ids, w, inp["w_gate"], inp["w_up"], inp["w_down"], f, zz,
-                        dtype=wl.dtype, saved=saved)
+                        dtype=wl.dtype, saved=saved, act=wl.act)
     # the kernels form dS = <dA', y> with the y the backward sees
     assert_close("ds", to_np(buf.ds), bw["ds_alt"] if saved == "ab" else bw["ds"], report=report)
     assert_close("dx", to_np(buf.dx), bw["dx"], report=report)
     assert_close("dwg", to_np(buf.dwg), bw["dwg"], report=report)
     assert_close("dw_gate", to_np(buf.dw_gate), bw["dw_gate"], report=report)
-    assert_close("dw_up", to_np(buf.dw_up), bw["dw_up"], report=report)
+    if gated:
+        assert_close("dw_up", to_np(buf.dw_up), bw["dw_up"], report=report)
     assert_close("dw_down", to_np(buf.dw_down), bw["dw_down"], report=report)
     # experts without rows: exact zeros
     empty = np.nonzero(np.diff(ix["offsets"]) == 0)[0]
-    for key in ("dw_gate", "dw_up", "dw_down", "dwg"):
+    for key in ("dw_gate", "dw_down", "dwg") + (("dw_up",) if gated else ()):
         assert np.all(to_np(getattr(buf, key))[empty] == 0.0), key
 
 
@@ -242,6 +247,31 @@ def test_staged_combine_repeatable_and_close_to_fold():
     c, _ = _gpu_layer(inp, wl, logits32=z32, backward=False, combine="fold")
     assert torch.equal(a.out, b.out)
     assert_close("staged_vs_fold", to_np(a.out), to_np(c.out))
+
+
+PLAIN_CASES = [
+    # name, T, d, E, K, h, dtype, act, saved
+    ("silu_ragged", 300, 256, 8, 2, 256, "bf16", "silu", "aby"),
+    ("relu_multi_tile", 1000, 384, 16, 4, 384, "bf16", "relu", "aby"),
+    ("silu_h_only", 700, 256, 32, 6, 256, "bf16", "silu", "ab"),
+    ("relu_h_only", 513, 256, 64, 8, 128, "bf16", "relu", "ab"),
+    ("silu_f32", 256, 128, 8, 2, 256, "f32", "silu", "aby"),
+    ("relu_k1", 200, 128, 4, 1, 128, "bf16", "relu", "aby"),
+]
+
+
+@pytest.mark.parametrize("case", PLAIN_CASES, ids=[c[0] for c in PLAIN_CASES])
+def test_layer_parity_plain_expert(case):
+    """Plain two-layer experts W_2 sigma(W_1 x), sigma = SiLU or ReLU."""
+    name, T, d, E, K, h, dtype, act, saved = case
+    _say("layer_plain", case)
+    wl = synth.small_workload(T, d, E, K, h, dtype=dtype, seed=sum(map(ord, name)), act=act)
+    inp = synth.make_inputs(wl)
+    assert inp["w_up"] is None
+    z32 = O.router_logits(inp["x"], inp["wg"], inp["bias"]).astype(np.float32)
+    buf, _ = _gpu_layer(inp, wl, logits32=z32, saved=saved)
+    assert buf.device_error_words() == [0, 0]
+    _compare_layer(buf, inp, wl, z32, saved=saved)
 
 
 @pytest.mark.parametrize("kind", ["one_expert_set", "zero_rows", "hot_expert"])

@@ -1,4 +1,5 @@
-"""GPU parity at the five full workload sizes, in the launch configuration the
+"""GPU parity at full workload sizes -- the five evaluation workloads and two of
+MoEBlaze's shapes with plain SiLU experts -- in the launch configuration the
 benchmark times (router on the GPU, the five entry points in order).
 
 The oracle evaluates sampled outputs one by one: 32 random tokens (out, dx,
@@ -27,18 +28,19 @@ def _say(*a):
 
 
 @pytest.mark.timeout(900)
-@pytest.mark.parametrize("idx", [1, 2, 3, 4, 5])
+@pytest.mark.parametrize("idx", [1, 2, 3, 4, 5, 6, 9])
 def test_workload_full_size(idx):
     if not torch.cuda.is_available():
         pytest.skip("no GPU")
     wl = synth.WORKLOADS[idx]
     _say("workload", idx, wl.name, "generate")
     T, d, E, K, h, dt = wl.T, wl.d, wl.E, wl.K, wl.h, wl.dtype
+    gated = wl.act == "swiglu"
     tensors = ("x", "wg", "w_gate", "w_up", "w_down") + (("dy",) if wl.backward else ())
     inp = synth.make_inputs(wl, tensors=tensors)
-    dev = {k: Lyr.to_device(inp[k], dt) for k in tensors}
+    dev = {k: (Lyr.to_device(inp[k], dt) if inp[k] is not None else None) for k in tensors}
     bias = torch.from_numpy(inp["bias"]).cuda() if inp["bias"] is not None else None
-    buf = Lyr.MoEBuffers(T, d, E, K, h, dt, backward=wl.backward)
+    buf = Lyr.MoEBuffers(T, d, E, K, h, dt, backward=wl.backward, act=wl.act)
 
     def run():
         Lyr.forward(buf, dev["x"], dev["wg"], bias, dev["w_gate"], dev["w_up"], dev["w_down"])
@@ -50,8 +52,8 @@ def test_workload_full_size(idx):
     run()
     assert buf.device_error_words() == [0, 0][: 2 if wl.backward else 1] or all(
         e == 0 for e in buf.device_error_words())
-    keep = {k: getattr(buf, k).clone() for k in ("out",) + (("dx", "dw_gate", "dw_up", "dw_down", "dwg")
-                                                            if wl.backward else ())}
+    keep = {k: getattr(buf, k).clone() for k in ("out",) + (("dx", "dw_gate", "dw_down", "dwg")
+                                                            + (("dw_up",) if gated else ()) if wl.backward else ())}
     _say("workload", idx, "gpu run 2 (repeatability)")
     run()
     for k, v in keep.items():
@@ -88,16 +90,18 @@ def test_workload_full_size(idx):
     ok_tokens = np.setdiff1d(np.arange(T), mism)
     sub = np.sort(rng.choice(ok_tokens, size=min(32, len(ok_tokens)), replace=False))
     _say("workload", idx, "oracle sampled tokens")
-    f = O.moe_forward(inp["x"][sub], ids_ref[sub], w_ref[sub], inp["w_gate"], inp["w_up"], inp["w_down"], dtype=dt)
+    f = O.moe_forward(inp["x"][sub], ids_ref[sub], w_ref[sub], inp["w_gate"], inp["w_up"], inp["w_down"], dtype=dt,
+                      act=wl.act)
     assert_close("out[sample]", to_np(buf.out[torch.from_numpy(sub).cuda()]), f["out"])
     pos = to_np(buf.tim).reshape(T, K)[sub]
-    hab = to_np(buf.h_ab[torch.from_numpy(pos.reshape(-1)).cuda()]).reshape(len(sub), K, 2 * h)
+    hab = to_np(buf.h_ab[torch.from_numpy(pos.reshape(-1)).cuda()]).reshape(len(sub), K, -1)
     assert_close("a[sample]", hab[..., :h], f["a_s"])
-    assert_close("b[sample]", hab[..., h:], f["b_s"])
+    if gated:
+        assert_close("b[sample]", hab[..., h:], f["b_s"])
     if not wl.backward:
         return
     b = O.moe_backward(inp["dy"][sub], inp["x"][sub], inp["wg"], ids_ref[sub], w_ref[sub], inp["w_gate"],
-                       inp["w_up"], inp["w_down"], f, z32[sub].astype(np.float64), dtype=dt)
+                       inp["w_up"], inp["w_down"], f, z32[sub].astype(np.float64), dtype=dt, act=wl.act)
     assert_close("dx[sample]", to_np(buf.dx[torch.from_numpy(sub).cuda()]), b["dx"])
     assert_close("ds[sample]", to_np(buf.ds)[sub], b["ds"])
 
@@ -108,18 +112,21 @@ def test_workload_full_size(idx):
         toks = np.nonzero((ids_ref == e).any(axis=1))[0]
         if np.isin(toks, mism).any():
             continue
+        if e == e_big and e != e_small and len(toks) * h * d > 4e10:
+            continue   # the largest expert of the widest shapes: too slow for the float64 oracle
         _say("workload", idx, "oracle expert", e, "rows", len(toks))
         full_k = e == e_small
         fe = O.moe_forward(inp["x"][toks], ids_ref[toks], w_ref[toks], inp["w_gate"], inp["w_up"], inp["w_down"],
-                           dtype=dt, only_experts=None if full_k else [e])
+                           dtype=dt, only_experts=None if full_k else [e], act=wl.act)
         be = O.moe_backward(inp["dy"][toks], inp["x"][toks], inp["wg"], ids_ref[toks], w_ref[toks], inp["w_gate"],
                             inp["w_up"], inp["w_down"], fe, z32[toks].astype(np.float64), dtype=dt,
-                            only_experts=None if full_k else [e])
+                            only_experts=None if full_k else [e], act=wl.act)
         assert_close(f"dw_gate[{e}]", to_np(buf.dw_gate[e]), be["dw_gate"][e])
-        assert_close(f"dw_up[{e}]", to_np(buf.dw_up[e]), be["dw_up"][e])
+        if gated:
+            assert_close(f"dw_up[{e}]", to_np(buf.dw_up[e]), be["dw_up"][e])
         assert_close(f"dw_down[{e}]", to_np(buf.dw_down[e]), be["dw_down"][e])
         if full_k:
             assert_close(f"dwg[{e}]", to_np(buf.dwg[e]), be["dwg"][e])
     for e in np.nonzero(counts == 0)[0]:
-        for key in ("dw_gate", "dw_up", "dw_down", "dwg"):
+        for key in ("dw_gate", "dw_down", "dwg") + (("dw_up",) if gated else ()):
             assert float(getattr(buf, key)[int(e)].abs().max()) == 0.0, (key, e)
