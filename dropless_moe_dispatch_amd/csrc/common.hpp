@@ -35,6 +35,28 @@ template <> struct ElemT<bf16_t> {
   static MOE_DEV void store(bf16_t* p, float v) { *p = (bf16_t)f32_to_bf16(v); }
 };
 
+// One 16-byte chunk of a row: 8 bf16 or 4 fp32 values, converted to/from fp32.
+MOE_DEV void ld16(const bf16_t* p, float (&v)[8]) {
+  const u32x4_t q = *(const u32x4_t*)p;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    v[2 * i] = bf16_to_f32(q[i] & 0xffffu);
+    v[2 * i + 1] = bf16_to_f32(q[i] >> 16);
+  }
+}
+MOE_DEV void ld16(const float* p, float (&v)[4]) {
+  const f32x4_t q = *(const f32x4_t*)p;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) v[i] = q[i];
+}
+MOE_DEV void st16(bf16_t* p, const float (&v)[8]) {
+  u32x4_t q;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) q[i] = f32_to_bf16(v[2 * i]) | (f32_to_bf16(v[2 * i + 1]) << 16);
+  *(u32x4_t*)p = q;
+}
+MOE_DEV void st16(float* p, const float (&v)[4]) { *(f32x4_t*)p = f32x4_t{v[0], v[1], v[2], v[3]}; }
+
 MOE_DEV float sigmoidf_(float u) { return 1.0f / (1.0f + expf(-u)); }
 
 // Activation of a plain two-layer expert (act: 1 = SiLU, 2 = ReLU) and its

@@ -674,76 +674,144 @@ __global__ __launch_bounds__(C::NT, C::WAVES_PER_EU) void dh_kernel(
   f32x16_t acc[C::FM][C::FN];
   gemm_mainloop<C>(la, lb, d / C::BK, smem, acc, wm, wn);
 
-  const int l = lane_id();
-  float* s_ds = (float*)smem;  // [WN][BM]
-  __syncthreads();
+  if constexpr (C::BM == 128 && C::BN == 128 && C::NT == NTHREADS) {
+    // Park dA' (fp32) in LDS; then each thread takes 16-byte row chunks, so a,
+    // b, y are read and dA, dB (and A') written as whole chunks.  dS of a row
+    // is reduced over the row's chunk-owning lanes in a fixed order.
+    static_assert(C::BM * FOLD_LD * 4 <= C::LDS_BYTES, "the parked tile fits the LDS stages");
+    float* s_c = (float*)smem;
+    const int l = lane_id();
+    __syncthreads();
 #pragma unroll
-  for (int fm = 0; fm < C::FM; ++fm) {
+    for (int fm = 0; fm < C::FM; ++fm)
 #pragma unroll
-    for (int rq = 0; rq < 16; rq += 4) {
-      // four accumulator rows at a time: their a, b, y loads are in flight
-      // together without holding the whole fragment's operands in registers
-      float rs[4];
+      for (int fn = 0; fn < C::FN; ++fn)
 #pragma unroll
-      for (int ri = 0; ri < 4; ++ri) {
-        const int r = rq + ri;
-        const int p = rt.r0 + C::a_row0(wm, fm) + frag_row(r, l);
-        float dsum = 0.0f;
-        if (p < rt.r1) {
-          const float w = w_pos[p];
+        for (int r = 0; r < 16; ++r)
+          s_c[(C::a_row0(wm, fm) + frag_row(r, l)) * FOLD_LD + C::b_row0(wn, fn) + frag_col(l)] = acc[fm][fn][r];
+    __syncthreads();
+    constexpr int VPC = 16 / sizeof(TIN);   // values per chunk
+    constexpr int CPR = C::BN / VPC;        // chunks per row
+    constexpr int RPI = C::NT / CPR;        // rows per pass
+    const int cc = (int)threadIdx.x % CPR;
+    const int rows = rt.r1 - rt.r0;
+    const int j0 = nb * C::BN + cc * VPC;   // h is a multiple of 128: the chunk is in range
+    const int hw = act == ACT_SWIGLU ? 2 * h : h;
+    for (int rr = (int)threadIdx.x / CPR; rr < C::BM; rr += RPI) {
+      float dsum = 0.0f;
+      if (rr < rows) {
+        const int p = rt.r0 + rr;
+        const float w = w_pos[p];
+        const float* dapr = s_c + rr * FOLD_LD + cc * VPC;
+        float a[VPC], y[VPC], da[VPC];
+        ld16(h_ab + (size_t)p * hw + j0, a);
+        if (act == ACT_SWIGLU) {
+          float b[VPC], db[VPC];
+          ld16(h_ab + (size_t)p * hw + h + j0, b);
+          if constexpr (!HONLY) ld16(y_swi + (size_t)p * h + j0, y);
 #pragma unroll
-          for (int fn = 0; fn < C::FN; ++fn) {
-            const int j = nb * C::BN + C::b_row0(wn, fn) + frag_col(l);
-            if (j >= h) continue;
-            const float dap = acc[fm][fn][r];
-            const float dy = w * dap;
-            float y;
-            if (act == ACT_SWIGLU) {
-              const float a = ld_f(h_ab + (size_t)p * 2 * h + j);
-              const float b = ld_f(h_ab + (size_t)p * 2 * h + h + j);
-              const float sg = sigmoidf_(a);
-              if constexpr (HONLY) {
-                y = a * sg * b;
-                st_f(a_prime + (size_t)p * h + j, w * y);
-              } else {
-                y = ld_f(y_swi + (size_t)p * h + j);
-              }
-              st_f(dh + (size_t)p * 2 * h + j, dy * b * sg * (1.0f + a * (1.0f - sg)));
-              st_f(dh + (size_t)p * 2 * h + h + j, dy * a * sg);
-            } else {  // plain expert: dA = dy * sigma'(a), a recomputed from the saved pre-activation
-              const float a = ld_f(h_ab + (size_t)p * h + j);
-              if constexpr (HONLY) {
-                y = act_fwd(a, act);
-                st_f(a_prime + (size_t)p * h + j, w * y);
-              } else {
-                y = ld_f(y_swi + (size_t)p * h + j);
-              }
-              st_f(dh + (size_t)p * h + j, dy * act_grad(a, act));
-            }
-            dsum += dap * y;
+          for (int v = 0; v < VPC; ++v) {
+            const float sg = sigmoidf_(a[v]);
+            if constexpr (HONLY) y[v] = a[v] * sg * b[v];
+            const float dy = w * dapr[v];
+            da[v] = dy * b[v] * sg * (1.0f + a[v] * (1.0f - sg));
+            db[v] = dy * a[v] * sg;
+            dsum += dapr[v] * y[v];
+          }
+          st16(dh + (size_t)p * hw + h + j0, db);
+        } else {  // plain expert: dA = dy * sigma'(a), from the saved pre-activation
+          if constexpr (!HONLY) ld16(y_swi + (size_t)p * h + j0, y);
+#pragma unroll
+          for (int v = 0; v < VPC; ++v) {
+            if constexpr (HONLY) y[v] = act_fwd(a[v], act);
+            da[v] = w * dapr[v] * act_grad(a[v], act);
+            dsum += dapr[v] * y[v];
           }
         }
-        // reduce the row's partial over the 32 columns of the half-wave, fixed order
-        dsum += __shfl_xor(dsum, 16, 32);
-        dsum += __shfl_xor(dsum, 8, 32);
-        dsum += __shfl_xor(dsum, 4, 32);
-        dsum += __shfl_xor(dsum, 2, 32);
-        dsum += __shfl_xor(dsum, 1, 32);
-        rs[ri] = dsum;
-      }
-      if ((l & 31) == 0) {
+        st16(dh + (size_t)p * hw + j0, da);
+        if constexpr (HONLY) {
+          float ap[VPC];
 #pragma unroll
-        for (int ri = 0; ri < 4; ++ri) s_ds[wn * C::BM + C::a_row0(wm, fm) + frag_row(rq + ri, l)] = rs[ri];
+          for (int v = 0; v < VPC; ++v) ap[v] = w * y[v];
+          st16(a_prime + (size_t)p * h + j0, ap);
+        }
       }
-      __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+      for (int off = CPR / 2; off > 0; off >>= 1) dsum += __shfl_xor(dsum, off, CPR);
+      if (cc == 0 && rr < rows) ds_part[(size_t)(rt.r0 + rr) * nbn + nb] = dsum;
     }
-  }
-  __syncthreads();
-  for (int i = threadIdx.x; i < rt.r1 - rt.r0; i += C::NT) {
-    float v = 0.0f;
-#pragma unroll
-    for (int w = 0; w < C::WN; ++w) v += s_ds[w * C::BM + i];
-    ds_part[(size_t)(rt.r0 + i) * nbn + nb] = v;
+  } else {
+    const int l = lane_id();
+    float* s_ds = (float*)smem;  // [WN][BM]
+    __syncthreads();
+  #pragma unroll
+    for (int fm = 0; fm < C::FM; ++fm) {
+  #pragma unroll
+      for (int rq = 0; rq < 16; rq += 4) {
+        // four accumulator rows at a time: their a, b, y loads are in flight
+        // together without holding the whole fragment's operands in registers
+        float rs[4];
+  #pragma unroll
+        for (int ri = 0; ri < 4; ++ri) {
+          const int r = rq + ri;
+          const int p = rt.r0 + C::a_row0(wm, fm) + frag_row(r, l);
+          float dsum = 0.0f;
+          if (p < rt.r1) {
+            const float w = w_pos[p];
+  #pragma unroll
+            for (int fn = 0; fn < C::FN; ++fn) {
+              const int j = nb * C::BN + C::b_row0(wn, fn) + frag_col(l);
+              if (j >= h) continue;
+              const float dap = acc[fm][fn][r];
+              const float dy = w * dap;
+              float y;
+              if (act == ACT_SWIGLU) {
+                const float a = ld_f(h_ab + (size_t)p * 2 * h + j);
+                const float b = ld_f(h_ab + (size_t)p * 2 * h + h + j);
+                const float sg = sigmoidf_(a);
+                if constexpr (HONLY) {
+                  y = a * sg * b;
+                  st_f(a_prime + (size_t)p * h + j, w * y);
+                } else {
+                  y = ld_f(y_swi + (size_t)p * h + j);
+                }
+                st_f(dh + (size_t)p * 2 * h + j, dy * b * sg * (1.0f + a * (1.0f - sg)));
+                st_f(dh + (size_t)p * 2 * h + h + j, dy * a * sg);
+              } else {  // plain expert: dA = dy * sigma'(a), a recomputed from the saved pre-activation
+                const float a = ld_f(h_ab + (size_t)p * h + j);
+                if constexpr (HONLY) {
+                  y = act_fwd(a, act);
+                  st_f(a_prime + (size_t)p * h + j, w * y);
+                } else {
+                  y = ld_f(y_swi + (size_t)p * h + j);
+                }
+                st_f(dh + (size_t)p * h + j, dy * act_grad(a, act));
+              }
+              dsum += dap * y;
+            }
+          }
+          // reduce the row's partial over the 32 columns of the half-wave, fixed order
+          dsum += __shfl_xor(dsum, 16, 32);
+          dsum += __shfl_xor(dsum, 8, 32);
+          dsum += __shfl_xor(dsum, 4, 32);
+          dsum += __shfl_xor(dsum, 2, 32);
+          dsum += __shfl_xor(dsum, 1, 32);
+          rs[ri] = dsum;
+        }
+        if ((l & 31) == 0) {
+  #pragma unroll
+          for (int ri = 0; ri < 4; ++ri) s_ds[wn * C::BM + C::a_row0(wm, fm) + frag_row(rq + ri, l)] = rs[ri];
+        }
+        __builtin_amdgcn_sched_barrier(0);
+      }
+    }
+    __syncthreads();
+    for (int i = threadIdx.x; i < rt.r1 - rt.r0; i += C::NT) {
+      float v = 0.0f;
+  #pragma unroll
+      for (int w = 0; w < C::WN; ++w) v += s_ds[w * C::BM + i];
+      ds_part[(size_t)(rt.r0 + i) * nbn + nb] = v;
+    }
   }
 }
 
@@ -789,36 +857,56 @@ __global__ __launch_bounds__(256) void router_bwd_kernel(const int32_t* __restri
   }
 }
 
-// dWg[e] = sum_{p in e} dz_p x[eti[p]]: one workgroup per (expert, column block);
-// each wave strides over rows, fixed-order reduction across the 4 waves.
+// dWg[e] = sum_{p in e} dz_p x[eti[p]], in two deterministic passes so that
+// the work spreads over the expert's rows, not over E workgroups:
+//   pass 1: one workgroup per (128-row block g of the GEMM tile map, column
+//           block): part[g][c] = sum over the block's rows in ascending order;
+//   pass 2: dWg[e][c] = sum of part[g][c] over the expert's blocks, ascending.
 template <typename TIN>
-__global__ __launch_bounds__(256) void dwg_kernel(const TIN* __restrict__ x, const int32_t* __restrict__ offsets,
-                                                  const int32_t* __restrict__ eti, const float* __restrict__ dz_pos,
-                                                  float* __restrict__ dwg, int d) {
-  constexpr int VPL = 16 / sizeof(TIN);  // values per lane per row
-  const int e = blockIdx.x;
-  const int c0 = blockIdx.y * 64 * VPL;
-  const int wave = threadIdx.x >> 6, l = lane_id();
-  const int col = c0 + l * VPL;
+__global__ __launch_bounds__(256) void dwg_part_kernel(const TIN* __restrict__ x, const int32_t* __restrict__ offsets,
+                                                       const int32_t* __restrict__ eti,
+                                                       const int32_t* __restrict__ mb_off,
+                                                       const float* __restrict__ dz_pos, float* __restrict__ part,
+                                                       int d, int E) {
+  constexpr int VPL = 16 / sizeof(TIN);  // values per thread (one 16-byte chunk per row)
+  const int g = blockIdx.x;
+  if (g >= mb_off[E]) return;
+  const RowTile rt = decode_row_tile<TILE_S>(mb_off, offsets, E, g);
+  const int col = (blockIdx.y * 256 + (int)threadIdx.x) * VPL;
+  if (col >= d) return;
   float acc[VPL];
 #pragma unroll
   for (int v = 0; v < VPL; ++v) acc[v] = 0.0f;
-  const int p0 = offsets[e], p1 = offsets[e + 1];
-  if (col < d) {
-    for (int p = p0 + wave; p < p1; p += 4) {
-      const float z = dz_pos[p];
-      const TIN* row = x + (size_t)eti[p] * d + col;
+  for (int p = rt.r0; p < rt.r1; ++p) {
+    const float z = dz_pos[p];
+    const TIN* row = x + (size_t)eti[p] * d + col;
+    if constexpr (sizeof(TIN) == 2) {
+      const u32x4_t q = *(const u32x4_t*)row;
 #pragma unroll
-      for (int v = 0; v < VPL; ++v) acc[v] += z * ElemT<TIN>::load(row + v);
+      for (int v = 0; v < 4; ++v) {
+        acc[2 * v] += z * bf16_to_f32(q[v] & 0xffffu);
+        acc[2 * v + 1] += z * bf16_to_f32(q[v] >> 16);
+      }
+    } else {
+      const f32x4_t q = *(const f32x4_t*)row;
+#pragma unroll
+      for (int v = 0; v < 4; ++v) acc[v] += z * q[v];
     }
   }
-  __shared__ float s[4][64 * VPL];
+  float* o = part + (size_t)g * d + col;
 #pragma unroll
-  for (int v = 0; v < VPL; ++v) s[wave][l * VPL + v] = acc[v];
-  __syncthreads();
-  for (int i = threadIdx.x; i < 64 * VPL; i += 256) {
-    if (c0 + i < d) dwg[(size_t)e * d + c0 + i] = ((s[0][i] + s[1][i]) + s[2][i]) + s[3][i];
-  }
+  for (int v = 0; v < VPL; v += 4) *(f32x4_t*)(o + v) = f32x4_t{acc[v], acc[v + 1], acc[v + 2], acc[v + 3]};
+}
+
+__global__ __launch_bounds__(256) void dwg_reduce_kernel(const float* __restrict__ part,
+                                                         const int32_t* __restrict__ mb_off, float* __restrict__ dwg,
+                                                         int d) {
+  const int e = blockIdx.x;
+  const int c = (blockIdx.y * 256 + (int)threadIdx.x) * 4;
+  if (c >= d) return;
+  f32x4_t acc{0.0f, 0.0f, 0.0f, 0.0f};
+  for (int g = mb_off[e]; g < mb_off[e + 1]; ++g) acc += *(const f32x4_t*)(part + (size_t)g * d + c);
+  *(f32x4_t*)(dwg + (size_t)e * d + c) = acc;
 }
 
 // dW_down[e] (d x h) = sum_p dO[eti[p]]^T (w_p y[p]): M = d, N = h, K = rows of e.
@@ -1012,8 +1100,11 @@ static hipError_t backward_t(const Shape& s, const void* dout, const void* x, co
   timing_mark(st, "dwg", true);
   {
     constexpr int VPL = 16 / sizeof(TIN);
-    const int ncb = (s.d + 64 * VPL - 1) / (64 * VPL);
-    dwg_kernel<TIN><<<dim3(s.E, ncb), dim3(256), 0, st>>>((const TIN*)x, offsets, eti, ws.dz_pos, dwg, s.d);
+    const int ncb = (s.d + 256 * VPL - 1) / (256 * VPL);
+    dwg_part_kernel<TIN><<<dim3((unsigned)max_row_blocks(s, TILE_S), ncb), dim3(256), 0, st>>>(
+        (const TIN*)x, offsets, eti, ws.tile_map(TILE_S), ws.dz_pos, ws.dwg_part, s.d, s.E);
+    dwg_reduce_kernel<<<dim3(s.E, (s.d + 1023) / 1024), dim3(256), 0, st>>>(ws.dwg_part, ws.tile_map(TILE_S), dwg,
+                                                                           s.d);
   }
   timing_mark(st, "dwg", false);
   if ((err = hipGetLastError()) != hipSuccess) return err;

@@ -83,6 +83,7 @@ struct ExpertWs {
   float* acc;          // [T][d] fp32 fold accumulator
   float* ds_part;      // [A][h/128] router-score partial sums (backward)
   float* dz_pos;       // [A] router logit gradient per position (backward)
+  float* dwg_part;     // [row blocks of 128][d] per-row-block partial sums of dWg (backward)
   void* dh;            // [A][hw] activation-dtype gradient of the pre-activations (backward)
   void* a_prime;       // [A][h] activation-dtype A' = w * y recomputed from a, b (H-only backward)
   void* ystage;        // [A][d] activation-dtype staged expert outputs (staged-Y combine ablation)
@@ -110,6 +111,7 @@ inline ExpertWs expert_ws(const Shape& s, int which, void* p) {
   if (bwd) {
     w.ds_part = (float*)take(A * col_blocks(s.h, TILE_S) * 4);
     w.dz_pos = (float*)take(A * 4);
+    w.dwg_part = (float*)take((size_t)max_row_blocks(s, TILE_S) * s.d * 4);
     w.dh = take(A * (size_t)s.hw() * s.elem());
   }
   if (which == WS_EXPERT_BWD_H) w.a_prime = take(A * (size_t)s.h * s.elem());
