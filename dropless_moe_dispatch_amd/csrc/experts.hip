@@ -26,6 +26,10 @@
 
 namespace moe {
 
+// A 128 x 128 fp32 tile parked in LDS for an epilogue uses rows of FOLD_LD floats
+// (128 + 8: the rows written by the two half-waves land on disjoint banks).
+constexpr int FOLD_LD = 136;  // floats per parked row (128 + 8: the two half-waves' rows land on disjoint banks)
+
 template <typename T> MOE_DEV float ld_f(const T* p) { return ElemT<T>::load(p); }
 template <typename T> MOE_DEV void st_f(T* p, float v) { ElemT<T>::store(p, v); }
 
@@ -107,22 +111,58 @@ __global__ __launch_bounds__(C::NT, C::WAVES_PER_EU) void gate_up_kernel(
   f32x16_t acc[C::FM][C::FN];
   gemm_mainloop<C>(la, lb, d / C::BK, smem, acc, wm, wn);
   const int l = lane_id();
-#pragma unroll
-  for (int f = 0; f < HF; ++f) {
-    const int j = j0 + C::b_row0(wn, f) + frag_col(l);
-    if (j >= h) continue;
+  if constexpr (C::BM == 128 && C::BN == 128 && C::NT == NTHREADS) {
+    // park the tile (gate columns in [0, HB), up columns in [HB, BN)) in LDS,
+    // then write a, b and y as whole 16-byte row chunks
+    static_assert(C::BM * FOLD_LD * 4 <= C::LDS_BYTES, "the parked tile fits the LDS stages");
+    float* s_c = (float*)smem;
+    __syncthreads();
 #pragma unroll
     for (int fm = 0; fm < C::FM; ++fm)
 #pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const int p = rt.r0 + C::a_row0(wm, fm) + frag_row(r, l);
-        if (p >= rt.r1) continue;
-        const float a = acc[fm][f][r];
-        const float b = acc[fm][f + HF][r];
-        st_f(h_ab + (size_t)p * 2 * h + j, a);
-        st_f(h_ab + (size_t)p * 2 * h + h + j, b);
-        st_f(y_swi + (size_t)p * h + j, a * sigmoidf_(a) * b);
+      for (int fn = 0; fn < C::FN; ++fn)
+#pragma unroll
+        for (int r = 0; r < 16; ++r)
+          s_c[(C::a_row0(wm, fm) + frag_row(r, l)) * FOLD_LD + C::b_row0(wn, fn) + frag_col(l)] = acc[fm][fn][r];
+    __syncthreads();
+    constexpr int VPC = 16 / sizeof(TIN);
+    constexpr int CPR = HB / VPC;           // output chunks per row (per half)
+    const int rows = rt.r1 - rt.r0;
+    for (int c = threadIdx.x; c < C::BM * CPR; c += C::NT) {
+      const int row = c / CPR, cc = c % CPR;
+      if (row >= rows) break;
+      const int p = rt.r0 + row;
+      const float* ar = s_c + row * FOLD_LD + cc * VPC;
+      float a[VPC], b[VPC], y[VPC];
+#pragma unroll
+      for (int v = 0; v < VPC; ++v) {
+        a[v] = ar[v];
+        b[v] = ar[HB + v];
+        y[v] = a[v] * sigmoidf_(a[v]) * b[v];
       }
+      const int j = j0 + cc * VPC;         // h is a multiple of the half tile: in range
+      st16(h_ab + (size_t)p * 2 * h + j, a);
+      st16(h_ab + (size_t)p * 2 * h + h + j, b);
+      st16(y_swi + (size_t)p * h + j, y);
+    }
+  } else {
+#pragma unroll
+    for (int f = 0; f < HF; ++f) {
+      const int j = j0 + C::b_row0(wn, f) + frag_col(l);
+      if (j >= h) continue;
+#pragma unroll
+      for (int fm = 0; fm < C::FM; ++fm)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const int p = rt.r0 + C::a_row0(wm, fm) + frag_row(r, l);
+          if (p >= rt.r1) continue;
+          const float a = acc[fm][f][r];
+          const float b = acc[fm][f + HF][r];
+          st_f(h_ab + (size_t)p * 2 * h + j, a);
+          st_f(h_ab + (size_t)p * 2 * h + h + j, b);
+          st_f(y_swi + (size_t)p * h + j, a * sigmoidf_(a) * b);
+        }
+    }
   }
 }
 
@@ -175,20 +215,53 @@ __global__ __launch_bounds__(C::NT, C::WAVES_PER_EU) void up_act_kernel(
   f32x16_t acc[C::FM][C::FN];
   gemm_mainloop<C>(la, lb, d / C::BK, smem, acc, wm, wn);
   const int l = lane_id();
-#pragma unroll
-  for (int fn = 0; fn < C::FN; ++fn) {
-    const int j = nb * C::BN + C::b_row0(wn, fn) + frag_col(l);
-    if (j >= h) continue;
+  if constexpr (C::BM == 128 && C::BN == 128 && C::NT == NTHREADS) {
+    // parked in LDS, written as 16-byte row chunks (as in the gated kernel)
+    static_assert(C::BM * FOLD_LD * 4 <= C::LDS_BYTES, "the parked tile fits the LDS stages");
+    float* s_c = (float*)smem;
+    __syncthreads();
 #pragma unroll
     for (int fm = 0; fm < C::FM; ++fm)
 #pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const int p = rt.r0 + C::a_row0(wm, fm) + frag_row(r, l);
-        if (p >= rt.r1) continue;
-        const float a = acc[fm][fn][r];
-        st_f(h_a + (size_t)p * h + j, a);
-        st_f(y_swi + (size_t)p * h + j, act_fwd(a, act));
+      for (int fn = 0; fn < C::FN; ++fn)
+#pragma unroll
+        for (int r = 0; r < 16; ++r)
+          s_c[(C::a_row0(wm, fm) + frag_row(r, l)) * FOLD_LD + C::b_row0(wn, fn) + frag_col(l)] = acc[fm][fn][r];
+    __syncthreads();
+    constexpr int VPC = 16 / sizeof(TIN);
+    constexpr int CPR = C::BN / VPC;
+    const int rows = rt.r1 - rt.r0;
+    for (int c = threadIdx.x; c < C::BM * CPR; c += C::NT) {
+      const int row = c / CPR, cc = c % CPR;
+      if (row >= rows) break;
+      const int p = rt.r0 + row;
+      const float* ar = s_c + row * FOLD_LD + cc * VPC;
+      float a[VPC], y[VPC];
+#pragma unroll
+      for (int v = 0; v < VPC; ++v) {
+        a[v] = ar[v];
+        y[v] = act_fwd(a[v], act);
       }
+      const int j = nb * C::BN + cc * VPC;
+      st16(h_a + (size_t)p * h + j, a);
+      st16(y_swi + (size_t)p * h + j, y);
+    }
+  } else {
+#pragma unroll
+    for (int fn = 0; fn < C::FN; ++fn) {
+      const int j = nb * C::BN + C::b_row0(wn, fn) + frag_col(l);
+      if (j >= h) continue;
+#pragma unroll
+      for (int fm = 0; fm < C::FM; ++fm)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const int p = rt.r0 + C::a_row0(wm, fm) + frag_row(r, l);
+          if (p >= rt.r1) continue;
+          const float a = acc[fm][fn][r];
+          st_f(h_a + (size_t)p * h + j, a);
+          st_f(y_swi + (size_t)p * h + j, act_fwd(a, act));
+        }
+    }
   }
 }
 
@@ -275,7 +348,6 @@ MOE_DEV void coherent_store2(float* p, float a, float b) {
 MOE_DEV void store2(float* p, float a, float b) { *(float2*)p = make_float2(a, b); }
 MOE_DEV void store2(bf16_t* p, float a, float b) { *(uint32_t*)p = f32_to_bf16(a) | (f32_to_bf16(b) << 16); }
 
-constexpr int FOLD_LD = 136;  // floats per parked row (128 + 8: the two half-waves' rows land on disjoint banks)
 constexpr int FOLD_ROWS_PER_WAVE = 32;
 constexpr int FOLD_BATCH = 16;
 
