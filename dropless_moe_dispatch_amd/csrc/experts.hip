@@ -664,15 +664,17 @@ hipError_t launch_combine_staged(const Shape& s, const void* y_swi, const void* 
 // Backward
 // ===========================================================================
 
-// Each source gives the buffer resource of a k-tile (rsrc), the byte offset
-// of k-row k at the tile's first column (row_off, OOB_OFF outside the
-// problem) and optionally a per-k-row scale.
+// Each source gives the buffer resource of a k-tile (rsrc), the value that
+// locates k-row k and has to be read from memory (key: the gathered row index,
+// or 0), the byte offset of k-row k at the tile's first column from it
+// (row_off, OOB_OFF outside the problem) and optionally a per-k-row scale.
 template <typename T>
 struct SrcWeightKN {   // B[k][n] = W[k][n0 + n], W one expert's [K, ld] matrix
   rsrc_t rs;
   uint32_t ld_bytes, col0;
   MOE_DEV rsrc_t rsrc(int) const { return rs; }
-  MOE_DEV uint32_t row_off(int k) const { return (uint32_t)k * ld_bytes + col0; }
+  MOE_DEV uint32_t key(int) const { return 0; }
+  MOE_DEV uint32_t row_off(int k, uint32_t) const { return (uint32_t)k * ld_bytes + col0; }
   MOE_DEV float scale(int) const { return 1.0f; }
 };
 template <typename T>
@@ -681,7 +683,8 @@ struct SrcWeightKN2 {  // k < h: W1[k][n0+n], else W2[k-h][n0+n]; a k-tile never
   uint32_t ld_bytes, col0;
   int h, kpt;
   MOE_DEV rsrc_t rsrc(int kt) const { return kt * kpt < h ? rs1 : rs2; }
-  MOE_DEV uint32_t row_off(int k) const { return (uint32_t)(k < h ? k : k - h) * ld_bytes + col0; }
+  MOE_DEV uint32_t key(int) const { return 0; }
+  MOE_DEV uint32_t row_off(int k, uint32_t) const { return (uint32_t)(k < h ? k : k - h) * ld_bytes + col0; }
   MOE_DEV float scale(int) const { return 1.0f; }
 };
 template <typename T>
@@ -689,22 +692,23 @@ struct SrcRowsContig {  // rows p0 + k < p1 of a [rows, ld] array (resource base
   rsrc_t rs;
   uint32_t ld_bytes, col0;
   int n;                // p1 - p0
-  int p0;
-  const float* scl;     // optional per-row scale, indexed by p
+  rsrc_t rscl;          // optional per-row scale: n floats from position p0 (reads 0 past them)
   MOE_DEV rsrc_t rsrc(int) const { return rs; }
-  MOE_DEV uint32_t row_off(int k) const { return k < n ? (uint32_t)k * ld_bytes + col0 : OOB_OFF; }
-  MOE_DEV float scale(int k) const { return scl[p0 + k]; }
+  MOE_DEV uint32_t key(int) const { return 0; }
+  MOE_DEV uint32_t row_off(int k, uint32_t) const { return k < n ? (uint32_t)k * ld_bytes + col0 : OOB_OFF; }
+  MOE_DEV float scale(int k) const { return __builtin_bit_cast(float, buf_load4(rscl, (uint32_t)k * 4u)); }
 };
 template <typename T>
-struct SrcRowsGather {  // rows eti[p], p = p0 + k < p1
+struct SrcRowsGather {  // rows eti[p0 + k], k < n
   rsrc_t rs;
   uint32_t ld_bytes, col0;
-  int p0, p1;
-  const int32_t* eti;
+  int n;                // p1 - p0
+  rsrc_t reti;          // n row indices from position p0 (read 0 past them)
   MOE_DEV rsrc_t rsrc(int) const { return rs; }
-  MOE_DEV uint32_t row_off(int k) const {
-    return p0 + k < p1 ? (uint32_t)eti[p0 + k] * ld_bytes + col0 : OOB_OFF;
-  }
+  // a buffer load, not a guarded one: no branch, so the compiler's wait
+  // counts stay exact and the index load is not waited for early
+  MOE_DEV uint32_t key(int k) const { return buf_load4(reti, (uint32_t)k * 4u); }
+  MOE_DEV uint32_t row_off(int k, uint32_t row) const { return k < n ? row * ld_bytes + col0 : OOB_OFF; }
   MOE_DEV float scale(int) const { return 1.0f; }
 };
 
@@ -1003,17 +1007,15 @@ __global__ __launch_bounds__(C::NT, C::WAVES_PER_EU) void dw_down_kernel(
   la.src.rs = make_rsrc(dout, (size_t)T * d * sizeof(TIN));
   la.src.ld_bytes = (uint32_t)d * sizeof(TIN);
   la.src.col0 = (uint32_t)(mb * C::BM) * sizeof(TIN);
-  la.src.p0 = p0;
-  la.src.p1 = p1;
-  la.src.eti = eti;
+  la.src.n = p1 - p0;
+  la.src.reti = make_rsrc(eti + p0, (size_t)(p1 - p0) * 4);
   la.ncols = min_i(C::BM, d - mb * C::BM);
   KSrcLoader<C, C::BKM, C::BN, SrcRowsContig<TIN>, SCALE> lb;
   lb.src.rs = make_rsrc(y_swi + (size_t)p0 * h, (size_t)(p1 - p0) * h * sizeof(TIN));
   lb.src.ld_bytes = (uint32_t)h * sizeof(TIN);
   lb.src.col0 = (uint32_t)(nb * C::BN) * sizeof(TIN);
   lb.src.n = p1 - p0;
-  lb.src.p0 = p0;
-  lb.src.scl = w_pos;
+  lb.src.rscl = make_rsrc(w_pos + p0, (size_t)(p1 - p0) * 4);
   lb.ncols = min_i(C::BN, h - nb * C::BN);
   f32x16_t acc[C::FM][C::FN];
   gemm_mainloop<C>(la, lb, (p1 - p0 + C::BK - 1) / C::BK, smem, acc, wm, wn);
@@ -1051,16 +1053,13 @@ __global__ __launch_bounds__(C::NT, C::WAVES_PER_EU) void dw_gate_up_kernel(
   la.src.ld_bytes = (uint32_t)hw * sizeof(TIN);
   la.src.col0 = (uint32_t)(mb * C::BM) * sizeof(TIN);
   la.src.n = p1 - p0;
-  la.src.p0 = p0;
-  la.src.scl = nullptr;
   la.ncols = min_i(C::BM, hw - mb * C::BM);
   KSrcLoader<C, C::BKM, C::BN, SrcRowsGather<TIN>, false> lb;
   lb.src.rs = make_rsrc(x, (size_t)T * d * sizeof(TIN));
   lb.src.ld_bytes = (uint32_t)d * sizeof(TIN);
   lb.src.col0 = (uint32_t)(nb * C::BN) * sizeof(TIN);
-  lb.src.p0 = p0;
-  lb.src.p1 = p1;
-  lb.src.eti = eti;
+  lb.src.n = p1 - p0;
+  lb.src.reti = make_rsrc(eti + p0, (size_t)(p1 - p0) * 4);
   lb.ncols = min_i(C::BN, d - nb * C::BN);
   f32x16_t acc[C::FM][C::FN];
   gemm_mainloop<C>(la, lb, (p1 - p0 + C::BK - 1) / C::BK, smem, acc, wm, wn);

@@ -104,6 +104,9 @@ MOE_DEV rsrc_t make_rsrc(const void* base, size_t bytes) {
 MOE_DEV u32x4_t buf_load16(rsrc_t r, uint32_t off) {
   return __builtin_bit_cast(u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(r, (int)off, 0, 0));
 }
+MOE_DEV uint32_t buf_load4(rsrc_t r, uint32_t off) {
+  return (uint32_t)__builtin_amdgcn_raw_buffer_load_b32(r, (int)off, 0, 0);
+}
 
 // ---------------------------------------------------------------------------
 // RowLoader<ROWS, SPLIT>: ROWS tile rows, each a 128-byte k-slice per stage.
@@ -140,14 +143,18 @@ struct RowLoader {
 
 // ---------------------------------------------------------------------------
 // KRowLoader<T, ROWS, Src, SCALED>: ROWS tile rows (m), k-rows from a source:
-//   Src::rsrc(kt)   -> buffer resource of k-tile kt (uniform);
-//   Src::row_off(k) -> byte offset of element (k-row k, tile column 0), or
-//                      OOB_OFF outside the problem (may read an index);
-//   Src::scale(k)   -> per-k-row scale (SCALED only).
+//   Src::rsrc(kt)        -> buffer resource of k-tile kt (uniform);
+//   Src::key(k)          -> what locates k-row k and must come from memory
+//                           (a gathered row index), 0 if nothing does;
+//   Src::row_off(k, key) -> byte offset of element (k-row k, tile column 0),
+//                           or OOB_OFF outside the problem;
+//   Src::scale(k)        -> per-k-row scale, 0 outside the problem (SCALED only).
 // ncols: valid tile columns (multiple of the chunk width); others read 0.
-// prefetch(kt) fetches the row offsets (and scales) of k-tile kt; load(kt)
-// issues the data loads with them, after which the next prefetch may reuse
-// the registers.
+// prefetch(kt) fetches the keys (and scales) of k-tile kt and load(kt)
+// issues the data loads.  The byte offsets are formed only in load(): a
+// prefetch that already multiplied its freshly loaded index would make the
+// compiler wait for that load, and for the data loads queued before it,
+// right where it is issued.
 // bf16: thread owns k-rows 4*(tid&15)+0..3, columns c*128 + 8*(tid>>4)+0..7.
 // fp32: thread owns k-rows 4*(tid&7)+0..3,  columns c*128 + 4*(tid>>3)+0..3.
 // ---------------------------------------------------------------------------
@@ -171,8 +178,8 @@ struct KRowLoader {
   static constexpr int NC = ROWS / 128;  // column chunks per thread
   Src src;
   int ncols;
-  uint32_t offs[4];
-  float spre[4];         // scales fetched with the offsets
+  uint32_t keys[4];
+  float spre[4];         // scales fetched with the keys
   float sdat[2][4];      // scales of the loaded data, per register set
   u32x4_t reg[2][NC][4];
 
@@ -182,19 +189,21 @@ struct KRowLoader {
     const int kbase = kt * G::KPT + 4 * G::kg();
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
-      offs[j] = src.row_off(kbase + j);
-      if constexpr (SCALED) spre[j] = offs[j] != OOB_OFF ? src.scale(kbase + j) : 0.0f;
+      keys[j] = src.key(kbase + j);
+      if constexpr (SCALED) spre[j] = src.scale(kbase + j);
     }
   }
   template <int SET>
   MOE_DEV void load(int kt) {
     const rsrc_t r = src.rsrc(kt);
+    const int kbase = kt * G::KPT + 4 * G::kg();
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
       if constexpr (SCALED) sdat[SET][j] = spre[j];
+      const uint32_t off = src.row_off(kbase + j, keys[j]);
 #pragma unroll
       for (int c = 0; c < NC; ++c) {
-        const uint32_t o = col(c) < ncols ? offs[j] + (uint32_t)(col(c) * (int)sizeof(T)) : OOB_OFF;
+        const uint32_t o = col(c) < ncols ? off + (uint32_t)(col(c) * (int)sizeof(T)) : OOB_OFF;
         reg[SET][c][j] = buf_load16(r, o);
       }
     }
@@ -261,7 +270,7 @@ struct KLoader {
   using G = KmGeom<ROWS, NT>;
   Src src;
   int ncols;
-  uint32_t offs[G::NPASS];
+  uint32_t keys[G::NPASS];
   float spre[G::NPASS];
   float sdat[2][G::NPASS];
   u32x4_t reg[2][G::NPASS];
@@ -272,8 +281,8 @@ struct KLoader {
   MOE_DEV void prefetch(int kt) {
 #pragma unroll
     for (int i = 0; i < G::NPASS; ++i) {
-      offs[i] = src.row_off(kt * 64 + kr(i));
-      if constexpr (SCALED) spre[i] = offs[i] != OOB_OFF ? src.scale(kt * 64 + kr(i)) : 0.0f;
+      keys[i] = src.key(kt * 64 + kr(i));
+      if constexpr (SCALED) spre[i] = src.scale(kt * 64 + kr(i));
     }
   }
   template <int SET>
@@ -283,7 +292,8 @@ struct KLoader {
 #pragma unroll
     for (int i = 0; i < G::NPASS; ++i) {
       if constexpr (SCALED) sdat[SET][i] = spre[i];
-      reg[SET][i] = buf_load16(r, offs[i] + co);  // OOB_OFF plus a chunk offset stays out of range
+      const uint32_t off = src.row_off(kt * 64 + kr(i), keys[i]);
+      reg[SET][i] = buf_load16(r, off + co);  // OOB_OFF plus a chunk offset stays out of range
     }
   }
   template <int SET, int PART, int NPART>
