@@ -894,42 +894,64 @@ __global__ __launch_bounds__(C::NT, C::WAVES_PER_EU) void dh_kernel(
 // router backward per token: dS, dz (closed form), and the router term of dX
 //   dz[t,S_k] = w_k (dS_k - sum_j w_j dS_j)          (renormalised softmax)
 //   dX_router[t] = sum_k dz[t,S_k] Wg[S_k]          -> fold accumulator init
+// One wave per token: lane k < K finishes dS_k from its h-block partials; the
+// weighted sum over k is a butterfly (every lane gets the same bits, since each
+// step adds the same two values); the router term is written 16 bytes of Wg
+// per lane per step, k in ascending order.
+constexpr int RB_TOKENS = 4;  // tokens (waves) per workgroup
 template <typename TIN>
-__global__ __launch_bounds__(256) void router_bwd_kernel(const int32_t* __restrict__ ids,
-                                                         const float* __restrict__ topk_w,
-                                                         const int32_t* __restrict__ tim,
-                                                         const float* __restrict__ ds_part, int nbh,
-                                                         const TIN* __restrict__ wg, float* __restrict__ dz_pos,
-                                                         float* __restrict__ ds_out, float* __restrict__ accws,
-                                                         int T, int d, int K) {
-  const int t = blockIdx.x;
-  __shared__ float s_dz[32];
-  __shared__ int s_e[32];
-  if (threadIdx.x == 0) {
-    float dsv[32], wv[32];
-    float c = 0.0f;
-    for (int k = 0; k < K; ++k) {
-      const int p = tim[(size_t)t * K + k];
-      float v = 0.0f;
-      for (int nb = 0; nb < nbh; ++nb) v += ds_part[(size_t)p * nbh + nb];
-      dsv[k] = v;
-      wv[k] = topk_w[(size_t)t * K + k];
-      c += wv[k] * v;
-    }
-    for (int k = 0; k < K; ++k) {
-      const int p = tim[(size_t)t * K + k];
-      const float dz = wv[k] * (dsv[k] - c);
-      dz_pos[p] = dz;
-      if (ds_out) ds_out[(size_t)t * K + k] = dsv[k];
-      s_dz[k] = dz;
-      s_e[k] = ids[(size_t)t * K + k];
-    }
+__global__ __launch_bounds__(64 * RB_TOKENS) void router_bwd_kernel(const int32_t* __restrict__ ids,
+                                                                    const float* __restrict__ topk_w,
+                                                                    const int32_t* __restrict__ tim,
+                                                                    const float* __restrict__ ds_part, int nbh,
+                                                                    const TIN* __restrict__ wg,
+                                                                    float* __restrict__ dz_pos,
+                                                                    float* __restrict__ ds_out,
+                                                                    float* __restrict__ accws, int T, int d, int K) {
+  const int t = blockIdx.x * RB_TOKENS + (int)(threadIdx.x >> 6);
+  if (t >= T) return;  // whole waves
+  const int l = lane_id();
+  float dsv = 0.0f, wv = 0.0f;
+  int e = 0, p = 0;
+  if (l < K) {
+    p = tim[(size_t)t * K + l];
+    for (int nb = 0; nb < nbh; ++nb) dsv += ds_part[(size_t)p * nbh + nb];
+    wv = topk_w[(size_t)t * K + l];
+    e = ids[(size_t)t * K + l];
   }
-  __syncthreads();
-  for (int i = threadIdx.x; i < d; i += 256) {
-    float v = 0.0f;
-    for (int k = 0; k < K; ++k) v += s_dz[k] * ElemT<TIN>::load(wg + (size_t)s_e[k] * d + i);
-    accws[(size_t)t * d + i] = v;
+  float c = wv * dsv;
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) c += __shfl_xor(c, off, 64);
+  const float dz = wv * (dsv - c);
+  if (l < K) {
+    dz_pos[p] = dz;
+    if (ds_out) ds_out[(size_t)t * K + l] = dsv;
+  }
+  constexpr int VPL = 16 / sizeof(TIN);  // values per 16-byte load
+  float* orow = accws + (size_t)t * d;
+  for (int col = l * VPL; col < d; col += 64 * VPL) {
+    float acc[VPL];
+#pragma unroll
+    for (int v = 0; v < VPL; ++v) acc[v] = 0.0f;
+    for (int k = 0; k < K; ++k) {
+      const float z = __shfl(dz, k, 64);
+      const int ek = __shfl(e, k, 64);
+      const TIN* wr = wg + (size_t)ek * d + col;
+      if constexpr (sizeof(TIN) == 2) {
+        const u32x4_t q = *(const u32x4_t*)wr;
+#pragma unroll
+        for (int v = 0; v < 4; ++v) {
+          acc[2 * v] += z * bf16_to_f32(q[v] & 0xffffu);
+          acc[2 * v + 1] += z * bf16_to_f32(q[v] >> 16);
+        }
+      } else {
+        const f32x4_t q = *(const f32x4_t*)wr;
+#pragma unroll
+        for (int v = 0; v < 4; ++v) acc[v] += z * q[v];
+      }
+    }
+#pragma unroll
+    for (int v = 0; v < VPL; v += 4) *(f32x4_t*)(orow + col + v) = f32x4_t{acc[v], acc[v + 1], acc[v + 2], acc[v + 3]};
   }
 }
 
@@ -1163,8 +1185,8 @@ static hipError_t backward_t(const Shape& s, const void* dout, const void* x, co
   if ((err = hipGetLastError()) != hipSuccess) return err;
 
   timing_mark(st, "router_bwd", true);
-  router_bwd_kernel<TIN><<<dim3(s.T), dim3(256), 0, st>>>(ids, topk_w, tim, ws.ds_part, nbh, (const TIN*)wg,
-                                                          ws.dz_pos, ds, ws.acc, s.T, s.d, s.K);
+  router_bwd_kernel<TIN><<<dim3((s.T + RB_TOKENS - 1) / RB_TOKENS), dim3(64 * RB_TOKENS), 0, st>>>(
+      ids, topk_w, tim, ws.ds_part, nbh, (const TIN*)wg, ws.dz_pos, ds, ws.acc, s.T, s.d, s.K);
   timing_mark(st, "router_bwd", false);
   if ((err = hipGetLastError()) != hipSuccess) return err;
 

@@ -24,6 +24,12 @@
 
 namespace moe {
 
+// Step 1 + counts.  Each lane first turns its token's K expert ids into an
+// E-bit set (NW words of 64 experts); the mask of expert e is then the ballot
+// of bit e over the wave, which is how a compare result is produced anyway.
+// Lane b keeps expert 64 w + b's mask, so the masks of 64 experts leave in one
+// coalesced store.
+template <int NW>
 __global__ __launch_bounds__(256) void index_hist_kernel(const int32_t* __restrict__ ids, uint64_t* __restrict__ masks,
                                                          int32_t* __restrict__ base, int T, int E, int K,
                                                          int nchunks) {
@@ -31,16 +37,32 @@ __global__ __launch_bounds__(256) void index_hist_kernel(const int32_t* __restri
   const int wave = threadIdx.x >> 6;
   const int l = lane_id();
   const int t = chunk * IDX_CHUNK + (int)threadIdx.x;
-  int my[32];
-#pragma unroll 4
-  for (int k = 0; k < K; ++k) my[k] = t < T ? ids[(size_t)t * K + k] : -1;
-  __shared__ uint32_t s_cnt[IDX_WAVES][1024];
-  for (int e = 0; e < E; ++e) {
-    bool has = false;
-    for (int k = 0; k < K; ++k) has |= (my[k] == e);
-    const uint64_t m = __ballot(has);
-    if (l == 0) {
-      masks[((size_t)chunk * IDX_WAVES + wave) * E + e] = m;
+  uint32_t bits[2 * NW];  // 32-bit halves of the expert set
+#pragma unroll
+  for (int w = 0; w < 2 * NW; ++w) bits[w] = 0;
+  if (t < T) {
+    for (int k = 0; k < K; ++k) {
+      const int e = ids[(size_t)t * K + k];
+#pragma unroll
+      for (int w = 0; w < 2 * NW; ++w) bits[w] |= (e >> 5) == w ? 1u << (e & 31) : 0u;
+    }
+  }
+  __shared__ uint32_t s_cnt[IDX_WAVES][NW * 64];
+  uint64_t* mrow = masks + ((size_t)chunk * IDX_WAVES + wave) * E;
+#pragma unroll
+  for (int w = 0; w < NW; ++w) {
+    if (w * 64 >= E) break;
+    uint32_t lo = 0, hi = 0;  // lane b: mask of expert 64 w + b
+#pragma unroll
+    for (int b = 0; b < 64; ++b) {
+      const uint64_t m = __ballot((bits[2 * w + (b >> 5)] >> (b & 31)) & 1u);
+      lo = l == b ? (uint32_t)m : lo;
+      hi = l == b ? (uint32_t)(m >> 32) : hi;
+    }
+    const int e = w * 64 + l;
+    if (e < E) {
+      const uint64_t m = ((uint64_t)hi << 32) | lo;
+      mrow[e] = m;
       s_cnt[wave][e] = (uint32_t)__popcll(m);
     }
   }
@@ -54,33 +76,41 @@ __global__ __launch_bounds__(256) void index_hist_kernel(const int32_t* __restri
 }
 
 // Exclusive scan of the [E][nchunks] count matrix in expert-major order by
-// one 1024-thread workgroup (each thread owns a contiguous segment).
+// one 1024-thread workgroup: each thread sums a contiguous segment, the
+// segment sums are scanned with wave shuffles (then across the 16 waves), and
+// each thread writes its segment's bases.  All sums are below T*K < 2^31.
 __global__ __launch_bounds__(1024) void index_scan_kernel(int32_t* __restrict__ base, int32_t* __restrict__ offsets,
                                                           int E, int nchunks) {
   const long long n = (long long)E * nchunks;
-  const int tid = threadIdx.x;
+  const int tid = threadIdx.x, l = lane_id(), wave = tid >> 6;
   const long long per = (n + 1023) / 1024;
-  const long long s0 = tid * per;
+  const long long s0 = tid * per < n ? tid * per : n;
   const long long s1 = s0 + per < n ? s0 + per : n;
-  long long sum = 0;
+  int sum = 0;
   for (long long i = s0; i < s1; ++i) sum += base[i];
-  __shared__ long long sh[1024];
-  sh[tid] = sum;
+  int incl = sum;  // inclusive scan inside the wave
+#pragma unroll
+  for (int off = 1; off < 64; off <<= 1) {
+    const int v = __shfl_up(incl, off, 64);
+    if (l >= off) incl += v;
+  }
+  __shared__ int wsum[16];
+  if (l == 63) wsum[wave] = incl;
   __syncthreads();
-  for (int off = 1; off < 1024; off <<= 1) {
-    const long long v = tid >= off ? sh[tid - off] : 0;
-    __syncthreads();
-    sh[tid] += v;
-    __syncthreads();
+  int before = 0;
+  for (int w = 0; w < wave; ++w) before += wsum[w];
+  int run = before + incl - sum;  // exclusive prefix of this segment
+  if (s0 < s1) {
+    int e = (int)(s0 / nchunks), c = (int)(s0 % nchunks);
+    for (long long i = s0; i < s1; ++i) {
+      const int v = base[i];
+      base[i] = run;
+      if (c == 0) offsets[e] = run;
+      run += v;
+      if (++c == nchunks) { c = 0; ++e; }
+    }
   }
-  long long run = sh[tid] - sum;  // exclusive prefix of this segment
-  for (long long i = s0; i < s1; ++i) {
-    const int c = base[i];
-    base[i] = (int32_t)run;
-    if (i % nchunks == 0) offsets[i / nchunks] = (int32_t)run;
-    run += c;
-  }
-  if (tid == 1023) offsets[E] = (int32_t)sh[1023];
+  if (tid == 1023) offsets[E] = run;
 }
 
 __global__ __launch_bounds__(256) void index_scatter_kernel(const int32_t* __restrict__ ids,
@@ -108,7 +138,14 @@ __global__ __launch_bounds__(256) void index_scatter_kernel(const int32_t* __res
 hipError_t launch_build_index(const Shape& s, const int32_t* ids, int32_t* offsets, int32_t* eti, int32_t* tim,
                               const IndexWs& ws, hipStream_t st) {
   timing_mark(st, "index", true);
-  index_hist_kernel<<<dim3(ws.nchunks), dim3(256), 0, st>>>(ids, ws.masks, ws.base, s.T, s.E, s.K, ws.nchunks);
+  {
+    const dim3 g(ws.nchunks), b(256);
+    if (s.E <= 64) index_hist_kernel<1><<<g, b, 0, st>>>(ids, ws.masks, ws.base, s.T, s.E, s.K, ws.nchunks);
+    else if (s.E <= 128) index_hist_kernel<2><<<g, b, 0, st>>>(ids, ws.masks, ws.base, s.T, s.E, s.K, ws.nchunks);
+    else if (s.E <= 256) index_hist_kernel<4><<<g, b, 0, st>>>(ids, ws.masks, ws.base, s.T, s.E, s.K, ws.nchunks);
+    else if (s.E <= 512) index_hist_kernel<8><<<g, b, 0, st>>>(ids, ws.masks, ws.base, s.T, s.E, s.K, ws.nchunks);
+    else index_hist_kernel<16><<<g, b, 0, st>>>(ids, ws.masks, ws.base, s.T, s.E, s.K, ws.nchunks);
+  }
   index_scan_kernel<<<dim3(1), dim3(1024), 0, st>>>(ws.base, offsets, s.E, ws.nchunks);
   index_scatter_kernel<<<dim3(ws.nchunks), dim3(256), 0, st>>>(ids, ws.masks, ws.base, eti, tim, s.T, s.E, s.K,
                                                                ws.nchunks);
@@ -168,16 +205,16 @@ __global__ __launch_bounds__(256) void prep_kernel(int T, int E, int K, const in
   const long long gsz = (long long)gridDim.x * 256;
   const long long gid = (long long)blockIdx.x * 256 + tid;
   if (w_pos) {
-    for (long long t = gid; t < T; t += gsz) {
-      int e[32];
-      for (int k = 0; k < K; ++k) e[k] = ids[t * K + k];
-      for (int k = 0; k < K; ++k) {
-        int r = 0;
-        for (int j = 0; j < K; ++j) r += e[j] < e[k];
-        const int p = tim[t * K + k];
-        w_pos[p] = topk_w[t * K + k];
-        rank_pos[p] = r;
-      }
+    // one thread per assignment a = t*K + k (T*K < 2^31)
+    const int A = T * K;
+    for (long long a = gid; a < A; a += gsz) {
+      const int ai = (int)a, t0 = ai - ai % K;
+      const int ek = ids[ai];
+      int r = 0;
+      for (int j = 0; j < K; ++j) r += ids[t0 + j] < ek;
+      const int p = tim[ai];
+      w_pos[p] = topk_w[ai];
+      rank_pos[p] = r;
     }
   }
   if (turn)
@@ -188,7 +225,7 @@ hipError_t launch_prep(const Shape& s, const ExpertWs& ws, const int32_t* offset
                        const float* topk_w, const int32_t* tim, bool per_position, hipStream_t st) {
   timing_mark(st, "prep", true);
   const long long n_turn = per_position ? (long long)s.T * col_blocks(s.d, TILE_S) : 0;
-  long long work = per_position ? (n_turn > s.T ? n_turn : s.T) : 1;
+  long long work = per_position ? (n_turn > s.A() ? n_turn : s.A()) : 1;
   int blocks = (int)((work + 255) / 256);
   if (blocks > 2048) blocks = 2048;
   if (blocks < 1) blocks = 1;

@@ -68,8 +68,14 @@ static hipError_t router_logits_t(const Shape& s, const void* x, const void* wg,
     const dim3 grd((s.T + C::BM - 1) / C::BM, (s.E + C::BN - 1) / C::BN);
     router_logits_kernel<C><<<grd, blk, 0, st>>>((const TIN*)x, (const TIN*)wg, bias, logits, s.T, s.d, s.E);
   } else if (s.E <= 64) {
-    using C = Cfg<TIN, 128, 64, 2, 2>;
+    // 64-token tiles: a grid of T/64 workgroups fills the chip from a few thousand tokens
+    using C = Cfg<TIN, 64, 64, 2, 2>;
     const dim3 grd((s.T + C::BM - 1) / C::BM, (s.E + C::BN - 1) / C::BN);
+    router_logits_kernel<C><<<grd, blk, 0, st>>>((const TIN*)x, (const TIN*)wg, bias, logits, s.T, s.d, s.E);
+  } else if (s.E <= 128) {
+    // one 128-expert column block: 32-token tiles keep enough workgroups in flight
+    using C = Cfg<TIN, 32, 128, 1, 4>;
+    const dim3 grd((s.T + C::BM - 1) / C::BM, 1);
     router_logits_kernel<C><<<grd, blk, 0, st>>>((const TIN*)x, (const TIN*)wg, bias, logits, s.T, s.d, s.E);
   } else {
     using C = Cfg<TIN, 128, 128, 2, 2>;
@@ -89,36 +95,52 @@ hipError_t launch_router_logits(const Shape& s, const void* x, const void* wg, c
 }
 
 // ---------------------------------------------------------------------------
-// top-K: a group of G lanes (G = power of two, 8..64) per token, each lane
-// holding up to V logits (experts lane, lane+G, ...).  K rounds of a group
-// arg-max (larger value wins, ties to the lower id), then the weights.
+// top-K: a group of G lanes (a power of two, 1..64) per token; lane gl holds
+// the V logits of experts gl*V .. gl*V+V-1 (contiguous, 16-byte loads when the
+// rows allow).  K rounds of a group arg-max (larger value wins, ties to the
+// lower id); the group's lane 0 writes each round's id at once and parks its
+// logit in LDS.  Every lane of a group sees the same arg-max bits, so the
+// softmax denominator over the chosen logits, sum_k exp(z_k - z_0) in k
+// order, is the same in all of them; the weights are then written in
+// parallel.
 // ---------------------------------------------------------------------------
 template <int G, int V>
 __global__ __launch_bounds__(256) void topk_kernel(const float* __restrict__ logits, int32_t* __restrict__ ids,
                                                    float* __restrict__ wts, int T, int E, int K) {
-  const int gpb = 256 / G;
-  const int t = blockIdx.x * gpb + (int)(threadIdx.x / G);
-  const int gl = (int)(threadIdx.x % G);
-  if (t >= T) return;  // the whole group exits together
+  constexpr int GPB = 256 / G;  // tokens per workgroup
+  __shared__ float s_z[GPB][32];
+  const int g = (int)(threadIdx.x / G), gl = (int)(threadIdx.x % G);
+  const int t = blockIdx.x * GPB + g;
+  const bool valid = t < T;
+  const int e0 = gl * V;
   float z[V];
-  const float* zr = logits + (size_t)t * E;
+  const float* zr = logits + (size_t)(valid ? t : 0) * E + e0;
+  if (valid && e0 + V <= E && (E & 3) == 0 && (V & 3) == 0) {
 #pragma unroll
-  for (int v = 0; v < V; ++v) {
-    const int e = gl + v * G;
-    z[v] = e < E ? zr[e] : -INFINITY;
+    for (int v = 0; v < V; v += 4) {
+      const f32x4_t q = *(const f32x4_t*)(zr + v);
+      z[v] = q[0];
+      z[v + 1] = q[1];
+      z[v + 2] = q[2];
+      z[v + 3] = q[3];
+    }
+  } else {
+#pragma unroll
+    for (int v = 0; v < V; ++v) z[v] = valid && e0 + v < E ? zr[v] : -INFINITY;
   }
-  uint32_t taken = 0;
-  float sel_z[32];
-  int sel_id[32];
+  uint32_t live = 0;  // experts of this lane still selectable
+#pragma unroll
+  for (int v = 0; v < V; ++v) live |= (e0 + v < E ? 1u : 0u) << v;
+  float m0 = 0.0f, ssum = 0.0f;
   for (int k = 0; k < K; ++k) {
     float bz = -INFINITY;
     int bid = 0x7fffffff;
 #pragma unroll
     for (int v = 0; v < V; ++v) {
-      const int e = gl + v * G;
-      if (e < E && !((taken >> v) & 1u) && (z[v] > bz || (z[v] == bz && e < bid))) {
+      // ascending ids inside the lane: a strict > keeps the lowest id of a tie
+      if (((live >> v) & 1u) && (z[v] > bz || bid == 0x7fffffff)) {
         bz = z[v];
-        bid = e;
+        bid = e0 + v;
       }
     }
 #pragma unroll
@@ -130,23 +152,18 @@ __global__ __launch_bounds__(256) void topk_kernel(const float* __restrict__ log
         bid = oid;
       }
     }
-    if (bid % G == gl) taken |= 1u << (bid / G);
-    sel_z[k & 31] = bz;
-    sel_id[k & 31] = bid;
+    if (bid - e0 >= 0 && bid - e0 < V) live &= ~(1u << (bid - e0));
+    if (k == 0) m0 = bz;
+    ssum += expf(bz - m0);
+    if (gl == 0 && valid) {
+      ids[(size_t)t * K + k] = bid;
+      s_z[g][k] = bz;
+    }
   }
-  if (gl == 0) {
-    const float m = sel_z[0];
-    float ssum = 0.0f;
-    float ex[32];
-    for (int k = 0; k < K; ++k) {
-      ex[k] = expf(sel_z[k] - m);
-      ssum += ex[k];
-    }
+  __syncthreads();
+  if (valid) {
     const float inv = 1.0f / ssum;
-    for (int k = 0; k < K; ++k) {
-      ids[(size_t)t * K + k] = sel_id[k];
-      wts[(size_t)t * K + k] = ex[k] * inv;
-    }
+    for (int j = gl; j < K; j += G) wts[(size_t)t * K + j] = expf(s_z[g][j] - m0) * inv;
   }
 }
 
@@ -157,12 +174,13 @@ hipError_t launch_topk(const Shape& s, const float* logits, int32_t* ids, float*
     const int gpb = 256 / G;
     kern<<<dim3((s.T + gpb - 1) / gpb), dim3(256), 0, st>>>(logits, ids, w, s.T, s.E, s.K);
   };
-  if (E <= 8) go(topk_kernel<8, 1>, 8);
-  else if (E <= 16) go(topk_kernel<16, 1>, 16);
-  else if (E <= 32) go(topk_kernel<32, 1>, 32);
-  else if (E <= 64) go(topk_kernel<64, 1>, 64);
-  else if (E <= 128) go(topk_kernel<64, 2>, 64);
-  else if (E <= 256) go(topk_kernel<64, 4>, 64);
+  // about eight logits per lane
+  if (E <= 8) go(topk_kernel<1, 8>, 1);
+  else if (E <= 16) go(topk_kernel<2, 8>, 2);
+  else if (E <= 32) go(topk_kernel<4, 8>, 4);
+  else if (E <= 64) go(topk_kernel<8, 8>, 8);
+  else if (E <= 128) go(topk_kernel<16, 8>, 16);
+  else if (E <= 256) go(topk_kernel<32, 8>, 32);
   else if (E <= 512) go(topk_kernel<64, 8>, 64);
   else go(topk_kernel<64, 16>, 64);
   hipError_t e = hipGetLastError();
