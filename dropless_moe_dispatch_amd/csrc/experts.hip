@@ -66,6 +66,18 @@ static int forced_tile() {
   }();
   return v;
 }
+// Row blocks per tile group (see grouped_tile).  Measured on MI355X: the
+// plain kernels gain a few percent from 8 at large d; the folds lose with
+// large groups (a token's turns come further apart) and take 2.
+// MOE_DISPATCH_GROUP_ROWS overrides both for tuning.
+static int tile_group_rows(bool fold = false) {
+  static int v = [] {
+    const char* e = getenv("MOE_DISPATCH_GROUP_ROWS");
+    const int r = e ? atoi(e) : 0;
+    return r >= 1 && r <= 64 ? r : 0;
+  }();
+  return v ? v : fold ? 2 : 8;
+}
 static bool pick_large(bool auto_choice) {
   const int f = forced_tile();
   return f ? f == TILE_L : auto_choice;
@@ -79,14 +91,13 @@ __global__ __launch_bounds__(C::NT, C::WAVES_PER_EU) void gate_up_kernel(
     const typename C::T* __restrict__ x, const int32_t* __restrict__ offsets, const int32_t* __restrict__ eti,
     const int32_t* __restrict__ mb_off, const typename C::T* __restrict__ w_gate,
     const typename C::T* __restrict__ w_up, typename C::T* __restrict__ h_ab, typename C::T* __restrict__ y_swi,
-    int T, int d, int E, int h, int nbn, int nblk) {
+    int T, int d, int E, int h, int nbn, int nblk, int grp) {
   __shared__ __attribute__((aligned(16))) char smem[C::LDS_BYTES];
   using TIN = typename C::T;
   constexpr int HB = C::BN / 2;     // gate (= up) columns per tile
   constexpr int HF = C::FN / 2;     // gate fragments per wave
-  const int id = xcd_swizzle(blockIdx.x, nblk);
-  const int g = id / nbn, nb = id % nbn;
-  if (g >= mb_off[E]) return;
+  int g, nb;
+  if (!grouped_tile(xcd_swizzle(blockIdx.x, nblk), mb_off[E], nbn, grp, g, nb)) return;
   const RowTile rt = decode_row_tile<C::BM>(mb_off, offsets, E, g);
   const int wave = threadIdx.x >> 6, wm = wave / C::WN, wn = wave % C::WN;
   const uint32_t ldx = (uint32_t)d * sizeof(TIN);
@@ -176,7 +187,7 @@ static hipError_t gate_up_t(const Shape& s, const void* x, const int32_t* offset
   nblk = (nblk + 7) / 8 * 8;
   gate_up_kernel<C><<<dim3((unsigned)nblk), dim3(C::NT), 0, st>>>(
       (const TIN*)x, offsets, eti, ws.tile_map(B), (const TIN*)w_gate, (const TIN*)w_up, (TIN*)h_ab, (TIN*)y_swi,
-      s.T, s.d, s.E, s.h, nbn, (int)nblk);
+      s.T, s.d, s.E, s.h, nbn, (int)nblk, tile_group_rows());
   return hipGetLastError();
 }
 
@@ -187,12 +198,11 @@ template <class C>
 __global__ __launch_bounds__(C::NT, C::WAVES_PER_EU) void up_act_kernel(
     const typename C::T* __restrict__ x, const int32_t* __restrict__ offsets, const int32_t* __restrict__ eti,
     const int32_t* __restrict__ mb_off, const typename C::T* __restrict__ w1, typename C::T* __restrict__ h_a,
-    typename C::T* __restrict__ y_swi, int T, int d, int E, int h, int act, int nbn, int nblk) {
+    typename C::T* __restrict__ y_swi, int T, int d, int E, int h, int act, int nbn, int nblk, int grp) {
   __shared__ __attribute__((aligned(16))) char smem[C::LDS_BYTES];
   using TIN = typename C::T;
-  const int id = xcd_swizzle(blockIdx.x, nblk);
-  const int g = id / nbn, nb = id % nbn;
-  if (g >= mb_off[E]) return;
+  int g, nb;
+  if (!grouped_tile(xcd_swizzle(blockIdx.x, nblk), mb_off[E], nbn, grp, g, nb)) return;
   const RowTile rt = decode_row_tile<C::BM>(mb_off, offsets, E, g);
   const int wave = threadIdx.x >> 6, wm = wave / C::WN, wn = wave % C::WN;
   const uint32_t ldx = (uint32_t)d * sizeof(TIN);
@@ -274,7 +284,7 @@ static hipError_t up_act_t(const Shape& s, const void* x, const int32_t* offsets
   nblk = (nblk + 7) / 8 * 8;
   up_act_kernel<C><<<dim3((unsigned)nblk), dim3(C::NT), 0, st>>>(
       (const TIN*)x, offsets, eti, ws.tile_map(B), (const TIN*)w1, (TIN*)h_a, (TIN*)y_swi, s.T, s.d, s.E, s.h,
-      s.act, nbn, (int)nblk);
+      s.act, nbn, (int)nblk, tile_group_rows());
   return hipGetLastError();
 }
 
@@ -459,13 +469,12 @@ __global__ __launch_bounds__(C::NT, C::WAVES_PER_EU) void down_combine_kernel(
     const typename C::T* __restrict__ y_swi, const typename C::T* __restrict__ w_down,
     const int32_t* __restrict__ offsets, const int32_t* __restrict__ eti, const int32_t* __restrict__ mb_off,
     const float* __restrict__ w_pos, const int32_t* __restrict__ rank_pos, int32_t* turn, float* accws,
-    typename C::T* __restrict__ out, int32_t* counters, int d, int E, int K, int h, int spin_limit) {
+    typename C::T* __restrict__ out, int32_t* counters, int d, int E, int K, int h, int spin_limit, int grp) {
   __shared__ __attribute__((aligned(16))) char smem[C::LDS_BYTES];
   using TIN = typename C::T;
   const int NB = col_blocks(d, C::BN);
-  const int tile = claim_ticket(counters, smem);
-  const int g = tile / NB, nb = tile % NB;
-  if (g >= mb_off[E]) return;
+  int g, nb;
+  if (!grouped_tile(claim_ticket(counters, smem), mb_off[E], NB, grp, g, nb)) return;
   const RowTile rt = decode_row_tile<C::BM>(mb_off, offsets, E, g);
   const int wave = threadIdx.x >> 6, wm = wave / C::WN, wn = wave % C::WN;
   const uint32_t ldy = (uint32_t)h * sizeof(TIN);
@@ -498,7 +507,7 @@ static hipError_t down_combine_t(const Shape& s, const void* y_swi, const void* 
   const long long nblk = max_row_blocks(s, B) * col_blocks(s.d, B);
   down_combine_kernel<C><<<dim3((unsigned)nblk), dim3(C::NT), 0, st>>>(
       (const TIN*)y_swi, (const TIN*)w_down, offsets, eti, ws.tile_map(B), ws.w_pos, ws.rank_pos, ws.turn, ws.acc,
-      (TIN*)out, ws.counters, s.d, s.E, s.K, s.h, spin_limit);
+      (TIN*)out, ws.counters, s.d, s.E, s.K, s.h, spin_limit, tile_group_rows(true));
   return hipGetLastError();
 }
 
@@ -524,13 +533,12 @@ template <class C>
 __global__ __launch_bounds__(C::NT, C::WAVES_PER_EU) void down_staged_kernel(
     const typename C::T* __restrict__ y_swi, const typename C::T* __restrict__ w_down,
     const int32_t* __restrict__ offsets, const int32_t* __restrict__ mb_off, typename C::T* __restrict__ ystage,
-    int d, int E, int h, int nbn, int nblk) {
+    int d, int E, int h, int nbn, int nblk, int grp) {
   static_assert(C::BM == 128 && C::BN == 128 && C::NT == NTHREADS, "128 x 128 tile, four waves");
   __shared__ __attribute__((aligned(16))) char smem[C::LDS_BYTES];
   using TIN = typename C::T;
-  const int id = xcd_swizzle(blockIdx.x, nblk);
-  const int g = id / nbn, nb = id % nbn;
-  if (g >= mb_off[E]) return;
+  int g, nb;
+  if (!grouped_tile(xcd_swizzle(blockIdx.x, nblk), mb_off[E], nbn, grp, g, nb)) return;
   const RowTile rt = decode_row_tile<C::BM>(mb_off, offsets, E, g);
   const int wave = threadIdx.x >> 6, wm = wave / C::WN, wn = wave % C::WN;
   const uint32_t ldy = (uint32_t)h * sizeof(TIN);
@@ -643,7 +651,7 @@ static hipError_t combine_staged_t(const Shape& s, const void* y_swi, const void
   timing_mark(st, "down_staged", true);
   down_staged_kernel<C><<<dim3((unsigned)nblk), dim3(C::NT), 0, st>>>(
       (const TIN*)y_swi, (const TIN*)w_down, offsets, ws.tile_map(TILE_S), (TIN*)ws.ystage, s.d, s.E, s.h, nbn,
-      (int)nblk);
+      (int)nblk, tile_group_rows());
   timing_mark(st, "down_staged", false);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
@@ -725,12 +733,11 @@ __global__ __launch_bounds__(C::NT, C::WAVES_PER_EU) void dh_kernel(
     const typename C::T* __restrict__ h_ab, const typename C::T* __restrict__ y_swi,
     const int32_t* __restrict__ offsets, const int32_t* __restrict__ eti, const int32_t* __restrict__ mb_off,
     const float* __restrict__ w_pos, typename C::T* __restrict__ dh, float* __restrict__ ds_part,
-    typename C::T* __restrict__ a_prime, int T, int d, int E, int h, int act, int nbn, int nblk) {
+    typename C::T* __restrict__ a_prime, int T, int d, int E, int h, int act, int nbn, int nblk, int grp) {
   __shared__ __attribute__((aligned(16))) char smem[C::LDS_BYTES];
   using TIN = typename C::T;
-  const int id = xcd_swizzle(blockIdx.x, nblk);
-  const int g = id / nbn, nb = id % nbn;
-  if (g >= mb_off[E]) return;
+  int g, nb;
+  if (!grouped_tile(xcd_swizzle(blockIdx.x, nblk), mb_off[E], nbn, grp, g, nb)) return;
   const RowTile rt = decode_row_tile<C::BM>(mb_off, offsets, E, g);
   const int wave = threadIdx.x >> 6, wm = wave / C::WN, wn = wave % C::WN;
   const uint32_t ldd = (uint32_t)d * sizeof(TIN);
@@ -1108,13 +1115,13 @@ __global__ __launch_bounds__(C::NT, C::WAVES_PER_EU) void dx_fold_kernel(
     const typename C::T* __restrict__ dh, const typename C::T* __restrict__ w_gate,
     const typename C::T* __restrict__ w_up, const int32_t* __restrict__ offsets, const int32_t* __restrict__ eti,
     const int32_t* __restrict__ mb_off, const int32_t* __restrict__ rank_pos, int32_t* turn, float* accws,
-    typename C::T* __restrict__ dx, int32_t* counters, int d, int E, int K, int h, int hw, int spin_limit) {
+    typename C::T* __restrict__ dx, int32_t* counters, int d, int E, int K, int h, int hw, int spin_limit,
+    int grp) {
   __shared__ __attribute__((aligned(16))) char smem[C::LDS_BYTES];
   using TIN = typename C::T;
   const int NB = col_blocks(d, C::BN);
-  const int tile = claim_ticket(counters, smem);
-  const int g = tile / NB, nb = tile % NB;
-  if (g >= mb_off[E]) return;
+  int g, nb;
+  if (!grouped_tile(claim_ticket(counters, smem), mb_off[E], NB, grp, g, nb)) return;
   const RowTile rt = decode_row_tile<C::BM>(mb_off, offsets, E, g);
   const int wave = threadIdx.x >> 6, wm = wave / C::WN, wn = wave % C::WN;
   const uint32_t ldh = (uint32_t)hw * sizeof(TIN);
@@ -1148,7 +1155,8 @@ static void launch_dh(const Shape& s, const void* dout, const void* w_down, cons
   const long long nblk = (max_row_blocks(s, B) * nbn + 7) / 8 * 8;
   dh_kernel<C, HONLY><<<dim3((unsigned)nblk), dim3(C::NT), 0, st>>>(
       (const TIN*)dout, (const TIN*)w_down, (const TIN*)h_ab, (const TIN*)y_swi, offsets, eti, ws.tile_map(B),
-      ws.w_pos, (TIN*)ws.dh, ws.ds_part, (TIN*)ws.a_prime, s.T, s.d, s.E, s.h, s.act, nbn, (int)nblk);
+      ws.w_pos, (TIN*)ws.dh, ws.ds_part, (TIN*)ws.a_prime, s.T, s.d, s.E, s.h, s.act, nbn, (int)nblk,
+      tile_group_rows());
 }
 
 template <typename TIN, int B>
@@ -1158,7 +1166,7 @@ static void launch_dx_fold(const Shape& s, const void* w_gate, const void* w_up,
   const long long nblk = max_row_blocks(s, B) * col_blocks(s.d, B);
   dx_fold_kernel<C><<<dim3((unsigned)nblk), dim3(C::NT), 0, st>>>(
       (const TIN*)ws.dh, (const TIN*)w_gate, (const TIN*)w_up, offsets, eti, ws.tile_map(B), ws.rank_pos, ws.turn,
-      ws.acc, (TIN*)dx, ws.counters, s.d, s.E, s.K, s.h, s.hw(), spin_limit);
+      ws.acc, (TIN*)dx, ws.counters, s.d, s.E, s.K, s.h, s.hw(), spin_limit, tile_group_rows(true));
 }
 
 template <typename TIN>

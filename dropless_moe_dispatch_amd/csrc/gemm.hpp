@@ -514,6 +514,21 @@ MOE_DEV RowTile decode_row_tile(const int32_t* __restrict__ mb_off, const int32_
 
 // Map a linear tile id to an id such that consecutive ids land on the same
 // XCD (the dispatcher hands consecutive workgroup ids to the 8 XCDs in turn).
+// Tile order of the varlen-M kernels: groups of R consecutive row blocks;
+// inside a group the column block is major and the row block minor, so
+// consecutive tiles share the B column block (weights) and a row block's A
+// rows come back every R tiles, both within the span of tiles one XCD runs
+// at a time.  Ids at or past ng * nbn (launch padding) return false.
+MOE_DEV bool grouped_tile(int id, int ng, int nbn, int R, int& g, int& nb) {
+  if (id >= ng * nbn) return false;
+  const int g0 = id / (R * nbn) * R;
+  const int rows = ng - g0 < R ? ng - g0 : R;
+  const int rem = id - g0 * nbn;
+  nb = rem / rows;
+  g = g0 + rem % rows;
+  return true;
+}
+
 MOE_DEV int xcd_swizzle(int bid, int nblk) {
   const int per = nblk >> 3;  // nblk is padded to a multiple of 8 by the launcher
   return (bid & 7) * per + (bid >> 3);
