@@ -1015,6 +1015,41 @@ __global__ __launch_bounds__(256) void dwg_reduce_kernel(const float* __restrict
 }
 
 // dW_down[e] (d x h) = sum_p dO[eti[p]]^T (w_p y[p]): M = d, N = h, K = rows of e.
+// Rows [p0, p1) of expert rows [q0, q1) that chunk blockIdx.z of gridDim.z
+// reduces: equal chunks, rounded up to whole k-tiles (the last may be short or
+// empty; an empty chunk writes a zero partial).
+template <int BK>
+MOE_DEV void split_rows(int q0, int q1, int& p0, int& p1) {
+  const int ns = (int)gridDim.z;
+  const int len = ((q1 - q0 + ns - 1) / ns + BK - 1) / BK * BK;
+  p0 = min_i(q1, q0 + (int)blockIdx.z * len);
+  p1 = min_i(q1, p0 + len);
+}
+
+// dW from its chunk partials [ns][E][M][N]: the sum over chunks in chunk
+// order; rows m < M0 of expert e go to out0 ([E][M0][N]), the others to out1
+// ([E][M - M0][N]).  Four floats per thread (N is a multiple of 128).
+__global__ __launch_bounds__(256) void dw_split_reduce_kernel(const float* __restrict__ part, int ns, long long stride,
+                                                              int M, int M0, int N, float* __restrict__ out0,
+                                                              float* __restrict__ out1) {
+  const long long i = ((long long)blockIdx.x * 256 + threadIdx.x) * 4;
+  if (i >= stride) return;
+  f32x4_t acc = *(const f32x4_t*)(part + i);
+  for (int c = 1; c < ns; ++c) acc += *(const f32x4_t*)(part + (size_t)c * stride + i);
+  const long long row = i / N;
+  const int n = (int)(i - row * N);
+  const long long e = row / M;
+  const int m = (int)(row - e * M);
+  float* o = m < M0 ? out0 + ((size_t)e * M0 + m) * N + n : out1 + ((size_t)e * (M - M0) + (m - M0)) * N + n;
+  *(f32x4_t*)o = acc;
+}
+static void launch_dw_split_reduce(const float* part, int ns, int E, int M, int M0, int N, float* out0, float* out1,
+                                   hipStream_t st) {
+  const long long stride = (long long)E * M * N;
+  dw_split_reduce_kernel<<<dim3((unsigned)((stride / 4 + 255) / 256)), dim3(256), 0, st>>>(part, ns, stride, M, M0,
+                                                                                         N, out0, out1);
+}
+
 // The score-scaled activation A' = w_p y[p] is formed while staging the B
 // operand and held in the activation dtype, as the SonicMoE analysis page
 // (sec. 3.4.1) defines A' = Broadcast(s) A for the dW2 grouped GEMM.
@@ -1024,13 +1059,14 @@ template <class C, bool SCALE>
 __global__ __launch_bounds__(C::NT, C::WAVES_PER_EU) void dw_down_kernel(
     const typename C::T* __restrict__ dout, const typename C::T* __restrict__ y_swi,
     const int32_t* __restrict__ offsets, const int32_t* __restrict__ eti, const float* __restrict__ w_pos,
-    float* __restrict__ dw_down, int T, int d, int h) {
+    float* __restrict__ dw_down, float* __restrict__ part, int T, int d, int h) {
   __shared__ __attribute__((aligned(16))) char smem[C::LDS_BYTES];
   using TIN = typename C::T;
   const int nnb = col_blocks(h, C::BN);
   const int e = blockIdx.y;
   const int mb = blockIdx.x / nnb, nb = blockIdx.x % nnb;
-  const int p0 = offsets[e], p1 = offsets[e + 1];
+  int p0, p1;
+  split_rows<C::BK>(offsets[e], offsets[e + 1], p0, p1);
   const int wave = threadIdx.x >> 6, wm = wave / C::WN, wn = wave % C::WN;
   KSrcLoader<C, C::AKM, C::BM, SrcRowsGather<TIN>, false> la;
   la.src.rs = make_rsrc(dout, (size_t)T * d * sizeof(TIN));
@@ -1049,7 +1085,8 @@ __global__ __launch_bounds__(C::NT, C::WAVES_PER_EU) void dw_down_kernel(
   f32x16_t acc[C::FM][C::FN];
   gemm_mainloop<C>(la, lb, (p1 - p0 + C::BK - 1) / C::BK, smem, acc, wm, wn);
   const int l = lane_id();
-  float* o = dw_down + (size_t)e * d * h;
+  // one chunk of a split writes its partial, laid out like dW_down
+  float* o = (gridDim.z > 1 ? part + (size_t)blockIdx.z * gridDim.y * d * h : dw_down) + (size_t)e * d * h;
 #pragma unroll
   for (int fm = 0; fm < C::FM; ++fm)
 #pragma unroll
@@ -1069,13 +1106,15 @@ __global__ __launch_bounds__(C::NT, C::WAVES_PER_EU) void dw_down_kernel(
 template <class C>
 __global__ __launch_bounds__(C::NT, C::WAVES_PER_EU) void dw_gate_up_kernel(
     const typename C::T* __restrict__ dh, const typename C::T* __restrict__ x, const int32_t* __restrict__ offsets,
-    const int32_t* __restrict__ eti, float* __restrict__ dw_gate, float* __restrict__ dw_up, int T, int d, int h, int hw) {
+    const int32_t* __restrict__ eti, float* __restrict__ dw_gate, float* __restrict__ dw_up, float* __restrict__ part,
+    int T, int d, int h, int hw) {
   __shared__ __attribute__((aligned(16))) char smem[C::LDS_BYTES];
   using TIN = typename C::T;
   const int nnb = col_blocks(d, C::BN);
   const int e = blockIdx.y;
   const int mb = blockIdx.x / nnb, nb = blockIdx.x % nnb;
-  const int p0 = offsets[e], p1 = offsets[e + 1];
+  int p0, p1;
+  split_rows<C::BK>(offsets[e], offsets[e + 1], p0, p1);
   const int wave = threadIdx.x >> 6, wm = wave / C::WN, wn = wave % C::WN;
   KSrcLoader<C, C::AKM, C::BM, SrcRowsContig<TIN>, false> la;
   la.src.rs = make_rsrc(dh + (size_t)p0 * hw, (size_t)(p1 - p0) * hw * sizeof(TIN));
@@ -1099,7 +1138,10 @@ __global__ __launch_bounds__(C::NT, C::WAVES_PER_EU) void dw_gate_up_kernel(
     for (int r = 0; r < 16; ++r) {
       const int m = mb * C::BM + C::a_row0(wm, fm) + frag_row(r, l);
       if (m >= hw) continue;
-      float* o = m < h ? dw_gate + ((size_t)e * h + m) * d : dw_up + ((size_t)e * h + (m - h)) * d;
+      // one chunk of a split writes its partial as [E][hw][d]
+      float* o = gridDim.z > 1 ? part + (((size_t)blockIdx.z * gridDim.y + e) * hw + m) * d
+                 : m < h       ? dw_gate + ((size_t)e * h + m) * d
+                               : dw_up + ((size_t)e * h + (m - h)) * d;
 #pragma unroll
       for (int fn = 0; fn < C::FN; ++fn) {
         const int n = nb * C::BN + C::b_row0(wn, fn) + frag_col(l);
@@ -1212,21 +1254,27 @@ static hipError_t backward_t(const Shape& s, const void* dout, const void* x, co
 
   timing_mark(st, "dw_down", true);
   {
-    const dim3 grid(col_blocks(s.d, CL::BM) * col_blocks(s.h, CL::BN), s.E);
+    const int ns = dw_down_split(s);
+    const dim3 grid(col_blocks(s.d, CL::BM) * col_blocks(s.h, CL::BN), s.E, ns);
     if (honly)
       dw_down_kernel<CL, false><<<grid, dim3(CL::NT), 0, st>>>((const TIN*)dout, (const TIN*)ws.a_prime, offsets,
-                                                               eti, ws.w_pos, dw_down, s.T, s.d, s.h);
+                                                               eti, ws.w_pos, dw_down, ws.dw_part, s.T, s.d, s.h);
     else
       dw_down_kernel<CL, true><<<grid, dim3(CL::NT), 0, st>>>((const TIN*)dout, (const TIN*)y_swi, offsets, eti,
-                                                              ws.w_pos, dw_down, s.T, s.d, s.h);
+                                                              ws.w_pos, dw_down, ws.dw_part, s.T, s.d, s.h);
+    if (ns > 1) launch_dw_split_reduce(ws.dw_part, ns, s.E, s.d, s.d, s.h, dw_down, nullptr, st);
   }
   timing_mark(st, "dw_down", false);
   if ((err = hipGetLastError()) != hipSuccess) return err;
 
   timing_mark(st, "dw_gate_up", true);
-  dw_gate_up_kernel<CL><<<dim3(col_blocks(s.hw(), CL::BM) * col_blocks(s.d, CL::BN), s.E), dim3(CL::NT), 0,
-                          st>>>((const TIN*)ws.dh, (const TIN*)x, offsets, eti, dw_gate, dw_up, s.T, s.d, s.h,
-                                s.hw());
+  {
+    const int ns = dw_gate_up_split(s);
+    dw_gate_up_kernel<CL><<<dim3(col_blocks(s.hw(), CL::BM) * col_blocks(s.d, CL::BN), s.E, ns), dim3(CL::NT), 0,
+                            st>>>((const TIN*)ws.dh, (const TIN*)x, offsets, eti, dw_gate, dw_up, ws.dw_part, s.T,
+                                  s.d, s.h, s.hw());
+    if (ns > 1) launch_dw_split_reduce(ws.dw_part, ns, s.E, s.hw(), s.h, s.d, dw_gate, dw_up, st);
+  }
   timing_mark(st, "dw_gate_up", false);
   if ((err = hipGetLastError()) != hipSuccess) return err;
 

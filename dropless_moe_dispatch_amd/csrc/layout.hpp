@@ -73,6 +73,21 @@ inline DenseIndexWs dense_index_ws(const Shape& s, void* p) {
   return w;
 }
 
+// Split of a dW GEMM's K (an expert's rows) into chunks when its 256 x 256
+// tiles alone cannot fill the chip: each chunk writes an fp32 partial and a
+// second pass sums the partials in chunk order.  m x n is the per-expert
+// output; the split depends on the shape only (average rows per expert), so
+// the workspace does too, and every chunk keeps 512 rows on average.
+inline int dw_split(const Shape& s, int m, int n) {
+  const long long tiles = (long long)s.E * col_blocks(m, TILE_L) * col_blocks(n, TILE_L);
+  const long long rows = s.A() / s.E;
+  int k = 1;
+  while (k < 8 && tiles * (2 * k) <= 512 && rows >= 512LL * (2 * k)) k *= 2;
+  return k;
+}
+inline int dw_down_split(const Shape& s) { return dw_split(s, s.d, s.h); }
+inline int dw_gate_up_split(const Shape& s) { return dw_split(s, s.hw(), s.d); }
+
 // ---- per-call expert workspace (tile map, per-position data, fold state) --
 struct ExpertWs {
   int32_t* counters;   // [N_COUNTERS]
@@ -84,6 +99,7 @@ struct ExpertWs {
   float* ds_part;      // [A][h/128] router-score partial sums (backward)
   float* dz_pos;       // [A] router logit gradient per position (backward)
   float* dwg_part;     // [row blocks of 128][d] per-row-block partial sums of dWg (backward)
+  float* dw_part;      // [split][E][m][n] dW chunk partials when a dW GEMM splits its rows (backward)
   void* dh;            // [A][hw] activation-dtype gradient of the pre-activations (backward)
   void* a_prime;       // [A][h] activation-dtype A' = w * y recomputed from a, b (H-only backward)
   void* ystage;        // [A][d] activation-dtype staged expert outputs (staged-Y combine ablation)
@@ -112,6 +128,10 @@ inline ExpertWs expert_ws(const Shape& s, int which, void* p) {
     w.ds_part = (float*)take(A * col_blocks(s.h, TILE_S) * 4);
     w.dz_pos = (float*)take(A * 4);
     w.dwg_part = (float*)take((size_t)max_row_blocks(s, TILE_S) * s.d * 4);
+    const int sd = dw_down_split(s), sg = dw_gate_up_split(s);
+    const size_t pd = sd > 1 ? (size_t)sd * s.E * s.d * s.h : 0;
+    const size_t pg = sg > 1 ? (size_t)sg * s.E * s.hw() * s.d : 0;
+    if (pd || pg) w.dw_part = (float*)take((pd > pg ? pd : pg) * 4);
     w.dh = take(A * (size_t)s.hw() * s.elem());
   }
   if (which == WS_EXPERT_BWD_H) w.a_prime = take(A * (size_t)s.h * s.elem());

@@ -122,6 +122,10 @@ LAYER_CASES = [
     ("k_eq_e", 130, 128, 4, 4, 128, "bf16", None),
     ("t1", 1, 128, 8, 3, 128, "bf16", None),
     ("f32_bwd", 300, 256, 16, 4, 256, "f32", None),
+    # few dW tiles, many rows per expert: the dW GEMMs split each expert's
+    # rows into 8 chunks and sum the partials
+    ("split_k", 4096, 256, 2, 2, 256, "bf16", None),
+    ("split_k_f32", 4096, 128, 2, 2, 128, "f32", None),
 ]
 
 
@@ -257,6 +261,7 @@ PLAIN_CASES = [
     ("relu_h_only", 513, 256, 64, 8, 128, "bf16", "relu", "ab"),
     ("silu_f32", 256, 128, 8, 2, 256, "f32", "silu", "aby"),
     ("relu_k1", 200, 128, 4, 1, 128, "bf16", "relu", "aby"),
+    ("silu_h_only_split_k", 8192, 256, 4, 1, 256, "bf16", "silu", "ab"),  # dW rows in 4 chunks
 ]
 
 
