@@ -66,17 +66,16 @@ static int forced_tile() {
   }();
   return v;
 }
-// Row blocks per tile group (see grouped_tile).  Measured on MI355X: the
-// plain kernels gain a few percent from 8 at large d; the folds lose with
-// large groups (a token's turns come further apart) and take 2.
-// MOE_DISPATCH_GROUP_ROWS overrides both for tuning.
-static int tile_group_rows(bool fold = false) {
+// Row blocks per tile group of the non-fold kernels (see grouped_tile); 8
+// gains a few percent at large d on MI355X.  MOE_DISPATCH_GROUP_ROWS
+// overrides it for tuning.
+static int tile_group_rows() {
   static int v = [] {
     const char* e = getenv("MOE_DISPATCH_GROUP_ROWS");
     const int r = e ? atoi(e) : 0;
-    return r >= 1 && r <= 64 ? r : 0;
+    return r >= 1 && r <= 64 ? r : 8;
   }();
-  return v ? v : fold ? 2 : 8;
+  return v;
 }
 static bool pick_large(bool auto_choice) {
   const int f = forced_tile();
@@ -452,13 +451,44 @@ MOE_DEV void fold_epilogue(const f32x16_t (&acc)[C::FM][C::FN], const RowTile& r
   }
 }
 
-MOE_DEV int claim_ticket(int32_t* counters, char* smem) {
+// Fold tiles come from eight queues, one per XCD: queue q holds the column
+// blocks nb = q, q + 8, ... of every row block, in ascending (row block,
+// column block) order.  A tile waits only on the same column block of a
+// token's lower experts, i.e. on earlier tiles of its own queue, so the claim
+// order per queue is all the fold needs.  A workgroup claims from its own
+// XCD's queue first (an expert's weight column block then stays in one L2,
+// and a row block's rows serve the XCD's two column blocks back to back),
+// then from the next queues when its own is empty, so every tile is taken
+// however the workgroups spread over the XCDs.  Counters [8, 16) of the
+// counters block (zeroed per call) are the queue heads.
+constexpr int FOLD_QUEUES = 8;
+MOE_DEV bool claim_fold_tile(int32_t* counters, char* smem, int ng, int nbn, int& g, int& nb) {
   int* s = (int*)smem;
-  if (threadIdx.x == 0) *s = atomicAdd(counters + 1, 1);
+  if (threadIdx.x == 0) {
+    const int x = (int)(__builtin_amdgcn_s_getreg((3 << 11) | 20) & (FOLD_QUEUES - 1));  // HW_REG_XCC_ID
+    int qt = -1, tt = 0;
+    for (int j = 0; j < FOLD_QUEUES; ++j) {
+      const int q = (x + j) & (FOLD_QUEUES - 1);
+      const int per = (nbn - q + FOLD_QUEUES - 1) / FOLD_QUEUES;  // column blocks of queue q
+      if (per <= 0) continue;
+      const int t = atomicAdd(counters + 8 + q, 1);
+      if (t < ng * per) {
+        qt = q;
+        tt = t;
+        break;
+      }
+    }
+    s[0] = qt;
+    s[1] = tt;
+  }
   __syncthreads();
-  const int v = *s;
+  const int q = s[0], t = s[1];
   __syncthreads();
-  return v;
+  if (q < 0) return false;
+  const int per = (nbn - q + FOLD_QUEUES - 1) / FOLD_QUEUES;
+  g = t / per;
+  nb = q + FOLD_QUEUES * (t - g * per);
+  return true;
 }
 
 // ===========================================================================
@@ -469,12 +499,12 @@ __global__ __launch_bounds__(C::NT, C::WAVES_PER_EU) void down_combine_kernel(
     const typename C::T* __restrict__ y_swi, const typename C::T* __restrict__ w_down,
     const int32_t* __restrict__ offsets, const int32_t* __restrict__ eti, const int32_t* __restrict__ mb_off,
     const float* __restrict__ w_pos, const int32_t* __restrict__ rank_pos, int32_t* turn, float* accws,
-    typename C::T* __restrict__ out, int32_t* counters, int d, int E, int K, int h, int spin_limit, int grp) {
+    typename C::T* __restrict__ out, int32_t* counters, int d, int E, int K, int h, int spin_limit) {
   __shared__ __attribute__((aligned(16))) char smem[C::LDS_BYTES];
   using TIN = typename C::T;
   const int NB = col_blocks(d, C::BN);
   int g, nb;
-  if (!grouped_tile(claim_ticket(counters, smem), mb_off[E], NB, grp, g, nb)) return;
+  if (!claim_fold_tile(counters, smem, mb_off[E], NB, g, nb)) return;
   const RowTile rt = decode_row_tile<C::BM>(mb_off, offsets, E, g);
   const int wave = threadIdx.x >> 6, wm = wave / C::WN, wn = wave % C::WN;
   const uint32_t ldy = (uint32_t)h * sizeof(TIN);
@@ -507,7 +537,7 @@ static hipError_t down_combine_t(const Shape& s, const void* y_swi, const void* 
   const long long nblk = max_row_blocks(s, B) * col_blocks(s.d, B);
   down_combine_kernel<C><<<dim3((unsigned)nblk), dim3(C::NT), 0, st>>>(
       (const TIN*)y_swi, (const TIN*)w_down, offsets, eti, ws.tile_map(B), ws.w_pos, ws.rank_pos, ws.turn, ws.acc,
-      (TIN*)out, ws.counters, s.d, s.E, s.K, s.h, spin_limit, tile_group_rows(true));
+      (TIN*)out, ws.counters, s.d, s.E, s.K, s.h, spin_limit);
   return hipGetLastError();
 }
 
@@ -1157,13 +1187,12 @@ __global__ __launch_bounds__(C::NT, C::WAVES_PER_EU) void dx_fold_kernel(
     const typename C::T* __restrict__ dh, const typename C::T* __restrict__ w_gate,
     const typename C::T* __restrict__ w_up, const int32_t* __restrict__ offsets, const int32_t* __restrict__ eti,
     const int32_t* __restrict__ mb_off, const int32_t* __restrict__ rank_pos, int32_t* turn, float* accws,
-    typename C::T* __restrict__ dx, int32_t* counters, int d, int E, int K, int h, int hw, int spin_limit,
-    int grp) {
+    typename C::T* __restrict__ dx, int32_t* counters, int d, int E, int K, int h, int hw, int spin_limit) {
   __shared__ __attribute__((aligned(16))) char smem[C::LDS_BYTES];
   using TIN = typename C::T;
   const int NB = col_blocks(d, C::BN);
   int g, nb;
-  if (!grouped_tile(claim_ticket(counters, smem), mb_off[E], NB, grp, g, nb)) return;
+  if (!claim_fold_tile(counters, smem, mb_off[E], NB, g, nb)) return;
   const RowTile rt = decode_row_tile<C::BM>(mb_off, offsets, E, g);
   const int wave = threadIdx.x >> 6, wm = wave / C::WN, wn = wave % C::WN;
   const uint32_t ldh = (uint32_t)hw * sizeof(TIN);
@@ -1208,7 +1237,7 @@ static void launch_dx_fold(const Shape& s, const void* w_gate, const void* w_up,
   const long long nblk = max_row_blocks(s, B) * col_blocks(s.d, B);
   dx_fold_kernel<C><<<dim3((unsigned)nblk), dim3(C::NT), 0, st>>>(
       (const TIN*)ws.dh, (const TIN*)w_gate, (const TIN*)w_up, offsets, eti, ws.tile_map(B), ws.rank_pos, ws.turn,
-      ws.acc, (TIN*)dx, ws.counters, s.d, s.E, s.K, s.h, s.hw(), spin_limit, tile_group_rows(true));
+      ws.acc, (TIN*)dx, ws.counters, s.d, s.E, s.K, s.h, s.hw(), spin_limit);
 }
 
 template <typename TIN>

@@ -14,7 +14,7 @@ constexpr int TILE_S = 128;
 constexpr int TILE_L = 256;
 constexpr int IDX_CHUNK = 256;      // tokens per index-build workgroup
 constexpr int IDX_WAVES = IDX_CHUNK / 64;
-constexpr int N_COUNTERS = 64;      // [0] error flag, [1] fold ticket, [2..] reserved
+constexpr int N_COUNTERS = 64;      // [0] error flag, [8..16) fold queue heads, others reserved
 
 enum { ACT_SWIGLU = 0, ACT_SILU = 1, ACT_RELU = 2 };
 
