@@ -1,27 +1,29 @@
 // Generic grouped-GEMM core for the expert projections (gfx950 MFMA).
 //
-// One workgroup = 256 threads = 4 wave64s computing a BM x BN fp32 tile of
-// C = A * B^T.  Both operands are staged in LDS as [row][k] (k contiguous),
-// 128 bytes of k per row per stage (64 bf16 or 32 fp32), rows padded to 144
-// bytes so that the 16-byte MFMA operand reads of 8 lanes hit distinct banks.
-// The expert GEMMs use 256 x 256 tiles with a 128 x 128 tile per wave: 16
-// MFMA 32x32x16 per 8 operand fragments read from LDS, accumulators in the
-// AGPR half of the register file, one workgroup per CU.
+// One workgroup computes a BM x BN fp32 tile of C = A * B^T with
+// v_mfma_f32_32x32x16_bf16 (32x32x2 in fp32).  Tiles:
+//   128 x 128: four waves of 64 x 64, two workgroups per CU;
+//   256 x 256 (bf16): eight waves of 64 x 128, one workgroup per CU, two waves
+//     per SIMD; in fp32 four waves of 128 x 128.
+// Operands are staged in LDS two k-tiles deep, 128 bytes of k per row per
+// stage, either [row][k] (k contiguous, rows padded to 144 bytes so that the
+// 16-byte operand reads of eight lanes hit distinct banks) or k-major (rows
+// padded by 64 bytes, MFMA operands formed by the LDS transpose read).
 //
-// Pipeline: two LDS stages.  The global loads of k-tile t+1 are issued
-// before the MFMAs of tile t and written to the other LDS stage after them;
-// one barrier per k-tile.  Loaders whose rows come through an index (gathered
-// token rows) fetch the indices of k-tile t+2 at the same time, so the data
-// loads never wait on an index load.
+// Pipeline: two LDS stages, one barrier per k-tile.  Global loads go through
+// registers (two sets on the 128 tile, one on the 256 tile) and are written to
+// the free stage between the MFMA k-steps.  Loaders whose rows come through an
+// index (gathered k-rows of the weight-gradient GEMMs) fetch the indices one
+// stage ahead and form the byte offsets only when they load.
 //
 // Operand sources:
 //   RowLoader  - rows that are contiguous in k in global memory (activations
 //                [rows, k] gathered through an index, weights [out, in]).
 //                8 consecutive threads fetch one row's 128-byte slice.
-//   KRowLoader - sources whose rows are k (activations [rows, m] reduced over
-//                rows, or weights [k, n]).  Each thread fetches four k-rows of
-//                16-byte column chunks and transposes them in registers so
-//                that LDS still holds [m][k].
+//   KLoader    - sources whose rows are k (weights read as [k][n], activations
+//                reduced over rows), staged k-major as they are (bf16).
+//   KRowLoader - the same sources in fp32, transposed in registers so that
+//                LDS holds [m][k].
 #pragma once
 #include <type_traits>
 
