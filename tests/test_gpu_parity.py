@@ -63,6 +63,8 @@ def test_topk_from_logits_bitexact(T, E, K, kind):
 INDEX_CASES = [
     (1, 8, 3, "gaussian"), (255, 8, 2, "gaussian"), (256, 16, 4, "one_expert_set"), (1000, 128, 8, "gaussian"),
     (777, 64, 6, "zero_rows"), (4096, 1024, 32, "gaussian"), (3000, 32, 32, "all_equal"), (2000, 64, 4, "hot_expert"),
+    # expert sets of four and eight 64-expert words, the last one ragged
+    (600, 200, 6, "gaussian"), (900, 300, 5, "zero_rows"),
 ]
 
 
