@@ -1126,7 +1126,7 @@ __global__ __launch_bounds__(C::NT, C::WAVES_PER_EU) void dw_down_kernel(
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
         const int m = mb * C::BM + C::a_row0(wm, fm) + frag_row(r, l);
-        if (m < d) o[(size_t)m * h + n] = acc[fm][fn][r];
+        if (m < d) __builtin_nontemporal_store(acc[fm][fn][r], &o[(size_t)m * h + n]);  // written once, read later
       }
     }
 }
@@ -1175,7 +1175,7 @@ __global__ __launch_bounds__(C::NT, C::WAVES_PER_EU) void dw_gate_up_kernel(
 #pragma unroll
       for (int fn = 0; fn < C::FN; ++fn) {
         const int n = nb * C::BN + C::b_row0(wn, fn) + frag_col(l);
-        if (n < d) o[n] = acc[fm][fn][r];
+        if (n < d) __builtin_nontemporal_store(acc[fm][fn][r], &o[n]);  // written once: keep it out of L2
       }
     }
 }
