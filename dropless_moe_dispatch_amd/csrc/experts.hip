@@ -81,6 +81,14 @@ static bool pick_large(bool auto_choice) {
   const int f = forced_tile();
   return f ? f == TILE_L : auto_choice;
 }
+// The folds can run the 256 x 256 tile (eight waves, parked and folded in two
+// 128-row passes) in bf16 when d is a multiple of 256.  It pays where each
+// tile's reduction (kdim) is long next to its two-pass fold: measured on
+// MI355X, down-combine 1.62 -> 1.35 ms at d = 4096, h = 14336, but 20-45%
+// slower at d = 4096-6144 with a reduction of 1536-4096.
+static bool wide_fold(const Shape& s, int kdim) {
+  return s.bf16 && s.d % TILE_L == 0 && pick_large(s.d >= 4096 && kdim >= 8192);
+}
 
 // ===========================================================================
 // Forward gate/up: M = rows of expert e, N = 128 gate + 128 up columns, K = d.
@@ -360,40 +368,16 @@ MOE_DEV void store2(bf16_t* p, float a, float b) { *(uint32_t*)p = f32_to_bf16(a
 constexpr int FOLD_ROWS_PER_WAVE = 32;
 constexpr int FOLD_BATCH = 16;
 
-template <class C, bool INIT_FIRST>
-MOE_DEV void fold_epilogue(const f32x16_t (&acc)[C::FM][C::FN], const RowTile& rt, int nb, int NB, int wm, int wn,
-                           const int32_t* __restrict__ eti, const float* __restrict__ w_pos,
-                           const int32_t* __restrict__ rank_pos, int K, int d, int32_t* turn,
-                           float* __restrict__ accws, typename C::T* __restrict__ out, int32_t* counters,
-                           int spin_limit, char* smem) {
-  static_assert(C::BM == 128 && C::BN == 128 && C::NT == NTHREADS, "the fold parks a 128 x 128 tile, four waves");
-  static_assert(C::BM * FOLD_LD * 4 + 3 * C::BM * 4 <= C::LDS_BYTES, "parked tile fits the LDS stages");
-  float* s_c = (float*)smem;
-  int* s_t = (int*)(smem + C::BM * FOLD_LD * 4);
-  float* s_w = (float*)(s_t + C::BM);
-  int* s_rank = (int*)(s_w + C::BM);
-  const int tid = threadIdx.x;
+// Fold of one parked 128 x 128 block (rows of 136 floats in s_c, per-row
+// token, weight and rank in s_t, s_w, s_rank) into the 128 accumulator
+// columns of column block nb (of NB), by four waves: wave w (0..3) folds block
+// rows w, w + 4, ..., w + 124.
+template <bool INIT_FIRST, typename TOUT>
+MOE_DEV void fold_rows(const float* s_c, const int* s_t, const float* s_w, const int* s_rank, int rows, int wave,
+                       int nb, int NB, int K, int d, int32_t* turn, float* __restrict__ accws, TOUT* __restrict__ out,
+                       int32_t* counters, int spin_limit) {
   const int l = lane_id();
-  const int rows = rt.r1 - rt.r0;
-  __syncthreads();  // the LDS stages are reused below
-  for (int i = tid; i < C::BM; i += NTHREADS) {  // rows past the tile read token 0 and are never stored
-    const int p = rt.r0 + i;
-    const bool in = i < rows;
-    s_t[i] = in ? eti[p] : 0;
-    s_w[i] = in && w_pos ? w_pos[p] : 1.0f;
-    s_rank[i] = in ? rank_pos[p] : 0;
-  }
-#pragma unroll
-  for (int fm = 0; fm < C::FM; ++fm)
-#pragma unroll
-    for (int fn = 0; fn < C::FN; ++fn)
-#pragma unroll
-      for (int r = 0; r < 16; ++r)
-        s_c[(C::a_row0(wm, fm) + frag_row(r, l)) * FOLD_LD + C::b_row0(wn, fn) + frag_col(l)] = acc[fm][fn][r];
-  __syncthreads();
-
   // wave w folds tile rows w, w + 4, ..., w + 124; lane j < 32 watches row w + 4j
-  const int wave = tid >> 6;
   const int j = l & 31;
   const int my_row = wave + 4 * j;
   const bool mine = l < 32 && my_row < rows;
@@ -401,7 +385,7 @@ MOE_DEV void fold_epilogue(const f32x16_t (&acc)[C::FM][C::FN], const RowTile& r
   const int my_rank = mine ? s_rank[my_row] : 0;
   int32_t* my_turn = turn + (size_t)my_t * NB + nb;
   const int col = 2 * l;  // each lane folds two adjacent columns of a row
-  const size_t cofs = (size_t)nb * C::BN + col;
+  const size_t cofs = (size_t)nb * 128 + col;
   uint64_t pending = __builtin_amdgcn_ballot_w64(mine);
   int spins = 0;
   while (pending) {
@@ -448,6 +432,83 @@ MOE_DEV void fold_epilogue(const f32x16_t (&acc)[C::FM][C::FN], const RowTile& r
     if ((m >> j) & 1 && l < 32)
       __hip_atomic_store(my_turn, my_rank + 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     pending &= ~m;
+  }
+}
+
+template <class C, bool INIT_FIRST>
+MOE_DEV void fold_epilogue(const f32x16_t (&acc)[C::FM][C::FN], const RowTile& rt, int nb, int NB, int wm, int wn,
+                           const int32_t* __restrict__ eti, const float* __restrict__ w_pos,
+                           const int32_t* __restrict__ rank_pos, int K, int d, int32_t* turn,
+                           float* __restrict__ accws, typename C::T* __restrict__ out, int32_t* counters,
+                           int spin_limit, char* smem) {
+  const int tid = threadIdx.x;
+  const int l = lane_id();
+  if constexpr (C::BM == 128) {
+    static_assert(C::BN == 128 && C::NT == NTHREADS, "the fold parks a 128 x 128 tile, four waves");
+    static_assert(C::BM * FOLD_LD * 4 + 3 * C::BM * 4 <= C::LDS_BYTES, "parked tile fits the LDS stages");
+    float* s_c = (float*)smem;
+    int* s_t = (int*)(smem + C::BM * FOLD_LD * 4);
+    float* s_w = (float*)(s_t + C::BM);
+    int* s_rank = (int*)(s_w + C::BM);
+    const int rows = rt.r1 - rt.r0;
+    __syncthreads();  // the LDS stages are reused below
+    for (int i = tid; i < C::BM; i += NTHREADS) {  // rows past the tile read token 0 and are never stored
+      const int p = rt.r0 + i;
+      const bool in = i < rows;
+      s_t[i] = in ? eti[p] : 0;
+      s_w[i] = in && w_pos ? w_pos[p] : 1.0f;
+      s_rank[i] = in ? rank_pos[p] : 0;
+    }
+#pragma unroll
+    for (int fm = 0; fm < C::FM; ++fm)
+#pragma unroll
+      for (int fn = 0; fn < C::FN; ++fn)
+#pragma unroll
+        for (int r = 0; r < 16; ++r)
+          s_c[(C::a_row0(wm, fm) + frag_row(r, l)) * FOLD_LD + C::b_row0(wn, fn) + frag_col(l)] = acc[fm][fn][r];
+    __syncthreads();
+    fold_rows<INIT_FIRST>(s_c, s_t, s_w, s_rank, rows, tid >> 6, nb, NB, K, d, turn, accws, out, counters,
+                          spin_limit);
+  } else {
+    // 256 x 256 tile, eight waves of 64 x 128: two passes of 128 rows.  In
+    // pass hp the waves holding rows hp*128 .. +127 park both 128-column
+    // halves; waves 0-3 then fold half 0 (column block 2 nb of the 128-wide
+    // turn grid) and waves 4-7 half 1 (column block 2 nb + 1).
+    static_assert(C::BM == 256 && C::BN == 256 && C::NT == 512 && C::WM == 4 && C::WN == 2, "eight-wave 256 tile");
+    static_assert(2 * 128 * FOLD_LD * 4 + 3 * 128 * 4 <= C::LDS_BYTES, "two parked halves fit the LDS stages");
+    float* s_c0 = (float*)smem;
+    float* s_c1 = s_c0 + 128 * FOLD_LD;
+    int* s_t = (int*)(s_c1 + 128 * FOLD_LD);
+    float* s_w = (float*)(s_t + 128);
+    int* s_rank = (int*)(s_w + 128);
+    const int wave = tid >> 6, group = wave >> 2;
+#pragma unroll 1
+    for (int hp = 0; hp < 2; ++hp) {
+      const int left = rt.r1 - rt.r0 - hp * 128;
+      const int rows = left < 0 ? 0 : left > 128 ? 128 : left;
+      __syncthreads();  // the LDS stages (pass 0) or the previous half (pass 1) are reused below
+      for (int i = tid; i < 128; i += C::NT) {
+        const int p = rt.r0 + hp * 128 + i;
+        const bool in = i < rows;
+        s_t[i] = in ? eti[p] : 0;
+        s_w[i] = in && w_pos ? w_pos[p] : 1.0f;
+        s_rank[i] = in ? rank_pos[p] : 0;
+      }
+      if ((wm >> 1) == hp) {
+        float* s_c = wn ? s_c1 : s_c0;
+#pragma unroll
+        for (int fm = 0; fm < C::FM; ++fm)
+#pragma unroll
+          for (int fn = 0; fn < C::FN; ++fn)
+#pragma unroll
+            for (int r = 0; r < 16; ++r)
+              s_c[((wm & 1) * 64 + fm * 32 + frag_row(r, l)) * FOLD_LD + fn * 32 + frag_col(l)] = acc[fm][fn][r];
+      }
+      __syncthreads();
+      if (rows > 0)
+        fold_rows<INIT_FIRST>(group ? s_c1 : s_c0, s_t, s_w, s_rank, rows, wave & 3, 2 * nb + group, 2 * NB, K, d,
+                              turn, accws, out, counters, spin_limit);
+    }
   }
 }
 
@@ -533,7 +594,7 @@ __global__ __launch_bounds__(C::NT, C::WAVES_PER_EU) void down_combine_kernel(
 template <typename TIN, int B>
 static hipError_t down_combine_t(const Shape& s, const void* y_swi, const void* w_down, const int32_t* offsets,
                                  const int32_t* eti, void* out, const ExpertWs& ws, int spin_limit, hipStream_t st) {
-  using C = GCfg<TIN, B>;
+  using C = XCfg<TIN, B, false, false, false>;
   const long long nblk = max_row_blocks(s, B) * col_blocks(s.d, B);
   down_combine_kernel<C><<<dim3((unsigned)nblk), dim3(C::NT), 0, st>>>(
       (const TIN*)y_swi, (const TIN*)w_down, offsets, eti, ws.tile_map(B), ws.w_pos, ws.rank_pos, ws.turn, ws.acc,
@@ -544,9 +605,10 @@ static hipError_t down_combine_t(const Shape& s, const void* y_swi, const void* 
 hipError_t launch_down_combine(const Shape& s, const void* y_swi, const void* w_down, const int32_t* offsets,
                                const int32_t* eti, void* out, const ExpertWs& ws, int spin_limit, hipStream_t st) {
   timing_mark(st, "down_combine", true);
-  // the fold parks 128 x 128 tiles (also the faster tile for every measured shape)
-  const hipError_t e = s.bf16 ? down_combine_t<bf16_t, TILE_S>(s, y_swi, w_down, offsets, eti, out, ws, spin_limit, st)
-                              : down_combine_t<float, TILE_S>(s, y_swi, w_down, offsets, eti, out, ws, spin_limit, st);
+  const hipError_t e =
+      !s.bf16        ? down_combine_t<float, TILE_S>(s, y_swi, w_down, offsets, eti, out, ws, spin_limit, st)
+      : wide_fold(s, s.h) ? down_combine_t<bf16_t, TILE_L>(s, y_swi, w_down, offsets, eti, out, ws, spin_limit, st)
+                     : down_combine_t<bf16_t, TILE_S>(s, y_swi, w_down, offsets, eti, out, ws, spin_limit, st);
   timing_mark(st, "down_combine", false);
   return e;
 }
@@ -1310,7 +1372,13 @@ static hipError_t backward_t(const Shape& s, const void* dout, const void* x, co
   timing_mark(st, "dx_fold", true);
   // a plain expert has no up projection: its k never reaches h, so the second
   // weight slot is never read
-  launch_dx_fold<TIN, TILE_S>(s, w_gate, s.gated() ? w_up : w_gate, offsets, eti, dx, ws, spin_limit, st);
+  const void* w2 = s.gated() ? w_up : w_gate;
+  if constexpr (sizeof(TIN) == 2) {
+    if (wide_fold(s, s.hw())) launch_dx_fold<TIN, TILE_L>(s, w_gate, w2, offsets, eti, dx, ws, spin_limit, st);
+    else launch_dx_fold<TIN, TILE_S>(s, w_gate, w2, offsets, eti, dx, ws, spin_limit, st);
+  } else {
+    launch_dx_fold<TIN, TILE_S>(s, w_gate, w2, offsets, eti, dx, ws, spin_limit, st);
+  }
   timing_mark(st, "dx_fold", false);
   return hipGetLastError();
 }
