@@ -97,6 +97,104 @@ def device_info():
     return info
 
 
+NOMINAL_CLOCK_MHZ = 2400.0  # the clock the published MFMA peaks assume
+
+
+class ClockSampler:
+    """GFX clock under the benchmark's load: amdsmi's current-clock query
+    (read-only), sampled every ``period`` seconds from a background thread
+    while the same step runs for ``duration`` seconds after the timed steps;
+    samples from the first ``settle`` seconds are dropped (the library's
+    metrics lag by a fraction of a second).  Under sustained MFMA load the
+    chip runs well below the clock the published peaks assume, so the
+    fractions are also reported against the peak at the measured clock.
+    Everything is None where amdsmi is unavailable."""
+
+    def __init__(self, period=0.05, duration=1.5, settle=0.6):
+        import threading
+        self.period = period
+        self.duration = duration
+        self.settle = settle
+        self.samples = []
+        self.error = None
+        self.handle = None
+        self._stop = threading.Event()
+        self._thread = None
+        try:
+            import amdsmi
+            self.amdsmi = amdsmi
+            amdsmi.amdsmi_init()
+            self.handle = self._pick(amdsmi.amdsmi_get_processor_handles())
+            if self.handle is None:
+                self.error = "no amdsmi handle matches the device"
+        except Exception as e:  # pragma: no cover - depends on the host
+            self.error = repr(e)[:160]
+
+    def _pick(self, handles):
+        if len(handles) == 1:
+            return handles[0]
+        import torch
+        bus = getattr(torch.cuda.get_device_properties(0), "pci_bus_id", None)
+        for h in handles:
+            try:
+                bdf = self.amdsmi.amdsmi_get_gpu_device_bdf(h)  # "dddd:bb:dd.f"
+                if bus is not None and int(bdf.split(":")[1], 16) == int(bus):
+                    return h
+            except Exception:
+                continue
+        return None
+
+    def _read(self):
+        info = self.amdsmi.amdsmi_get_clock_info(self.handle, self.amdsmi.AmdSmiClkType.GFX)
+        return float(info.get("clk", info.get("cur_clk")))
+
+    def _run(self):
+        t0 = time.perf_counter()
+        while not self._stop.is_set():
+            try:
+                v = self._read()
+            except Exception as e:  # pragma: no cover
+                self.error = repr(e)[:160]
+                return
+            if time.perf_counter() - t0 >= self.settle:
+                self.samples.append(v)
+            time.sleep(self.period)
+
+    def measure(self, step):
+        """Run ``step`` back to back for ``duration`` seconds while sampling."""
+        if self.handle is None:
+            return
+        import torch
+        self.start()
+        t0 = time.perf_counter()
+        while time.perf_counter() - t0 < self.duration:
+            for _ in range(4):
+                step()
+            torch.cuda.synchronize()
+        self.stop()
+
+    def start(self):
+        if self.handle is None:
+            return
+        import threading
+        self._thread = threading.Thread(target=self._run, daemon=True)
+        self._thread.start()
+
+    def stop(self):
+        if self._thread is not None:
+            self._stop.set()
+            self._thread.join()
+
+    def summary(self):
+        if not self.samples:
+            return {"gfx_mhz_mean": None, "samples": 0, "source": "amdsmi", "error": self.error}
+        return {"gfx_mhz_mean": round(float(sum(self.samples) / len(self.samples)), 1),
+                "gfx_mhz_min": min(self.samples), "gfx_mhz_max": max(self.samples),
+                "samples": len(self.samples),
+                "source": f"amdsmi current GFX clock every {self.period * 1e3:g} ms while the same step runs "
+                          f"for {self.duration:g} s after the timed steps (first {self.settle:g} s dropped)"}
+
+
 def cpu_baseline(wl, inp, sample_tokens):
     """The CPU oracle (float64 numpy) on the first ``sample_tokens`` tokens of
     the same workload, forward + backward."""
@@ -185,6 +283,13 @@ def main():
     t1 = time.perf_counter()
     recs = B.timing_read() if not args.no_timing else []
     B.timing_enable(False)
+    # the clock the same step runs at (measured after the timed region, not inside it)
+    clock = ClockSampler()
+    if not args.no_timing:
+        clock.measure(step)
+    clk = clock.summary()
+    # peak scale at the measured clock (the published peaks assume 2.4 GHz)
+    cscale = clk["gfx_mhz_mean"] / NOMINAL_CLOCK_MHZ if clk.get("gfx_mhz_mean") else None
     peak_alloc = torch.cuda.max_memory_allocated()
     if args.calib_copy_mb > 0:
         n = args.calib_copy_mb * (1 << 20)
@@ -216,7 +321,9 @@ def main():
         roofline = {"bound": "mfma", "kernel": dom, "achieved": round(ach, 2), "peak": peak, "unit": "TFLOP/s",
                     "frac": round(ach / peak, 4), "traffic": committed_traffic(wl.name, dom),
                     "avg_launch_ms": round(gemms[dom]["avg_ms"], 4), "algorithmic_flop_per_launch": fl,
-                    "src_sha": kernel_source_hash()}
+                    "src_sha": kernel_source_hash(),
+                    "peak_at_measured_clock": round(peak * cscale, 1) if cscale else None,
+                    "frac_at_measured_clock": round(ach / (peak * cscale), 4) if cscale else None}
     peak = PEAK_BF16_TFLOPS if dt == "bf16" else PEAK_F32_MFMA_TFLOPS
     eb = 2 if dt == "bf16" else 4
     kernels = {}
@@ -251,6 +358,9 @@ def main():
                    "combine": args.combine},
         "tflops": round(tflops, 2),
         "mfma_peak_frac": round(tflops / (PEAK_BF16_TFLOPS if dt == "bf16" else PEAK_F32_MFMA_TFLOPS), 4),
+        "mfma_peak_frac_at_measured_clock": (
+            round(tflops / ((PEAK_BF16_TFLOPS if dt == "bf16" else PEAK_F32_MFMA_TFLOPS) * cscale), 4) if cscale else None),
+        "clock": clk,
         "model_flop_per_step": flops,
         "roofline": roofline,
         "cpu_baseline": cpu,
