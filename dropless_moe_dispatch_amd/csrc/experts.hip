@@ -30,6 +30,24 @@ namespace moe {
 // (128 + 8: the rows written by the two half-waves land on disjoint banks).
 constexpr int FOLD_LD = 136;  // floats per parked row (128 + 8: the two half-waves' rows land on disjoint banks)
 
+// Park rows [r0, r0 + PR) of an accumulator tile in LDS, rows of PITCH floats
+// holding tile columns 0 .. BN-1: the waves whose fragments fall in the range
+// write them (fragments are 32-row aligned, so the test is per wave and
+// fragment).  PITCH = BN + 8 puts the two half-waves' rows on disjoint banks.
+template <class C, int PR, int PITCH>
+MOE_DEV void park_rows(const f32x16_t (&acc)[C::FM][C::FN], float* s_c, int r0, int wm, int wn) {
+  const int l = lane_id();
+#pragma unroll
+  for (int fm = 0; fm < C::FM; ++fm) {
+    const int row0 = C::a_row0(wm, fm) - r0;
+    if (row0 < 0 || row0 >= PR) continue;
+#pragma unroll
+    for (int fn = 0; fn < C::FN; ++fn)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) s_c[(row0 + frag_row(r, l)) * PITCH + C::b_row0(wn, fn) + frag_col(l)] = acc[fm][fn][r];
+  }
+}
+
 template <typename T> MOE_DEV float ld_f(const T* p) { return ElemT<T>::load(p); }
 template <typename T> MOE_DEV void st_f(T* p, float v) { ElemT<T>::store(p, v); }
 
@@ -128,58 +146,38 @@ __global__ __launch_bounds__(C::NT, C::WAVES_PER_EU) void gate_up_kernel(
   }
   f32x16_t acc[C::FM][C::FN];
   gemm_mainloop<C>(la, lb, d / C::BK, smem, acc, wm, wn);
-  const int l = lane_id();
-  if constexpr (C::BM == 128 && C::BN == 128 && C::NT == NTHREADS) {
+  {
     // park the tile (gate columns in [0, HB), up columns in [HB, BN)) in LDS,
-    // then write a, b and y as whole 16-byte row chunks
-    static_assert(C::BM * FOLD_LD * 4 <= C::LDS_BYTES, "the parked tile fits the LDS stages");
+    // 128 rows at a time, then write a, b and y as whole 16-byte row chunks
+    constexpr int PR = 128, PITCH = C::BN + 8;
+    static_assert(PR * PITCH * 4 <= C::LDS_BYTES, "the parked rows fit the LDS stages");
     float* s_c = (float*)smem;
-    __syncthreads();
-#pragma unroll
-    for (int fm = 0; fm < C::FM; ++fm)
-#pragma unroll
-      for (int fn = 0; fn < C::FN; ++fn)
-#pragma unroll
-        for (int r = 0; r < 16; ++r)
-          s_c[(C::a_row0(wm, fm) + frag_row(r, l)) * FOLD_LD + C::b_row0(wn, fn) + frag_col(l)] = acc[fm][fn][r];
-    __syncthreads();
     constexpr int VPC = 16 / sizeof(TIN);
     constexpr int CPR = HB / VPC;           // output chunks per row (per half)
-    const int rows = rt.r1 - rt.r0;
-    for (int c = threadIdx.x; c < C::BM * CPR; c += C::NT) {
-      const int row = c / CPR, cc = c % CPR;
-      if (row >= rows) break;
-      const int p = rt.r0 + row;
-      const float* ar = s_c + row * FOLD_LD + cc * VPC;
-      float a[VPC], b[VPC], y[VPC];
+#pragma unroll 1
+    for (int r0 = 0; r0 < C::BM; r0 += PR) {
+      __syncthreads();  // the LDS stages (first pass) or the previous rows are reused
+      park_rows<C, PR, PITCH>(acc, s_c, r0, wm, wn);
+      __syncthreads();
+      const int left = rt.r1 - rt.r0 - r0;
+      const int rows = left < PR ? left : PR;
+      for (int c = threadIdx.x; c < PR * CPR; c += C::NT) {
+        const int row = c / CPR, cc = c % CPR;
+        if (row >= rows) break;
+        const int p = rt.r0 + r0 + row;
+        const float* ar = s_c + row * PITCH + cc * VPC;
+        float a[VPC], b[VPC], y[VPC];
 #pragma unroll
-      for (int v = 0; v < VPC; ++v) {
-        a[v] = ar[v];
-        b[v] = ar[HB + v];
-        y[v] = a[v] * sigmoidf_(a[v]) * b[v];
-      }
-      const int j = j0 + cc * VPC;         // h is a multiple of the half tile: in range
-      st16(h_ab + (size_t)p * 2 * h + j, a);
-      st16(h_ab + (size_t)p * 2 * h + h + j, b);
-      st16(y_swi + (size_t)p * h + j, y);
-    }
-  } else {
-#pragma unroll
-    for (int f = 0; f < HF; ++f) {
-      const int j = j0 + C::b_row0(wn, f) + frag_col(l);
-      if (j >= h) continue;
-#pragma unroll
-      for (int fm = 0; fm < C::FM; ++fm)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const int p = rt.r0 + C::a_row0(wm, fm) + frag_row(r, l);
-          if (p >= rt.r1) continue;
-          const float a = acc[fm][f][r];
-          const float b = acc[fm][f + HF][r];
-          st_f(h_ab + (size_t)p * 2 * h + j, a);
-          st_f(h_ab + (size_t)p * 2 * h + h + j, b);
-          st_f(y_swi + (size_t)p * h + j, a * sigmoidf_(a) * b);
+        for (int v = 0; v < VPC; ++v) {
+          a[v] = ar[v];
+          b[v] = ar[HB + v];
+          y[v] = a[v] * sigmoidf_(a[v]) * b[v];
         }
+        const int j = j0 + cc * VPC;         // h is a multiple of the half tile: in range
+        st16(h_ab + (size_t)p * 2 * h + j, a);
+        st16(h_ab + (size_t)p * 2 * h + h + j, b);
+        st16(y_swi + (size_t)p * h + j, y);
+      }
     }
   }
 }
@@ -231,53 +229,36 @@ __global__ __launch_bounds__(C::NT, C::WAVES_PER_EU) void up_act_kernel(
   }
   f32x16_t acc[C::FM][C::FN];
   gemm_mainloop<C>(la, lb, d / C::BK, smem, acc, wm, wn);
-  const int l = lane_id();
-  if constexpr (C::BM == 128 && C::BN == 128 && C::NT == NTHREADS) {
-    // parked in LDS, written as 16-byte row chunks (as in the gated kernel)
-    static_assert(C::BM * FOLD_LD * 4 <= C::LDS_BYTES, "the parked tile fits the LDS stages");
+  {
+    // parked in LDS 128 rows at a time, written as 16-byte row chunks (as in the gated kernel)
+    constexpr int PR = 128, PITCH = C::BN + 8;
+    static_assert(PR * PITCH * 4 <= C::LDS_BYTES, "the parked rows fit the LDS stages");
     float* s_c = (float*)smem;
-    __syncthreads();
-#pragma unroll
-    for (int fm = 0; fm < C::FM; ++fm)
-#pragma unroll
-      for (int fn = 0; fn < C::FN; ++fn)
-#pragma unroll
-        for (int r = 0; r < 16; ++r)
-          s_c[(C::a_row0(wm, fm) + frag_row(r, l)) * FOLD_LD + C::b_row0(wn, fn) + frag_col(l)] = acc[fm][fn][r];
-    __syncthreads();
     constexpr int VPC = 16 / sizeof(TIN);
     constexpr int CPR = C::BN / VPC;
-    const int rows = rt.r1 - rt.r0;
-    for (int c = threadIdx.x; c < C::BM * CPR; c += C::NT) {
-      const int row = c / CPR, cc = c % CPR;
-      if (row >= rows) break;
-      const int p = rt.r0 + row;
-      const float* ar = s_c + row * FOLD_LD + cc * VPC;
-      float a[VPC], y[VPC];
+#pragma unroll 1
+    for (int r0 = 0; r0 < C::BM; r0 += PR) {
+      __syncthreads();
+      park_rows<C, PR, PITCH>(acc, s_c, r0, wm, wn);
+      __syncthreads();
+      const int left = rt.r1 - rt.r0 - r0;
+      const int rows = left < PR ? left : PR;
+      for (int c = threadIdx.x; c < PR * CPR; c += C::NT) {
+        const int row = c / CPR, cc = c % CPR;
+        if (row >= rows) break;
+        const int j = nb * C::BN + cc * VPC;
+        if (j >= h) continue;  // a 256-column tile can pass h (a multiple of 128): whole chunks out
+        const int p = rt.r0 + r0 + row;
+        const float* ar = s_c + row * PITCH + cc * VPC;
+        float a[VPC], y[VPC];
 #pragma unroll
-      for (int v = 0; v < VPC; ++v) {
-        a[v] = ar[v];
-        y[v] = act_fwd(a[v], act);
-      }
-      const int j = nb * C::BN + cc * VPC;
-      st16(h_a + (size_t)p * h + j, a);
-      st16(y_swi + (size_t)p * h + j, y);
-    }
-  } else {
-#pragma unroll
-    for (int fn = 0; fn < C::FN; ++fn) {
-      const int j = nb * C::BN + C::b_row0(wn, fn) + frag_col(l);
-      if (j >= h) continue;
-#pragma unroll
-      for (int fm = 0; fm < C::FM; ++fm)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const int p = rt.r0 + C::a_row0(wm, fm) + frag_row(r, l);
-          if (p >= rt.r1) continue;
-          const float a = acc[fm][fn][r];
-          st_f(h_a + (size_t)p * h + j, a);
-          st_f(y_swi + (size_t)p * h + j, act_fwd(a, act));
+        for (int v = 0; v < VPC; ++v) {
+          a[v] = ar[v];
+          y[v] = act_fwd(a[v], act);
         }
+        st16(h_a + (size_t)p * h + j, a);
+        st16(y_swi + (size_t)p * h + j, y);
+      }
     }
   }
 }
