@@ -830,143 +830,72 @@ __global__ __launch_bounds__(C::NT, C::WAVES_PER_EU) void dh_kernel(
   f32x16_t acc[C::FM][C::FN];
   gemm_mainloop<C>(la, lb, d / C::BK, smem, acc, wm, wn);
 
-  if constexpr (C::BM == 128 && C::BN == 128 && C::NT == NTHREADS) {
-    // Park dA' (fp32) in LDS; then each thread takes 16-byte row chunks, so a,
-    // b, y are read and dA, dB (and A') written as whole chunks.  dS of a row
-    // is reduced over the row's chunk-owning lanes in a fixed order.
-    static_assert(C::BM * FOLD_LD * 4 <= C::LDS_BYTES, "the parked tile fits the LDS stages");
+  {
+    // Park dA' (fp32) in LDS, 128 rows at a time; then each thread takes
+    // 16-byte row chunks, so a, b, y are read and dA, dB (and A') written as
+    // whole chunks.  dS of a row is reduced over the row's chunk-owning lanes
+    // in a fixed order.
+    constexpr int PR = 128, PITCH = C::BN + 8;
+    static_assert(PR * PITCH * 4 <= C::LDS_BYTES, "the parked rows fit the LDS stages");
     float* s_c = (float*)smem;
-    const int l = lane_id();
-    __syncthreads();
-#pragma unroll
-    for (int fm = 0; fm < C::FM; ++fm)
-#pragma unroll
-      for (int fn = 0; fn < C::FN; ++fn)
-#pragma unroll
-        for (int r = 0; r < 16; ++r)
-          s_c[(C::a_row0(wm, fm) + frag_row(r, l)) * FOLD_LD + C::b_row0(wn, fn) + frag_col(l)] = acc[fm][fn][r];
-    __syncthreads();
     constexpr int VPC = 16 / sizeof(TIN);   // values per chunk
     constexpr int CPR = C::BN / VPC;        // chunks per row
-    constexpr int RPI = C::NT / CPR;        // rows per pass
+    constexpr int RPI = C::NT / CPR;        // rows per pass of the workgroup
+    static_assert(CPR <= 64 && C::NT % CPR == 0, "a row's chunks within one wave");
     const int cc = (int)threadIdx.x % CPR;
-    const int rows = rt.r1 - rt.r0;
-    const int j0 = nb * C::BN + cc * VPC;   // h is a multiple of 128: the chunk is in range
+    const int j0 = nb * C::BN + cc * VPC;
+    const bool jin = j0 < h;                // a 256-column tile can pass h (a multiple of 128)
     const int hw = act == ACT_SWIGLU ? 2 * h : h;
-    for (int rr = (int)threadIdx.x / CPR; rr < C::BM; rr += RPI) {
-      float dsum = 0.0f;
-      if (rr < rows) {
-        const int p = rt.r0 + rr;
-        const float w = w_pos[p];
-        const float* dapr = s_c + rr * FOLD_LD + cc * VPC;
-        float a[VPC], y[VPC], da[VPC];
-        ld16(h_ab + (size_t)p * hw + j0, a);
-        if (act == ACT_SWIGLU) {
-          float b[VPC], db[VPC];
-          ld16(h_ab + (size_t)p * hw + h + j0, b);
-          if constexpr (!HONLY) ld16(y_swi + (size_t)p * h + j0, y);
+#pragma unroll 1
+    for (int r0 = 0; r0 < C::BM; r0 += PR) {
+      __syncthreads();  // the LDS stages (first pass) or the previous rows are reused
+      park_rows<C, PR, PITCH>(acc, s_c, r0, wm, wn);
+      __syncthreads();
+      const int left = rt.r1 - rt.r0 - r0;
+      const int rows = left < PR ? left : PR;
+      for (int rr = (int)threadIdx.x / CPR; rr < PR; rr += RPI) {
+        float dsum = 0.0f;
+        if (rr < rows && jin) {
+          const int p = rt.r0 + r0 + rr;
+          const float w = w_pos[p];
+          const float* dapr = s_c + rr * PITCH + cc * VPC;
+          float a[VPC], y[VPC], da[VPC];
+          ld16(h_ab + (size_t)p * hw + j0, a);
+          if (act == ACT_SWIGLU) {
+            float b[VPC], db[VPC];
+            ld16(h_ab + (size_t)p * hw + h + j0, b);
+            if constexpr (!HONLY) ld16(y_swi + (size_t)p * h + j0, y);
 #pragma unroll
-          for (int v = 0; v < VPC; ++v) {
-            const float sg = sigmoidf_(a[v]);
-            if constexpr (HONLY) y[v] = a[v] * sg * b[v];
-            const float dy = w * dapr[v];
-            da[v] = dy * b[v] * sg * (1.0f + a[v] * (1.0f - sg));
-            db[v] = dy * a[v] * sg;
-            dsum += dapr[v] * y[v];
-          }
-          st16(dh + (size_t)p * hw + h + j0, db);
-        } else {  // plain expert: dA = dy * sigma'(a), from the saved pre-activation
-          if constexpr (!HONLY) ld16(y_swi + (size_t)p * h + j0, y);
+            for (int v = 0; v < VPC; ++v) {
+              const float sg = sigmoidf_(a[v]);
+              if constexpr (HONLY) y[v] = a[v] * sg * b[v];
+              const float dy = w * dapr[v];
+              da[v] = dy * b[v] * sg * (1.0f + a[v] * (1.0f - sg));
+              db[v] = dy * a[v] * sg;
+              dsum += dapr[v] * y[v];
+            }
+            st16(dh + (size_t)p * hw + h + j0, db);
+          } else {  // plain expert: dA = dy * sigma'(a), from the saved pre-activation
+            if constexpr (!HONLY) ld16(y_swi + (size_t)p * h + j0, y);
 #pragma unroll
-          for (int v = 0; v < VPC; ++v) {
-            if constexpr (HONLY) y[v] = act_fwd(a[v], act);
-            da[v] = w * dapr[v] * act_grad(a[v], act);
-            dsum += dapr[v] * y[v];
-          }
-        }
-        st16(dh + (size_t)p * hw + j0, da);
-        if constexpr (HONLY) {
-          float ap[VPC];
-#pragma unroll
-          for (int v = 0; v < VPC; ++v) ap[v] = w * y[v];
-          st16(a_prime + (size_t)p * h + j0, ap);
-        }
-      }
-#pragma unroll
-      for (int off = CPR / 2; off > 0; off >>= 1) dsum += __shfl_xor(dsum, off, CPR);
-      if (cc == 0 && rr < rows) ds_part[(size_t)(rt.r0 + rr) * nbn + nb] = dsum;
-    }
-  } else {
-    const int l = lane_id();
-    float* s_ds = (float*)smem;  // [WN][BM]
-    __syncthreads();
-  #pragma unroll
-    for (int fm = 0; fm < C::FM; ++fm) {
-  #pragma unroll
-      for (int rq = 0; rq < 16; rq += 4) {
-        // four accumulator rows at a time: their a, b, y loads are in flight
-        // together without holding the whole fragment's operands in registers
-        float rs[4];
-  #pragma unroll
-        for (int ri = 0; ri < 4; ++ri) {
-          const int r = rq + ri;
-          const int p = rt.r0 + C::a_row0(wm, fm) + frag_row(r, l);
-          float dsum = 0.0f;
-          if (p < rt.r1) {
-            const float w = w_pos[p];
-  #pragma unroll
-            for (int fn = 0; fn < C::FN; ++fn) {
-              const int j = nb * C::BN + C::b_row0(wn, fn) + frag_col(l);
-              if (j >= h) continue;
-              const float dap = acc[fm][fn][r];
-              const float dy = w * dap;
-              float y;
-              if (act == ACT_SWIGLU) {
-                const float a = ld_f(h_ab + (size_t)p * 2 * h + j);
-                const float b = ld_f(h_ab + (size_t)p * 2 * h + h + j);
-                const float sg = sigmoidf_(a);
-                if constexpr (HONLY) {
-                  y = a * sg * b;
-                  st_f(a_prime + (size_t)p * h + j, w * y);
-                } else {
-                  y = ld_f(y_swi + (size_t)p * h + j);
-                }
-                st_f(dh + (size_t)p * 2 * h + j, dy * b * sg * (1.0f + a * (1.0f - sg)));
-                st_f(dh + (size_t)p * 2 * h + h + j, dy * a * sg);
-              } else {  // plain expert: dA = dy * sigma'(a), a recomputed from the saved pre-activation
-                const float a = ld_f(h_ab + (size_t)p * h + j);
-                if constexpr (HONLY) {
-                  y = act_fwd(a, act);
-                  st_f(a_prime + (size_t)p * h + j, w * y);
-                } else {
-                  y = ld_f(y_swi + (size_t)p * h + j);
-                }
-                st_f(dh + (size_t)p * h + j, dy * act_grad(a, act));
-              }
-              dsum += dap * y;
+            for (int v = 0; v < VPC; ++v) {
+              if constexpr (HONLY) y[v] = act_fwd(a[v], act);
+              da[v] = w * dapr[v] * act_grad(a[v], act);
+              dsum += dapr[v] * y[v];
             }
           }
-          // reduce the row's partial over the 32 columns of the half-wave, fixed order
-          dsum += __shfl_xor(dsum, 16, 32);
-          dsum += __shfl_xor(dsum, 8, 32);
-          dsum += __shfl_xor(dsum, 4, 32);
-          dsum += __shfl_xor(dsum, 2, 32);
-          dsum += __shfl_xor(dsum, 1, 32);
-          rs[ri] = dsum;
+          st16(dh + (size_t)p * hw + j0, da);
+          if constexpr (HONLY) {
+            float ap[VPC];
+#pragma unroll
+            for (int v = 0; v < VPC; ++v) ap[v] = w * y[v];
+            st16(a_prime + (size_t)p * h + j0, ap);
+          }
         }
-        if ((l & 31) == 0) {
-  #pragma unroll
-          for (int ri = 0; ri < 4; ++ri) s_ds[wn * C::BM + C::a_row0(wm, fm) + frag_row(rq + ri, l)] = rs[ri];
-        }
-        __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+        for (int off = CPR / 2; off > 0; off >>= 1) dsum += __shfl_xor(dsum, off, CPR);
+        if (cc == 0 && rr < rows) ds_part[(size_t)(rt.r0 + r0 + rr) * nbn + nb] = dsum;
       }
-    }
-    __syncthreads();
-    for (int i = threadIdx.x; i < rt.r1 - rt.r0; i += C::NT) {
-      float v = 0.0f;
-  #pragma unroll
-      for (int w = 0; w < C::WN; ++w) v += s_ds[w * C::BM + i];
-      ds_part[(size_t)(rt.r0 + i) * nbn + nb] = v;
     }
   }
 }
@@ -1290,7 +1219,9 @@ static hipError_t backward_t(const Shape& s, const void* dout, const void* x, co
                              const void* y_swi, void* dx, float* dwg, float* dw_gate, float* dw_up,
                              float* dw_down, float* ds, const ExpertWs& ws, int spin_limit, hipStream_t st) {
   using CL = KCfg<TIN, TILE_L, true, true>;
-  // the large-tile dH epilogue spills; the small tile is used for every shape
+  // dH on the 256 x 256 tile measured no faster on MI355X (4.23 vs 4.21 ms at
+  // d = 4096, h = 14336; 0.88 vs 0.75 ms at d = 2048, h = 1536): the small
+  // tile is used unless the large one is forced.
   const bool dh_big = forced_tile() == TILE_L;
   const int nbh = col_blocks(s.h, dh_big ? TILE_L : TILE_S);
   hipError_t err;
