@@ -75,6 +75,7 @@ def kernel_bytes(name, T, d, E, K, h, eb):
     return {
         "router_logits": eb * T * d + eb * E * d + 4 * T * E,
         "topk": 4 * T * E + 8 * A,
+        "route": eb * T * d + eb * E * d + 4 * T * E + 8 * A,
         "index": 4 * A + 8 * A + 8 * E * ((T + 63) // 64),
         "router_bwd": 4 * T * d + eb * E * d + 16 * A,
         "dwg": eb * A * d + 4 * E * d + 8 * A,

@@ -141,6 +141,7 @@ int moe_route_topk(const moe_shape* s, const void* x, const void* wg, const floa
     OPT(x);
     if (!aligned16(x)) return MOE_ERR_INVALID_ARG;
     OPT(bias);
+    if (route_fused_applies(sh)) return hip_status(launch_route_fused(sh, x, wg, bias, logits, topk_ids, topk_w, st));
     rc = hip_status(launch_router_logits(sh, x, wg, bias, logits, st));
     if (rc) return rc;
   }

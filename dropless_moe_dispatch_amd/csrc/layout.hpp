@@ -144,6 +144,9 @@ inline ExpertWs expert_ws(const Shape& s, int which, void* p) {
 hipError_t launch_router_logits(const Shape& s, const void* x, const void* wg, const float* bias, float* logits,
                                 hipStream_t st);
 hipError_t launch_topk(const Shape& s, const float* logits, int32_t* ids, float* w, hipStream_t st);
+bool route_fused_applies(const Shape& s);
+hipError_t launch_route_fused(const Shape& s, const void* x, const void* wg, const float* bias, float* logits,
+                              int32_t* ids, float* w, hipStream_t st);
 hipError_t launch_build_index(const Shape& s, const int32_t* ids, int32_t* offsets, int32_t* eti, int32_t* tim,
                               const IndexWs& ws, hipStream_t st);
 hipError_t launch_build_index_dense(const Shape& s, const int32_t* ids, int32_t* offsets, int32_t* eti, int32_t* tim,

@@ -117,7 +117,10 @@ size_t moe_workspace_bytes(const moe_shape* s, int which);
  *     token_expert_indices structure of the index.
  *   topk_w[T,K] (fp32, output): softmax of the chosen K logits, i.e. the
  *     softmax probabilities renormalised over the chosen experts.
- *   bias[E] (fp32, nullable): fixed per-expert logit offset. */
+ *   bias[E] (fp32, nullable): fixed per-expert logit offset.
+ * The selection and the weights are computed from the fp32 logits as written,
+ * so routing from x and routing from the logits it wrote give the same ids
+ * and weights bit for bit. */
 int moe_route_topk(const moe_shape* s, const void* x, const void* wg, const float* bias, float* logits,
                    int32_t* topk_ids, float* topk_w, void* stream);
 

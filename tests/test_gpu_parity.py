@@ -93,8 +93,17 @@ def test_index_bitexact(T, E, K, kind, backend):
 # ---------------------------------------------------------------------------
 # a1: router logits
 # ---------------------------------------------------------------------------
-@pytest.mark.parametrize("T,d,E,dtype", [(300, 256, 8, "bf16"), (1000, 384, 128, "bf16"), (129, 128, 64, "f32"),
-                                         (77, 512, 200, "bf16")])
+ROUTER_CASES = [
+    (300, 256, 8, "bf16"), (1000, 384, 128, "bf16"), (129, 128, 64, "f32"), (77, 512, 200, "bf16"),
+    # the fused router (under 16384 tokens, d a multiple of 256) with 32, 64
+    # and 96-128 expert columns, ragged token tails and a ring longer than the
+    # slice; and the separate logits GEMM + top-K just past its bounds
+    (3000, 1024, 64, "bf16"), (16351, 256, 100, "bf16"), (40, 256, 33, "bf16"), (100, 2048, 128, "bf16"),
+    (16400, 256, 100, "bf16"), (40, 128, 33, "bf16"), (17000, 512, 4, "bf16"),
+]
+
+
+@pytest.mark.parametrize("T,d,E,dtype", ROUTER_CASES)
 def test_router_logits(T, d, E, dtype):
     _say("router_logits", T, d, E, dtype)
     wl = synth.small_workload(T, d, E, 2, 128, dtype=dtype, seed=T, zipf_s=1.2)
@@ -108,6 +117,30 @@ def test_router_logits(T, d, E, dtype):
     z = O.router_logits(inp["x"], inp["wg"], inp["bias"])
     err = np.abs(to_np(buf.logits) - z).max()
     assert err < 2e-5 * np.sqrt(d / 128), err
+
+
+@pytest.mark.parametrize("T,d,E,dtype", ROUTER_CASES)
+def test_route_from_x_selects_on_its_logits(T, d, E, dtype):
+    """Routing from x (the fused router where it applies) gives the ids and
+    weights that top-K from the logits it wrote gives, bit for bit, and the
+    oracle's top-K of those logits (the selection is taken on the same fp32
+    values on both sides)."""
+    _say("route_from_x", T, d, E, dtype)
+    K = min(4, E)
+    wl = synth.small_workload(T, d, E, K, 128, dtype=dtype, seed=T + 7, zipf_s=1.2)
+    inp = synth.make_inputs(wl, tensors=("x", "wg"))
+    buf = Lyr.MoEBuffers(T, d, E, K, 128, dtype, backward=False)
+    Lyr.route(buf, Lyr.to_device(inp["x"], dtype), Lyr.to_device(inp["wg"], dtype),
+              torch.from_numpy(inp["bias"]).cuda())
+    ref = Lyr.MoEBuffers(T, d, E, K, 128, dtype, backward=False)
+    ref.logits.copy_(buf.logits)
+    Lyr.route(ref, None, None, None, logits_in=True)
+    torch.cuda.synchronize()
+    assert torch.equal(buf.topk_ids, ref.topk_ids)
+    assert torch.equal(buf.topk_w, ref.topk_w)
+    ids_ref, w_ref = O.route(to_np(buf.logits).astype(np.float64), K)
+    assert np.array_equal(to_np(buf.topk_ids), ids_ref)
+    np.testing.assert_allclose(to_np(buf.topk_w), w_ref, rtol=2e-6, atol=1e-7)
 
 
 # ---------------------------------------------------------------------------
