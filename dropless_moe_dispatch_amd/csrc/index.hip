@@ -14,11 +14,13 @@
 //      mask per (wave, expert) -- bit i set iff token i of the wave chose the
 //      expert.  Each mask has a single writer.
 //   2. expert lengths: popcounts of the masks give the per-(expert, chunk)
-//      counts; one workgroup scans the [E][chunks] count matrix (expert-major)
-//      into absolute bases, which also yields expert_token_offsets.
-//   3. conflict-free scatter: a token's position is its (expert, chunk) base
-//      plus the popcount of the lower tokens' bits in the same masks; every
-//      destination is written exactly once.
+//      counts; one wave per expert scans its row of the [E][chunks] count
+//      matrix into bases inside the expert and leaves the expert's length.
+//   3. conflict-free scatter: every workgroup scans the E lengths in LDS
+//      (the expert offsets, which workgroup 0 also writes out as
+//      expert_token_offsets); a token's position is its expert's offset plus
+//      its (expert, chunk) base plus the popcount of the lower tokens' bits in
+//      the same masks; every destination is written exactly once.
 #include "common.hpp"
 #include "layout.hpp"
 
@@ -75,52 +77,80 @@ __global__ __launch_bounds__(256) void index_hist_kernel(const int32_t* __restri
   }
 }
 
-// Exclusive scan of the [E][nchunks] count matrix in expert-major order by
-// one 1024-thread workgroup: each thread sums a contiguous segment, the
-// segment sums are scanned with wave shuffles (then across the 16 waves), and
-// each thread writes its segment's bases.  All sums are below T*K < 2^31.
-__global__ __launch_bounds__(1024) void index_scan_kernel(int32_t* __restrict__ base, int32_t* __restrict__ offsets,
-                                                          int E, int nchunks) {
-  const long long n = (long long)E * nchunks;
-  const int tid = threadIdx.x, l = lane_id(), wave = tid >> 6;
-  const long long per = (n + 1023) / 1024;
-  const long long s0 = tid * per < n ? tid * per : n;
-  const long long s1 = s0 + per < n ? s0 + per : n;
-  int sum = 0;
-  for (long long i = s0; i < s1; ++i) sum += base[i];
-  int incl = sum;  // inclusive scan inside the wave
+// Step 2: one wave per expert e scans row e of the [E][nchunks] count matrix,
+// 64 chunks at a time (coalesced), replacing each count by the number of the
+// expert's tokens in lower chunks; tot[e] gets the row's total.
+__global__ __launch_bounds__(256) void index_rowscan_kernel(int32_t* __restrict__ base, int32_t* __restrict__ tot,
+                                                            int E, int nchunks) {
+  const int e = blockIdx.x * 4 + (int)(threadIdx.x >> 6);
+  if (e >= E) return;  // whole waves
+  const int l = lane_id();
+  int32_t* row = base + (size_t)e * nchunks;
+  int carry = 0;
+  for (int c0 = 0; c0 < nchunks; c0 += 64) {
+    const int c = c0 + l;
+    const int v = c < nchunks ? row[c] : 0;
+    int incl = v;
 #pragma unroll
-  for (int off = 1; off < 64; off <<= 1) {
-    const int v = __shfl_up(incl, off, 64);
-    if (l >= off) incl += v;
-  }
-  __shared__ int wsum[16];
-  if (l == 63) wsum[wave] = incl;
-  __syncthreads();
-  int before = 0;
-  for (int w = 0; w < wave; ++w) before += wsum[w];
-  int run = before + incl - sum;  // exclusive prefix of this segment
-  if (s0 < s1) {
-    int e = (int)(s0 / nchunks), c = (int)(s0 % nchunks);
-    for (long long i = s0; i < s1; ++i) {
-      const int v = base[i];
-      base[i] = run;
-      if (c == 0) offsets[e] = run;
-      run += v;
-      if (++c == nchunks) { c = 0; ++e; }
+    for (int off = 1; off < 64; off <<= 1) {
+      const int u = __shfl_up(incl, off, 64);
+      if (l >= off) incl += u;
     }
+    if (c < nchunks) row[c] = carry + incl - v;
+    carry += __shfl(incl, 63, 64);
   }
-  if (tid == 1023) offsets[E] = run;
+  if (l == 0) tot[e] = carry;
 }
 
+// Step 3.  The expert offsets (exclusive scan of tot, E <= 1024) are formed
+// in LDS by every workgroup: each thread sums IDX_SCAN_PER consecutive
+// experts, the 256 sums are scanned (wave shuffles, then the four wave
+// totals), and each thread writes its experts' offsets.  All sums are below
+// T*K < 2^31.
+constexpr int IDX_SCAN_PER = 4;  // experts per thread: 256 * 4 = 1024 = the largest E
 __global__ __launch_bounds__(256) void index_scatter_kernel(const int32_t* __restrict__ ids,
                                                             const uint64_t* __restrict__ masks,
                                                             const int32_t* __restrict__ base,
+                                                            const int32_t* __restrict__ tot,
                                                             int32_t* __restrict__ eti, int32_t* __restrict__ tim,
-                                                            int T, int E, int K, int nchunks) {
+                                                            int32_t* __restrict__ offsets, int T, int E, int K,
+                                                            int nchunks) {
+  __shared__ int32_t s_off[256 * IDX_SCAN_PER + 1];
+  __shared__ int32_t s_wsum[IDX_WAVES];
   const int chunk = blockIdx.x;
   const int wave = threadIdx.x >> 6;
   const int l = lane_id();
+  {
+    const int e0 = (int)threadIdx.x * IDX_SCAN_PER;
+    int v[IDX_SCAN_PER];
+    int sum = 0;
+#pragma unroll
+    for (int i = 0; i < IDX_SCAN_PER; ++i) {
+      v[i] = e0 + i < E ? tot[e0 + i] : 0;
+      sum += v[i];
+    }
+    int incl = sum;
+#pragma unroll
+    for (int off = 1; off < 64; off <<= 1) {
+      const int u = __shfl_up(incl, off, 64);
+      if (l >= off) incl += u;
+    }
+    if (l == 63) s_wsum[wave] = incl;
+    __syncthreads();
+    int run = incl - sum;
+    for (int w = 0; w < wave; ++w) run += s_wsum[w];
+#pragma unroll
+    for (int i = 0; i < IDX_SCAN_PER; ++i) {
+      s_off[e0 + i] = run;
+      run += v[i];
+    }
+    if (threadIdx.x == 255) s_off[256 * IDX_SCAN_PER] = run;
+    __syncthreads();
+    if (chunk == 0) {
+      for (int e = threadIdx.x; e < E; e += 256) offsets[e] = s_off[e];
+      if (threadIdx.x == 0) offsets[E] = s_off[256 * IDX_SCAN_PER];  // = T*K: experts past E add nothing
+    }
+  }
   const int t = chunk * IDX_CHUNK + (int)threadIdx.x;
   if (t >= T) return;
   const uint64_t lower = (l == 0) ? 0ull : (~0ull >> (64 - l));
@@ -129,7 +159,7 @@ __global__ __launch_bounds__(256) void index_scatter_kernel(const int32_t* __res
     const int e = ids[(size_t)t * K + k];
     int r = __popcll(mchunk[(size_t)wave * E + e] & lower);
     for (int w = 0; w < wave; ++w) r += __popcll(mchunk[(size_t)w * E + e]);
-    const int pos = base[(size_t)e * nchunks + chunk] + r;
+    const int pos = s_off[e] + base[(size_t)e * nchunks + chunk] + r;
     eti[pos] = t;
     tim[(size_t)t * K + k] = pos;
   }
@@ -146,9 +176,9 @@ hipError_t launch_build_index(const Shape& s, const int32_t* ids, int32_t* offse
     else if (s.E <= 512) index_hist_kernel<8><<<g, b, 0, st>>>(ids, ws.masks, ws.base, s.T, s.E, s.K, ws.nchunks);
     else index_hist_kernel<16><<<g, b, 0, st>>>(ids, ws.masks, ws.base, s.T, s.E, s.K, ws.nchunks);
   }
-  index_scan_kernel<<<dim3(1), dim3(1024), 0, st>>>(ws.base, offsets, s.E, ws.nchunks);
-  index_scatter_kernel<<<dim3(ws.nchunks), dim3(256), 0, st>>>(ids, ws.masks, ws.base, eti, tim, s.T, s.E, s.K,
-                                                               ws.nchunks);
+  index_rowscan_kernel<<<dim3((s.E + 3) / 4), dim3(256), 0, st>>>(ws.base, ws.tot, s.E, ws.nchunks);
+  index_scatter_kernel<<<dim3(ws.nchunks), dim3(256), 0, st>>>(ids, ws.masks, ws.base, ws.tot, eti, tim, offsets,
+                                                               s.T, s.E, s.K, ws.nchunks);
   hipError_t e = hipGetLastError();
   timing_mark(st, "index", false);
   return e;

@@ -39,7 +39,8 @@ inline long long max_row_blocks(const Shape& s, int bm) {
 // ---- index workspace ------------------------------------------------------
 struct IndexWs {
   uint64_t* masks;     // [nchunks][IDX_WAVES][E] token bitmaps per (chunk, wave, expert)
-  int32_t* base;       // [E][nchunks] counts, scanned in place to absolute bases
+  int32_t* base;       // [E][nchunks] counts, scanned in place to bases inside each expert
+  int32_t* tot;        // [E] tokens per expert
   size_t bytes;
   int nchunks;
 };
@@ -51,6 +52,8 @@ inline IndexWs index_ws(const Shape& s, void* p) {
   off = align_up(off + (size_t)w.nchunks * IDX_WAVES * s.E * 8, 256);
   w.base = (int32_t*)((char*)p + off);
   off = align_up(off + (size_t)s.E * w.nchunks * 4, 256);
+  w.tot = (int32_t*)((char*)p + off);
+  off = align_up(off + (size_t)s.E * 4, 256);
   w.bytes = off;
   return w;
 }

@@ -127,7 +127,10 @@ int moe_route_topk(const moe_shape* s, const void* x, const void* wg, const floa
 /* Routing index by counting sort, without a global sort or atomics
  * (MoEBlaze analysis page, "Dispatch Data Structures" and "Dispatch Data
  * Structure Construction"; MoEBlaze reading notes sec. 4.1, Figure 2).
- *   topk_ids[T*K]: input (token_expert_indices).
+ *   topk_ids[T*K]: input (token_expert_indices).  Every entry must lie in
+ *     [0, E) and a token's K entries must be distinct, as moe_route_topk
+ *     writes them; the ids live on the device and are not checked, and other
+ *     values give undefined results.
  *   offsets[E+1] (output): expert_token_offsets, offsets[E] = T*K.
  *   expert_token_indices[T*K] (output): token ids grouped by ascending
  *     expert, ascending token id within an expert.
