@@ -73,7 +73,7 @@ def kernel_bytes(name, T, d, E, K, h, eb):
     """Algorithmic HBM bytes of the memory-bound stages (operands once, outputs once)."""
     A = T * K
     return {
-        "router_logits": eb * T * d + eb * E * d + 4 * T * E,
+        "router_logits": eb * T * d + eb * E * d + 4 * T * E + (8 * A if E <= 128 else 0),
         "topk": 4 * T * E + 8 * A,
         "route": eb * T * d + eb * E * d + 4 * T * E + 8 * A,
         "index": 4 * A + 8 * A + 8 * E * ((T + 63) // 64),

@@ -142,8 +142,8 @@ int moe_route_topk(const moe_shape* s, const void* x, const void* wg, const floa
     if (!aligned16(x)) return MOE_ERR_INVALID_ARG;
     OPT(bias);
     if (route_fused_applies(sh)) return hip_status(launch_route_fused(sh, x, wg, bias, logits, topk_ids, topk_w, st));
-    rc = hip_status(launch_router_logits(sh, x, wg, bias, logits, st));
-    if (rc) return rc;
+    rc = hip_status(launch_router_logits(sh, x, wg, bias, logits, topk_ids, topk_w, st));
+    if (rc || router_logits_has_topk(sh)) return rc;
   }
   return hip_status(launch_topk(sh, logits, topk_ids, topk_w, st));
 }

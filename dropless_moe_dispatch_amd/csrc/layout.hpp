@@ -145,7 +145,8 @@ inline ExpertWs expert_ws(const Shape& s, int which, void* p) {
 
 // ---- kernel launchers (defined in the kernel translation units) -----------
 hipError_t launch_router_logits(const Shape& s, const void* x, const void* wg, const float* bias, float* logits,
-                                hipStream_t st);
+                                int32_t* ids, float* w, hipStream_t st);
+bool router_logits_has_topk(const Shape& s);  // the logits kernel also writes ids and w
 hipError_t launch_topk(const Shape& s, const float* logits, int32_t* ids, float* w, hipStream_t st);
 bool route_fused_applies(const Shape& s);
 hipError_t launch_route_fused(const Shape& s, const void* x, const void* wg, const float* bias, float* logits,

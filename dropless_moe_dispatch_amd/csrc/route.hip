@@ -14,87 +14,6 @@
 namespace moe {
 
 // ---------------------------------------------------------------------------
-// logits GEMM: M = T tokens, N = E experts, K = d.
-// ---------------------------------------------------------------------------
-template <class C>
-__global__ __launch_bounds__(NTHREADS, 2) void router_logits_kernel(const typename C::T* __restrict__ x,
-                                                                    const typename C::T* __restrict__ wg,
-                                                                    const float* __restrict__ bias,
-                                                                    float* __restrict__ logits, int T, int d, int E) {
-  __shared__ __attribute__((aligned(16))) char smem[C::LDS_BYTES];
-  using TIN = typename C::T;
-  const int m0 = blockIdx.x * C::BM;
-  const int n0 = blockIdx.y * C::BN;
-  const int wave = threadIdx.x >> 6, wm = wave / C::WN, wn = wave % C::WN;
-  const uint32_t ld = (uint32_t)d * sizeof(TIN);
-  RowLoader<C::BM> la;
-  RowLoader<C::BN> lb;
-  la.rs[0] = make_rsrc(x + (size_t)m0 * d, (size_t)(T - m0) * ld);
-#pragma unroll
-  for (int i = 0; i < RowLoader<C::BM>::CPT; ++i) {
-    const int r = RowLoader<C::BM>::my_row(i);
-    la.roff[i] = m0 + r < T ? (uint32_t)r * ld : OOB_OFF;
-  }
-  lb.rs[0] = make_rsrc(wg, (size_t)E * ld);
-#pragma unroll
-  for (int i = 0; i < RowLoader<C::BN>::CPT; ++i) {
-    const int e = n0 + RowLoader<C::BN>::my_row(i);
-    lb.roff[i] = e < E ? (uint32_t)e * ld : OOB_OFF;
-  }
-  f32x16_t acc[C::FM][C::FN];
-  gemm_mainloop<C>(la, lb, d / C::BK, smem, acc, wm, wn);
-  const int l = lane_id();
-#pragma unroll
-  for (int fn = 0; fn < C::FN; ++fn) {
-    const int e = n0 + C::b_row0(wn, fn) + frag_col(l);
-    if (e >= E) continue;
-    const float b = bias ? bias[e] : 0.0f;
-#pragma unroll
-    for (int fm = 0; fm < C::FM; ++fm)
-#pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const int t = m0 + C::a_row0(wm, fm) + frag_row(r, l);
-        if (t < T) logits[(size_t)t * E + e] = acc[fm][fn][r] + b;
-      }
-  }
-}
-
-template <typename TIN>
-static hipError_t router_logits_t(const Shape& s, const void* x, const void* wg, const float* bias, float* logits,
-                                  hipStream_t st) {
-  const dim3 blk(NTHREADS);
-  if (s.E <= 32) {
-    using C = Cfg<TIN, 128, 32, 4, 1>;
-    const dim3 grd((s.T + C::BM - 1) / C::BM, (s.E + C::BN - 1) / C::BN);
-    router_logits_kernel<C><<<grd, blk, 0, st>>>((const TIN*)x, (const TIN*)wg, bias, logits, s.T, s.d, s.E);
-  } else if (s.E <= 64) {
-    // 64-token tiles: a grid of T/64 workgroups fills the chip from a few thousand tokens
-    using C = Cfg<TIN, 64, 64, 2, 2>;
-    const dim3 grd((s.T + C::BM - 1) / C::BM, (s.E + C::BN - 1) / C::BN);
-    router_logits_kernel<C><<<grd, blk, 0, st>>>((const TIN*)x, (const TIN*)wg, bias, logits, s.T, s.d, s.E);
-  } else if (s.E <= 128) {
-    // one 128-expert column block: 32-token tiles keep enough workgroups in flight
-    using C = Cfg<TIN, 32, 128, 1, 4>;
-    const dim3 grd((s.T + C::BM - 1) / C::BM, 1);
-    router_logits_kernel<C><<<grd, blk, 0, st>>>((const TIN*)x, (const TIN*)wg, bias, logits, s.T, s.d, s.E);
-  } else {
-    using C = Cfg<TIN, 128, 128, 2, 2>;
-    const dim3 grd((s.T + C::BM - 1) / C::BM, (s.E + C::BN - 1) / C::BN);
-    router_logits_kernel<C><<<grd, blk, 0, st>>>((const TIN*)x, (const TIN*)wg, bias, logits, s.T, s.d, s.E);
-  }
-  return hipGetLastError();
-}
-
-hipError_t launch_router_logits(const Shape& s, const void* x, const void* wg, const float* bias, float* logits,
-                                hipStream_t st) {
-  timing_mark(st, "router_logits", true);
-  hipError_t e = s.bf16 ? router_logits_t<bf16_t>(s, x, wg, bias, logits, st)
-                        : router_logits_t<float>(s, x, wg, bias, logits, st);
-  timing_mark(st, "router_logits", false);
-  return e;
-}
-
-// ---------------------------------------------------------------------------
 // top-K of one token's logits, by a group of G lanes (a power of two, 1..64,
 // aligned inside a wave); lane gl holds the V logits of experts gl*V ..
 // gl*V+V-1 in z.  K rounds of a group arg-max (larger value wins, ties to the
@@ -159,6 +78,114 @@ MOE_DEV void topk_group(const float (&z)[V], int e0, int E, int K, int gl, bool 
       }
     }
   }
+}
+
+// ---------------------------------------------------------------------------
+// logits GEMM: M = T tokens, N = E experts, K = d.  With TOPK the tile holds
+// every expert (E <= BN): the logits are parked in LDS after they are
+// written, and the NTHREADS / BM lanes of each token run topk_group on them.
+// ---------------------------------------------------------------------------
+template <class C, bool TOPK>
+__global__ __launch_bounds__(NTHREADS, 2) void router_logits_kernel(const typename C::T* __restrict__ x,
+                                                                    const typename C::T* __restrict__ wg,
+                                                                    const float* __restrict__ bias,
+                                                                    float* __restrict__ logits,
+                                                                    int32_t* __restrict__ ids,
+                                                                    float* __restrict__ wts, int T, int d, int E,
+                                                                    int K) {
+  __shared__ __attribute__((aligned(16))) char smem[C::LDS_BYTES];
+  using TIN = typename C::T;
+  const int m0 = blockIdx.x * C::BM;
+  const int n0 = blockIdx.y * C::BN;
+  const int wave = threadIdx.x >> 6, wm = wave / C::WN, wn = wave % C::WN;
+  const uint32_t ld = (uint32_t)d * sizeof(TIN);
+  RowLoader<C::BM> la;
+  RowLoader<C::BN> lb;
+  la.rs[0] = make_rsrc(x + (size_t)m0 * d, (size_t)(T - m0) * ld);
+#pragma unroll
+  for (int i = 0; i < RowLoader<C::BM>::CPT; ++i) {
+    const int r = RowLoader<C::BM>::my_row(i);
+    la.roff[i] = m0 + r < T ? (uint32_t)r * ld : OOB_OFF;
+  }
+  lb.rs[0] = make_rsrc(wg, (size_t)E * ld);
+#pragma unroll
+  for (int i = 0; i < RowLoader<C::BN>::CPT; ++i) {
+    const int e = n0 + RowLoader<C::BN>::my_row(i);
+    lb.roff[i] = e < E ? (uint32_t)e * ld : OOB_OFF;
+  }
+  f32x16_t acc[C::FM][C::FN];
+  gemm_mainloop<C>(la, lb, d / C::BK, smem, acc, wm, wn);
+  const int l = lane_id();
+  constexpr int PITCH = C::BN + 4;  // floats per parked row
+  float* s_z = (float*)smem;
+  if constexpr (TOPK) {
+    static_assert(C::BM * PITCH * 4 <= C::LDS_BYTES, "parked logits fit the LDS stages");
+    __syncthreads();  // the LDS stages are reused below
+  }
+#pragma unroll
+  for (int fn = 0; fn < C::FN; ++fn) {
+    const int e = n0 + C::b_row0(wn, fn) + frag_col(l);
+    const float b = e < E && bias ? bias[e] : 0.0f;
+#pragma unroll
+    for (int fm = 0; fm < C::FM; ++fm)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int tr = C::a_row0(wm, fm) + frag_row(r, l);
+        const int t = m0 + tr;
+        const float z = acc[fm][fn][r] + b;
+        if (t < T && e < E) logits[(size_t)t * E + e] = z;
+        if constexpr (TOPK) s_z[tr * PITCH + e] = z;
+      }
+  }
+  if constexpr (TOPK) {
+    constexpr int G = NTHREADS / C::BM;  // lanes per token
+    constexpr int V = C::BN / G;         // logits per lane
+    __syncthreads();
+    const int g = (int)threadIdx.x / G, gl = (int)threadIdx.x % G;
+    const int t = m0 + g;
+    const int e0 = gl * V;
+    float z[V];
+#pragma unroll
+    for (int v = 0; v < V; ++v) z[v] = e0 + v < E ? s_z[g * PITCH + e0 + v] : -INFINITY;
+    const bool valid = t < T;
+    const size_t o = (size_t)(valid ? t : 0) * K;
+    topk_group<G, V>(z, e0, E, K, gl, valid, ids + o, wts + o);
+  }
+}
+
+// E <= 128 takes one column block, so the top-K runs in the epilogue (TOPK)
+// and ids, wts are written too; beyond, the logits only.
+template <typename TIN>
+static hipError_t router_logits_t(const Shape& s, const void* x, const void* wg, const float* bias, float* logits,
+                                  int32_t* ids, float* w, hipStream_t st) {
+  const dim3 blk(NTHREADS);
+  auto go = [&](auto kern, int bm, int bn) {
+    const dim3 grd((s.T + bm - 1) / bm, (s.E + bn - 1) / bn);
+    kern<<<grd, blk, 0, st>>>((const TIN*)x, (const TIN*)wg, bias, logits, ids, w, s.T, s.d, s.E, s.K);
+  };
+  if (s.E <= 32) {
+    go(router_logits_kernel<Cfg<TIN, 128, 32, 4, 1>, true>, 128, 32);
+  } else if (s.E <= 64) {
+    // 64-token tiles: a grid of T/64 workgroups fills the chip from a few thousand tokens
+    go(router_logits_kernel<Cfg<TIN, 64, 64, 2, 2>, true>, 64, 64);
+  } else if (s.E <= 128) {
+    // one 128-expert column block: 32-token tiles keep enough workgroups in flight
+    go(router_logits_kernel<Cfg<TIN, 32, 128, 1, 4>, true>, 32, 128);
+  } else {
+    go(router_logits_kernel<Cfg<TIN, 128, 128, 2, 2>, false>, 128, 128);
+  }
+  return hipGetLastError();
+}
+
+bool router_logits_has_topk(const Shape& s) { return s.E <= 128; }
+
+hipError_t launch_router_logits(const Shape& s, const void* x, const void* wg, const float* bias, float* logits,
+                                int32_t* ids, float* w, hipStream_t st) {
+  timing_mark(st, "router_logits", true);
+  hipError_t e = s.bf16 ? router_logits_t<bf16_t>(s, x, wg, bias, logits, ids, w, st)
+                        : router_logits_t<float>(s, x, wg, bias, logits, ids, w, st);
+  timing_mark(st, "router_logits", false);
+  return e;
 }
 
 template <int G, int V>
