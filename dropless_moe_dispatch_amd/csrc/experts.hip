@@ -915,6 +915,7 @@ __global__ __launch_bounds__(64 * RB_TOKENS) void router_bwd_kernel(const int32_
                                                                     const float* __restrict__ ds_part, int nbh,
                                                                     const TIN* __restrict__ wg,
                                                                     float* __restrict__ dz_pos,
+                                                                    float* __restrict__ dz_tok,
                                                                     float* __restrict__ ds_out,
                                                                     float* __restrict__ accws, int T, int d, int K) {
   const int t = blockIdx.x * RB_TOKENS + (int)(threadIdx.x >> 6);
@@ -934,17 +935,23 @@ __global__ __launch_bounds__(64 * RB_TOKENS) void router_bwd_kernel(const int32_
   const float dz = wv * (dsv - c);
   if (l < K) {
     dz_pos[p] = dz;
+    dz_tok[(size_t)t * K + l] = dz;
     if (ds_out) ds_out[(size_t)t * K + l] = dsv;
   }
   constexpr int VPL = 16 / sizeof(TIN);  // values per 16-byte load
   float* orow = accws + (size_t)t * d;
-  for (int col = l * VPL; col < d; col += 64 * VPL) {
+  // every lane runs every pass, so that the shuffles below read slot k's dz
+  // and expert from lane k even where d has fewer columns than the wave
+  for (int c0 = 0; c0 < d; c0 += 64 * VPL) {
+    const int col = c0 + l * VPL;
+    const bool in = col < d;
     float acc[VPL];
 #pragma unroll
     for (int v = 0; v < VPL; ++v) acc[v] = 0.0f;
     for (int k = 0; k < K; ++k) {
       const float z = __shfl(dz, k, 64);
       const int ek = __shfl(e, k, 64);
+      if (!in) continue;
       const TIN* wr = wg + (size_t)ek * d + col;
       if constexpr (sizeof(TIN) == 2) {
         const u32x4_t q = *(const u32x4_t*)wr;
@@ -959,8 +966,11 @@ __global__ __launch_bounds__(64 * RB_TOKENS) void router_bwd_kernel(const int32_
         for (int v = 0; v < 4; ++v) acc[v] += z * q[v];
       }
     }
+    if (in) {
 #pragma unroll
-    for (int v = 0; v < VPL; v += 4) *(f32x4_t*)(orow + col + v) = f32x4_t{acc[v], acc[v + 1], acc[v + 2], acc[v + 3]};
+      for (int v = 0; v < VPL; v += 4)
+        *(f32x4_t*)(orow + col + v) = f32x4_t{acc[v], acc[v + 1], acc[v + 2], acc[v + 3]};
+    }
   }
 }
 
@@ -1014,6 +1024,170 @@ __global__ __launch_bounds__(256) void dwg_reduce_kernel(const float* __restrict
   f32x4_t acc{0.0f, 0.0f, 0.0f, 0.0f};
   for (int g = mb_off[e]; g < mb_off[e + 1]; ++g) acc += *(const f32x4_t*)(part + (size_t)g * d + c);
   *(f32x4_t*)(dwg + (size_t)e * d + c) = acc;
+}
+
+// dWg on MFMA (bf16): dWg = dZ^T X, with dZ [T][E] the router-logit
+// gradients, dense: token t's K entries dz[t,k] at columns ids[t,k] and zeros
+// elsewhere.  X is read once (as rows of tokens), where the per-position form
+// above reads a gathered row for each of the K assignments of a token.
+//
+// Workgroup (column block nb, expert block eb, token chunk z): the 128 x 128
+// tile dWg[eb*128 .., nb*128 ..] summed over the chunk's tokens, 64 at a
+// time.  For each 64-token k-tile the A operand (experts x tokens) is built in
+// LDS: cleared, then each (token, slot) entry of the tile's experts written
+// at [expert][token].  dz enters as two bf16 operands, hi = bf16(dz) and
+// lo = bf16(dz - hi), whose products with the bf16 x are exact in the fp32
+// accumulation; hi + lo carries dz to about 2^-18.  The B operand (tokens x
+// columns of x) is staged k-major and read with the LDS transpose read.  The
+// x rows and the ids and dz are loaded two k-tiles ahead, in two register
+// sets.  Each chunk's tile goes to part[z]; dwg_mfma_reduce
+// sums the chunks in ascending order.
+// BM experts per tile (32, 64 or 128: the smallest that holds E, else 128).
+template <int BM, int EPT>  // EPT: (token, slot) entries per thread per k-tile, 64 K / 256 rounded up
+__global__ __launch_bounds__(256, 2) void dwg_mfma_kernel(const bf16_t* __restrict__ x,
+                                                          const int32_t* __restrict__ ids,
+                                                          const float* __restrict__ dz_tok, float* __restrict__ part,
+                                                          int T, int d, int E, int K, int chunk_tokens) {
+  using M = Mfma<bf16_t>;
+  using G = KmGeom<128>;
+  constexpr int WM = BM >= 64 ? 2 : 1, WN = 4 / WM;  // wave grid
+  constexpr int FM = BM / WM / 32, FN = 128 / WN / 32;
+  constexpr int A_BYTES = BM * LDS_ROW;
+  __shared__ __attribute__((aligned(16))) char smem[2 * A_BYTES + G::BYTES];
+  char* s_hi = smem;
+  char* s_lo = smem + A_BYTES;
+  char* s_b = smem + 2 * A_BYTES;
+  const int nb = blockIdx.x, e0 = blockIdx.y * BM, z = blockIdx.z;
+  const int t0 = z * chunk_tokens;
+  const int t1 = min_i(T, t0 + chunk_tokens);
+  const int nkt = (t1 - t0 + 63) / 64;
+  const int tid = threadIdx.x, l = lane_id(), wave = tid >> 6, wm = wave / WN, wn = wave % WN;
+  // B: k-row r of k-tile kt is token t0 + 64 kt + r, columns nb*128 + 8 cc ..
+  const rsrc_t rx = make_rsrc(x + (size_t)t0 * d, (size_t)(t1 - t0) * d * 2);
+  const int cc = tid % G::CPR, kr0 = tid / G::CPR;
+  const uint32_t col_off = (uint32_t)(nb * 128 + cc * 8) * 2u;
+  // entries (token, slot) i = tid + 256 j of the k-tile: ids / dz_tok index t0*K + 64 kt K + i
+  const rsrc_t rid = make_rsrc(ids + (size_t)t0 * K, (size_t)(t1 - t0) * K * 4);
+  const rsrc_t rdz = make_rsrc(dz_tok + (size_t)t0 * K, (size_t)(t1 - t0) * K * 4);
+  // two register sets: k-tile kt's loads go to set kt % 2, two k-tiles ahead
+  u32x4_t xb[2][G::NPASS];
+  int ide[2][EPT];
+  float dze[2][EPT];
+  auto load = [&](auto setc, int kt) {
+    constexpr int SET = decltype(setc)::value;
+#pragma unroll
+    for (int i = 0; i < G::NPASS; ++i) {
+      const int r = kt * 64 + kr0 + G::RPP * i;
+      xb[SET][i] = buf_load16(rx, (uint32_t)r * (uint32_t)d * 2u + col_off);  // past t1: out of range, zeros
+    }
+#pragma unroll
+    for (int j = 0; j < EPT; ++j) {
+      const uint32_t o = (uint32_t)(kt * 64 * K + tid + 256 * j) * 4u;
+      ide[SET][j] = (int)buf_load4(rid, o);  // past the chunk: 0, never used
+      dze[SET][j] = __builtin_bit_cast(float, buf_load4(rdz, o));
+    }
+  };
+  f32x16_t acc[FM][FN];
+#pragma unroll
+  for (int fm = 0; fm < FM; ++fm)
+#pragma unroll
+    for (int fn = 0; fn < FN; ++fn) acc[fm][fn] = f32x16_t{};
+  const int a_lane = (l & 31) * LDS_ROW + (l >> 5) * 16;  // row l % 32, k-group l / 32
+  const int b_lane = km_lane_off(G::PITCH);
+  auto tile = [&](auto setc, int kt) {
+    constexpr int SET = decltype(setc)::value;
+    __syncthreads();  // the previous k-tile's operands have been read
+    // clear A (hi and lo): 2 * BM rows of LDS_ROW bytes
+    for (int o = tid * 16; o < 2 * A_BYTES; o += 256 * 16) *(u32x4_t*)(smem + o) = u32x4_t{0u, 0u, 0u, 0u};
+#pragma unroll
+    for (int i = 0; i < G::NPASS; ++i) *(u32x4_t*)(s_b + (kr0 + G::RPP * i) * G::PITCH + cc * 16) = xb[SET][i];
+    int my_e[EPT];
+    float my_z[EPT];
+#pragma unroll
+    for (int j = 0; j < EPT; ++j) {
+      my_e[j] = ide[SET][j];
+      my_z[j] = dze[SET][j];
+    }
+    if (kt + 2 < nkt) load(setc, kt + 2);
+    __syncthreads();
+#pragma unroll
+    for (int j = 0; j < EPT; ++j) {
+      const int i = tid + 256 * j;
+      const int tk = i / K;  // token within the k-tile
+      const int e = my_e[j] - e0;
+      if (i < 64 * K && t0 + kt * 64 + tk < t1 && e >= 0 && e < BM) {
+        const uint32_t hi = f32_to_bf16(my_z[j]);
+        const uint32_t lo = f32_to_bf16(my_z[j] - bf16_to_f32(hi));
+        *(bf16_t*)(s_hi + e * LDS_ROW + tk * 2) = (bf16_t)hi;
+        *(bf16_t*)(s_lo + e * LDS_ROW + tk * 2) = (bf16_t)lo;
+      }
+    }
+    __syncthreads();
+#pragma unroll
+    for (int st = 0; st < 4; ++st) {  // k-steps of 16 tokens
+      typename M::Frag ah[FM], al[FM], b[FN];
+#pragma unroll
+      for (int fm = 0; fm < FM; ++fm) {
+        const int off = a_lane + (wm * (BM / WM) + fm * 32) * LDS_ROW + st * 32;
+        ah[fm] = M::lds_read(s_hi + off);
+        al[fm] = M::lds_read(s_lo + off);
+      }
+#pragma unroll
+      for (int fn = 0; fn < FN; ++fn)
+        b[fn].v = km_read(s_b + b_lane + st * 16 * G::PITCH + (wn * (128 / WN) + fn * 32) * 2, G::PITCH);
+#pragma unroll
+      for (int fm = 0; fm < FM; ++fm)
+#pragma unroll
+        for (int fn = 0; fn < FN; ++fn) {
+          M::mma(acc[fm][fn], ah[fm], b[fn]);
+          M::mma(acc[fm][fn], al[fm], b[fn]);
+        }
+    }
+  };
+  using S0 = std::integral_constant<int, 0>;
+  using S1 = std::integral_constant<int, 1>;
+  if (nkt > 0) load(S0{}, 0);
+  if (nkt > 1) load(S1{}, 1);
+  for (int kt = 0; kt < nkt; kt += 2) {
+    tile(S0{}, kt);
+    if (kt + 1 < nkt) tile(S1{}, kt + 1);
+  }
+  float* o = part + (size_t)z * E * d;
+#pragma unroll
+  for (int fm = 0; fm < FM; ++fm)
+#pragma unroll
+    for (int fn = 0; fn < FN; ++fn) {
+      const int c = nb * 128 + wn * (128 / WN) + fn * 32 + frag_col(l);
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int e = e0 + wm * (BM / WM) + fm * 32 + frag_row(r, l);
+        if (e < E && c < d) o[(size_t)e * d + c] = acc[fm][fn][r];
+      }
+    }
+}
+
+// dWg[e][c] = sum over the token chunks z of part[z][e][c], in a fixed order:
+// a workgroup takes 64 consecutive floats (16 quads) of the n = E*d; its 16
+// z-lanes g sum the chunks z = g, g + 16, ... in ascending order, and the 16
+// lane sums are added in ascending g.  Many loads in flight per output even
+// where n is small and the chunks many.
+constexpr int DWG_ZL = 16;
+__global__ __launch_bounds__(256) void dwg_mfma_reduce_kernel(const float* __restrict__ part, float* __restrict__ dwg,
+                                                              long long n, int nz) {
+  __shared__ f32x4_t s_p[DWG_ZL][16];
+  const int q = (int)threadIdx.x & 15, g = (int)threadIdx.x >> 4;
+  const long long i = (long long)blockIdx.x * 64 + q * 4;
+  f32x4_t a{0.0f, 0.0f, 0.0f, 0.0f};
+  if (i < n)
+    for (int zz = g; zz < nz; zz += DWG_ZL) a += *(const f32x4_t*)(part + (size_t)zz * n + i);
+  s_p[g][q] = a;
+  __syncthreads();
+  if (g == 0 && i < n) {
+    f32x4_t r = s_p[0][q];
+#pragma unroll
+    for (int j = 1; j < DWG_ZL; ++j) r += s_p[j][q];
+    *(f32x4_t*)(dwg + i) = r;
+  }
 }
 
 // dW_down[e] (d x h) = sum_p dO[eti[p]]^T (w_p y[p]): M = d, N = h, K = rows of e.
@@ -1239,12 +1413,32 @@ static hipError_t backward_t(const Shape& s, const void* dout, const void* x, co
 
   timing_mark(st, "router_bwd", true);
   router_bwd_kernel<TIN><<<dim3((s.T + RB_TOKENS - 1) / RB_TOKENS), dim3(64 * RB_TOKENS), 0, st>>>(
-      ids, topk_w, tim, ws.ds_part, nbh, (const TIN*)wg, ws.dz_pos, ds, ws.acc, s.T, s.d, s.K);
+      ids, topk_w, tim, ws.ds_part, nbh, (const TIN*)wg, ws.dz_pos, ws.dz_tok, ds, ws.acc, s.T, s.d, s.K);
   timing_mark(st, "router_bwd", false);
   if ((err = hipGetLastError()) != hipSuccess) return err;
 
   timing_mark(st, "dwg", true);
-  {
+  if constexpr (sizeof(TIN) == 2) {
+    const int ct = dwg_chunk_tokens(s), nz = dwg_chunks(s);
+    const int bm = dwg_expert_tile(s);
+    const dim3 grid(col_blocks(s.d, 128), (s.E + bm - 1) / bm, nz);
+    const int ept = (64 * s.K + 255) / 256;
+    auto go = [&](auto bmc) {
+      constexpr int BM = decltype(bmc)::value;
+      auto run = [&](auto kern) {
+        kern<<<grid, dim3(256), 0, st>>>((const bf16_t*)x, ids, ws.dz_tok, ws.dwg_part, s.T, s.d, s.E, s.K, ct);
+      };
+      if (ept <= 1) run(dwg_mfma_kernel<BM, 1>);
+      else if (ept <= 2) run(dwg_mfma_kernel<BM, 2>);
+      else if (ept <= 4) run(dwg_mfma_kernel<BM, 4>);
+      else run(dwg_mfma_kernel<BM, 8>);
+    };
+    if (bm == 32) go(std::integral_constant<int, 32>{});
+    else if (bm == 64) go(std::integral_constant<int, 64>{});
+    else go(std::integral_constant<int, 128>{});
+    const long long n = (long long)s.E * s.d;
+    dwg_mfma_reduce_kernel<<<dim3((unsigned)((n + 63) / 64)), dim3(256), 0, st>>>(ws.dwg_part, dwg, n, nz);
+  } else {
     constexpr int VPL = 16 / sizeof(TIN);
     const int ncb = (s.d + 256 * VPL - 1) / (256 * VPL);
     dwg_part_kernel<TIN><<<dim3((unsigned)max_row_blocks(s, TILE_S), ncb), dim3(256), 0, st>>>(

@@ -92,6 +92,26 @@ inline int dw_down_split(const Shape& s) { return dw_split(s, s.d, s.h); }
 inline int dw_gate_up_split(const Shape& s) { return dw_split(s, s.hw(), s.d); }
 
 // ---- per-call expert workspace (tile map, per-position data, fold state) --
+// dWg on MFMA (bf16): the tokens are cut into dwg_chunks(s) chunks of
+// dwg_chunk_tokens(s) (a multiple of 64) so that the grid of (128-column
+// block, expert block of dwg_expert_tile(s), chunk) workgroups has about 512 of them, and a
+// chunk's rows of x stay under 1 GiB (32-bit buffer offsets).  Shape only:
+// the partial buffer never depends on the routing.
+inline int dwg_expert_tile(const Shape& s) { return s.E <= 32 ? 32 : s.E <= 64 ? 64 : 128; }
+inline int dwg_chunk_tokens(const Shape& s) {
+  const int bm = dwg_expert_tile(s);
+  const long long tiles = (long long)col_blocks(s.d, 128) * ((s.E + bm - 1) / bm);
+  const long long ktiles = (s.T + 63) / 64;
+  long long want = (512 + tiles - 1) / tiles;
+  if (want > ktiles) want = ktiles;
+  if (want < 1) want = 1;
+  long long per = (ktiles + want - 1) / want;  // k-tiles per chunk
+  const long long cap = (1LL << 23) / s.d;     // 64 tokens * d * 2 bytes * cap <= 2^30
+  if (per > cap) per = cap > 0 ? cap : 1;
+  return (int)(per * 64);
+}
+inline int dwg_chunks(const Shape& s) { return (s.T + dwg_chunk_tokens(s) - 1) / dwg_chunk_tokens(s); }
+
 struct ExpertWs {
   int32_t* counters;   // [N_COUNTERS]
   int32_t* mb_off;     // [2][E+1] exclusive prefix of ceil(count_e / bm), bm = 128 then 256
@@ -101,7 +121,8 @@ struct ExpertWs {
   float* acc;          // [T][d] fp32 fold accumulator
   float* ds_part;      // [A][h/128] router-score partial sums (backward)
   float* dz_pos;       // [A] router logit gradient per position (backward)
-  float* dwg_part;     // [row blocks of 128][d] per-row-block partial sums of dWg (backward)
+  float* dz_tok;       // [A] the same per (token, slot), token-major (backward)
+  float* dwg_part;     // dWg partial sums (backward): bf16 [token chunks][E][d], fp32 [row blocks of 128][d]
   float* dw_part;      // [split][E][m][n] dW chunk partials when a dW GEMM splits its rows (backward)
   void* dh;            // [A][hw] activation-dtype gradient of the pre-activations (backward)
   void* a_prime;       // [A][h] activation-dtype A' = w * y recomputed from a, b (H-only backward)
@@ -130,7 +151,9 @@ inline ExpertWs expert_ws(const Shape& s, int which, void* p) {
   if (bwd) {
     w.ds_part = (float*)take(A * col_blocks(s.h, TILE_S) * 4);
     w.dz_pos = (float*)take(A * 4);
-    w.dwg_part = (float*)take((size_t)max_row_blocks(s, TILE_S) * s.d * 4);
+    w.dz_tok = (float*)take(A * 4);
+    w.dwg_part = (float*)take(s.bf16 ? (size_t)dwg_chunks(s) * s.E * s.d * 4
+                                     : (size_t)max_row_blocks(s, TILE_S) * s.d * 4);
     const int sd = dw_down_split(s), sg = dw_gate_up_split(s);
     const size_t pd = sd > 1 ? (size_t)sd * s.E * s.d * s.h : 0;
     const size_t pg = sg > 1 ? (size_t)sg * s.E * s.hw() * s.d : 0;

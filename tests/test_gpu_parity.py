@@ -161,6 +161,11 @@ LAYER_CASES = [
     # rows into 8 chunks and sum the partials
     ("split_k", 4096, 256, 2, 2, 256, "bf16", None),
     ("split_k_f32", 4096, 128, 2, 2, 128, "f32", None),
+    # router weight gradient on MFMA: two 128-expert blocks (the second
+    # ragged), and 16 or 32 slots per token (more entries per thread)
+    ("experts_200", 600, 128, 200, 4, 128, "bf16", None),
+    ("k16", 300, 128, 32, 16, 128, "bf16", None),
+    ("k32", 130, 128, 64, 32, 128, "bf16", 1.2),
 ]
 
 
