@@ -223,7 +223,9 @@ def _rows_of(ids, k, e):
 
 def moe_forward(x, ids, w, w_gate, w_up, w_down, dtype="bf16", only_experts=None, act="swiglu"):
     """Forward pass.  Returns out [T,d] plus the per-assignment tensors
-    a_s, b_s, y_s [T,K,h] (storage-rounded) and ye [T,K,d] (expert output).
+    a_s, b_s, y_s [T,K,h] (storage-rounded), a_u, b_u, y_u (the same before
+    the storage rounding, for judging which stored values sit on a rounding
+    boundary; nothing here uses them) and ye [T,K,d] (expert output).
 
     ``only_experts`` (for sampled checks) evaluates only the assignments of
     those experts; quantities of the other assignments stay zero.
@@ -240,6 +242,9 @@ def moe_forward(x, ids, w, w_gate, w_up, w_down, dtype="bf16", only_experts=None
     a_s = np.zeros((T, K, h))
     b_s = np.zeros((T, K, h))
     y_s = np.zeros((T, K, h))
+    a_u = np.zeros((T, K, h))
+    b_u = np.zeros((T, K, h))
+    y_u = np.zeros((T, K, h))
     ye = np.zeros((T, K, d))
     out = np.zeros((T, d))
     for k in range(K):                       # slot order of the weighted sum
@@ -251,16 +256,20 @@ def moe_forward(x, ids, w, w_gate, w_up, w_down, dtype="bf16", only_experts=None
             a = xe @ _f64(w_gate[e]).T       # gate projection (W_1 of a plain expert)
             if act == "swiglu":
                 b = xe @ _f64(w_up[e]).T     # up projection
-                y = st(silu(a) * b)          # SiLU(a) * b from the unrounded a, b
+                yu = silu(a) * b             # SiLU(a) * b from the unrounded a, b
                 b_s[r, k] = st(b)
+                b_u[r, k] = b
             else:
-                y = st(ACTS[act][0](a))      # sigma(a) from the unrounded a
+                yu = ACTS[act][0](a)         # sigma(a) from the unrounded a
+            y = st(yu)
             yo = y @ _f64(w_down[e]).T       # down projection
             a_s[r, k] = st(a)
+            a_u[r, k] = a
             y_s[r, k] = y
+            y_u[r, k] = yu
             ye[r, k] = yo
             out[r] += w[r, k][:, None] * yo
-    return dict(out=st(out), out_f64=out, a_s=a_s, b_s=b_s, y_s=y_s, ye=ye)
+    return dict(out=st(out), out_f64=out, a_s=a_s, b_s=b_s, y_s=y_s, a_u=a_u, b_u=b_u, y_u=y_u, ye=ye)
 
 
 # ---------------------------------------------------------------------------
@@ -286,7 +295,11 @@ def moe_backward(dy, x, wg, ids, w, w_gate, w_up, w_down, fwd, z, dtype="bf16", 
 
     Returns dx [T,d], dwg [E,d], dw_gate/dw_up [E,h,d], dw_down [E,d,h],
     ds [T,K] (= dL/dw), ds_alt [T,K] (= <dA', y>), dz [T,E] (closed form),
-    dz_long [T,E] (through the full softmax), dh_a/dh_b [T,K,h].
+    dz_long [T,E] (through the full softmax), dh_a/dh_b [T,K,h] as stored,
+    and dh_a_u/dh_b_u/a_prime_u [T,K,h]: the same values and A' before the
+    storage rounding, and dyv [T,K,h], the gradient reaching y (for judging
+    which stored values sit on a rounding boundary and what a one-ulp change
+    of them moves; nothing here uses them).
     """
     if saved not in ("aby", "ab"):
         raise ValueError(f"saved must be 'aby' or 'ab', not {saved!r}")
@@ -305,6 +318,10 @@ def moe_backward(dy, x, wg, ids, w, w_gate, w_up, w_down, fwd, z, dtype="bf16", 
     ds_alt = np.zeros((T, K))
     dh_a = np.zeros((T, K, h))
     dh_b = np.zeros((T, K, h))
+    dh_a_u = np.zeros((T, K, h))
+    dh_b_u = np.zeros((T, K, h))
+    a_prime_u = np.zeros((T, K, h))
+    dyv_all = np.zeros((T, K, h))
     for k in range(K):
         for e in range(E) if only_experts is None else only_experts:
             r = _rows_of(ids, k, e)
@@ -323,16 +340,23 @@ def moe_backward(dy, x, wg, ids, w, w_gate, w_up, w_down, fwd, z, dtype="bf16", 
             ds[r, k] = np.einsum("rd,rd->r", g, fwd["ye"][r, k])      # <dO, Y>
             ds_alt[r, k] = np.einsum("rh,rh->r", da_p, y_b)           # <dA', y>
             dyv = w[r, k][:, None] * da_p              # gradient reaching y
+            dyv_all[r, k] = dyv
             if act == "swiglu":
-                da = st(dyv * b * silu_grad(a))        # SiLU recomputed from stored a
-                db = st(dyv * silu(a))
+                da_u = dyv * b * silu_grad(a)          # SiLU recomputed from stored a
+                db_u = dyv * silu(a)
+                db = st(db_u)
                 dh_b[r, k] = db
+                dh_b_u[r, k] = db_u
             else:
-                da = st(dyv * ACTS[act][1](a))         # sigma' recomputed from stored a
+                da_u = dyv * ACTS[act][1](a)           # sigma' recomputed from stored a
                 db = None
+            da = st(da_u)
             dh_a[r, k] = da
+            dh_a_u[r, k] = da_u
             # A' = w * y, held in the storage type (SonicMoE sec. 3.4.1: dW2 = A'^T dO)
-            a_prime = st(w[r, k][:, None] * y_b)
+            ap_u = w[r, k][:, None] * y_b
+            a_prime_u[r, k] = ap_u
+            a_prime = st(ap_u)
             dw_down[e] += g.T @ a_prime
             dw_gate[e] += da.T @ x[r]
             dx[r] += da @ _f64(w_gate[e])
@@ -350,7 +374,8 @@ def moe_backward(dy, x, wg, ids, w, w_gate, w_up, w_down, fwd, z, dtype="bf16", 
     dx = dx + dz @ _f64(wg)
     return dict(dx=st(dx), dx_f64=dx, dwg=dwg, dw_gate=dw_gate, dw_up=dw_up,
                 dw_down=dw_down, ds=ds, ds_alt=ds_alt, ds_router=ds_r, dz=dz,
-                dz_long=router_backward_long(z, ids, ds_r), dh_a=dh_a, dh_b=dh_b)
+                dz_long=router_backward_long(z, ids, ds_r), dh_a=dh_a, dh_b=dh_b, dh_a_u=dh_a_u,
+                dh_b_u=dh_b_u, a_prime_u=a_prime_u, dyv=dyv_all)
 
 
 def router_backward_long(z, ids, ds) -> np.ndarray:

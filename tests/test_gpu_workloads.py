@@ -18,7 +18,7 @@ from dropless_moe_dispatch_amd import binding as B
 from dropless_moe_dispatch_amd import layer as Lyr
 from dropless_moe_dispatch_amd import synth
 from oracle import moe_oracle as O
-from tests.gpu_util import assert_close, to_np, topk_margin
+from tests.gpu_util import assert_close, dw_flip_allowance, stored_flip_bounds, to_np, topk_margin
 
 pytestmark = pytest.mark.gpu
 
@@ -121,10 +121,17 @@ def test_workload_full_size(idx):
         be = O.moe_backward(inp["dy"][toks], inp["x"][toks], inp["wg"], ids_ref[toks], w_ref[toks], inp["w_gate"],
                             inp["w_up"], inp["w_down"], fe, z32[toks].astype(np.float64), dtype=dt,
                             only_experts=None if full_k else [e], act=wl.act)
-        assert_close(f"dw_gate[{e}]", to_np(buf.dw_gate[e]), be["dw_gate"][e])
+        it = ids_ref[toks]
+        fl = stored_flip_bounds(fe, be, w_ref[toks], dt, wl.act)
+
+        def allow(key, rows, transpose=False):
+            return dw_flip_allowance(fl[key], it, rows, E, transpose, experts=[e])[e]
+
+        assert_close(f"dw_gate[{e}]", to_np(buf.dw_gate[e]), be["dw_gate"][e], allow=allow("da", inp["x"][toks]))
         if gated:
-            assert_close(f"dw_up[{e}]", to_np(buf.dw_up[e]), be["dw_up"][e])
-        assert_close(f"dw_down[{e}]", to_np(buf.dw_down[e]), be["dw_down"][e])
+            assert_close(f"dw_up[{e}]", to_np(buf.dw_up[e]), be["dw_up"][e], allow=allow("db", inp["x"][toks]))
+        assert_close(f"dw_down[{e}]", to_np(buf.dw_down[e]), be["dw_down"][e],
+                     allow=allow("ap", inp["dy"][toks], True))
         if full_k:
             assert_close(f"dwg[{e}]", to_np(buf.dwg[e]), be["dwg"][e])
     for e in np.nonzero(counts == 0)[0]:
