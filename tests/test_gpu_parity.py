@@ -173,6 +173,10 @@ LAYER_CASES = [
     ("wide_fold", 200, 4096, 4, 2, 4096, "bf16", None),
     ("many_empty", 50, 128, 256, 2, 128, "bf16", None),
     ("f32_k8", 200, 128, 16, 8, 128, "f32", 1.2),
+    # the largest E (eight 128-expert blocks in dWg, almost every expert
+    # empty) and the largest K with K = E
+    ("experts_1024", 300, 128, 1024, 2, 128, "bf16", None),
+    ("k_eq_e_32", 70, 128, 32, 32, 128, "bf16", None),
 ]
 
 
