@@ -69,16 +69,21 @@ def kernel_flops(name, T, d, E, K, h, gated=True):
     }.get(name)
 
 
-def kernel_bytes(name, T, d, E, K, h, eb):
-    """Algorithmic HBM bytes of the memory-bound stages (operands once, outputs once)."""
+def kernel_bytes(name, T, d, E, K, h, eb, gated=True):
+    """Algorithmic HBM bytes (operands once, outputs once): the memory-bound
+    stages, and the two GEMMs with the fused combine, whose ordered fold moves
+    (8K-6)·T·d (forward) and (8K-4)·T·d (dX) accumulator and output bytes."""
     A = T * K
+    hw = 2 * h if gated else h
     return {
         "router_logits": eb * T * d + eb * E * d + 4 * T * E + (8 * A if E <= 128 else 0),
         "topk": 4 * T * E + 8 * A,
         "route": eb * T * d + eb * E * d + 4 * T * E + 8 * A,
         "index": 4 * A + 8 * A + 8 * E * ((T + 63) // 64),
         "router_bwd": 4 * T * d + eb * E * d + 16 * A,
-        "dwg": eb * A * d + 4 * E * d + 8 * A,
+        "dwg": eb * T * d + 4 * E * d + 8 * A,
+        "down_combine": eb * A * h + eb * E * d * h + (8 * K - 6) * T * d,
+        "dx_fold": eb * A * hw + eb * E * hw * d + (8 * K - 4) * T * d,
         "gather_sum": eb * A * d + eb * T * d + 8 * A,
     }.get(name)
 
@@ -334,7 +339,7 @@ def main():
         if fl is not None:
             rec["tflops"] = round(fl / (v["avg_ms"] * 1e-3) / 1e12, 1)
             rec["mfma_peak_frac"] = round(rec["tflops"] / peak, 4)
-        by = kernel_bytes(k, T, d, E, K, h, eb)
+        by = kernel_bytes(k, T, d, E, K, h, eb, gated)
         if by is not None:
             rec["gbs"] = round(by / (v["avg_ms"] * 1e-3) / 1e9, 1)
             rec["hbm_peak_frac"] = round(rec["gbs"] / PEAK_HBM_GBS, 4)
