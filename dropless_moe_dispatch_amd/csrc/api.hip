@@ -70,6 +70,15 @@ int check_shape(const moe_shape* s, Shape* out) {
   if (s->E > 1024 || s->K > 32) return MOE_ERR_UNSUPPORTED;
   if (s->d % 128 != 0 || s->h % 128 != 0) return MOE_ERR_UNSUPPORTED;
   if (s->act != MOE_ACT_SWIGLU && s->act != MOE_ACT_SILU && s->act != MOE_ACT_RELU) return MOE_ERR_INVALID_ARG;
+  {
+    // the kernels read whole tensors through buffer resources with 32-bit
+    // byte offsets: x and dY [T,d] (gathered rows), one expert's weights
+    // [h,d], and up to T rows of H or dH [*, 2h] (an expert's rows)
+    const long long eb = s->dtype == MOE_BF16 ? 2 : 4, lim = 0x7ffffff0LL;
+    const long long hw = s->act == MOE_ACT_SWIGLU ? 2LL * s->h : s->h;
+    if ((long long)s->T * s->d * eb > lim || (long long)s->h * s->d * eb > lim || (long long)s->T * hw * eb > lim)
+      return MOE_ERR_UNSUPPORTED;
+  }
   out->T = s->T;
   out->act = s->act;
   out->d = s->d;

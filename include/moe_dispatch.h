@@ -53,7 +53,11 @@
  *     nonzero after the call if a bounded wait of the ordered combine ran out
  *     (see moe_set_spin_limit); it is cleared at the start of each call.
  *   - Supported shapes: 1 <= K <= min(E, 32), E <= 1024, T*K < 2^31,
- *     d and h multiples of 128; device pointers 16-byte aligned.
+ *     d and h multiples of 128, and under 2 GiB each for x [T,d], one
+ *     expert's weight matrix [h,d] and T rows of the saved pre-activations
+ *     [T, 2h] (2h -> h for the plain experts) in the activation dtype (the
+ *     kernels address them with 32-bit offsets); otherwise
+ *     MOE_ERR_UNSUPPORTED.  Device pointers 16-byte aligned.
  */
 #ifndef MOE_DISPATCH_H
 #define MOE_DISPATCH_H

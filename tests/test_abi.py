@@ -63,6 +63,10 @@ FAKE = 0x10000  # 16-byte aligned fake device address: never dereferenced
     (16, 96, 8, 2, 128, "bf16", B.MOE_ERR_UNSUPPORTED),       # d % 128
     (16, 128, 8, 2, 200, "f32", B.MOE_ERR_UNSUPPORTED),       # h % 128
     (1 << 29, 128, 8, 8, 128, "bf16", B.MOE_ERR_INVALID_ARG),  # T*K >= 2^31
+    (1 << 20, 1024, 8, 2, 128, "bf16", B.MOE_ERR_UNSUPPORTED),   # x [T,d] of 2 GiB: past 32-bit offsets
+    (1 << 19, 1024, 8, 2, 128, "f32", B.MOE_ERR_UNSUPPORTED),    # the same in fp32
+    (64, 8192, 8, 2, 131072, "bf16", B.MOE_ERR_UNSUPPORTED),     # one expert's [h,d] of 2 GiB
+    (1 << 18, 128, 8, 2, 2048, "bf16", B.MOE_ERR_UNSUPPORTED),   # T rows of [a|b]: 2^18 * 4096 * 2 B
 ])
 def test_shape_validation_happens_on_host(T, d, E, K, h, dt, code):
     s = B.shape(T, d, E, K, h, dt)
