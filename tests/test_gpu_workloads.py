@@ -1,6 +1,7 @@
-"""GPU parity at full workload sizes -- the five evaluation workloads and two of
-MoEBlaze's shapes with plain SiLU experts -- in the launch configuration the
-benchmark times (router on the GPU, the five entry points in order).
+"""GPU parity at full workload sizes -- the five evaluation workloads and
+MoEBlaze's four printed shapes with plain SiLU experts -- in the launch
+configuration the benchmark times (router on the GPU, the five entry points in
+order).
 
 The oracle evaluates sampled outputs one by one: 32 random tokens (out, dx,
 dS, saved a/b/y), the weight gradients of the smallest and the largest
@@ -28,7 +29,7 @@ def _say(*a):
 
 
 @pytest.mark.timeout(900)
-@pytest.mark.parametrize("idx", [1, 2, 3, 4, 5, 6, 9])
+@pytest.mark.parametrize("idx", [1, 2, 3, 4, 5, 6, 7, 8, 9])
 def test_workload_full_size(idx):
     if not torch.cuda.is_available():
         pytest.skip("no GPU")
