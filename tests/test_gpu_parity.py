@@ -378,3 +378,27 @@ def test_bitwise_repeatable():
     for key in ("topk_ids", "topk_w", "eti", "tim", "h_ab", "y_swi", "out", "dx", "dwg", "dw_gate", "dw_up",
                 "dw_down", "ds"):
         assert torch.equal(getattr(b1, key), getattr(b2, key)), key
+
+
+def test_bounded_wait_reports_and_finishes():
+    """Error path of the ordered fold, forced from the host: with a wait limit
+    of one poll, a contribution whose predecessor has not folded yet gives up,
+    sets the workspace error word and its kernel still finishes.  Every token
+    chooses every expert (K = E), so the rows of expert e wait on those of
+    expert e - 1, whose tiles run at the same time.  The next call, with the
+    normal limit, is clean and matches the oracle."""
+    T, d, E, K, h = 512, 128, 4, 4, 128
+    _say("bounded_wait", T, d, E, K, h)
+    wl = synth.small_workload(T, d, E, K, h, seed=17)
+    inp = synth.make_inputs(wl)
+    z32 = O.router_logits(inp["x"], inp["wg"], inp["bias"]).astype(np.float32)
+    prev = B.set_spin_limit(1)
+    try:
+        bad, _ = _gpu_layer(inp, wl, logits32=z32)
+        words = bad.device_error_words()
+    finally:
+        B.set_spin_limit(prev)
+    assert words != [0, 0], "no wait ran out with a limit of one poll"
+    good, _ = _gpu_layer(inp, wl, logits32=z32)
+    assert good.device_error_words() == [0, 0]
+    _compare_layer(good, inp, wl, z32)
