@@ -239,6 +239,8 @@ def main():
     ap.add_argument("--combine", default="fold", choices=("fold", "staged"),
                     help="forward combine: the ordered fold (default) or the staged-Y ablation")
     ap.add_argument("--no-timing", action="store_true", help="do not record per-kernel events")
+    ap.add_argument("--graph", action="store_true",
+                    help="time replays of one HIP graph of the step instead of eager launches")
     ap.add_argument("--calib-copy-mb", type=int, default=0,
                     help="after the timed steps, run one plain device copy of this many MB "
                          "(reference kernel for scaling the HBM byte counters)")
@@ -277,10 +279,21 @@ def main():
     for _ in range(args.warmup):
         step()
     torch.cuda.synchronize()
+    run = step
+    if args.graph:
+        side = torch.cuda.Stream()
+        side.wait_stream(torch.cuda.current_stream())
+        graph = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(graph, stream=side):
+            step()
+        torch.cuda.synchronize()
+        run = graph.replay
+        run()
+        torch.cuda.synchronize()
     print("[bench] timed", file=sys.stderr, flush=True)
     t0 = time.perf_counter()
     for _ in range(args.steps):
-        step()
+        run()
     torch.cuda.synchronize()
     t1 = time.perf_counter()
     # per-kernel durations: the library's HIP events around each launch, on
@@ -372,7 +385,7 @@ def main():
         "data": "synthetic (seeded Philox normals, random-init weights)",
         "config": {"workload": wl.name, "T": T, "d": d, "E": E, "K": K, "h": h,
                    "backward": wl.backward, "zipf_s": wl.zipf_s, "seed": wl.seed, "act": wl.act, "saved": args.saved,
-                   "combine": args.combine},
+                   "combine": args.combine, "launch": "hip_graph" if args.graph else "eager"},
         "tflops": round(tflops, 2),
         "mfma_peak_frac": round(tflops / (PEAK_BF16_TFLOPS if dt == "bf16" else PEAK_F32_MFMA_TFLOPS), 4),
         "mfma_peak_frac_at_measured_clock": (
