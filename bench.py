@@ -234,8 +234,8 @@ def main():
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--workload", type=int, default=3, help="1..9 (default 3: fine-grained fwd+bwd; 6..9: MoEBlaze's shapes, SiLU experts)")
     ap.add_argument("--cpu-sample", type=int, default=64, help="tokens for the CPU oracle baseline (0 = skip)")
-    ap.add_argument("--saved", default="aby", choices=("aby", "ab"),
-                    help="saved for backward: a, b and y (default) or H-only (y recomputed)")
+    ap.add_argument("--saved", default="ab", choices=("aby", "ab"),
+                    help="saved for backward: H-only (a and b; y recomputed; default) or a, b and y")
     ap.add_argument("--combine", default="fold", choices=("fold", "staged"),
                     help="forward combine: the ordered fold (default) or the staged-Y ablation")
     ap.add_argument("--no-timing", action="store_true", help="do not record per-kernel events")

@@ -1,7 +1,7 @@
 """GPU parity at full workload sizes -- the five evaluation workloads and
 MoEBlaze's four printed shapes with plain SiLU experts -- in the launch
 configuration the benchmark times (router on the GPU, the five entry points in
-order).
+order, H-only saving).
 
 The oracle evaluates sampled outputs one by one: 32 random tokens (out, dx,
 dS, saved a/b/y), the weight gradients of the smallest and the largest
@@ -23,6 +23,10 @@ from tests.gpu_util import assert_close, dw_flip_allowance, stored_flip_bounds, 
 
 pytestmark = pytest.mark.gpu
 
+# what the forward saves for the backward, as bench.py runs it: H-only (a and
+# b; the backward recomputes y), SonicMoE's minimal cached set
+SAVED = "ab"
+
 
 def _say(*a):
     print("[case]", *a, file=sys.stderr, flush=True)
@@ -41,7 +45,7 @@ def test_workload_full_size(idx):
     inp = synth.make_inputs(wl, tensors=tensors)
     dev = {k: (Lyr.to_device(inp[k], dt) if inp[k] is not None else None) for k in tensors}
     bias = torch.from_numpy(inp["bias"]).cuda() if inp["bias"] is not None else None
-    buf = Lyr.MoEBuffers(T, d, E, K, h, dt, backward=wl.backward, act=wl.act)
+    buf = Lyr.MoEBuffers(T, d, E, K, h, dt, backward=wl.backward, act=wl.act, saved=SAVED)
 
     def run():
         Lyr.forward(buf, dev["x"], dev["wg"], bias, dev["w_gate"], dev["w_up"], dev["w_down"])
@@ -102,9 +106,10 @@ def test_workload_full_size(idx):
     if not wl.backward:
         return
     b = O.moe_backward(inp["dy"][sub], inp["x"][sub], inp["wg"], ids_ref[sub], w_ref[sub], inp["w_gate"],
-                       inp["w_up"], inp["w_down"], f, z32[sub].astype(np.float64), dtype=dt, act=wl.act)
+                       inp["w_up"], inp["w_down"], f, z32[sub].astype(np.float64), dtype=dt, act=wl.act,
+                       saved=SAVED)
     assert_close("dx[sample]", to_np(buf.dx[torch.from_numpy(sub).cuda()]), b["dx"])
-    assert_close("ds[sample]", to_np(buf.ds)[sub], b["ds"])
+    assert_close("ds[sample]", to_np(buf.ds)[sub], b["ds_router"])
 
     nz = np.nonzero(counts > 0)[0]
     e_small = int(nz[np.argmin(counts[nz])])
@@ -121,9 +126,9 @@ def test_workload_full_size(idx):
                            dtype=dt, only_experts=None if full_k else [e], act=wl.act)
         be = O.moe_backward(inp["dy"][toks], inp["x"][toks], inp["wg"], ids_ref[toks], w_ref[toks], inp["w_gate"],
                             inp["w_up"], inp["w_down"], fe, z32[toks].astype(np.float64), dtype=dt,
-                            only_experts=None if full_k else [e], act=wl.act)
+                            only_experts=None if full_k else [e], act=wl.act, saved=SAVED)
         it = ids_ref[toks]
-        fl = stored_flip_bounds(fe, be, w_ref[toks], dt, wl.act)
+        fl = stored_flip_bounds(fe, be, w_ref[toks], dt, wl.act, SAVED)
 
         def allow(key, rows, transpose=False):
             return dw_flip_allowance(fl[key], it, rows, E, transpose, experts=[e])[e]
