@@ -427,3 +427,26 @@ def test_relu_expert_rows_with_negative_preactivation_are_inert():
     np.testing.assert_array_equal(f["out"][3], 0.0)
     np.testing.assert_array_equal(b["dh_a"][3], 0.0)
     np.testing.assert_allclose(b["dx"][3], b["dz"][3] @ wg, rtol=1e-12, atol=1e-14)
+
+
+@pytest.mark.parametrize("act", ["swiglu", "silu"])
+def test_unrounded_intermediates_round_to_the_stored_ones(act):
+    """The unrounded a, b, y, dA, dB and A' the oracle reports (for the
+    parity tests' rounding-flip allowance) are the values its stored ones
+    were rounded from, and dyv is w times dA' = dO W_down."""
+    x, wg, wgt, wup, wdn, dy = _small_layer(T=20, E=4, K=2, seed=5)
+    st = O.storage_rounder("bf16")
+    xs, wgs, wgts, wups, wdns, dys = (st(v) for v in (x, wg, wgt, wup, wdn, dy))
+    z = O.router_logits(xs, wgs, None)
+    ids, w = O.route(z, 2)
+    f = O.moe_forward(xs, ids, w, wgts, wups, wdns, dtype="bf16", act=act)
+    b = O.moe_backward(dys, xs, wgs, ids, w, wgts, wups, wdns, f, z, dtype="bf16", act=act)
+    for u, s_ in (("a_u", "a_s"), ("y_u", "y_s")) + ((("b_u", "b_s"),) if act == "swiglu" else ()):
+        assert np.array_equal(st(f[u]), f[s_]), u
+    assert np.array_equal(st(b["dh_a_u"]), b["dh_a"])
+    if act == "swiglu":
+        assert np.array_equal(st(b["dh_b_u"]), b["dh_b"])
+    t, k = 3, 1
+    e = ids[t, k]
+    np.testing.assert_allclose(b["dyv"][t, k], w[t, k] * (dys[t] @ wdns[e]), rtol=1e-12)
+    np.testing.assert_allclose(b["a_prime_u"][t, k], w[t, k] * f["y_s"][t, k], rtol=1e-12)
