@@ -250,7 +250,9 @@ def test_layer_parity_from_logits(case):
     _compare_layer(buf, inp, wl, z32)
 
 
-H_ONLY_CASES = [c for c in LAYER_CASES if c[0] in ("ragged", "multi_tile", "skewed", "t1", "f32_bwd")]
+# H-only is what the benchmark runs: every layer case, except the slowest
+# oracle run (d = h = 4096), whose kernels the stored-y case above covers
+H_ONLY_CASES = [c for c in LAYER_CASES if c[0] != "wide_fold"]
 
 
 @pytest.mark.parametrize("case", H_ONLY_CASES, ids=[c[0] for c in H_ONLY_CASES])
