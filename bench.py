@@ -267,8 +267,9 @@ def main():
     torch.cuda.synchronize()
     base_alloc = torch.cuda.memory_allocated()
     torch.cuda.reset_peak_memory_stats()
+    # a forward-only workload saves nothing for a backward (h_ab not written)
     buf = L.MoEBuffers(T, d, E, K, h, dt, backward=wl.backward, saved=args.saved, combine=args.combine,
-                       act=wl.act)
+                       act=wl.act, save=wl.backward)
 
     def step():
         L.forward(buf, dev["x"], dev["wg"], bias, dev["w_gate"], dev["w_up"], dev["w_down"])

@@ -202,7 +202,7 @@ int moe_expert_fwd(const moe_shape* s, const void* x, const int32_t* offsets, co
   REQ(w_gate);
   if (sh.gated()) REQ(w_up);
   else OPT(w_up);  // plain two-layer expert: no up projection
-  REQ(h_ab);
+  OPT(h_ab);  // NULL: nothing is saved for a backward
   REQ(y_swi);
   REQ(ws);
   const ExpertWs w = expert_ws(sh, WS_EXPERT_FWD, ws);

@@ -174,8 +174,10 @@ __global__ __launch_bounds__(C::NT, C::WAVES_PER_EU) void gate_up_kernel(
           y[v] = a[v] * sigmoidf_(a[v]) * b[v];
         }
         const int j = j0 + cc * VPC;         // h is a multiple of the half tile: in range
-        st16(h_ab + (size_t)p * 2 * h + j, a);
-        st16(h_ab + (size_t)p * 2 * h + h + j, b);
+        if (h_ab) {  // NULL: a forward that saves nothing for a backward
+          st16(h_ab + (size_t)p * 2 * h + j, a);
+          st16(h_ab + (size_t)p * 2 * h + h + j, b);
+        }
         st16(y_swi + (size_t)p * h + j, y);
       }
     }
@@ -256,7 +258,7 @@ __global__ __launch_bounds__(C::NT, C::WAVES_PER_EU) void up_act_kernel(
           a[v] = ar[v];
           y[v] = act_fwd(a[v], act);
         }
-        st16(h_a + (size_t)p * h + j, a);
+        if (h_a) st16(h_a + (size_t)p * h + j, a);  // NULL: nothing saved
         st16(y_swi + (size_t)p * h + j, y);
       }
     }

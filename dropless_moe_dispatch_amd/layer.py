@@ -39,6 +39,9 @@ class MoEBuffers:
     # expert kind: "swiglu" (gated) or "silu" / "relu" (plain two-layer
     # expert: W_1 in the w_gate slot, no w_up, h_ab holds a only)
     act: str = "swiglu"
+    # keep a|b from the forward (always, when a backward follows); a forward
+    # alone may save nothing (h_ab is then None and not written)
+    save: bool = True
 
     def __post_init__(self):
         dev, td = self.device, torch_dtype(self.dtype)
@@ -53,7 +56,7 @@ class MoEBuffers:
         self.offsets = torch.empty(E + 1, dtype=i32, device=dev)
         self.eti = torch.empty(A, dtype=i32, device=dev)
         self.tim = torch.empty(A, dtype=i32, device=dev)
-        self.h_ab = torch.empty(A, hw, dtype=td, device=dev)
+        self.h_ab = torch.empty(A, hw, dtype=td, device=dev) if (self.save or self.backward) else None
         self.y_swi = torch.empty(A, h, dtype=td, device=dev)
         self.out = torch.empty(T, d, dtype=td, device=dev)
         self.ws_index = self._ws(B.MOE_WS_INDEX)
@@ -82,6 +85,8 @@ class MoEBuffers:
     def saved_for_backward_bytes(self) -> int:
         """Activations kept from the forward for the backward: a|b, y_swi
         (unless H-only), the top-K ids and weights, and the index arrays."""
+        if self.h_ab is None:
+            return 0
         ts = [self.h_ab, self.topk_ids, self.topk_w, self.offsets, self.eti, self.tim]
         if self.saved == "aby":
             ts.append(self.y_swi)

@@ -164,8 +164,11 @@ int moe_build_index_dense(const moe_shape* s, const int32_t* topk_ids, int32_t* 
  *   h_ab[p, 0:h]  = a = x[t] W_gate[e]^T     (rounded to dtype)
  *   h_ab[p, h:2h] = b = x[t] W_up[e]^T       (rounded to dtype)
  *   y_swi[p, :]   = SiLU(a) * b, from the unrounded fp32 a and b.
- * h_ab: [T*K, 2h], y_swi: [T*K, h], both dtype, outputs (saved for the
- * backward).  No permuted copy of x is made.  ws: MOE_WS_EXPERT_FWD. */
+ * h_ab: [T*K, 2h], y_swi: [T*K, h], both dtype, outputs (h_ab, and y_swi
+ * unless the backward takes the H-only path, are saved for the backward).
+ * h_ab may be NULL for a forward that no moe_expert_bwd follows: then
+ * nothing is stored but y_swi, which moe_combine reads.  No permuted copy of
+ * x is made.  ws: MOE_WS_EXPERT_FWD. */
 int moe_expert_fwd(const moe_shape* s, const void* x, const int32_t* offsets, const int32_t* expert_token_indices,
                    const void* w_gate, const void* w_up, void* h_ab, void* y_swi, void* ws, size_t ws_bytes,
                    void* stream);

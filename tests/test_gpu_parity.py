@@ -446,3 +446,30 @@ def test_graph_capture_replays_match_eager():
         assert buf.device_error_words() == [0, 0], i
         for k in keys:
             assert torch.equal(getattr(buf, k), ref[k]), (i, k)
+
+
+@pytest.mark.parametrize("act", ["swiglu", "silu"])
+def test_forward_without_saving(act):
+    """A forward that no backward follows may pass h_ab = NULL: nothing is
+    stored but y_swi, and the output and y are those of the saving forward,
+    bit for bit, and the oracle's."""
+    T, d, E, K, h = 300, 256, 8, 2, 256
+    _say("forward_no_save", act)
+    wl = synth.small_workload(T, d, E, K, h, seed=31, act=act, backward=False)
+    inp = synth.make_inputs(wl)
+    z32 = O.router_logits(inp["x"], inp["wg"], inp["bias"]).astype(np.float32)
+    dev = {k: Lyr.to_device(inp[k], "bf16") for k in ("x", "wg", "w_gate", "w_up", "w_down") if inp[k] is not None}
+    outs = []
+    for save in (True, False):
+        buf = Lyr.MoEBuffers(T, d, E, K, h, "bf16", backward=False, act=act, save=save)
+        assert (buf.h_ab is None) == (not save)
+        buf.logits.copy_(torch.from_numpy(z32))
+        Lyr.forward(buf, dev["x"], dev["wg"], None, dev["w_gate"], dev.get("w_up"), dev["w_down"], logits_in=True)
+        torch.cuda.synchronize()
+        assert buf.device_error_words() == [0]
+        outs.append(buf)
+    assert torch.equal(outs[0].out, outs[1].out)
+    assert torch.equal(outs[0].y_swi, outs[1].y_swi)
+    ids, w = O.route(z32.astype(np.float64), K)
+    f = O.moe_forward(inp["x"], ids, w, inp["w_gate"], inp["w_up"], inp["w_down"], dtype="bf16", act=act)
+    assert_close("out", to_np(outs[1].out), f["out"])

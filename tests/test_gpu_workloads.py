@@ -1,7 +1,7 @@
 """GPU parity at full workload sizes -- the five evaluation workloads and
 MoEBlaze's four printed shapes with plain SiLU experts -- in the launch
 configuration the benchmark times (router on the GPU, the five entry points in
-order, H-only saving).
+order, H-only saving, nothing saved by a forward-only workload).
 
 The oracle evaluates sampled outputs one by one: 32 random tokens (out, dx,
 dS, saved a/b/y), the weight gradients of the smallest and the largest
@@ -45,7 +45,7 @@ def test_workload_full_size(idx):
     inp = synth.make_inputs(wl, tensors=tensors)
     dev = {k: (Lyr.to_device(inp[k], dt) if inp[k] is not None else None) for k in tensors}
     bias = torch.from_numpy(inp["bias"]).cuda() if inp["bias"] is not None else None
-    buf = Lyr.MoEBuffers(T, d, E, K, h, dt, backward=wl.backward, act=wl.act, saved=SAVED)
+    buf = Lyr.MoEBuffers(T, d, E, K, h, dt, backward=wl.backward, act=wl.act, saved=SAVED, save=wl.backward)
 
     def run():
         Lyr.forward(buf, dev["x"], dev["wg"], bias, dev["w_gate"], dev["w_up"], dev["w_down"])
@@ -99,10 +99,13 @@ def test_workload_full_size(idx):
                       act=wl.act)
     assert_close("out[sample]", to_np(buf.out[torch.from_numpy(sub).cuda()]), f["out"])
     pos = to_np(buf.tim).reshape(T, K)[sub]
-    hab = to_np(buf.h_ab[torch.from_numpy(pos.reshape(-1)).cuda()]).reshape(len(sub), K, -1)
-    assert_close("a[sample]", hab[..., :h], f["a_s"])
-    if gated:
-        assert_close("b[sample]", hab[..., h:], f["b_s"])
+    yv = to_np(buf.y_swi[torch.from_numpy(pos.reshape(-1)).cuda()]).reshape(len(sub), K, -1)
+    assert_close("y[sample]", yv, f["y_s"])
+    if buf.h_ab is not None:   # a forward-only workload saves nothing
+        hab = to_np(buf.h_ab[torch.from_numpy(pos.reshape(-1)).cuda()]).reshape(len(sub), K, -1)
+        assert_close("a[sample]", hab[..., :h], f["a_s"])
+        if gated:
+            assert_close("b[sample]", hab[..., h:], f["b_s"])
     if not wl.backward:
         return
     b = O.moe_backward(inp["dy"][sub], inp["x"][sub], inp["wg"], ids_ref[sub], w_ref[sub], inp["w_gate"],
