@@ -56,6 +56,30 @@ MOE_DEV void st16(bf16_t* p, const float (&v)[8]) {
   *(u32x4_t*)p = q;
 }
 MOE_DEV void st16(float* p, const float (&v)[4]) { *(f32x4_t*)p = f32x4_t{v[0], v[1], v[2], v[3]}; }
+// The same with the non-temporal cache policy, for data a kernel streams
+// through once (read once here, or written here and read by a later kernel).
+MOE_DEV void ld16nt(const bf16_t* p, float (&v)[8]) {
+  const u32x4_t q = __builtin_nontemporal_load((const u32x4_t*)p);
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    v[2 * i] = bf16_to_f32(q[i] & 0xffffu);
+    v[2 * i + 1] = bf16_to_f32(q[i] >> 16);
+  }
+}
+MOE_DEV void ld16nt(const float* p, float (&v)[4]) {
+  const f32x4_t q = __builtin_nontemporal_load((const f32x4_t*)p);
+#pragma unroll
+  for (int i = 0; i < 4; ++i) v[i] = q[i];
+}
+MOE_DEV void st16nt(bf16_t* p, const float (&v)[8]) {
+  u32x4_t q;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) q[i] = f32_to_bf16(v[2 * i]) | (f32_to_bf16(v[2 * i + 1]) << 16);
+  __builtin_nontemporal_store(q, (u32x4_t*)p);
+}
+MOE_DEV void st16nt(float* p, const float (&v)[4]) {
+  __builtin_nontemporal_store(f32x4_t{v[0], v[1], v[2], v[3]}, (f32x4_t*)p);
+}
 
 MOE_DEV float sigmoidf_(float u) { return 1.0f / (1.0f + expf(-u)); }
 

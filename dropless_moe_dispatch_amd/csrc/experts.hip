@@ -835,7 +835,8 @@ __global__ __launch_bounds__(C::NT, C::WAVES_PER_EU) void dh_kernel(
   {
     // Park dA' (fp32) in LDS, 128 rows at a time; then each thread takes
     // 16-byte row chunks, so a, b, y are read and dA, dB (and A') written as
-    // whole chunks.  dS of a row is reduced over the row's chunk-owning lanes
+    // whole chunks (a, b and the outputs with the non-temporal policy: each
+    // is touched once here; measured 1-3% faster).  dS of a row is reduced over the row's chunk-owning lanes
     // in a fixed order.
     constexpr int PR = 128, PITCH = C::BN + 8;
     static_assert(PR * PITCH * 4 <= C::LDS_BYTES, "the parked rows fit the LDS stages");
@@ -862,10 +863,10 @@ __global__ __launch_bounds__(C::NT, C::WAVES_PER_EU) void dh_kernel(
           const float w = w_pos[p];
           const float* dapr = s_c + rr * PITCH + cc * VPC;
           float a[VPC], y[VPC], da[VPC];
-          ld16(h_ab + (size_t)p * hw + j0, a);
+          ld16nt(h_ab + (size_t)p * hw + j0, a);
           if (act == ACT_SWIGLU) {
             float b[VPC], db[VPC];
-            ld16(h_ab + (size_t)p * hw + h + j0, b);
+            ld16nt(h_ab + (size_t)p * hw + h + j0, b);
             if constexpr (!HONLY) ld16(y_swi + (size_t)p * h + j0, y);
 #pragma unroll
             for (int v = 0; v < VPC; ++v) {
@@ -876,7 +877,7 @@ __global__ __launch_bounds__(C::NT, C::WAVES_PER_EU) void dh_kernel(
               db[v] = dy * a[v] * sg;
               dsum += dapr[v] * y[v];
             }
-            st16(dh + (size_t)p * hw + h + j0, db);
+            st16nt(dh + (size_t)p * hw + h + j0, db);
           } else {  // plain expert: dA = dy * sigma'(a), from the saved pre-activation
             if constexpr (!HONLY) ld16(y_swi + (size_t)p * h + j0, y);
 #pragma unroll
@@ -886,12 +887,12 @@ __global__ __launch_bounds__(C::NT, C::WAVES_PER_EU) void dh_kernel(
               dsum += dapr[v] * y[v];
             }
           }
-          st16(dh + (size_t)p * hw + j0, da);
+          st16nt(dh + (size_t)p * hw + j0, da);
           if constexpr (HONLY) {
             float ap[VPC];
 #pragma unroll
             for (int v = 0; v < VPC; ++v) ap[v] = w * y[v];
-            st16(a_prime + (size_t)p * h + j0, ap);
+            st16nt(a_prime + (size_t)p * h + j0, ap);
           }
         }
 #pragma unroll
