@@ -51,21 +51,31 @@ MOE_DEV void park_rows(const f32x16_t (&acc)[C::FM][C::FN], float* s_c, int r0, 
 template <typename T> MOE_DEV float ld_f(const T* p) { return ElemT<T>::load(p); }
 template <typename T> MOE_DEV void st_f(T* p, float v) { ElemT<T>::store(p, v); }
 
-// The host picks a tile per kernel and shape (128 x 128 or 256 x 256, see
-// XCfg below); the folds always use 128 x 128.
+// The host picks a tile per kernel and shape (see XCfg below).
 template <typename TIN, int B> using GCfg = Cfg<TIN, B, B, 2, 2>;
 // Operands whose source is k-major (weights read as [k][n], activations
 // reduced over rows) are staged k-major and read with the LDS transpose in
 // bf16; fp32 operands are transposed in registers (KRowLoader).
 template <typename TIN> constexpr bool kTr = sizeof(TIN) == 2;
-// Tile configurations.  128 x 128: four waves of 64 x 64, two workgroups per
-// CU.  256 x 256 in bf16: eight waves of 64 x 128, one workgroup per CU and
-// two waves per SIMD (half the operand traffic per MFMA of the small tile,
-// with a second wave per SIMD to cover latencies); in fp32 four waves of
-// 128 x 128.  AK / BK: operand staged k-major (bf16 only).
-template <typename TIN, int B, bool PAIRED, bool AK, bool BK>
-using XCfg = Cfg<TIN, B, B, (B == TILE_L && kTr<TIN>) ? 4 : 2, 2, PAIRED, AK && kTr<TIN>, BK && kTr<TIN>>;
-template <typename TIN, int B, bool AK, bool BK> using KCfg = XCfg<TIN, B, false, AK, BK>;
+// Tile configurations (BM rows x BN columns).  128 x 128: four waves of
+// 64 x 64, two workgroups per CU.  128 x 256 (bf16): eight waves of 64 x 64,
+// one workgroup per CU and two waves per SIMD, a quarter less operand traffic
+// per MFMA than 128 x 128 with the same row padding.  256 x 256 in bf16:
+// eight waves of 64 x 128, one workgroup per CU and two waves per SIMD (half
+// the operand traffic per MFMA of the small tile, with a second wave per SIMD
+// to cover latencies); in fp32 four waves of 128 x 128.  AK / BK: operand
+// staged k-major (bf16 only).
+template <typename TIN, int BM, int BN, bool PAIRED, bool AK, bool BK>
+using XCfg = Cfg<TIN, BM, BN, (BM == TILE_L && kTr<TIN>) ? 4 : 2, (BM == TILE_S && BN == TILE_L) ? 4 : 2, PAIRED,
+                 AK && kTr<TIN>, BK && kTr<TIN>>;
+template <typename TIN, int BM, int BN, bool AK, bool BK> using KCfg = XCfg<TIN, BM, BN, false, AK, BK>;
+// LDS of an expert kernel: its two operand stages, or its parked epilogue
+// rows where those take more (the 128 x 256 tile parks two 128 x 128 fp32
+// halves plus the fold's per-row token, weight and rank).
+template <class C> constexpr int smem_bytes() {
+  constexpr int park = C::BN > 128 && C::BM == 128 ? 2 * 128 * FOLD_LD * 4 + 3 * 128 * 4 : 0;
+  return C::LDS_BYTES > park ? C::LDS_BYTES : park;
+}
 template <class C, bool KM, int ROWS, class Src, bool SCALED>
 struct KSrcSel {
   static_assert(KM || C::NT == NTHREADS, "the register transpose assumes four waves");
@@ -99,6 +109,16 @@ static bool pick_large(bool auto_choice) {
   const int f = forced_tile();
   return f ? f == TILE_L : auto_choice;
 }
+// 128 x 256 (bf16) where the 256 x 256 tile is not taken.  MOE_DISPATCH_MID=0|1
+// forces it off or on (tuning aid; MOE_DISPATCH_TILE takes precedence).
+static bool pick_mid(const Shape& s, bool auto_choice) {
+  static int v = [] {
+    const char* e = getenv("MOE_DISPATCH_MID");
+    return e ? (atoi(e) ? 1 : 0) : -1;
+  }();
+  if (!s.bf16 || forced_tile()) return false;
+  return v >= 0 ? v == 1 : auto_choice;
+}
 // The folds can run the 256 x 256 tile (eight waves, parked and folded in two
 // 128-row passes) in bf16 when d is a multiple of 256.  It pays where each
 // tile's reduction (kdim) is long next to its two-pass fold: measured on
@@ -106,6 +126,15 @@ static bool pick_large(bool auto_choice) {
 // slower at d = 4096-6144 with a reduction of 1536-4096.
 static bool wide_fold(const Shape& s, int kdim) {
   return s.bf16 && s.d % TILE_L == 0 && pick_large(s.d >= 4096 && kdim >= 8192);
+}
+// Otherwise the folds take the 128 x 256 tile where d is a multiple of 256
+// (it folds its two 128-column halves against their own turn columns).
+// Measured on MI355X against 128 x 128: down-combine 1-6% and dX fold 0-3%
+// faster on the fine-grained and large-d workloads and MoEBlaze's conf3 and
+// conf4 (dX fold 0.5-1.7% slower on the skewed workload and conf3).  The
+// gate/up and dH kernels measured 2-14% slower on it and keep 128 x 128.
+static bool mid_fold(const Shape& s, int kdim) {
+  return !wide_fold(s, kdim) && s.d % TILE_L == 0 && pick_mid(s, true);
 }
 
 // ===========================================================================
@@ -117,7 +146,7 @@ __global__ __launch_bounds__(C::NT, C::WAVES_PER_EU) void gate_up_kernel(
     const int32_t* __restrict__ mb_off, const typename C::T* __restrict__ w_gate,
     const typename C::T* __restrict__ w_up, typename C::T* __restrict__ h_ab, typename C::T* __restrict__ y_swi,
     int T, int d, int E, int h, int nbn, int nblk, int grp) {
-  __shared__ __attribute__((aligned(16))) char smem[C::LDS_BYTES];
+  __shared__ __attribute__((aligned(16))) char smem[smem_bytes<C>()];
   using TIN = typename C::T;
   constexpr int HB = C::BN / 2;     // gate (= up) columns per tile
   constexpr int HF = C::FN / 2;     // gate fragments per wave
@@ -150,7 +179,7 @@ __global__ __launch_bounds__(C::NT, C::WAVES_PER_EU) void gate_up_kernel(
     // park the tile (gate columns in [0, HB), up columns in [HB, BN)) in LDS,
     // 128 rows at a time, then write a, b and y as whole 16-byte row chunks
     constexpr int PR = 128, PITCH = C::BN + 8;
-    static_assert(PR * PITCH * 4 <= C::LDS_BYTES, "the parked rows fit the LDS stages");
+    static_assert(PR * PITCH * 4 <= smem_bytes<C>(), "the parked rows fit the LDS");
     float* s_c = (float*)smem;
     constexpr int VPC = 16 / sizeof(TIN);
     constexpr int CPR = HB / VPC;           // output chunks per row (per half)
@@ -184,16 +213,16 @@ __global__ __launch_bounds__(C::NT, C::WAVES_PER_EU) void gate_up_kernel(
   }
 }
 
-template <typename TIN, int B>
+template <typename TIN, int BM, int BN>
 static hipError_t gate_up_t(const Shape& s, const void* x, const int32_t* offsets, const int32_t* eti,
                             const void* w_gate, const void* w_up, void* h_ab, void* y_swi, const ExpertWs& ws,
                             hipStream_t st) {
-  using C = XCfg<TIN, B, true, false, false>;
+  using C = XCfg<TIN, BM, BN, true, false, false>;
   const int nbn = col_blocks(s.h, C::BN / 2);
-  long long nblk = max_row_blocks(s, B) * nbn;
+  long long nblk = max_row_blocks(s, BM) * nbn;
   nblk = (nblk + 7) / 8 * 8;
   gate_up_kernel<C><<<dim3((unsigned)nblk), dim3(C::NT), 0, st>>>(
-      (const TIN*)x, offsets, eti, ws.tile_map(B), (const TIN*)w_gate, (const TIN*)w_up, (TIN*)h_ab, (TIN*)y_swi,
+      (const TIN*)x, offsets, eti, ws.tile_map(BM), (const TIN*)w_gate, (const TIN*)w_up, (TIN*)h_ab, (TIN*)y_swi,
       s.T, s.d, s.E, s.h, nbn, (int)nblk, tile_group_rows());
   return hipGetLastError();
 }
@@ -206,7 +235,7 @@ __global__ __launch_bounds__(C::NT, C::WAVES_PER_EU) void up_act_kernel(
     const typename C::T* __restrict__ x, const int32_t* __restrict__ offsets, const int32_t* __restrict__ eti,
     const int32_t* __restrict__ mb_off, const typename C::T* __restrict__ w1, typename C::T* __restrict__ h_a,
     typename C::T* __restrict__ y_swi, int T, int d, int E, int h, int act, int nbn, int nblk, int grp) {
-  __shared__ __attribute__((aligned(16))) char smem[C::LDS_BYTES];
+  __shared__ __attribute__((aligned(16))) char smem[smem_bytes<C>()];
   using TIN = typename C::T;
   int g, nb;
   if (!grouped_tile(xcd_swizzle(blockIdx.x, nblk), mb_off[E], nbn, grp, g, nb)) return;
@@ -234,7 +263,7 @@ __global__ __launch_bounds__(C::NT, C::WAVES_PER_EU) void up_act_kernel(
   {
     // parked in LDS 128 rows at a time, written as 16-byte row chunks (as in the gated kernel)
     constexpr int PR = 128, PITCH = C::BN + 8;
-    static_assert(PR * PITCH * 4 <= C::LDS_BYTES, "the parked rows fit the LDS stages");
+    static_assert(PR * PITCH * 4 <= smem_bytes<C>(), "the parked rows fit the LDS");
     float* s_c = (float*)smem;
     constexpr int VPC = 16 / sizeof(TIN);
     constexpr int CPR = C::BN / VPC;
@@ -265,15 +294,15 @@ __global__ __launch_bounds__(C::NT, C::WAVES_PER_EU) void up_act_kernel(
   }
 }
 
-template <typename TIN, int B>
+template <typename TIN, int BM, int BN>
 static hipError_t up_act_t(const Shape& s, const void* x, const int32_t* offsets, const int32_t* eti,
                            const void* w1, void* h_a, void* y_swi, const ExpertWs& ws, hipStream_t st) {
-  using C = XCfg<TIN, B, false, false, false>;
+  using C = XCfg<TIN, BM, BN, false, false, false>;
   const int nbn = col_blocks(s.h, C::BN);
-  long long nblk = max_row_blocks(s, B) * nbn;
+  long long nblk = max_row_blocks(s, BM) * nbn;
   nblk = (nblk + 7) / 8 * 8;
   up_act_kernel<C><<<dim3((unsigned)nblk), dim3(C::NT), 0, st>>>(
-      (const TIN*)x, offsets, eti, ws.tile_map(B), (const TIN*)w1, (TIN*)h_a, (TIN*)y_swi, s.T, s.d, s.E, s.h,
+      (const TIN*)x, offsets, eti, ws.tile_map(BM), (const TIN*)w1, (TIN*)h_a, (TIN*)y_swi, s.T, s.d, s.E, s.h,
       s.act, nbn, (int)nblk, tile_group_rows());
   return hipGetLastError();
 }
@@ -285,20 +314,23 @@ hipError_t launch_gate_up(const Shape& s, const void* x, const int32_t* offsets,
   // measured on MI355X: the large tile wins from d = 4096 on (the small one
   // wastes less on partial row tiles for short reductions)
   const bool big = pick_large(s.d >= 4096);
+  const bool mid = !big && pick_mid(s, false);
   hipError_t e;
   if (!s.gated()) {
     if (s.bf16)
-      e = big ? up_act_t<bf16_t, TILE_L>(s, x, offsets, eti, w_gate, h_ab, y_swi, ws, st)
-              : up_act_t<bf16_t, TILE_S>(s, x, offsets, eti, w_gate, h_ab, y_swi, ws, st);
+      e = big   ? up_act_t<bf16_t, TILE_L, TILE_L>(s, x, offsets, eti, w_gate, h_ab, y_swi, ws, st)
+          : mid ? up_act_t<bf16_t, TILE_S, TILE_L>(s, x, offsets, eti, w_gate, h_ab, y_swi, ws, st)
+                : up_act_t<bf16_t, TILE_S, TILE_S>(s, x, offsets, eti, w_gate, h_ab, y_swi, ws, st);
     else
-      e = big ? up_act_t<float, TILE_L>(s, x, offsets, eti, w_gate, h_ab, y_swi, ws, st)
-              : up_act_t<float, TILE_S>(s, x, offsets, eti, w_gate, h_ab, y_swi, ws, st);
+      e = big ? up_act_t<float, TILE_L, TILE_L>(s, x, offsets, eti, w_gate, h_ab, y_swi, ws, st)
+              : up_act_t<float, TILE_S, TILE_S>(s, x, offsets, eti, w_gate, h_ab, y_swi, ws, st);
   } else if (s.bf16)
-    e = big ? gate_up_t<bf16_t, TILE_L>(s, x, offsets, eti, w_gate, w_up, h_ab, y_swi, ws, st)
-            : gate_up_t<bf16_t, TILE_S>(s, x, offsets, eti, w_gate, w_up, h_ab, y_swi, ws, st);
+    e = big   ? gate_up_t<bf16_t, TILE_L, TILE_L>(s, x, offsets, eti, w_gate, w_up, h_ab, y_swi, ws, st)
+        : mid ? gate_up_t<bf16_t, TILE_S, TILE_L>(s, x, offsets, eti, w_gate, w_up, h_ab, y_swi, ws, st)
+              : gate_up_t<bf16_t, TILE_S, TILE_S>(s, x, offsets, eti, w_gate, w_up, h_ab, y_swi, ws, st);
   else
-    e = big ? gate_up_t<float, TILE_L>(s, x, offsets, eti, w_gate, w_up, h_ab, y_swi, ws, st)
-            : gate_up_t<float, TILE_S>(s, x, offsets, eti, w_gate, w_up, h_ab, y_swi, ws, st);
+    e = big ? gate_up_t<float, TILE_L, TILE_L>(s, x, offsets, eti, w_gate, w_up, h_ab, y_swi, ws, st)
+            : gate_up_t<float, TILE_S, TILE_S>(s, x, offsets, eti, w_gate, w_up, h_ab, y_swi, ws, st);
   timing_mark(st, "gate_up", false);
   return e;
 }
@@ -426,8 +458,8 @@ MOE_DEV void fold_epilogue(const f32x16_t (&acc)[C::FM][C::FN], const RowTile& r
                            int spin_limit, char* smem) {
   const int tid = threadIdx.x;
   const int l = lane_id();
-  if constexpr (C::BM == 128) {
-    static_assert(C::BN == 128 && C::NT == NTHREADS, "the fold parks a 128 x 128 tile, four waves");
+  if constexpr (C::BM == 128 && C::BN == 128) {
+    static_assert(C::NT == NTHREADS, "the fold parks a 128 x 128 tile, four waves");
     static_assert(C::BM * FOLD_LD * 4 + 3 * C::BM * 4 <= C::LDS_BYTES, "parked tile fits the LDS stages");
     float* s_c = (float*)smem;
     int* s_t = (int*)(smem + C::BM * FOLD_LD * 4);
@@ -452,6 +484,39 @@ MOE_DEV void fold_epilogue(const f32x16_t (&acc)[C::FM][C::FN], const RowTile& r
     __syncthreads();
     fold_rows<INIT_FIRST>(s_c, s_t, s_w, s_rank, rows, tid >> 6, nb, NB, K, d, turn, accws, out, counters,
                           spin_limit);
+  } else if constexpr (C::BM == 128) {
+    // 128 x 256 tile, eight waves of 64 x 64: both 128-column halves are
+    // parked at once; waves 0-3 then fold half 0 (column block 2 nb of the
+    // 128-wide turn grid) and waves 4-7 half 1 (column block 2 nb + 1).
+    static_assert(C::BN == 256 && C::NT == 512 && C::WM == 2 && C::WN == 4, "eight-wave 128 x 256 tile");
+    static_assert(2 * 128 * FOLD_LD * 4 + 3 * 128 * 4 <= smem_bytes<C>(), "two parked halves fit the LDS");
+    float* s_c0 = (float*)smem;
+    float* s_c1 = s_c0 + 128 * FOLD_LD;
+    int* s_t = (int*)(s_c1 + 128 * FOLD_LD);
+    float* s_w = (float*)(s_t + 128);
+    int* s_rank = (int*)(s_w + 128);
+    const int wave = tid >> 6, group = wave >> 2;
+    const int rows = rt.r1 - rt.r0;
+    __syncthreads();  // the LDS stages are reused below
+    for (int i = tid; i < 128; i += C::NT) {  // rows past the tile read token 0 and are never stored
+      const int p = rt.r0 + i;
+      const bool in = i < rows;
+      s_t[i] = in ? eti[p] : 0;
+      s_w[i] = in && w_pos ? w_pos[p] : 1.0f;
+      s_rank[i] = in ? rank_pos[p] : 0;
+    }
+    float* s_c = (wn >> 1) ? s_c1 : s_c0;
+#pragma unroll
+    for (int fm = 0; fm < C::FM; ++fm)
+#pragma unroll
+      for (int fn = 0; fn < C::FN; ++fn)
+#pragma unroll
+        for (int r = 0; r < 16; ++r)
+          s_c[(C::a_row0(wm, fm) + frag_row(r, l)) * FOLD_LD + (wn & 1) * 64 + fn * 32 + frag_col(l)] =
+              acc[fm][fn][r];
+    __syncthreads();
+    fold_rows<INIT_FIRST>(group ? s_c1 : s_c0, s_t, s_w, s_rank, rows, wave & 3, 2 * nb + group, 2 * NB, K, d, turn,
+                          accws, out, counters, spin_limit);
   } else {
     // 256 x 256 tile, eight waves of 64 x 128: two passes of 128 rows.  In
     // pass hp the waves holding rows hp*128 .. +127 park both 128-column
@@ -544,7 +609,7 @@ __global__ __launch_bounds__(C::NT, C::WAVES_PER_EU) void down_combine_kernel(
     const int32_t* __restrict__ offsets, const int32_t* __restrict__ eti, const int32_t* __restrict__ mb_off,
     const float* __restrict__ w_pos, const int32_t* __restrict__ rank_pos, int32_t* turn, float* accws,
     typename C::T* __restrict__ out, int32_t* counters, int d, int E, int K, int h, int spin_limit) {
-  __shared__ __attribute__((aligned(16))) char smem[C::LDS_BYTES];
+  __shared__ __attribute__((aligned(16))) char smem[smem_bytes<C>()];
   using TIN = typename C::T;
   const int NB = col_blocks(d, C::BN);
   int g, nb;
@@ -574,13 +639,13 @@ __global__ __launch_bounds__(C::NT, C::WAVES_PER_EU) void down_combine_kernel(
                          spin_limit, smem);
 }
 
-template <typename TIN, int B>
+template <typename TIN, int BM, int BN>
 static hipError_t down_combine_t(const Shape& s, const void* y_swi, const void* w_down, const int32_t* offsets,
                                  const int32_t* eti, void* out, const ExpertWs& ws, int spin_limit, hipStream_t st) {
-  using C = XCfg<TIN, B, false, false, false>;
-  const long long nblk = max_row_blocks(s, B) * col_blocks(s.d, B);
+  using C = XCfg<TIN, BM, BN, false, false, false>;
+  const long long nblk = max_row_blocks(s, BM) * col_blocks(s.d, BN);
   down_combine_kernel<C><<<dim3((unsigned)nblk), dim3(C::NT), 0, st>>>(
-      (const TIN*)y_swi, (const TIN*)w_down, offsets, eti, ws.tile_map(B), ws.w_pos, ws.rank_pos, ws.turn, ws.acc,
+      (const TIN*)y_swi, (const TIN*)w_down, offsets, eti, ws.tile_map(BM), ws.w_pos, ws.rank_pos, ws.turn, ws.acc,
       (TIN*)out, ws.counters, s.d, s.E, s.K, s.h, spin_limit);
   return hipGetLastError();
 }
@@ -589,9 +654,10 @@ hipError_t launch_down_combine(const Shape& s, const void* y_swi, const void* w_
                                const int32_t* eti, void* out, const ExpertWs& ws, int spin_limit, hipStream_t st) {
   timing_mark(st, "down_combine", true);
   const hipError_t e =
-      !s.bf16        ? down_combine_t<float, TILE_S>(s, y_swi, w_down, offsets, eti, out, ws, spin_limit, st)
-      : wide_fold(s, s.h) ? down_combine_t<bf16_t, TILE_L>(s, y_swi, w_down, offsets, eti, out, ws, spin_limit, st)
-                     : down_combine_t<bf16_t, TILE_S>(s, y_swi, w_down, offsets, eti, out, ws, spin_limit, st);
+      !s.bf16               ? down_combine_t<float, TILE_S, TILE_S>(s, y_swi, w_down, offsets, eti, out, ws, spin_limit, st)
+      : wide_fold(s, s.h) ? down_combine_t<bf16_t, TILE_L, TILE_L>(s, y_swi, w_down, offsets, eti, out, ws, spin_limit, st)
+      : mid_fold(s, s.h)  ? down_combine_t<bf16_t, TILE_S, TILE_L>(s, y_swi, w_down, offsets, eti, out, ws, spin_limit, st)
+                          : down_combine_t<bf16_t, TILE_S, TILE_S>(s, y_swi, w_down, offsets, eti, out, ws, spin_limit, st);
   timing_mark(st, "down_combine", false);
   return e;
 }
@@ -610,7 +676,7 @@ __global__ __launch_bounds__(C::NT, C::WAVES_PER_EU) void down_staged_kernel(
     const int32_t* __restrict__ offsets, const int32_t* __restrict__ mb_off, typename C::T* __restrict__ ystage,
     int d, int E, int h, int nbn, int nblk, int grp) {
   static_assert(C::BM == 128 && C::BN == 128 && C::NT == NTHREADS, "128 x 128 tile, four waves");
-  __shared__ __attribute__((aligned(16))) char smem[C::LDS_BYTES];
+  __shared__ __attribute__((aligned(16))) char smem[smem_bytes<C>()];
   using TIN = typename C::T;
   int g, nb;
   if (!grouped_tile(xcd_swizzle(blockIdx.x, nblk), mb_off[E], nbn, grp, g, nb)) return;
@@ -809,7 +875,7 @@ __global__ __launch_bounds__(C::NT, C::WAVES_PER_EU) void dh_kernel(
     const int32_t* __restrict__ offsets, const int32_t* __restrict__ eti, const int32_t* __restrict__ mb_off,
     const float* __restrict__ w_pos, typename C::T* __restrict__ dh, float* __restrict__ ds_part,
     typename C::T* __restrict__ a_prime, int T, int d, int E, int h, int act, int nbn, int nblk, int grp) {
-  __shared__ __attribute__((aligned(16))) char smem[C::LDS_BYTES];
+  __shared__ __attribute__((aligned(16))) char smem[smem_bytes<C>()];
   using TIN = typename C::T;
   int g, nb;
   if (!grouped_tile(xcd_swizzle(blockIdx.x, nblk), mb_off[E], nbn, grp, g, nb)) return;
@@ -839,7 +905,7 @@ __global__ __launch_bounds__(C::NT, C::WAVES_PER_EU) void dh_kernel(
     // is touched once here; measured 1-3% faster).  dS of a row is reduced over the row's chunk-owning lanes
     // in a fixed order.
     constexpr int PR = 128, PITCH = C::BN + 8;
-    static_assert(PR * PITCH * 4 <= C::LDS_BYTES, "the parked rows fit the LDS stages");
+    static_assert(PR * PITCH * 4 <= smem_bytes<C>(), "the parked rows fit the LDS");
     float* s_c = (float*)smem;
     constexpr int VPC = 16 / sizeof(TIN);   // values per chunk
     constexpr int CPR = C::BN / VPC;        // chunks per row
@@ -1239,7 +1305,7 @@ __global__ __launch_bounds__(C::NT, C::WAVES_PER_EU) void dw_down_kernel(
     const typename C::T* __restrict__ dout, const typename C::T* __restrict__ y_swi,
     const int32_t* __restrict__ offsets, const int32_t* __restrict__ eti, const float* __restrict__ w_pos,
     float* __restrict__ dw_down, float* __restrict__ part, int T, int d, int h) {
-  __shared__ __attribute__((aligned(16))) char smem[C::LDS_BYTES];
+  __shared__ __attribute__((aligned(16))) char smem[smem_bytes<C>()];
   using TIN = typename C::T;
   const int nnb = col_blocks(h, C::BN);
   const int e = blockIdx.y;
@@ -1287,7 +1353,7 @@ __global__ __launch_bounds__(C::NT, C::WAVES_PER_EU) void dw_gate_up_kernel(
     const typename C::T* __restrict__ dh, const typename C::T* __restrict__ x, const int32_t* __restrict__ offsets,
     const int32_t* __restrict__ eti, float* __restrict__ dw_gate, float* __restrict__ dw_up, float* __restrict__ part,
     int T, int d, int h, int hw) {
-  __shared__ __attribute__((aligned(16))) char smem[C::LDS_BYTES];
+  __shared__ __attribute__((aligned(16))) char smem[smem_bytes<C>()];
   using TIN = typename C::T;
   const int nnb = col_blocks(d, C::BN);
   const int e = blockIdx.y;
@@ -1337,7 +1403,7 @@ __global__ __launch_bounds__(C::NT, C::WAVES_PER_EU) void dx_fold_kernel(
     const typename C::T* __restrict__ w_up, const int32_t* __restrict__ offsets, const int32_t* __restrict__ eti,
     const int32_t* __restrict__ mb_off, const int32_t* __restrict__ rank_pos, int32_t* turn, float* accws,
     typename C::T* __restrict__ dx, int32_t* counters, int d, int E, int K, int h, int hw, int spin_limit) {
-  __shared__ __attribute__((aligned(16))) char smem[C::LDS_BYTES];
+  __shared__ __attribute__((aligned(16))) char smem[smem_bytes<C>()];
   using TIN = typename C::T;
   const int NB = col_blocks(d, C::BN);
   int g, nb;
@@ -1367,25 +1433,25 @@ __global__ __launch_bounds__(C::NT, C::WAVES_PER_EU) void dx_fold_kernel(
                           spin_limit, smem);
 }
 
-template <typename TIN, int B, bool HONLY>
+template <typename TIN, int BM, int BN, bool HONLY>
 static void launch_dh(const Shape& s, const void* dout, const void* w_down, const void* h_ab, const void* y_swi,
                       const int32_t* offsets, const int32_t* eti, const ExpertWs& ws, hipStream_t st) {
-  using C = KCfg<TIN, B, false, true>;
-  const int nbn = col_blocks(s.h, B);
-  const long long nblk = (max_row_blocks(s, B) * nbn + 7) / 8 * 8;
+  using C = KCfg<TIN, BM, BN, false, true>;
+  const int nbn = col_blocks(s.h, BN);
+  const long long nblk = (max_row_blocks(s, BM) * nbn + 7) / 8 * 8;
   dh_kernel<C, HONLY><<<dim3((unsigned)nblk), dim3(C::NT), 0, st>>>(
-      (const TIN*)dout, (const TIN*)w_down, (const TIN*)h_ab, (const TIN*)y_swi, offsets, eti, ws.tile_map(B),
+      (const TIN*)dout, (const TIN*)w_down, (const TIN*)h_ab, (const TIN*)y_swi, offsets, eti, ws.tile_map(BM),
       ws.w_pos, (TIN*)ws.dh, ws.ds_part, (TIN*)ws.a_prime, s.T, s.d, s.E, s.h, s.act, nbn, (int)nblk,
       tile_group_rows());
 }
 
-template <typename TIN, int B>
+template <typename TIN, int BM, int BN>
 static void launch_dx_fold(const Shape& s, const void* w_gate, const void* w_up, const int32_t* offsets,
                            const int32_t* eti, void* dx, const ExpertWs& ws, int spin_limit, hipStream_t st) {
-  using C = KCfg<TIN, B, false, true>;
-  const long long nblk = max_row_blocks(s, B) * col_blocks(s.d, B);
+  using C = KCfg<TIN, BM, BN, false, true>;
+  const long long nblk = max_row_blocks(s, BM) * col_blocks(s.d, BN);
   dx_fold_kernel<C><<<dim3((unsigned)nblk), dim3(C::NT), 0, st>>>(
-      (const TIN*)ws.dh, (const TIN*)w_gate, (const TIN*)w_up, offsets, eti, ws.tile_map(B), ws.rank_pos, ws.turn,
+      (const TIN*)ws.dh, (const TIN*)w_gate, (const TIN*)w_up, offsets, eti, ws.tile_map(BM), ws.rank_pos, ws.turn,
       ws.acc, (TIN*)dx, ws.counters, s.d, s.E, s.K, s.h, s.hw(), spin_limit);
 }
 
@@ -1395,21 +1461,27 @@ static hipError_t backward_t(const Shape& s, const void* dout, const void* x, co
                              const int32_t* offsets, const int32_t* eti, const int32_t* tim, const void* h_ab,
                              const void* y_swi, void* dx, float* dwg, float* dw_gate, float* dw_up,
                              float* dw_down, float* ds, const ExpertWs& ws, int spin_limit, hipStream_t st) {
-  using CL = KCfg<TIN, TILE_L, true, true>;
+  using CL = KCfg<TIN, TILE_L, TILE_L, true, true>;
   // dH on the 256 x 256 tile measured no faster on MI355X (4.23 vs 4.21 ms at
   // d = 4096, h = 14336; 0.88 vs 0.75 ms at d = 2048, h = 1536): the small
   // tile is used unless the large one is forced.
   const bool dh_big = forced_tile() == TILE_L;
-  const int nbh = col_blocks(s.h, dh_big ? TILE_L : TILE_S);
+  const bool dh_mid = pick_mid(s, false);
+  const int nbh = col_blocks(s.h, dh_big || dh_mid ? TILE_L : TILE_S);
   hipError_t err;
   timing_mark(st, "dh", true);
   const bool honly = y_swi == nullptr;
   if (dh_big) {
-    if (honly) launch_dh<TIN, TILE_L, true>(s, dout, w_down, h_ab, y_swi, offsets, eti, ws, st);
-    else launch_dh<TIN, TILE_L, false>(s, dout, w_down, h_ab, y_swi, offsets, eti, ws, st);
+    if (honly) launch_dh<TIN, TILE_L, TILE_L, true>(s, dout, w_down, h_ab, y_swi, offsets, eti, ws, st);
+    else launch_dh<TIN, TILE_L, TILE_L, false>(s, dout, w_down, h_ab, y_swi, offsets, eti, ws, st);
+  } else if (dh_mid) {
+    if constexpr (sizeof(TIN) == 2) {
+      if (honly) launch_dh<TIN, TILE_S, TILE_L, true>(s, dout, w_down, h_ab, y_swi, offsets, eti, ws, st);
+      else launch_dh<TIN, TILE_S, TILE_L, false>(s, dout, w_down, h_ab, y_swi, offsets, eti, ws, st);
+    }
   } else {
-    if (honly) launch_dh<TIN, TILE_S, true>(s, dout, w_down, h_ab, y_swi, offsets, eti, ws, st);
-    else launch_dh<TIN, TILE_S, false>(s, dout, w_down, h_ab, y_swi, offsets, eti, ws, st);
+    if (honly) launch_dh<TIN, TILE_S, TILE_S, true>(s, dout, w_down, h_ab, y_swi, offsets, eti, ws, st);
+    else launch_dh<TIN, TILE_S, TILE_S, false>(s, dout, w_down, h_ab, y_swi, offsets, eti, ws, st);
   }
   timing_mark(st, "dh", false);
   if ((err = hipGetLastError()) != hipSuccess) return err;
@@ -1483,10 +1555,11 @@ static hipError_t backward_t(const Shape& s, const void* dout, const void* x, co
   // weight slot is never read
   const void* w2 = s.gated() ? w_up : w_gate;
   if constexpr (sizeof(TIN) == 2) {
-    if (wide_fold(s, s.hw())) launch_dx_fold<TIN, TILE_L>(s, w_gate, w2, offsets, eti, dx, ws, spin_limit, st);
-    else launch_dx_fold<TIN, TILE_S>(s, w_gate, w2, offsets, eti, dx, ws, spin_limit, st);
+    if (wide_fold(s, s.hw())) launch_dx_fold<TIN, TILE_L, TILE_L>(s, w_gate, w2, offsets, eti, dx, ws, spin_limit, st);
+    else if (mid_fold(s, s.hw())) launch_dx_fold<TIN, TILE_S, TILE_L>(s, w_gate, w2, offsets, eti, dx, ws, spin_limit, st);
+    else launch_dx_fold<TIN, TILE_S, TILE_S>(s, w_gate, w2, offsets, eti, dx, ws, spin_limit, st);
   } else {
-    launch_dx_fold<TIN, TILE_S>(s, w_gate, w2, offsets, eti, dx, ws, spin_limit, st);
+    launch_dx_fold<TIN, TILE_S, TILE_S>(s, w_gate, w2, offsets, eti, dx, ws, spin_limit, st);
   }
   timing_mark(st, "dx_fold", false);
   return hipGetLastError();

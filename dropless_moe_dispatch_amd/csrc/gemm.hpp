@@ -3,6 +3,8 @@
 // One workgroup computes a BM x BN fp32 tile of C = A * B^T with
 // v_mfma_f32_32x32x16_bf16 (32x32x2 in fp32).  Tiles:
 //   128 x 128: four waves of 64 x 64, two workgroups per CU;
+//   128 x 256 (bf16): eight waves of 64 x 64, one workgroup per CU, two waves
+//     per SIMD;
 //   256 x 256 (bf16): eight waves of 64 x 128, one workgroup per CU, two waves
 //     per SIMD; in fp32 four waves of 128 x 128.
 // Operands are staged in LDS two k-tiles deep, 128 bytes of k per row per
@@ -11,7 +13,7 @@
 // padded by 64 bytes, MFMA operands formed by the LDS transpose read).
 //
 // Pipeline: two LDS stages, one barrier per k-tile.  Global loads go through
-// registers (two sets on the 128 tile, one on the 256 tile) and are written to
+// registers (two sets on the 128-row tiles, one on the 256 tile) and are written to
 // the free stage between the MFMA k-steps.  Loaders whose rows come through an
 // index (gathered k-rows of the weight-gradient GEMMs) fetch the indices one
 // stage ahead and form the byte offsets only when they load.
@@ -67,13 +69,13 @@ struct Cfg {
   static constexpr int B_BYTES = BKM ? KmGeom<BN>::BYTES : BN * LDS_ROW;
   static constexpr int STAGE = A_BYTES + B_BYTES;
   static constexpr int LDS_BYTES = 2 * STAGE;
-  // workgroup size follows the wave grid: 4 waves, or 8 for a 256 x 256 tile
-  // with 128 x 64 (or 64 x 128) per wave and two waves per SIMD
+  // workgroup size follows the wave grid: 4 waves, or 8 with two waves per
+  // SIMD (a 256 x 256 tile with 64 x 128 per wave, or 128 x 256 with 64 x 64)
   static constexpr int NT = WM * WN * 64;
   static constexpr int WAVES_PER_EU = (BM * BN >= 256 * 256) ? NT / 256 : 2;
   // register sets for staging global loads (the 256 x 256 tile has no room for two)
   static constexpr int NSETS = NSETS_ ? NSETS_ : (BM * BN >= 256 * 256) ? 1 : 2;
-  static_assert(WM * WN == 4 || (WM * WN == 8 && BM * BN >= 256 * 256), "four or eight waves per workgroup");
+  static_assert(WM * WN == 4 || (WM * WN == 8 && BM * BN >= 128 * 256), "four or eight waves per workgroup");
   static_assert(FM >= 1 && FN >= 1 && FM * WM * 32 == BM && FN * WN * 32 == BN, "tile shape");
   static_assert(!PAIRED || (FN % 2 == 0), "paired layout");
 

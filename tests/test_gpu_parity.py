@@ -171,6 +171,9 @@ LAYER_CASES = [
     # the wide (two-pass) fold; more experts than assignments (most empty,
     # E > 128 in the separate top-K); fp32 with eight slots
     ("wide_fold", 200, 4096, 4, 2, 4096, "bf16", None),
+    # d = 1024: the folds on the 128 x 256 tile over four column blocks
+    # (four of the eight fold queues), rows ragged in every expert
+    ("mid_fold", 700, 1024, 16, 4, 256, "bf16", None),
     ("many_empty", 50, 128, 256, 2, 128, "bf16", None),
     ("f32_k8", 200, 128, 16, 8, 128, "f32", 1.2),
     # the largest E (eight 128-expert blocks in dWg, almost every expert
