@@ -28,14 +28,20 @@ PEAK_HBM_GBS = 8000.0
 METRIC = "MoE layer fwd+bwd tokens/s and TFLOP/s at 1 GPU; % bf16 MFMA peak; peak act MB"
 
 
-def kernel_source_hash():
-    """Hash of the HIP sources; counter data taken with other sources is stale."""
+def kernel_source_hash(csrc=None):
+    """Hash of the HIP sources with their comments and blank lines taken out;
+    counter data taken with other code is stale (a comment edit is not)."""
     import hashlib
+    import re
     h = hashlib.sha256()
-    csrc = os.path.join(ROOT, "dropless_moe_dispatch_amd", "csrc")
+    csrc = csrc or os.path.join(ROOT, "dropless_moe_dispatch_amd", "csrc")
     for f in sorted(os.listdir(csrc)):
         if f.endswith((".hip", ".hpp")):
-            h.update(open(os.path.join(csrc, f), "rb").read())
+            text = open(os.path.join(csrc, f), encoding="utf-8").read()
+            text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+            text = re.sub(r"//[^\n]*", "", text)
+            lines = [ln.rstrip() for ln in text.splitlines() if ln.strip()]
+            h.update(f.encode() + b"\0" + "\n".join(lines).encode())
     return h.hexdigest()[:16]
 
 

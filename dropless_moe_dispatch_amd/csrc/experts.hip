@@ -129,10 +129,11 @@ static bool wide_fold(const Shape& s, int kdim) {
 }
 // Otherwise the folds take the 128 x 256 tile where d is a multiple of 256
 // (it folds its two 128-column halves against their own turn columns).
-// Measured on MI355X against 128 x 128: down-combine 1-6% and dX fold 0-3%
-// faster on the fine-grained and large-d workloads and MoEBlaze's conf3 and
-// conf4 (dX fold 0.5-1.7% slower on the skewed workload and conf3).  The
-// gate/up and dH kernels measured 2-14% slower on it and keep 128 x 128.
+// Measured on MI355X against 128 x 128: down-combine 3-6% faster on the
+// fine-grained and large-d workloads and MoEBlaze's conf3 and conf4 (level on
+// the skewed one); dX fold 1.5-3% faster on fine-grained, large-d and conf4,
+// 0.5-1.7% slower on skewed and conf3.  The gate/up and dH kernels measured
+// 2-14% slower on it and keep 128 x 128.
 static bool mid_fold(const Shape& s, int kdim) {
   return !wide_fold(s, kdim) && s.d % TILE_L == 0 && pick_mid(s, true);
 }
