@@ -71,6 +71,22 @@ MOE_DEV void ld16nt(const float* p, float (&v)[4]) {
 #pragma unroll
   for (int i = 0; i < 4; ++i) v[i] = q[i];
 }
+// 16 bytes as they are (plain or non-temporal), unpacked to floats where
+// they are used: a batch of such loads is not split by the waits that each
+// unpacking needs.
+MOE_DEV u32x4_t raw16(const void* p) { return *(const u32x4_t*)p; }
+MOE_DEV u32x4_t raw16nt(const void* p) { return __builtin_nontemporal_load((const u32x4_t*)p); }
+MOE_DEV void unpack16(const u32x4_t& q, float (&v)[8]) {  // 8 bf16
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    v[2 * i] = bf16_to_f32(q[i] & 0xffffu);
+    v[2 * i + 1] = bf16_to_f32(q[i] >> 16);
+  }
+}
+MOE_DEV void unpack16(const u32x4_t& q, float (&v)[4]) {  // 4 fp32
+#pragma unroll
+  for (int i = 0; i < 4; ++i) v[i] = __uint_as_float(q[i]);
+}
 MOE_DEV void st16nt(bf16_t* p, const float (&v)[8]) {
   u32x4_t q;
 #pragma unroll

@@ -923,48 +923,70 @@ __global__ __launch_bounds__(C::NT, C::WAVES_PER_EU) void dh_kernel(
       __syncthreads();
       const int left = rt.r1 - rt.r0 - r0;
       const int rows = left < PR ? left : PR;
-      for (int rr = (int)threadIdx.x / CPR; rr < PR; rr += RPI) {
-        float dsum = 0.0f;
-        if (rr < rows && jin) {
-          const int p = rt.r0 + r0 + rr;
-          const float w = w_pos[p];
-          const float* dapr = s_c + rr * PITCH + cc * VPC;
-          float a[VPC], y[VPC], da[VPC];
-          ld16nt(h_ab + (size_t)p * hw + j0, a);
-          if (act == ACT_SWIGLU) {
-            float b[VPC], db[VPC];
-            ld16nt(h_ab + (size_t)p * hw + h + j0, b);
-            if constexpr (!HONLY) ld16(y_swi + (size_t)p * h + j0, y);
+      // RB rows per thread at a time: their loads of a, b (and y) are issued
+      // together, so that the thread waits once per batch rather than per row
+      // (one row on the 256 x 256 tile, whose other half's accumulators are
+      // still live here: more would spill)
+      constexpr int RB = C::BM == 256 ? 1 : 4;
+      static_assert(PR % (RB * RPI) == 0, "whole batches of rows");
+      const bool gated = act == ACT_SWIGLU;
+      for (int rb = (int)threadIdx.x / CPR; rb < PR; rb += RB * RPI) {
+        u32x4_t qa[RB] = {}, qb[RB] = {}, qy[RB] = {};
+        float w[RB] = {};
 #pragma unroll
-            for (int v = 0; v < VPC; ++v) {
-              const float sg = sigmoidf_(a[v]);
-              if constexpr (HONLY) y[v] = a[v] * sg * b[v];
-              const float dy = w * dapr[v];
-              da[v] = dy * b[v] * sg * (1.0f + a[v] * (1.0f - sg));
-              db[v] = dy * a[v] * sg;
-              dsum += dapr[v] * y[v];
-            }
-            st16nt(dh + (size_t)p * hw + h + j0, db);
-          } else {  // plain expert: dA = dy * sigma'(a), from the saved pre-activation
-            if constexpr (!HONLY) ld16(y_swi + (size_t)p * h + j0, y);
-#pragma unroll
-            for (int v = 0; v < VPC; ++v) {
-              if constexpr (HONLY) y[v] = act_fwd(a[v], act);
-              da[v] = w * dapr[v] * act_grad(a[v], act);
-              dsum += dapr[v] * y[v];
-            }
-          }
-          st16nt(dh + (size_t)p * hw + j0, da);
-          if constexpr (HONLY) {
-            float ap[VPC];
-#pragma unroll
-            for (int v = 0; v < VPC; ++v) ap[v] = w * y[v];
-            st16nt(a_prime + (size_t)p * h + j0, ap);
+        for (int i = 0; i < RB; ++i) {
+          const int rr = rb + i * RPI;
+          if (rr < rows && jin) {
+            const int p = rt.r0 + r0 + rr;
+            w[i] = w_pos[p];
+            qa[i] = raw16nt(h_ab + (size_t)p * hw + j0);
+            if (gated) qb[i] = raw16nt(h_ab + (size_t)p * hw + h + j0);
+            if constexpr (!HONLY) qy[i] = raw16(y_swi + (size_t)p * h + j0);
           }
         }
 #pragma unroll
-        for (int off = CPR / 2; off > 0; off >>= 1) dsum += __shfl_xor(dsum, off, CPR);
-        if (cc == 0 && rr < rows) ds_part[(size_t)(rt.r0 + r0 + rr) * nbn + nb] = dsum;
+        for (int i = 0; i < RB; ++i) {
+          const int rr = rb + i * RPI;
+          float dsum = 0.0f;
+          if (rr < rows && jin) {
+            const int p = rt.r0 + r0 + rr;
+            const float* dapr = s_c + rr * PITCH + cc * VPC;
+            float a[VPC], y[VPC], da[VPC];
+            unpack16(qa[i], a);
+            if constexpr (!HONLY) unpack16(qy[i], y);
+            if (gated) {
+              float b[VPC], db[VPC];
+              unpack16(qb[i], b);
+#pragma unroll
+              for (int v = 0; v < VPC; ++v) {
+                const float sg = sigmoidf_(a[v]);
+                if constexpr (HONLY) y[v] = a[v] * sg * b[v];
+                const float dy = w[i] * dapr[v];
+                da[v] = dy * b[v] * sg * (1.0f + a[v] * (1.0f - sg));
+                db[v] = dy * a[v] * sg;
+                dsum += dapr[v] * y[v];
+              }
+              st16nt(dh + (size_t)p * hw + h + j0, db);
+            } else {  // plain expert: dA = dy * sigma'(a), from the saved pre-activation
+#pragma unroll
+              for (int v = 0; v < VPC; ++v) {
+                if constexpr (HONLY) y[v] = act_fwd(a[v], act);
+                da[v] = w[i] * dapr[v] * act_grad(a[v], act);
+                dsum += dapr[v] * y[v];
+              }
+            }
+            st16nt(dh + (size_t)p * hw + j0, da);
+            if constexpr (HONLY) {
+              float ap[VPC];
+#pragma unroll
+              for (int v = 0; v < VPC; ++v) ap[v] = w[i] * y[v];
+              st16nt(a_prime + (size_t)p * h + j0, ap);
+            }
+          }
+#pragma unroll
+          for (int off = CPR / 2; off > 0; off >>= 1) dsum += __shfl_xor(dsum, off, CPR);
+          if (cc == 0 && rr < rows) ds_part[(size_t)(rt.r0 + r0 + rr) * nbn + nb] = dsum;
+        }
       }
     }
   }
