@@ -451,12 +451,33 @@ MOE_DEV void fold_rows(const float* s_c, const int* s_t, const float* s_w, const
   }
 }
 
+// Token, weight and rank of tile row threadIdx.x (< 128) for the fold of a
+// 128-row tile (down-combine fetches them before its main loop, so that their
+// latency hides behind it); rows past the tile get token 0, weight 1 and rank
+// 0 and are never stored.
+struct FoldRowMeta {
+  int t = 0;
+  float w = 1.0f;
+  int rank = 0;
+};
+MOE_DEV FoldRowMeta fold_row_meta(const RowTile& rt, const int32_t* __restrict__ eti, const float* __restrict__ w_pos,
+                                  const int32_t* __restrict__ rank_pos) {
+  FoldRowMeta m;
+  const int p = rt.r0 + (int)threadIdx.x;
+  if (threadIdx.x < 128 && p < rt.r1) {
+    m.t = eti[p];
+    if (w_pos) m.w = w_pos[p];
+    m.rank = rank_pos[p];
+  }
+  return m;
+}
+
 template <class C, bool INIT_FIRST>
 MOE_DEV void fold_epilogue(const f32x16_t (&acc)[C::FM][C::FN], const RowTile& rt, int nb, int NB, int wm, int wn,
-                           const int32_t* __restrict__ eti, const float* __restrict__ w_pos,
-                           const int32_t* __restrict__ rank_pos, int K, int d, int32_t* turn,
-                           float* __restrict__ accws, typename C::T* __restrict__ out, int32_t* counters,
-                           int spin_limit, char* smem) {
+                           const FoldRowMeta& meta, const int32_t* __restrict__ eti,
+                           const float* __restrict__ w_pos, const int32_t* __restrict__ rank_pos, int K, int d,
+                           int32_t* turn, float* __restrict__ accws, typename C::T* __restrict__ out,
+                           int32_t* counters, int spin_limit, char* smem) {
   const int tid = threadIdx.x;
   const int l = lane_id();
   if constexpr (C::BM == 128 && C::BN == 128) {
@@ -468,12 +489,10 @@ MOE_DEV void fold_epilogue(const f32x16_t (&acc)[C::FM][C::FN], const RowTile& r
     int* s_rank = (int*)(s_w + C::BM);
     const int rows = rt.r1 - rt.r0;
     __syncthreads();  // the LDS stages are reused below
-    for (int i = tid; i < C::BM; i += NTHREADS) {  // rows past the tile read token 0 and are never stored
-      const int p = rt.r0 + i;
-      const bool in = i < rows;
-      s_t[i] = in ? eti[p] : 0;
-      s_w[i] = in && w_pos ? w_pos[p] : 1.0f;
-      s_rank[i] = in ? rank_pos[p] : 0;
+    if (tid < 128) {
+      s_t[tid] = meta.t;
+      s_w[tid] = meta.w;
+      s_rank[tid] = meta.rank;
     }
 #pragma unroll
     for (int fm = 0; fm < C::FM; ++fm)
@@ -499,12 +518,10 @@ MOE_DEV void fold_epilogue(const f32x16_t (&acc)[C::FM][C::FN], const RowTile& r
     const int wave = tid >> 6, group = wave >> 2;
     const int rows = rt.r1 - rt.r0;
     __syncthreads();  // the LDS stages are reused below
-    for (int i = tid; i < 128; i += C::NT) {  // rows past the tile read token 0 and are never stored
-      const int p = rt.r0 + i;
-      const bool in = i < rows;
-      s_t[i] = in ? eti[p] : 0;
-      s_w[i] = in && w_pos ? w_pos[p] : 1.0f;
-      s_rank[i] = in ? rank_pos[p] : 0;
+    if (tid < 128) {
+      s_t[tid] = meta.t;
+      s_w[tid] = meta.w;
+      s_rank[tid] = meta.rank;
     }
     float* s_c = (wn >> 1) ? s_c1 : s_c0;
 #pragma unroll
@@ -634,9 +651,10 @@ __global__ __launch_bounds__(C::NT, C::WAVES_PER_EU) void down_combine_kernel(
     const int n = nb * C::BN + LB::my_row(i);
     lb.roff[i] = n < d ? (uint32_t)n * ldy : OOB_OFF;
   }
+  const FoldRowMeta meta = C::BM == 128 ? fold_row_meta(rt, eti, w_pos, rank_pos) : FoldRowMeta{};
   f32x16_t acc[C::FM][C::FN];
   gemm_mainloop<C>(la, lb, h / C::BK, smem, acc, wm, wn);
-  fold_epilogue<C, true>(acc, rt, nb, NB, wm, wn, eti, w_pos, rank_pos, K, d, turn, accws, out, counters,
+  fold_epilogue<C, true>(acc, rt, nb, NB, wm, wn, meta, eti, w_pos, rank_pos, K, d, turn, accws, out, counters,
                          spin_limit, smem);
 }
 
@@ -1452,7 +1470,10 @@ __global__ __launch_bounds__(C::NT, C::WAVES_PER_EU) void dx_fold_kernel(
   lb.ncols = min_i(C::BN, d - nb * C::BN);
   f32x16_t acc[C::FM][C::FN];
   gemm_mainloop<C>(la, lb, hw / C::BK, smem, acc, wm, wn);
-  fold_epilogue<C, false>(acc, rt, nb, NB, wm, wn, eti, nullptr, rank_pos, K, d, turn, accws, dx, counters,
+  // fetched after the main loop here: before it, down-combine gained 1% and
+  // this kernel lost 0.2-0.5% (MI355X, three workloads)
+  const FoldRowMeta meta = C::BM == 128 ? fold_row_meta(rt, eti, nullptr, rank_pos) : FoldRowMeta{};
+  fold_epilogue<C, false>(acc, rt, nb, NB, wm, wn, meta, eti, nullptr, rank_pos, K, d, turn, accws, dx, counters,
                           spin_limit, smem);
 }
 
