@@ -133,7 +133,8 @@ static bool wide_fold(const Shape& s, int kdim) {
 // fine-grained and large-d workloads and MoEBlaze's conf3 and conf4 (level on
 // the skewed one); dX fold 1.5-3% faster on fine-grained, large-d and conf4,
 // 0.5-1.7% slower on skewed and conf3.  The gate/up and dH kernels measured
-// 2-14% slower on it and keep 128 x 128.
+// 2-14% slower on it and keep 128 x 128 (dH except for a long reduction,
+// see the backward).
 static bool mid_fold(const Shape& s, int kdim) {
   return !wide_fold(s, kdim) && s.d % TILE_L == 0 && pick_mid(s, true);
 }
@@ -1508,9 +1509,11 @@ static hipError_t backward_t(const Shape& s, const void* dout, const void* x, co
   using CL = KCfg<TIN, TILE_L, TILE_L, true, true>;
   // dH on the 256 x 256 tile measured no faster on MI355X (4.23 vs 4.21 ms at
   // d = 4096, h = 14336; 0.88 vs 0.75 ms at d = 2048, h = 1536): the small
-  // tile is used unless the large one is forced.
+  // tile is used unless the large one is forced.  The 128 x 256 tile pays
+  // only for a long reduction (d): 4.28 -> 4.05 ms at d = 6144, h = 2048, but
+  // 3-9% slower at d = 2048-4096.
   const bool dh_big = forced_tile() == TILE_L;
-  const bool dh_mid = pick_mid(s, false);
+  const bool dh_mid = pick_mid(s, s.d >= 6144);
   const int nbh = col_blocks(s.h, dh_big || dh_mid ? TILE_L : TILE_S);
   hipError_t err;
   timing_mark(st, "dh", true);
