@@ -281,10 +281,15 @@ def moe_forward(x, ids, w, w_gate, w_up, w_down, dtype="bf16", only_experts=None
 
 
 def moe_backward(dy, x, wg, ids, w, w_gate, w_up, w_down, fwd, z, dtype="bf16", only_experts=None,
-                 saved="aby", act="swiglu"):
+                 saved="aby", act="swiglu", router_only=False):
     """Backward pass.  ``z`` are the logits the weights were computed from.
     ``only_experts`` restricts the expert path to those experts (the weight
     gradients of those experts are then complete; dx, ds, dwg are not).
+    ``router_only`` computes only what the router gradient needs (ds, ds_alt,
+    dz, dwg): the score gradients of every assignment, without dH and the
+    expert weight gradients (they stay zero), and dx then holds the router
+    term alone; what is computed goes through the same arithmetic as in the
+    full pass.
 
     ``saved`` names what the forward kept for the backward:
       "aby" -- a, b and y (MoEBlaze Algorithm 1 stores A, B and Y_swi);
@@ -341,6 +346,8 @@ def moe_backward(dy, x, wg, ids, w, w_gate, w_up, w_down, fwd, z, dtype="bf16", 
             ds_alt[r, k] = np.einsum("rh,rh->r", da_p, y_b)           # <dA', y>
             dyv = w[r, k][:, None] * da_p              # gradient reaching y
             dyv_all[r, k] = dyv
+            if router_only:
+                continue
             if act == "swiglu":
                 da_u = dyv * b * silu_grad(a)          # SiLU recomputed from stored a
                 db_u = dyv * silu(a)

@@ -39,30 +39,39 @@ def test_figure2_worked_example():
     assert ix["token_index_map"].tolist() == g["derived"]["token_index_map"]
 
 
-def _reference_semantics_index(ids, E):
-    """Second plain definition: the sort/permute pipeline of the
-    'A reference implementation' section (stable argsort of the flattened
-    expert ids, token = order // K, counts by bincount)."""
+def _rank_definition_index(ids, E):
+    """Second plain definition, from what the index means rather than from
+    how it is built (the "Dropless MoE, in depth" page, "A reference
+    implementation", states the grouping as a stable sort of the flattened
+    expert ids): assignment (t, k) of expert e sits at offsets[e] plus the
+    number of earlier tokens that also chose e, and every position holds the
+    token of the assignment placed there."""
     T, K = ids.shape
-    flat = ids.reshape(-1)
-    order = np.argsort(flat, kind="stable")
-    counts = np.bincount(flat, minlength=E)
-    offsets = np.concatenate([[0], np.cumsum(counts)])
-    pos = np.empty_like(order)
-    pos[order] = np.arange(len(order))
-    return counts, offsets, order // K, pos
+    counts = [sum(1 for t in range(T) if e in ids[t]) for e in range(E)]
+    offsets = [0]
+    for c in counts:
+        offsets.append(offsets[-1] + c)
+    pos = [0] * (T * K)
+    eti = [-1] * (T * K)
+    for t in range(T):
+        for k in range(K):
+            e = int(ids[t, k])
+            p = offsets[e] + sum(1 for u in range(t) if e in ids[u])
+            pos[t * K + k] = p
+            eti[p] = t
+    return counts, offsets, eti, pos
 
 
 @pytest.mark.parametrize("T,E,K", [(1, 1, 1), (1, 8, 8), (7, 4, 2), (33, 8, 3), (64, 16, 16), (100, 32, 5)])
-def test_index_matches_stable_sort_definition(T, E, K):
+def test_index_matches_rank_definition(T, E, K):
     rng = np.random.default_rng(T * 131 + E * 7 + K)
     ids = _rand_ids(rng, T, E, K)
     ix = O.build_index(ids, E)
-    counts, offsets, src_tok, pos = _reference_semantics_index(ids, E)
-    assert ix["counts"].tolist() == counts.tolist()
-    assert ix["offsets"].tolist() == offsets.tolist()
-    assert ix["expert_token_indices"].tolist() == src_tok.tolist()
-    assert ix["token_index_map"].tolist() == pos.tolist()
+    counts, offsets, src_tok, pos = _rank_definition_index(ids, E)
+    assert ix["counts"].tolist() == counts
+    assert ix["offsets"].tolist() == offsets
+    assert ix["expert_token_indices"].tolist() == src_tok
+    assert ix["token_index_map"].tolist() == pos
 
 
 @pytest.mark.parametrize("kind", ["gaussian", "one_expert_set", "zero_rows", "ties", "hot_expert", "all_equal"])
@@ -450,3 +459,60 @@ def test_unrounded_intermediates_round_to_the_stored_ones(act):
     e = ids[t, k]
     np.testing.assert_allclose(b["dyv"][t, k], w[t, k] * (dys[t] @ wdns[e]), rtol=1e-12)
     np.testing.assert_allclose(b["a_prime_u"][t, k], w[t, k] * f["y_s"][t, k], rtol=1e-12)
+
+
+# --------------------------------------------------------------------------
+# the restricted modes the full-size parity tests use
+# --------------------------------------------------------------------------
+
+@pytest.mark.parametrize("saved", ["aby", "ab"])
+@pytest.mark.parametrize("act", ["swiglu", "silu"])
+def test_only_experts_equals_the_full_run_on_those_experts(saved, act):
+    """moe_forward / moe_backward restricted to experts [e] give, for e's
+    assignments and e's weight gradients, exactly what the unrestricted run
+    gives (the full-size tests check the largest experts this way), and
+    zeros elsewhere."""
+    x, wg, wgt, wup, wdn, dy = _small_layer(T=40, E=5, K=2, seed=31)
+    x, wg, wgt, wup, wdn, dy = (O.round_bf16(v) for v in (x, wg, wgt, wup, wdn, dy))
+    if act != "swiglu":
+        wup = None
+    z = O.router_logits(x, wg, None)
+    ids, w = O.route(z, 2)
+    f = O.moe_forward(x, ids, w, wgt, wup, wdn, dtype="bf16", act=act)
+    b = O.moe_backward(dy, x, wg, ids, w, wgt, wup, wdn, f, z, dtype="bf16", saved=saved, act=act)
+    for e in (1, 3):
+        fe = O.moe_forward(x, ids, w, wgt, wup, wdn, dtype="bf16", only_experts=[e], act=act)
+        be = O.moe_backward(dy, x, wg, ids, w, wgt, wup, wdn, fe, z, dtype="bf16", only_experts=[e],
+                            saved=saved, act=act)
+        mine = ids == e
+        assert mine.any()
+        for key in ("a_s", "b_s", "y_s", "ye", "a_u", "y_u"):
+            np.testing.assert_array_equal(fe[key][mine], f[key][mine], err_msg=key)
+            assert np.all(fe[key][~mine] == 0.0), key
+        for key in ("dh_a", "dh_b", "a_prime_u", "dyv"):
+            np.testing.assert_array_equal(be[key][mine], b[key][mine], err_msg=key)
+            assert np.all(be[key][~mine] == 0.0), key
+        np.testing.assert_array_equal(be["ds"][mine], b["ds"][mine])
+        np.testing.assert_array_equal(be["ds_alt"][mine], b["ds_alt"][mine])
+        for key in ("dw_gate", "dw_up", "dw_down"):
+            np.testing.assert_array_equal(be[key][e], b[key][e], err_msg=key)
+            others = [j for j in range(5) if j != e]
+            assert np.all(be[key][others] == 0.0), key
+
+
+@pytest.mark.parametrize("saved", ["aby", "ab"])
+def test_router_only_backward_equals_the_full_run(saved):
+    """The router-only backward (score gradients, dz, dWg) matches the full
+    backward bit for bit, and leaves the expert gradients at zero."""
+    x, wg, wgt, wup, wdn, dy = _small_layer(T=30, E=6, K=3, seed=12)
+    x, wg, wgt, wup, wdn, dy = (O.round_bf16(v) for v in (x, wg, wgt, wup, wdn, dy))
+    z = O.router_logits(x, wg, None)
+    ids, w = O.route(z, 3)
+    f = O.moe_forward(x, ids, w, wgt, wup, wdn, dtype="bf16")
+    b = O.moe_backward(dy, x, wg, ids, w, wgt, wup, wdn, f, z, dtype="bf16", saved=saved)
+    r = O.moe_backward(dy, x, wg, ids, w, wgt, wup, wdn, f, z, dtype="bf16", saved=saved, router_only=True)
+    for key in ("ds", "ds_alt", "ds_router", "dz", "dwg"):
+        np.testing.assert_array_equal(r[key], b[key], err_msg=key)
+    np.testing.assert_array_equal(r["dx_f64"], b["dz"] @ wg)
+    for key in ("dw_gate", "dw_up", "dw_down", "dh_a", "dh_b"):
+        assert np.all(r[key] == 0.0), key
