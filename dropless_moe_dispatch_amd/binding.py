@@ -35,6 +35,11 @@ class MoeError(RuntimeError):
         self.code = code
 
 
+class MoeDeviceError(RuntimeError):
+    """A bounded wait of an ordered fold ran out on the device: the call
+    returned MOE_OK when it enqueued, but its output (out or dx) is invalid."""
+
+
 _lib = None
 _P = ctypes.c_void_p
 
@@ -55,7 +60,7 @@ def lib():
         L.moe_expert_fwd.argtypes = [sp, _P, _P, _P, _P, _P, _P, _P, _P, ctypes.c_size_t, _P]
         L.moe_combine.argtypes = [sp, _P, _P, _P, _P, _P, _P, _P, _P, _P, ctypes.c_size_t, _P]
         L.moe_combine_staged.argtypes = [sp, _P, _P, _P, _P, _P, _P, _P, _P, _P, ctypes.c_size_t, _P]
-        L.moe_expert_bwd.argtypes = [sp] + [_P] * 20 + [ctypes.c_size_t, _P]
+        L.moe_expert_bwd.argtypes = [sp] + [_P] * 21 + [ctypes.c_size_t, _P]
         for f in ("moe_route_topk", "moe_build_index", "moe_build_index_dense", "moe_expert_fwd", "moe_combine", "moe_combine_staged", "moe_expert_bwd"):
             getattr(L, f).restype = ctypes.c_int
         L.moe_status_string.argtypes = [ctypes.c_int]
@@ -158,11 +163,11 @@ def moe_combine_staged(s, y_swi, w_down, offsets, eti, tim, topk_ids, topk_w, ou
 
 
 def moe_expert_bwd(s, dout, x, wg, w_gate, w_up, w_down, topk_ids, topk_w, offsets, eti, tim, h_ab, y_swi,
-                   dx, dwg, dw_gate, dw_up, dw_down, ds, ws, stream=None, check=True):
+                   a_prime, dx, dwg, dw_gate, dw_up, dw_down, ds, ws, stream=None, check=True):
     rc = lib().moe_expert_bwd(ctypes.byref(s), _ptr(dout), _ptr(x), _ptr(wg), _ptr(w_gate), _ptr(w_up),
                               _ptr(w_down), _ptr(topk_ids), _ptr(topk_w), _ptr(offsets), _ptr(eti), _ptr(tim),
-                              _ptr(h_ab), _ptr(y_swi), _ptr(dx), _ptr(dwg), _ptr(dw_gate), _ptr(dw_up),
-                              _ptr(dw_down), _ptr(ds), _ptr(ws), _nbytes(ws), _stream(stream))
+                              _ptr(h_ab), _ptr(y_swi), _ptr(a_prime), _ptr(dx), _ptr(dwg), _ptr(dw_gate),
+                              _ptr(dw_up), _ptr(dw_down), _ptr(ds), _ptr(ws), _nbytes(ws), _stream(stream))
     if check:
         _check("moe_expert_bwd", rc)
     return rc

@@ -1,4 +1,5 @@
 // C-ABI entry points: host-side validation, workspace carving, launches.
+#include <atomic>
 #include <mutex>
 #include <string>
 #include <vector>
@@ -20,7 +21,9 @@ std::mutex g_tmu;
 bool g_timing = false;
 std::vector<TimingRec> g_recs;
 std::vector<hipEvent_t> g_pool;
-int g_spin_limit = 1 << 20;
+// read by every call that launches an ordered fold, set by moe_set_spin_limit
+// from any thread
+std::atomic<int> g_spin_limit{1 << 20};
 
 hipEvent_t take_event() {
   if (!g_pool.empty()) {
@@ -131,9 +134,8 @@ const char* moe_status_string(int code) {
 }
 
 int moe_set_spin_limit(int polls) {
-  const int prev = g_spin_limit;
-  if (polls > 0) g_spin_limit = polls;
-  return prev;
+  if (polls > 0) return g_spin_limit.exchange(polls, std::memory_order_relaxed);
+  return g_spin_limit.load(std::memory_order_relaxed);
 }
 
 int moe_route_topk(const moe_shape* s, const void* x, const void* wg, const float* bias, float* logits,
@@ -208,7 +210,7 @@ int moe_expert_fwd(const moe_shape* s, const void* x, const int32_t* offsets, co
   const ExpertWs w = expert_ws(sh, WS_EXPERT_FWD, ws);
   if (ws_bytes < w.bytes) return MOE_ERR_WORKSPACE;
   hipStream_t st = (hipStream_t)stream;
-  rc = hip_status(launch_prep(sh, w, offsets, nullptr, nullptr, nullptr, false, st));
+  rc = hip_status(launch_prep(sh, w, offsets, nullptr, nullptr, nullptr, false, -1, st));
   if (rc) return rc;
   return hip_status(launch_gate_up(sh, x, offsets, expert_token_indices, w_gate, w_up, h_ab, y_swi, w, st));
 }
@@ -231,9 +233,10 @@ int moe_combine(const moe_shape* s, const void* y_swi, const void* w_down, const
   const ExpertWs w = expert_ws(sh, WS_COMBINE, ws);
   if (ws_bytes < w.bytes) return MOE_ERR_WORKSPACE;
   hipStream_t st = (hipStream_t)stream;
-  rc = hip_status(launch_prep(sh, w, offsets, topk_ids, topk_w, token_index_map, true, st));
+  rc = hip_status(launch_prep(sh, w, offsets, topk_ids, topk_w, token_index_map, true, ERR_COMBINE, st));
   if (rc) return rc;
-  return hip_status(launch_down_combine(sh, y_swi, w_down, offsets, expert_token_indices, out, w, g_spin_limit, st));
+  return hip_status(launch_down_combine(sh, y_swi, w_down, offsets, expert_token_indices, out, w,
+                                        g_spin_limit.load(std::memory_order_relaxed), st));
 }
 
 int moe_combine_staged(const moe_shape* s, const void* y_swi, const void* w_down, const int32_t* offsets,
@@ -254,7 +257,7 @@ int moe_combine_staged(const moe_shape* s, const void* y_swi, const void* w_down
   const ExpertWs w = expert_ws(sh, WS_COMBINE_STAGED, ws);
   if (ws_bytes < w.bytes) return MOE_ERR_WORKSPACE;
   hipStream_t st = (hipStream_t)stream;
-  rc = hip_status(launch_prep(sh, w, offsets, nullptr, nullptr, nullptr, false, st));
+  rc = hip_status(launch_prep(sh, w, offsets, nullptr, nullptr, nullptr, false, -1, st));
   if (rc) return rc;
   return hip_status(launch_combine_staged(sh, y_swi, w_down, offsets, token_index_map, topk_w, out, w, st));
 }
@@ -262,8 +265,8 @@ int moe_combine_staged(const moe_shape* s, const void* y_swi, const void* w_down
 int moe_expert_bwd(const moe_shape* s, const void* dout, const void* x, const void* wg, const void* w_gate,
                    const void* w_up, const void* w_down, const int32_t* topk_ids, const float* topk_w,
                    const int32_t* offsets, const int32_t* expert_token_indices, const int32_t* token_index_map,
-                   const void* h_ab, const void* y_swi, void* dx, float* dwg, float* dw_gate, float* dw_up,
-                   float* dw_down, float* ds, void* ws, size_t ws_bytes, void* stream) {
+                   const void* h_ab, const void* y_swi, void* a_prime, void* dx, float* dwg, float* dw_gate,
+                   float* dw_up, float* dw_down, float* ds, void* ws, size_t ws_bytes, void* stream) {
   Shape sh;
   int rc = check_shape(s, &sh);
   if (rc) return rc;
@@ -281,6 +284,9 @@ int moe_expert_bwd(const moe_shape* s, const void* dout, const void* x, const vo
   REQ(token_index_map);
   REQ(h_ab);
   OPT(y_swi);  // NULL: H-only saving, y recomputed from h_ab
+  OPT(a_prime);  // H-only: where A' goes (else the workspace); must be NULL with a saved y_swi
+  if (y_swi && a_prime) return MOE_ERR_INVALID_ARG;
+  if (a_prime && a_prime == h_ab) return MOE_ERR_INVALID_ARG;
   REQ(dx);
   REQ(dwg);
   REQ(dw_gate);
@@ -289,14 +295,14 @@ int moe_expert_bwd(const moe_shape* s, const void* dout, const void* x, const vo
   REQ(dw_down);
   OPT(ds);
   REQ(ws);
-  const ExpertWs w = expert_ws(sh, y_swi ? WS_EXPERT_BWD : WS_EXPERT_BWD_H, ws);
+  const ExpertWs w = expert_ws(sh, (y_swi || a_prime) ? WS_EXPERT_BWD : WS_EXPERT_BWD_H, ws);
   if (ws_bytes < w.bytes) return MOE_ERR_WORKSPACE;
   hipStream_t st = (hipStream_t)stream;
-  rc = hip_status(launch_prep(sh, w, offsets, topk_ids, topk_w, token_index_map, true, st));
+  rc = hip_status(launch_prep(sh, w, offsets, topk_ids, topk_w, token_index_map, true, ERR_BWD, st));
   if (rc) return rc;
   return hip_status(launch_backward(sh, dout, x, wg, w_gate, w_up, w_down, topk_ids, topk_w, offsets,
-                                    expert_token_indices, token_index_map, h_ab, y_swi, dx, dwg, dw_gate, dw_up,
-                                    dw_down, ds, w, g_spin_limit, st));
+                                    expert_token_indices, token_index_map, h_ab, y_swi, a_prime, dx, dwg, dw_gate,
+                                    dw_up, dw_down, ds, w, g_spin_limit.load(std::memory_order_relaxed), st));
 }
 
 int moe_timing_enable(int on) {

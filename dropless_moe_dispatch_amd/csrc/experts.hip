@@ -392,7 +392,7 @@ constexpr int FOLD_BATCH = 16;
 template <bool INIT_FIRST, typename TOUT>
 MOE_DEV void fold_rows(const float* s_c, const int* s_t, const float* s_w, const int* s_rank, int rows, int wave,
                        int nb, int NB, int K, int d, int32_t* turn, float* __restrict__ accws, TOUT* __restrict__ out,
-                       int32_t* counters, int spin_limit) {
+                       int32_t* err, int spin_limit) {
   const int l = lane_id();
   // wave w folds tile rows w, w + 4, ..., w + 124; lane j < 32 watches row w + 4j
   const int j = l & 31;
@@ -411,7 +411,7 @@ MOE_DEV void fold_rows(const float* s_c, const int* s_t, const float* s_w, const
     const uint64_t m = __builtin_amdgcn_ballot_w64(ready) & pending;
     if (m == 0) {
       if (++spins > spin_limit) {
-        __hip_atomic_store(counters, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        __hip_atomic_store(err, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
         break;
       }
       __builtin_amdgcn_s_sleep(2);
@@ -655,8 +655,8 @@ __global__ __launch_bounds__(C::NT, C::WAVES_PER_EU) void down_combine_kernel(
   const FoldRowMeta meta = C::BM == 128 ? fold_row_meta(rt, eti, w_pos, rank_pos) : FoldRowMeta{};
   f32x16_t acc[C::FM][C::FN];
   gemm_mainloop<C>(la, lb, h / C::BK, smem, acc, wm, wn);
-  fold_epilogue<C, true>(acc, rt, nb, NB, wm, wn, meta, eti, w_pos, rank_pos, K, d, turn, accws, out, counters,
-                         spin_limit, smem);
+  fold_epilogue<C, true>(acc, rt, nb, NB, wm, wn, meta, eti, w_pos, rank_pos, K, d, turn, accws, out,
+                         counters + ERR_COMBINE, spin_limit, smem);
 }
 
 template <typename TIN, int BM, int BN>
@@ -1474,19 +1474,19 @@ __global__ __launch_bounds__(C::NT, C::WAVES_PER_EU) void dx_fold_kernel(
   // fetched after the main loop here: before it, down-combine gained 1% and
   // this kernel lost 0.2-0.5% (MI355X, three workloads)
   const FoldRowMeta meta = C::BM == 128 ? fold_row_meta(rt, eti, nullptr, rank_pos) : FoldRowMeta{};
-  fold_epilogue<C, false>(acc, rt, nb, NB, wm, wn, meta, eti, nullptr, rank_pos, K, d, turn, accws, dx, counters,
-                          spin_limit, smem);
+  fold_epilogue<C, false>(acc, rt, nb, NB, wm, wn, meta, eti, nullptr, rank_pos, K, d, turn, accws, dx,
+                          counters + ERR_BWD, spin_limit, smem);
 }
 
 template <typename TIN, int BM, int BN, bool HONLY>
 static void launch_dh(const Shape& s, const void* dout, const void* w_down, const void* h_ab, const void* y_swi,
-                      const int32_t* offsets, const int32_t* eti, const ExpertWs& ws, hipStream_t st) {
+                      void* a_prime, const int32_t* offsets, const int32_t* eti, const ExpertWs& ws, hipStream_t st) {
   using C = KCfg<TIN, BM, BN, false, true>;
   const int nbn = col_blocks(s.h, BN);
   const long long nblk = (max_row_blocks(s, BM) * nbn + 7) / 8 * 8;
   dh_kernel<C, HONLY><<<dim3((unsigned)nblk), dim3(C::NT), 0, st>>>(
       (const TIN*)dout, (const TIN*)w_down, (const TIN*)h_ab, (const TIN*)y_swi, offsets, eti, ws.tile_map(BM),
-      ws.w_pos, (TIN*)ws.dh, ws.ds_part, (TIN*)ws.a_prime, s.T, s.d, s.E, s.h, s.act, nbn, (int)nblk,
+      ws.w_pos, (TIN*)ws.dh, ws.ds_part, (TIN*)a_prime, s.T, s.d, s.E, s.h, s.act, nbn, (int)nblk,
       tile_group_rows());
 }
 
@@ -1504,8 +1504,10 @@ template <typename TIN>
 static hipError_t backward_t(const Shape& s, const void* dout, const void* x, const void* wg, const void* w_gate,
                              const void* w_up, const void* w_down, const int32_t* ids, const float* topk_w,
                              const int32_t* offsets, const int32_t* eti, const int32_t* tim, const void* h_ab,
-                             const void* y_swi, void* dx, float* dwg, float* dw_gate, float* dw_up,
+                             const void* y_swi, void* a_prime, void* dx, float* dwg, float* dw_gate, float* dw_up,
                              float* dw_down, float* ds, const ExpertWs& ws, int spin_limit, hipStream_t st) {
+  // H-only: A' goes to the caller's buffer when one is passed, else to the workspace
+  void* ap = a_prime ? a_prime : ws.a_prime;
   using CL = KCfg<TIN, TILE_L, TILE_L, true, true>;
   // dH on the 256 x 256 tile measured no faster on MI355X (4.23 vs 4.21 ms at
   // d = 4096, h = 14336; 0.88 vs 0.75 ms at d = 2048, h = 1536): the small
@@ -1519,16 +1521,16 @@ static hipError_t backward_t(const Shape& s, const void* dout, const void* x, co
   timing_mark(st, "dh", true);
   const bool honly = y_swi == nullptr;
   if (dh_big) {
-    if (honly) launch_dh<TIN, TILE_L, TILE_L, true>(s, dout, w_down, h_ab, y_swi, offsets, eti, ws, st);
-    else launch_dh<TIN, TILE_L, TILE_L, false>(s, dout, w_down, h_ab, y_swi, offsets, eti, ws, st);
+    if (honly) launch_dh<TIN, TILE_L, TILE_L, true>(s, dout, w_down, h_ab, y_swi, ap, offsets, eti, ws, st);
+    else launch_dh<TIN, TILE_L, TILE_L, false>(s, dout, w_down, h_ab, y_swi, ap, offsets, eti, ws, st);
   } else if (dh_mid) {
     if constexpr (sizeof(TIN) == 2) {
-      if (honly) launch_dh<TIN, TILE_S, TILE_L, true>(s, dout, w_down, h_ab, y_swi, offsets, eti, ws, st);
-      else launch_dh<TIN, TILE_S, TILE_L, false>(s, dout, w_down, h_ab, y_swi, offsets, eti, ws, st);
+      if (honly) launch_dh<TIN, TILE_S, TILE_L, true>(s, dout, w_down, h_ab, y_swi, ap, offsets, eti, ws, st);
+      else launch_dh<TIN, TILE_S, TILE_L, false>(s, dout, w_down, h_ab, y_swi, ap, offsets, eti, ws, st);
     }
   } else {
-    if (honly) launch_dh<TIN, TILE_S, TILE_S, true>(s, dout, w_down, h_ab, y_swi, offsets, eti, ws, st);
-    else launch_dh<TIN, TILE_S, TILE_S, false>(s, dout, w_down, h_ab, y_swi, offsets, eti, ws, st);
+    if (honly) launch_dh<TIN, TILE_S, TILE_S, true>(s, dout, w_down, h_ab, y_swi, ap, offsets, eti, ws, st);
+    else launch_dh<TIN, TILE_S, TILE_S, false>(s, dout, w_down, h_ab, y_swi, ap, offsets, eti, ws, st);
   }
   timing_mark(st, "dh", false);
   if ((err = hipGetLastError()) != hipSuccess) return err;
@@ -1576,7 +1578,7 @@ static hipError_t backward_t(const Shape& s, const void* dout, const void* x, co
     const int ns = dw_down_split(s);
     const dim3 grid(col_blocks(s.d, CL::BM) * col_blocks(s.h, CL::BN), s.E, ns);
     if (honly)
-      dw_down_kernel<CL, false><<<grid, dim3(CL::NT), 0, st>>>((const TIN*)dout, (const TIN*)ws.a_prime, offsets,
+      dw_down_kernel<CL, false><<<grid, dim3(CL::NT), 0, st>>>((const TIN*)dout, (const TIN*)ap, offsets,
                                                                eti, ws.w_pos, dw_down, ws.dw_part, s.T, s.d, s.h);
     else
       dw_down_kernel<CL, true><<<grid, dim3(CL::NT), 0, st>>>((const TIN*)dout, (const TIN*)y_swi, offsets, eti,
@@ -1615,13 +1617,13 @@ static hipError_t backward_t(const Shape& s, const void* dout, const void* x, co
 hipError_t launch_backward(const Shape& s, const void* dout, const void* x, const void* wg, const void* w_gate,
                            const void* w_up, const void* w_down, const int32_t* ids, const float* topk_w,
                            const int32_t* offsets, const int32_t* eti, const int32_t* tim, const void* h_ab,
-                           const void* y_swi, void* dx, float* dwg, float* dw_gate, float* dw_up, float* dw_down,
-                           float* ds, const ExpertWs& ws, int spin_limit, hipStream_t st) {
+                           const void* y_swi, void* a_prime, void* dx, float* dwg, float* dw_gate, float* dw_up,
+                           float* dw_down, float* ds, const ExpertWs& ws, int spin_limit, hipStream_t st) {
   if (s.bf16)
     return backward_t<bf16_t>(s, dout, x, wg, w_gate, w_up, w_down, ids, topk_w, offsets, eti, tim, h_ab, y_swi,
-                              dx, dwg, dw_gate, dw_up, dw_down, ds, ws, spin_limit, st);
-  return backward_t<float>(s, dout, x, wg, w_gate, w_up, w_down, ids, topk_w, offsets, eti, tim, h_ab, y_swi, dx,
-                           dwg, dw_gate, dw_up, dw_down, ds, ws, spin_limit, st);
+                              a_prime, dx, dwg, dw_gate, dw_up, dw_down, ds, ws, spin_limit, st);
+  return backward_t<float>(s, dout, x, wg, w_gate, w_up, w_down, ids, topk_w, offsets, eti, tim, h_ab, y_swi,
+                           a_prime, dx, dwg, dw_gate, dw_up, dw_down, ds, ws, spin_limit, st);
 }
 
 }  // namespace moe

@@ -190,14 +190,17 @@ hipError_t launch_build_index(const Shape& s, const int32_t* ids, int32_t* offse
 //            (tile maps of the two row blockings);
 //   all blocks: per position p = token_index_map[t*K+k]:
 //     w_pos[p] = topk_w[t,k], rank_pos[p] = #{j : ids[t,j] < ids[t,k]};
-//   zero the fold turn counters and the counters block.
+//   zero the fold turn counters and the counters block, except the error
+//   word of the other call that may share the workspace (counters[0] is
+//   moe_combine's, counters[1] moe_expert_bwd's; own_err names the calling
+//   entry's word, which is cleared, or -1 for neither).
 // ---------------------------------------------------------------------------
 __global__ __launch_bounds__(256) void prep_kernel(int T, int E, int K, const int32_t* __restrict__ offsets,
                                                    const int32_t* __restrict__ ids, const float* __restrict__ topk_w,
                                                    const int32_t* __restrict__ tim, int32_t* __restrict__ mb_off,
                                                    float* __restrict__ w_pos, int32_t* __restrict__ rank_pos,
                                                    int32_t* __restrict__ turn, long long n_turn,
-                                                   int32_t* __restrict__ counters) {
+                                                   int32_t* __restrict__ counters, int own_err) {
   const int tid = threadIdx.x;
   if (blockIdx.x == 0) {
     __shared__ int sh[256];
@@ -230,7 +233,7 @@ __global__ __launch_bounds__(256) void prep_kernel(int T, int E, int K, const in
       }
       if (tid == 255) mo[E] = sh[255];
     }
-    if (tid < N_COUNTERS) counters[tid] = 0;
+    if (tid < N_COUNTERS && (tid >= N_ERR_WORDS || tid == own_err)) counters[tid] = 0;
   }
   const long long gsz = (long long)gridDim.x * 256;
   const long long gid = (long long)blockIdx.x * 256 + tid;
@@ -252,7 +255,7 @@ __global__ __launch_bounds__(256) void prep_kernel(int T, int E, int K, const in
 }
 
 hipError_t launch_prep(const Shape& s, const ExpertWs& ws, const int32_t* offsets, const int32_t* ids,
-                       const float* topk_w, const int32_t* tim, bool per_position, hipStream_t st) {
+                       const float* topk_w, const int32_t* tim, bool per_position, int own_err, hipStream_t st) {
   timing_mark(st, "prep", true);
   const long long n_turn = per_position ? (long long)s.T * col_blocks(s.d, TILE_S) : 0;
   long long work = per_position ? (n_turn > s.A() ? n_turn : s.A()) : 1;
@@ -262,7 +265,8 @@ hipError_t launch_prep(const Shape& s, const ExpertWs& ws, const int32_t* offset
   prep_kernel<<<dim3(blocks), dim3(256), 0, st>>>(s.T, s.E, s.K, offsets, ids, topk_w, tim, ws.mb_off,
                                                   per_position ? ws.w_pos : nullptr,
                                                   per_position ? ws.rank_pos : nullptr,
-                                                  per_position ? ws.turn : nullptr, n_turn, ws.counters);
+                                                  per_position ? ws.turn : nullptr, n_turn, ws.counters,
+                                                  own_err);
   hipError_t e = hipGetLastError();
   timing_mark(st, "prep", false);
   return e;

@@ -14,7 +14,11 @@ constexpr int TILE_S = 128;
 constexpr int TILE_L = 256;
 constexpr int IDX_CHUNK = 256;      // tokens per index-build workgroup
 constexpr int IDX_WAVES = IDX_CHUNK / 64;
-constexpr int N_COUNTERS = 64;      // [0] error flag, [8..16) fold queue heads, others reserved
+constexpr int N_COUNTERS = 64;      // [0], [1] error words, [8..16) fold queue heads, others reserved
+// Error words of the two calls with an ordered fold, so that one workspace
+// may serve both: moe_combine sets counters[ERR_COMBINE], moe_expert_bwd
+// counters[ERR_BWD] when a bounded wait runs out; each call clears only its own.
+constexpr int ERR_COMBINE = 0, ERR_BWD = 1, N_ERR_WORDS = 2;
 
 enum { ACT_SWIGLU = 0, ACT_SILU = 1, ACT_RELU = 2 };
 
@@ -28,6 +32,10 @@ struct Shape {
 };
 
 inline size_t align_up(size_t v, size_t a) { return (v + a - 1) / a * a; }
+// Address `off` bytes into a workspace based at p, in integer arithmetic:
+// sizing a workspace carves it from a null base, where pointer arithmetic
+// would be undefined.
+inline void* ws_at(void* p, size_t off) { return (void*)((uintptr_t)p + off); }
 // column blocks of width bn covering n columns (the last may be partial)
 __host__ __device__ inline int col_blocks(int n, int bn) { return (n + bn - 1) / bn; }
 
@@ -48,11 +56,11 @@ inline IndexWs index_ws(const Shape& s, void* p) {
   IndexWs w{};
   w.nchunks = (s.T + IDX_CHUNK - 1) / IDX_CHUNK;
   size_t off = 0;
-  w.masks = (uint64_t*)((char*)p + off);
+  w.masks = (uint64_t*)ws_at(p, off);
   off = align_up(off + (size_t)w.nchunks * IDX_WAVES * s.E * 8, 256);
-  w.base = (int32_t*)((char*)p + off);
+  w.base = (int32_t*)ws_at(p, off);
   off = align_up(off + (size_t)s.E * w.nchunks * 4, 256);
-  w.tot = (int32_t*)((char*)p + off);
+  w.tot = (int32_t*)ws_at(p, off);
   off = align_up(off + (size_t)s.E * 4, 256);
   w.bytes = off;
   return w;
@@ -68,7 +76,7 @@ struct DenseIndexWs {
 inline DenseIndexWs dense_index_ws(const Shape& s, void* p) {
   DenseIndexWs w{};
   size_t off = 0;
-  auto take = [&](size_t bytes) { void* q = (char*)p + off; off = align_up(off + bytes, 256); return q; };
+  auto take = [&](size_t bytes) { void* q = ws_at(p, off); off = align_up(off + bytes, 256); return q; };
   w.d5 = (int32_t*)take((size_t)s.E * s.T * 4);
   w.loc = (int32_t*)take((size_t)s.E * s.T * 4);
   w.lengths = (int32_t*)take((size_t)s.E * 4);
@@ -125,7 +133,8 @@ struct ExpertWs {
   float* dwg_part;     // dWg partial sums (backward): bf16 [token chunks][E][d], fp32 [row blocks of 128][d]
   float* dw_part;      // [split][E][m][n] dW chunk partials when a dW GEMM splits its rows (backward)
   void* dh;            // [A][hw] activation-dtype gradient of the pre-activations (backward)
-  void* a_prime;       // [A][h] activation-dtype A' = w * y recomputed from a, b (H-only backward)
+  void* a_prime;       // [A][h] activation-dtype A' = w * y recomputed from a, b (H-only backward,
+                       // unless the caller passes a buffer for it)
   void* ystage;        // [A][d] activation-dtype staged expert outputs (staged-Y combine ablation)
   size_t bytes;
   int E;
@@ -138,7 +147,7 @@ inline ExpertWs expert_ws(const Shape& s, int which, void* p) {
   w.E = s.E;
   const size_t A = (size_t)s.A();
   size_t off = 0;
-  auto take = [&](size_t bytes) { void* q = (char*)p + off; off = align_up(off + bytes, 256); return q; };
+  auto take = [&](size_t bytes) { void* q = ws_at(p, off); off = align_up(off + bytes, 256); return q; };
   w.counters = (int32_t*)take(N_COUNTERS * 4);
   w.mb_off = (int32_t*)take((size_t)2 * (s.E + 1) * 4);
   const bool bwd = which == WS_EXPERT_BWD || which == WS_EXPERT_BWD_H;
@@ -179,7 +188,7 @@ hipError_t launch_build_index(const Shape& s, const int32_t* ids, int32_t* offse
 hipError_t launch_build_index_dense(const Shape& s, const int32_t* ids, int32_t* offsets, int32_t* eti, int32_t* tim,
                                     const DenseIndexWs& ws, hipStream_t st);
 hipError_t launch_prep(const Shape& s, const ExpertWs& ws, const int32_t* offsets, const int32_t* ids,
-                       const float* topk_w, const int32_t* tim, bool per_position, hipStream_t st);
+                       const float* topk_w, const int32_t* tim, bool per_position, int own_err, hipStream_t st);
 hipError_t launch_gate_up(const Shape& s, const void* x, const int32_t* offsets, const int32_t* eti,
                           const void* w_gate, const void* w_up, void* h_ab, void* y_swi, const ExpertWs& ws,
                           hipStream_t st);
@@ -191,8 +200,8 @@ hipError_t launch_combine_staged(const Shape& s, const void* y_swi, const void* 
 hipError_t launch_backward(const Shape& s, const void* dout, const void* x, const void* wg, const void* w_gate,
                            const void* w_up, const void* w_down, const int32_t* ids, const float* topk_w,
                            const int32_t* offsets, const int32_t* eti, const int32_t* tim, const void* h_ab,
-                           const void* y_swi, void* dx, float* dwg, float* dw_gate, float* dw_up, float* dw_down,
-                           float* ds, const ExpertWs& ws, int spin_limit, hipStream_t st);
+                           const void* y_swi, void* a_prime, void* dx, float* dwg, float* dw_gate, float* dw_up,
+                           float* dw_down, float* ds, const ExpertWs& ws, int spin_limit, hipStream_t st);
 
 // Optional per-kernel timing hooks (set by the C-ABI timing calls).
 void timing_mark(hipStream_t st, const char* name, bool begin);

@@ -4,6 +4,11 @@ torch is used for device memory and the stream only; every computation is a
 library kernel.  ``MoEBuffers`` allocates every output and workspace once for
 a shape (sizes do not depend on the routing); ``forward``/``backward`` enqueue
 the five entry points in order on the current stream with no host sync.
+
+Memory: the expert forward, the combine and the backward share one workspace
+(the library allows it for calls ordered on one stream), and under H-only
+saving the backward writes A' = w * y into the forward's y_swi buffer, which
+is dead once the combine has read it.  So y_swi holds A' after a backward.
 """
 from __future__ import annotations
 
@@ -60,10 +65,16 @@ class MoEBuffers:
         self.y_swi = torch.empty(A, h, dtype=td, device=dev)
         self.out = torch.empty(T, d, dtype=td, device=dev)
         self.ws_index = self._ws(B.MOE_WS_INDEX)
-        self.ws_fwd = self._ws(B.MOE_WS_EXPERT_FWD)
         if self.combine not in ("fold", "staged"):
             raise ValueError(f"combine must be 'fold' or 'staged', not {self.combine!r}")
-        self.ws_comb = self._ws(B.MOE_WS_COMBINE if self.combine == "fold" else B.MOE_WS_COMBINE_STAGED)
+        if self.saved not in ("aby", "ab"):
+            raise ValueError(f"saved must be 'aby' or 'ab', not {self.saved!r}")
+        # one workspace for the expert forward, the ordered combine and the
+        # backward (H-only: A' goes to y_swi, so the smaller backward kind)
+        kinds = [B.MOE_WS_EXPERT_FWD] + ([B.MOE_WS_COMBINE] if self.combine == "fold" else []) \
+            + ([B.MOE_WS_EXPERT_BWD] if self.backward else [])
+        self.ws_main = self._ws(*kinds)
+        self.ws_comb = self.ws_main if self.combine == "fold" else self._ws(B.MOE_WS_COMBINE_STAGED)
         if self.backward:
             self.dx = torch.empty(T, d, dtype=td, device=dev)
             self.dwg = torch.empty(E, d, dtype=f32, device=dev)
@@ -71,15 +82,12 @@ class MoEBuffers:
             self.dw_up = torch.empty(E, h, d, dtype=f32, device=dev) if self.act == "swiglu" else None
             self.dw_down = torch.empty(E, d, h, dtype=f32, device=dev)
             self.ds = torch.empty(T, K, dtype=f32, device=dev)
-            if self.saved not in ("aby", "ab"):
-                raise ValueError(f"saved must be 'aby' or 'ab', not {self.saved!r}")
-            self.ws_bwd = self._ws(B.MOE_WS_EXPERT_BWD if self.saved == "aby" else B.MOE_WS_EXPERT_BWD_H)
 
-    def _ws(self, which):
-        n = B.workspace_bytes(self.shape, which)
-        if n == 0:
+    def _ws(self, *kinds):
+        sizes = [B.workspace_bytes(self.shape, k) for k in kinds]
+        if min(sizes) == 0:
             raise B.MoeError("moe_workspace_bytes", B.MOE_ERR_INVALID_ARG)
-        return torch.empty(n, dtype=torch.uint8, device=self.device)
+        return torch.empty(max(sizes), dtype=torch.uint8, device=self.device)
 
     # -- accounting ---------------------------------------------------------
     def saved_for_backward_bytes(self) -> int:
@@ -100,13 +108,24 @@ class MoEBuffers:
                    if t is not None)
 
     def workspace_bytes(self) -> int:
-        ws = [self.ws_index, self.ws_fwd, self.ws_comb] + ([self.ws_bwd] if self.backward else [])
+        ws = [self.ws_index, self.ws_main] + ([self.ws_comb] if self.ws_comb is not self.ws_main else [])
         return sum(t.numel() for t in ws)
 
     def device_error_words(self):
-        """Ordered-combine error words (nonzero: a bounded wait ran out)."""
-        w = ([self.ws_comb[:4]] if self.combine == "fold" else []) + ([self.ws_bwd[:4]] if self.backward else [])
+        """Error words of the ordered folds (nonzero: a bounded wait ran
+        out): the combine's (bytes 0-3 of its workspace), then the
+        backward's (bytes 4-7).  Synchronises with the device."""
+        w = ([self.ws_comb[0:4]] if self.combine == "fold" else []) + ([self.ws_main[4:8]] if self.backward else [])
         return [int(x.view(torch.int32).item()) for x in w]
+
+    def check_device_errors(self):
+        """Raise MoeDeviceError if a fold's bounded wait ran out: out (or dx)
+        of that call is then invalid although the call returned MOE_OK."""
+        words = self.device_error_words()
+        if any(words):
+            names = (["moe_combine"] if self.combine == "fold" else []) + (["moe_expert_bwd"] if self.backward else [])
+            bad = [n for n, w in zip(names, words) if w]
+            raise B.MoeDeviceError(f"ordered fold wait ran out in {', '.join(bad)}: its output is invalid")
 
 
 def route(buf: MoEBuffers, x, wg, bias=None, logits_in: bool = False, stream=None):
@@ -117,17 +136,19 @@ def forward(buf: MoEBuffers, x, wg, bias, w_gate, w_up, w_down, logits_in: bool 
     s = buf.shape
     route(buf, x, wg, bias, logits_in, stream)
     B.moe_build_index(s, buf.topk_ids, buf.offsets, buf.eti, buf.tim, buf.ws_index, stream)
-    B.moe_expert_fwd(s, x, buf.offsets, buf.eti, w_gate, w_up, buf.h_ab, buf.y_swi, buf.ws_fwd, stream)
+    B.moe_expert_fwd(s, x, buf.offsets, buf.eti, w_gate, w_up, buf.h_ab, buf.y_swi, buf.ws_main, stream)
     comb = B.moe_combine if buf.combine == "fold" else B.moe_combine_staged
     comb(s, buf.y_swi, w_down, buf.offsets, buf.eti, buf.tim, buf.topk_ids, buf.topk_w, buf.out, buf.ws_comb, stream)
     return buf.out
 
 
 def backward(buf: MoEBuffers, dy, x, wg, w_gate, w_up, w_down, stream=None, want_ds: bool = True):
+    """H-only saving: y_swi is not passed as y, and receives A' (it is dead
+    after the forward's combine)."""
+    honly = buf.saved == "ab"
     B.moe_expert_bwd(buf.shape, dy, x, wg, w_gate, w_up, w_down, buf.topk_ids, buf.topk_w, buf.offsets, buf.eti,
-                     buf.tim, buf.h_ab, buf.y_swi if buf.saved == "aby" else None, buf.dx, buf.dwg, buf.dw_gate,
-                     buf.dw_up, buf.dw_down,
-                     buf.ds if want_ds else None, buf.ws_bwd, stream)
+                     buf.tim, buf.h_ab, None if honly else buf.y_swi, buf.y_swi if honly else None, buf.dx, buf.dwg,
+                     buf.dw_gate, buf.dw_up, buf.dw_down, buf.ds if want_ds else None, buf.ws_main, stream)
     return buf.dx
 
 

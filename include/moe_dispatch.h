@@ -48,16 +48,31 @@
  *     launch (hipGetLastError after the enqueue).
  *   - Workspaces hold no state between calls; size them with
  *     moe_workspace_bytes, which depends on the shape only (never on the
- *     routing, so skewed routing cannot exhaust it).  The first 4 bytes of a
- *     MOE_WS_COMBINE / MOE_WS_EXPERT_BWD workspace are a device error word:
- *     nonzero after the call if a bounded wait of the ordered combine ran out
- *     (see moe_set_spin_limit); it is cleared at the start of each call.
+ *     routing, so skewed routing cannot exhaust it).
+ *   - One workspace may serve moe_expert_fwd, moe_combine and
+ *     moe_expert_bwd of the same shape (their layouts share a prefix and no
+ *     call reads what an earlier one left there), sized as the largest of
+ *     MOE_WS_EXPERT_FWD, MOE_WS_COMBINE and MOE_WS_EXPERT_BWD(_H).  Calls
+ *     that share a workspace must not overlap in time (enqueue them on one
+ *     stream, or order their streams).
+ *   - Device error words (int32, in the workspace): bytes 0-3 belong to
+ *     moe_combine, bytes 4-7 to moe_expert_bwd.  Each call clears its own at
+ *     its start and leaves the other's, so after a forward and a backward
+ *     through a shared workspace both are readable.  A word is nonzero when
+ *     a bounded wait of that call's ordered fold ran out (moe_set_spin_limit):
+ *     the call still returns MOE_OK, because it only enqueues work and the
+ *     wait happens later on the device, but its output (out or dx) is then
+ *     NOT valid.  A caller must read the word after the stream completes
+ *     before trusting out / dx.
  *   - Supported shapes: 1 <= K <= min(E, 32), E <= 1024, T*K < 2^31,
  *     d and h multiples of 128, and under 2 GiB each for x [T,d], one
  *     expert's weight matrix [h,d] and T rows of the saved pre-activations
  *     [T, 2h] (2h -> h for the plain experts) in the activation dtype (the
  *     kernels address them with 32-bit offsets); otherwise
- *     MOE_ERR_UNSUPPORTED.  Device pointers 16-byte aligned.
+ *     MOE_ERR_UNSUPPORTED.  (Multiples of 128, where multiples of 8 would
+ *     satisfy the 16-byte row alignment: the expert GEMM tiles are 128 or
+ *     256 wide and have no masked column tail for d; h is masked per
+ *     128-column block.)  Device pointers 16-byte aligned.
  */
 #ifndef MOE_DISPATCH_H
 #define MOE_DISPATCH_H
@@ -224,20 +239,28 @@ int moe_combine_staged(const moe_shape* s, const void* y_swi, const void* w_down
  * it before the backward).  The dH kernel recomputes y = SiLU(a) * b from the
  * saved bf16 a and b, uses it for dS = <dA', y>, and writes A' = w * y in
  * the activation dtype into the workspace, where dW_down reads it as its
- * right-hand operand (dw_down[e] += dout[t]^T A'[p]).  ws:
- * MOE_WS_EXPERT_BWD_H (MOE_ERR_WORKSPACE if smaller). */
+ * right-hand operand (dw_down[e] += dout[t]^T A'[p]).
+ *   a_prime [T*K, h] dtype (nullable; H-only only): where A' is written.
+ *     The forward's y_swi buffer, dead once moe_combine has read it, is the
+ *     intended one.  With a_prime == NULL, A' lives in the workspace, which
+ *     must then be MOE_WS_EXPERT_BWD_H; with a_prime given, MOE_WS_EXPERT_BWD
+ *     suffices.  It is overwritten, must not overlap any other argument, and
+ *     must be NULL when y_swi is passed (MOE_ERR_INVALID_ARG otherwise). */
 int moe_expert_bwd(const moe_shape* s, const void* dout, const void* x, const void* wg, const void* w_gate,
                    const void* w_up, const void* w_down, const int32_t* topk_ids, const float* topk_w,
                    const int32_t* offsets, const int32_t* expert_token_indices, const int32_t* token_index_map,
-                   const void* h_ab, const void* y_swi, void* dx, float* dwg, float* dw_gate, float* dw_up,
-                   float* dw_down, float* ds, void* ws, size_t ws_bytes, void* stream);
+                   const void* h_ab, const void* y_swi, void* a_prime, void* dx, float* dwg, float* dw_gate,
+                   float* dw_up, float* dw_down, float* ds, void* ws, size_t ws_bytes, void* stream);
 
 /* Static string for a moe_status value (host). */
 const char* moe_status_string(int code);
 
 /* Bound on the polls of one wait in the ordered combine (default 1<<20,
- * about a second); a wait that runs out sets the workspace error word and
- * proceeds, so every kernel always finishes.  Returns the previous value. */
+ * about a second); a wait that runs out sets the calling entry's workspace
+ * error word and proceeds, so every kernel always finishes, but that call's
+ * output is then invalid (see the error words above).  polls <= 0 only
+ * reads the value.  Returns the previous value.  Thread-safe; a call reads
+ * the limit once, when it enqueues its kernels. */
 int moe_set_spin_limit(int polls);
 
 /* Per-kernel timing (profiling aid).  While enabled, each internal kernel

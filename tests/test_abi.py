@@ -90,18 +90,34 @@ def test_pointer_and_workspace_validation():
     need = B.workspace_bytes(s, B.MOE_WS_EXPERT_FWD)
     assert L.moe_expert_fwd(sp, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, need - 1, 0) == B.MOE_ERR_WORKSPACE
     need = B.workspace_bytes(s, B.MOE_WS_EXPERT_BWD)
-    req = [FAKE] * 18            # dout .. dw_down
+
+    def bwd_args():
+        a = [FAKE] * 19          # dout .. dw_down
+        a[13] = None             # a_prime: only with H-only saving
+        return a
+    req = bwd_args()
     assert L.moe_expert_bwd(sp, *req, None, FAKE, need - 1, 0) == B.MOE_ERR_WORKSPACE   # ds is optional
-    req[14] = None               # dwg missing
+    req[15] = None               # dwg missing
     assert L.moe_expert_bwd(sp, *req, None, FAKE, need, 0) == B.MOE_ERR_INVALID_ARG
-    # y_swi == NULL (H-only saving) needs the larger MOE_WS_EXPERT_BWD_H workspace
-    req = [FAKE] * 18
+    # y_swi == NULL (H-only saving) needs the larger MOE_WS_EXPERT_BWD_H workspace ...
+    req = bwd_args()
     req[12] = None               # y_swi
     need_h = B.workspace_bytes(s, B.MOE_WS_EXPERT_BWD_H)
     assert need_h > need
     assert L.moe_expert_bwd(sp, *req, None, FAKE, need, 0) == B.MOE_ERR_WORKSPACE
     req[11] = None               # h_ab is still required
     assert L.moe_expert_bwd(sp, *req, None, FAKE, need_h, 0) == B.MOE_ERR_INVALID_ARG
+    # ... unless the caller gives A' a buffer of its own (the forward's dead y_swi)
+    req = bwd_args()
+    req[12], req[13] = None, FAKE + 0x100
+    assert L.moe_expert_bwd(sp, *req, None, FAKE, need - 1, 0) == B.MOE_ERR_WORKSPACE
+    req[13] = FAKE + 0x104       # misaligned
+    assert L.moe_expert_bwd(sp, *req, None, FAKE, need, 0) == B.MOE_ERR_INVALID_ARG
+    req[13] = req[11]            # A' over the saved a|b
+    assert L.moe_expert_bwd(sp, *req, None, FAKE, need, 0) == B.MOE_ERR_INVALID_ARG
+    req = bwd_args()
+    req[13] = FAKE + 0x100       # a saved y and an A' buffer: ambiguous
+    assert L.moe_expert_bwd(sp, *req, None, FAKE, need, 0) == B.MOE_ERR_INVALID_ARG
 
 
 def test_activation_kind_validation():
@@ -130,4 +146,17 @@ def test_activation_kind_validation():
 
 def test_spin_limit_setter_roundtrip():
     prev = B.set_spin_limit(1000)
+    assert B.set_spin_limit(0) == 1000          # polls <= 0 only reads
     assert B.set_spin_limit(prev) == 1000
+
+
+def test_one_workspace_serves_forward_combine_and_backward():
+    """The shared-workspace rule: every expert call's layout starts with the
+    same carving, so the largest kind serves all three."""
+    s = B.shape(16384, 2048, 128, 8, 768)
+    fwd, comb, bwd = (B.workspace_bytes(s, k) for k in (B.MOE_WS_EXPERT_FWD, B.MOE_WS_COMBINE, B.MOE_WS_EXPERT_BWD))
+    assert fwd < comb < bwd
+    # the backward adds dH [T*K, 2h] and small buffers to the combine's carving;
+    # it does not repeat the fp32 [T, d] accumulator
+    dh = 16384 * 8 * 2 * 768 * 2
+    assert dh <= bwd - comb < dh + 16384 * 2048 * 4

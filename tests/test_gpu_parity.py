@@ -4,6 +4,8 @@ Small shapes (several 128-row tiles, ragged tails, edge cases) are compared
 element by element; routing ids, counts, offsets and the index bit-exact,
 floats within max_rel 2e-2 / mean_rel 2e-3.
 """
+import os
+import subprocess
 import sys
 
 import numpy as np
@@ -15,7 +17,7 @@ from dropless_moe_dispatch_amd import binding as B
 from dropless_moe_dispatch_amd import layer as Lyr
 from dropless_moe_dispatch_amd import synth
 from oracle import moe_oracle as O
-from tests.gpu_util import assert_close, dw_flip_allowance, stored_flip_bounds, to_np, topk_margin
+from tests.gpu_util import assert_close, dw_flip_allowance, fp32_windows, stored_flip_bounds, to_np, topk_margin
 
 pytestmark = pytest.mark.gpu
 
@@ -180,6 +182,9 @@ LAYER_CASES = [
     # empty) and the largest K with K = E
     ("experts_1024", 300, 128, 1024, 2, 128, "bf16", None),
     ("k_eq_e_32", 70, 128, 32, 32, 128, "bf16", None),
+    # d = 6144: dH on the 128 x 256 tile (a long reduction), with h = 384 an
+    # odd multiple of 128, so its last column block runs past h
+    ("dh_mid_d6144", 200, 6144, 4, 2, 384, "bf16", None),
 ]
 
 
@@ -194,6 +199,7 @@ def _gpu_layer(inp, wl, logits32=None, backward=True, saved="aby", combine="fold
         buf.logits.copy_(torch.from_numpy(logits32))
     Lyr.forward(buf, dev["x"], dev["wg"], bias, dev["w_gate"], dev["w_up"], dev["w_down"],
                 logits_in=logits32 is not None)
+    buf.y_fwd = buf.y_swi.clone()       # an H-only backward writes A' over y_swi
     if backward:
         Lyr.backward(buf, dev["dy"], dev["x"], dev["wg"], dev["w_gate"], dev["w_up"], dev["w_down"])
     torch.cuda.synchronize()
@@ -217,7 +223,7 @@ def _compare_layer(buf, inp, wl, z32, backward=True, report=None, w_rtol=2e-6, s
     assert_close("a", hab[..., :h], f["a_s"], report=report)
     if gated:
         assert_close("b", hab[..., h:], f["b_s"], report=report)
-    assert_close("y_swi", to_np(buf.y_swi)[pos], f["y_s"], report=report)
+    assert_close("y_swi", to_np(buf.y_fwd)[pos], f["y_s"], report=report)
     assert_close("out", to_np(buf.out), f["out"], report=report)
     if not backward:
         return
@@ -227,7 +233,8 @@ def _compare_layer(buf, inp, wl, z32, backward=True, report=None, w_rtol=2e-6, s
     assert_close("ds", to_np(buf.ds), bw["ds_alt"] if saved == "ab" else bw["ds"], report=report)
     assert_close("dx", to_np(buf.dx), bw["dx"], report=report)
     assert_close("dwg", to_np(buf.dwg), bw["dwg"], report=report)
-    fl = stored_flip_bounds(f, bw, w, wl.dtype, wl.act, saved)
+    win = fp32_windows(inp["x"], inp["dy"], ids, inp["w_gate"], inp["w_up"], inp["w_down"], act=wl.act)
+    fl = stored_flip_bounds(f, bw, w, wl.dtype, wl.act, saved, win)
     assert_close("dw_gate", to_np(buf.dw_gate), bw["dw_gate"], report=report,
                  allow=dw_flip_allowance(fl["da"], ids, inp["x"], E))
     if gated:
@@ -380,8 +387,8 @@ def test_bitwise_repeatable():
     inp = synth.make_inputs(wl)
     b1, _ = _gpu_layer(inp, wl)
     b2, _ = _gpu_layer(inp, wl)
-    for key in ("topk_ids", "topk_w", "eti", "tim", "h_ab", "y_swi", "out", "dx", "dwg", "dw_gate", "dw_up",
-                "dw_down", "ds"):
+    for key in ("topk_ids", "topk_w", "eti", "tim", "h_ab", "y_fwd", "y_swi", "out", "dx", "dwg", "dw_gate",
+                "dw_up", "dw_down", "ds"):
         assert torch.equal(getattr(b1, key), getattr(b2, key)), key
 
 
@@ -476,3 +483,123 @@ def test_forward_without_saving(act):
     ids, w = O.route(z32.astype(np.float64), K)
     f = O.moe_forward(inp["x"], ids, w, inp["w_gate"], inp["w_up"], inp["w_down"], dtype="bf16", act=act)
     assert_close("out", to_np(outs[1].out), f["out"])
+
+
+# ---------------------------------------------------------------------------
+# forced tile choices (the tuning switches are read once per process, so each
+# setting runs in a child process of its own)
+# ---------------------------------------------------------------------------
+FORCED_TILE_CASES = ["ragged", "multi_tile", "skewed", "mid_fold", "dh_mid_d6144", "f32_bwd", "k16"]
+
+
+def run_cases_in_this_process(names):
+    """Run the named layer cases (both savings) and report; used by the child processes."""
+    byname = {c[0]: c for c in LAYER_CASES}
+    B.lib()
+    for name in names:
+        for saved in ("aby", "ab"):
+            _, T, d, E, K, h, dtype, zipf = byname[name]
+            print("[child case]", name, saved, os.environ.get("MOE_DISPATCH_TILE"),
+                  os.environ.get("MOE_DISPATCH_MID"), file=sys.stderr, flush=True)
+            wl = synth.small_workload(T, d, E, K, h, dtype=dtype, seed=sum(map(ord, name)) + 11, zipf_s=zipf)
+            inp = synth.make_inputs(wl)
+            z32 = O.router_logits(inp["x"], inp["wg"], inp["bias"]).astype(np.float32)
+            buf, _ = _gpu_layer(inp, wl, logits32=z32, saved=saved)
+            assert buf.device_error_words() == [0, 0]
+            _compare_layer(buf, inp, wl, z32, saved=saved)
+    print("child ok", flush=True)
+
+
+@pytest.mark.timeout(600)
+@pytest.mark.parametrize("env", [{"MOE_DISPATCH_TILE": "256"}, {"MOE_DISPATCH_TILE": "128"},
+                                 {"MOE_DISPATCH_MID": "1"}, {"MOE_DISPATCH_MID": "0"}],
+                         ids=["tile256", "tile128", "mid_on", "mid_off"])
+def test_layer_parity_under_forced_tiles(env):
+    """Layer parity with every expert GEMM forced onto one tile (256 x 256 or
+    128 x 128), or the 128 x 256 tile forced on or off, one child process per
+    setting (the switches are read once per process)."""
+    _say("forced tiles", env)
+    root = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+    code = ("import sys; sys.path.insert(0, %r); from tests.test_gpu_parity import run_cases_in_this_process as r; "
+            "r(%r)" % (root, FORCED_TILE_CASES))
+    child_env = dict(os.environ, **env)
+    p = subprocess.run([sys.executable, "-c", code], env=child_env, cwd=root, capture_output=True, text=True,
+                       timeout=540)
+    assert p.returncode == 0 and "child ok" in p.stdout, (p.returncode, p.stdout[-2000:], p.stderr[-4000:])
+
+
+# ---------------------------------------------------------------------------
+# HIP graph replay under changed routing
+# ---------------------------------------------------------------------------
+def test_graph_replay_follows_changed_routing():
+    """A forward + backward captured once, replayed after x and the router
+    bias change in place: new routing each time (one replay with an expert
+    emptied by the bias, one with a hot expert), so the counts, tile maps and
+    fold order all differ from those at capture.  Every replay equals an
+    eager run on the same inputs bit for bit, and matches the oracle."""
+    T, d, E, K, h = 500, 256, 16, 4, 256
+    _say("graph_routing", T, d, E, K, h)
+    wl = synth.small_workload(T, d, E, K, h, seed=61)
+    inp = synth.make_inputs(wl)
+    dev = {k: Lyr.to_device(inp[k], "bf16") for k in ("x", "wg", "w_gate", "w_up", "w_down", "dy")}
+    bias_dev = torch.zeros(E, dtype=torch.float32, device="cuda")
+    keys = ("logits", "topk_ids", "topk_w", "offsets", "eti", "tim", "h_ab", "out", "dx", "dwg", "dw_gate", "dw_up",
+            "dw_down", "ds")
+    gbuf = Lyr.MoEBuffers(T, d, E, K, h, "bf16", backward=True, saved="ab")
+    ebuf = Lyr.MoEBuffers(T, d, E, K, h, "bf16", backward=True, saved="ab")
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+
+    def step(buf):
+        sp = torch.cuda.current_stream().cuda_stream
+        Lyr.forward(buf, dev["x"], dev["wg"], bias_dev, dev["w_gate"], dev["w_up"], dev["w_down"], stream=sp)
+        Lyr.backward(buf, dev["dy"], dev["x"], dev["wg"], dev["w_gate"], dev["w_up"], dev["w_down"], stream=sp)
+
+    with torch.cuda.stream(side):
+        step(gbuf)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g, stream=side):
+        step(gbuf)
+    torch.cuda.synchronize()
+    rng = np.random.default_rng(5)
+    variants = []
+    for i in range(3):
+        x = synth.round_to_bf16(rng.standard_normal((T, d)).astype(np.float32))
+        b = np.zeros(E, np.float32)
+        if i == 1:
+            b[3] = -60.0          # expert 3 gets no rows
+        if i == 2:
+            b[9] = 8.0            # expert 9 is in nearly every token's set
+        variants.append((x, b))
+    seen_counts = []
+    for i, (x, b) in enumerate(variants):
+        dev["x"].copy_(torch.from_numpy(x))
+        bias_dev.copy_(torch.from_numpy(b))
+        for k in keys:                        # eager work between the replays
+            getattr(gbuf, k).zero_()
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        step(ebuf)
+        torch.cuda.synchronize()
+        assert gbuf.device_error_words() == [0, 0], i
+        for k in keys:
+            assert torch.equal(getattr(gbuf, k), getattr(ebuf, k)), (i, k)
+        counts = np.diff(to_np(gbuf.offsets))
+        seen_counts.append(counts)
+        if i == 1:
+            assert counts[3] == 0
+        if i == 2:
+            assert counts[9] > 0.9 * T
+        # the oracle routes on its own logits; the ids must agree but at near ties
+        inp_i = dict(inp, x=x, bias=b)
+        z = O.router_logits(x, inp["wg"], b)
+        dz = float(np.abs(to_np(gbuf.logits) - z).max())
+        assert dz < 1e-4, dz
+        z32 = z.astype(np.float32)
+        mism = np.nonzero((to_np(gbuf.topk_ids) != O.topk_select(z32, K)).any(axis=1))[0]
+        assert np.all(topk_margin(z32, K)[mism] <= 4 * dz), "routing differs away from a near tie"
+        if len(mism) == 0:
+            _compare_layer(gbuf, inp_i, wl, z32, w_rtol=1e-4, saved="ab")
+    assert not np.array_equal(seen_counts[0], seen_counts[1]) and not np.array_equal(seen_counts[1], seen_counts[2])
