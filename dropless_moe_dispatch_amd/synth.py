@@ -39,6 +39,7 @@ class Workload:
     seed: int = 0
     note: str = field(default="", compare=False)
     act: str = "swiglu"   # "swiglu" (gated expert) or "silu" / "relu" (plain two-layer expert)
+    zipf_draw: int = 0    # which draw of the Zipf permutation stream ranks the experts
 
 
 # The five evaluation workloads.  Index i (1-based) uses seed 1000 + i.
@@ -51,8 +52,17 @@ WORKLOADS = {
                 note="fine-grained experts, forward + backward"),
     4: Workload("large_d_fwdbwd_bf16", 32768, 6144, 64, 4, 2048, "bf16", True, seed=1004,
                 note="large model dimension, forward + backward"),
+    # The skewed workload names its outcome: a few experts above 10% of the
+    # assignments and several under 16 rows.  The Zipf(1.2) offset (zipf_bias)
+    # fixes the shape of the skew; which expert gets which popularity rank is
+    # a seeded permutation, and draw 11 of its stream is the first whose
+    # routing of this workload's tokens shows that outcome (3 experts above
+    # 10%, 4 under 16 rows, the smallest with 11; draws 0-10 leave at most 2
+    # under 16 rows).  tests/test_workloads_cpu.py recomputes this with the
+    # oracle.  No draw empties an expert: the least popular one is offset by
+    # -1.2 ln 64 = -5.0 against N(0,1) logits.
     5: Workload("skewed_fwdbwd_bf16", 16384, 4096, 64, 6, 1536, "bf16", True, zipf_s=1.2,
-                seed=1005, note="Zipf(1.2) per-expert logit offset, forward + backward"),
+                seed=1005, note="Zipf(1.2) per-expert logit offset, forward + backward", zipf_draw=11),
     # MoEBlaze's own evaluation shapes (reading notes, Table 1: the printed
     # conf1, conf3, conf4 and conf7; T = batch x sequence, h = 4d) with the
     # plain two-layer SiLU expert of its Figure 3 comparison.
@@ -85,8 +95,8 @@ def bf16_bits(a: np.ndarray) -> np.ndarray:
     return (a.view(np.uint32) >> np.uint32(16)).astype(np.uint16)
 
 
-def _rng(seed: int, tensor: str) -> np.random.Generator:
-    return np.random.Generator(np.random.Philox(key=seed * 64 + _TENSOR_KEYS[tensor]))
+def _rng(seed: int, tensor: str, draw: int = 0) -> np.random.Generator:
+    return np.random.Generator(np.random.Philox(key=seed * 64 + _TENSOR_KEYS[tensor] + draw * (1 << 40)))
 
 
 def normal(seed: int, tensor: str, shape, std: float, dtype: str, chunk: int = 1 << 26) -> np.ndarray:
@@ -105,13 +115,14 @@ def normal(seed: int, tensor: str, shape, std: float, dtype: str, chunk: int = 1
     return out.reshape(shape)
 
 
-def zipf_bias(seed: int, E: int, s: float) -> np.ndarray:
-    """Per-expert logit offset b_e = -s * ln(r_e), r a seeded permutation of 1..E.
+def zipf_bias(seed: int, E: int, s: float, draw: int = 0) -> np.ndarray:
+    """Per-expert logit offset b_e = -s * ln(r_e), r a seeded permutation of 1..E
+    (draw ``draw`` of the permutation stream).
 
     Adding b to Gaussian logits multiplies expert e's odds by r_e^-s, i.e. a
     Zipf(s) popularity profile over a random ranking of the experts.
     """
-    r = _rng(seed, "zipf_perm").permutation(E).astype(np.float64) + 1.0
+    r = _rng(seed, "zipf_perm", draw).permutation(E).astype(np.float64) + 1.0
     return (-s * np.log(r)).astype(np.float32)
 
 
@@ -142,7 +153,7 @@ def make_inputs(wl: Workload, tensors=("x", "wg", "w_gate", "w_up", "w_down", "d
             out[name] = normal(wl.seed, "w_down", (wl.E, wl.d, wl.h), 1.0 / np.sqrt(wl.h), wl.dtype)
         else:
             raise KeyError(name)
-    out["bias"] = zipf_bias(wl.seed, wl.E, wl.zipf_s) if wl.zipf_s else None
+    out["bias"] = zipf_bias(wl.seed, wl.E, wl.zipf_s, wl.zipf_draw) if wl.zipf_s else None
     return out
 
 
@@ -174,6 +185,15 @@ def structured_logits(T: int, E: int, K: int, kind: str, seed: int = 11) -> np.n
     elif kind == "hot_expert":
         # one expert is in nearly every token's set (skew).
         z[:, E - 1] += np.float32(6.0)
+    elif kind == "sparse_experts":
+        # extreme imbalance: experts 0-2 are never chosen, experts 3, 4 and 5
+        # by exactly 1, 5 and 15 tokens (seeded choice), experts 6 and 7 by
+        # nearly every token (needs E >= 10 and K >= 4).
+        z[:, 0:6] -= np.float32(50.0)
+        for i, n in enumerate((1, 5, 15)):
+            z[g.choice(T, size=n, replace=False), 3 + i] += np.float32(100.0)
+        z[:, 6] += np.float32(5.0)
+        z[:, 7] += np.float32(4.0)
     else:
         raise KeyError(kind)
     return np.ascontiguousarray(z)

@@ -1,35 +1,221 @@
-"""GPU parity at full workload sizes -- the five evaluation workloads and
-MoEBlaze's four printed shapes with plain SiLU experts -- in the launch
-configuration the benchmark times (router on the GPU, the five entry points in
-order, H-only saving, nothing saved by a forward-only workload).
+"""GPU parity at full workload sizes -- the five evaluation workloads,
+MoEBlaze's four printed shapes with plain SiLU experts, and the skewed shape
+under extreme routing -- in the launch configuration the benchmark times
+(the five entry points in order, H-only saving, nothing saved by a
+forward-only workload).
 
-The oracle evaluates sampled outputs one by one: 32 random tokens (out, dx,
-dS, saved a/b/y), the weight gradients of the smallest and the largest
-expert, dWg of the smallest expert; index arrays are checked bit-exact in
-full, and exact zeros for experts without rows.
+Checked, against the oracle:
+  * routing: the GPU's fp32 logits within 1e-4 of the oracle's; the top-K ids
+    equal the oracle's decision on its own logits (rounded to fp32) at every
+    token but near ties (counted, and reported in every message); the weights
+    of every token against the renormalised softmax of the chosen logits;
+  * the index, bit-exact in full, against the oracle's index of the ids it
+    was built from;
+  * 256 sampled tokens: out, dx, dS and the saved a, b and y;
+  * the weight gradients of the smallest expert and of every expert under 16
+    rows (with dWg: the oracle runs every assignment of their tokens), of the
+    largest expert whose expert-only oracle run fits ORACLE_FLOP_BUDGET, and
+    dWg of the largest expert whose router-only oracle run fits it;
+  * exact zeros for experts without rows.
 """
 import sys
+import time
 
 import numpy as np
 import pytest
 
 torch = pytest.importorskip("torch")
 
-from dropless_moe_dispatch_amd import binding as B
 from dropless_moe_dispatch_amd import layer as Lyr
 from dropless_moe_dispatch_amd import synth
 from oracle import moe_oracle as O
-from tests.gpu_util import assert_close, dw_flip_allowance, stored_flip_bounds, to_np, topk_margin
+from tests.gpu_util import (assert_close, dw_flip_allowance, fp32_windows, stored_flip_bounds, to_np,
+                            topk_margin)
 
 pytestmark = pytest.mark.gpu
 
 # what the forward saves for the backward, as bench.py runs it: H-only (a and
 # b; the backward recomputes y), SonicMoE's minimal cached set
 SAVED = "ab"
+SAMPLE = 256
+# float64 FLOP of one oracle run that a check may take (a few seconds on the host)
+ORACLE_FLOP_BUDGET = 1.0e12
+# the skewed workload's named outcome: a few experts above 10% of the
+# assignments, several with 0 or fewer than 16 rows
+FEW_HOT, HOT_SHARE, SEVERAL_COLD, COLD_ROWS = 2, 0.10, 3, 16
+
+_T0 = time.perf_counter()
 
 
 def _say(*a):
-    print("[case]", *a, file=sys.stderr, flush=True)
+    print(f"[case {time.perf_counter() - _T0:7.1f}s]", *a, file=sys.stderr, flush=True)
+
+
+def _run_layer(wl, inp, logits32=None):
+    T, d, E, K, h, dt = wl.T, wl.d, wl.E, wl.K, wl.h, wl.dtype
+    dev = {k: (Lyr.to_device(inp[k], dt) if inp.get(k) is not None else None)
+           for k in ("x", "wg", "w_gate", "w_up", "w_down", "dy")}
+    bias = torch.from_numpy(inp["bias"]).cuda() if inp.get("bias") is not None else None
+    buf = Lyr.MoEBuffers(T, d, E, K, h, dt, backward=wl.backward, act=wl.act, saved=SAVED, save=wl.backward)
+
+    def run():
+        if logits32 is not None:
+            buf.logits.copy_(torch.from_numpy(logits32))
+        Lyr.forward(buf, dev["x"], dev["wg"], bias, dev["w_gate"], dev["w_up"], dev["w_down"],
+                    logits_in=logits32 is not None)
+        buf.y_fwd = buf.y_swi.clone()   # the H-only backward writes A' over y_swi
+        if wl.backward:
+            Lyr.backward(buf, dev["dy"], dev["x"], dev["wg"], dev["w_gate"], dev["w_up"], dev["w_down"])
+        torch.cuda.synchronize()
+
+    gated = wl.act == "swiglu"
+    _say(wl.name, "gpu run 1")
+    run()
+    assert all(e == 0 for e in buf.device_error_words()), buf.device_error_words()
+    keep = {k: getattr(buf, k).clone() for k in ("out",) + (("dx", "dw_gate", "dw_down", "dwg")
+                                                            + (("dw_up",) if gated else ()) if wl.backward else ())}
+    _say(wl.name, "gpu run 2 (repeatability)")
+    run()
+    for k, v in keep.items():
+        assert torch.equal(v, getattr(buf, k)), f"run-to-run difference in {k}"
+    return buf
+
+
+def _oracle_cost(n_tokens, slots, wl):
+    """float64 FLOP of an oracle forward + backward over n_tokens tokens and
+    ``slots`` of their assignments each."""
+    per = 18.0 if wl.act == "swiglu" else 12.0
+    return per * n_tokens * slots * wl.d * wl.h
+
+
+def _router_cost(n_tokens, wl):
+    """float64 FLOP of an oracle forward + router-only backward over n_tokens tokens."""
+    per = 8.0 if wl.act == "swiglu" else 6.0
+    return per * n_tokens * wl.K * wl.d * wl.h
+
+
+def _check(wl, inp, buf, z, given):
+    """z: the oracle's float64 logits (given: the fp32 logits the GPU routed on)."""
+    T, d, E, K, h, dt = wl.T, wl.d, wl.E, wl.K, wl.h, wl.dtype
+    gated = wl.act == "swiglu"
+    name = wl.name
+    zg = to_np(buf.logits)
+    dz = float(np.abs(zg - z).max())
+    assert dz < 1e-4, dz
+    z32 = z.astype(np.float32)
+    ids_ref = O.topk_select(z32, K)
+    ids_gpu = to_np(buf.topk_ids)
+    mism = np.nonzero((ids_gpu != ids_ref).any(axis=1))[0]
+    tag = f"({len(mism)} near-tie tokens, max |dz| {dz:.2e})"
+    _say(name, "routing", tag)
+    if given:
+        assert len(mism) == 0, f"routing differs on identical logits {tag}"
+    margin = topk_margin(z32, K)
+    assert np.all(margin[mism] <= 4 * dz), f"routing differs away from a near tie {tag}"
+    # the index is bit-exact on the ids it was built from (the oracle's own
+    # everywhere but at the near ties)
+    ix = O.build_index(ids_gpu, E)
+    assert np.array_equal(to_np(buf.offsets), ix["offsets"]), f"offsets {tag}"
+    assert np.array_equal(to_np(buf.eti), ix["expert_token_indices"]), f"expert_token_indices {tag}"
+    assert np.array_equal(to_np(buf.tim), ix["token_index_map"]), f"token_index_map {tag}"
+    # the weights of every token: the renormalised softmax of its chosen logits
+    np.testing.assert_allclose(to_np(buf.topk_w), O.topk_weights(z32.astype(np.float64), ids_gpu),
+                               rtol=1e-4, atol=1e-7, err_msg=f"topk_w {tag}")
+    w_ref = O.topk_weights(z32.astype(np.float64), ids_ref)
+    counts = np.bincount(ids_ref.reshape(-1), minlength=E)
+    _say(name, "rows per expert: max", counts.max(), "min", counts.min(), "zero", int((counts == 0).sum()),
+         f"under {COLD_ROWS}", int((counts < COLD_ROWS).sum()))
+
+    rng = np.random.default_rng(wl.seed)
+    ok_tokens = np.setdiff1d(np.arange(T), mism)
+    sub = np.sort(rng.choice(ok_tokens, size=min(SAMPLE, len(ok_tokens)), replace=False))
+    subd = torch.from_numpy(sub).cuda()
+    _say(name, "oracle on", len(sub), "sampled tokens")
+    f = O.moe_forward(inp["x"][sub], ids_ref[sub], w_ref[sub], inp["w_gate"], inp["w_up"], inp["w_down"], dtype=dt,
+                      act=wl.act)
+    assert_close(f"out[sample] {tag}", to_np(buf.out[subd]), f["out"])
+    pos = torch.from_numpy(to_np(buf.tim).reshape(T, K)[sub].reshape(-1)).cuda()
+    assert_close("y[sample]", to_np(buf.y_fwd[pos]).reshape(len(sub), K, -1), f["y_s"])
+    if buf.h_ab is not None:   # a forward-only workload saves nothing
+        hab = to_np(buf.h_ab[pos]).reshape(len(sub), K, -1)
+        assert_close("a[sample]", hab[..., :h], f["a_s"])
+        if gated:
+            assert_close("b[sample]", hab[..., h:], f["b_s"])
+    if not wl.backward:
+        return counts
+    b = O.moe_backward(inp["dy"][sub], inp["x"][sub], inp["wg"], ids_ref[sub], w_ref[sub], inp["w_gate"],
+                       inp["w_up"], inp["w_down"], f, z32[sub].astype(np.float64), dtype=dt, act=wl.act,
+                       saved=SAVED)
+    assert_close(f"dx[sample] {tag}", to_np(buf.dx[subd]), b["dx"])
+    assert_close("ds[sample]", to_np(buf.ds)[sub], b["ds_router"])
+
+    def toks_of(e):
+        toks = np.nonzero((ids_ref == e).any(axis=1))[0]
+        return None if np.isin(toks, mism).any() else toks
+
+    def check_dw(e, toks, full):
+        """dW of expert e from an oracle run over its tokens: every assignment
+        of them (full: dWg too), or e's alone."""
+        only = None if full else [e]
+        _say(name, "oracle expert", e, "rows", len(toks), "full" if full else "expert-only")
+        x_t, dy_t = inp["x"][toks], inp["dy"][toks]
+        fe = O.moe_forward(x_t, ids_ref[toks], w_ref[toks], inp["w_gate"], inp["w_up"], inp["w_down"], dtype=dt,
+                           only_experts=only, act=wl.act)
+        be = O.moe_backward(dy_t, x_t, inp["wg"], ids_ref[toks], w_ref[toks], inp["w_gate"], inp["w_up"],
+                            inp["w_down"], fe, z32[toks].astype(np.float64), dtype=dt, only_experts=only,
+                            act=wl.act, saved=SAVED)
+        win = fp32_windows(x_t, dy_t, ids_ref[toks], inp["w_gate"], inp["w_up"], inp["w_down"], act=wl.act,
+                           only_experts=[e])
+        fl = stored_flip_bounds(fe, be, w_ref[toks], dt, wl.act, SAVED, win)
+        it = ids_ref[toks]
+
+        def allow(key, rows, transpose=False):
+            return dw_flip_allowance(fl[key], it, rows, E, transpose, experts=[e])[e]
+
+        assert_close(f"dw_gate[{e}]", to_np(buf.dw_gate[e]), be["dw_gate"][e], allow=allow("da", x_t))
+        if gated:
+            assert_close(f"dw_up[{e}]", to_np(buf.dw_up[e]), be["dw_up"][e], allow=allow("db", x_t))
+        assert_close(f"dw_down[{e}]", to_np(buf.dw_down[e]), be["dw_down"][e], allow=allow("ap", dy_t, True))
+        if full:
+            assert_close(f"dwg[{e}]", to_np(buf.dwg[e]), be["dwg"][e])
+
+    nz = np.nonzero(counts > 0)[0]
+    by_size = nz[np.argsort(counts[nz], kind="stable")]
+    e_small = int(by_size[0])
+    full = sorted({e_small} | {int(e) for e in nz if counts[e] < COLD_ROWS})
+    for e in full:
+        toks = toks_of(e)
+        if toks is not None and _oracle_cost(len(toks), K, wl) <= ORACLE_FLOP_BUDGET:
+            check_dw(e, toks, True)
+    # the largest expert whose expert-only oracle run fits the budget
+    for e in by_size[::-1]:
+        toks = toks_of(int(e))
+        if toks is not None and _oracle_cost(len(toks), 1, wl) <= ORACLE_FLOP_BUDGET:
+            if int(e) not in full:
+                check_dw(int(e), toks, False)
+            break
+    # dWg of the largest expert whose router-only oracle run fits the budget:
+    # dz of its tokens needs the score gradients of all their assignments
+    for e in by_size[::-1]:
+        e = int(e)
+        toks = toks_of(e)
+        if toks is None or _router_cost(len(toks), wl) > ORACLE_FLOP_BUDGET:
+            continue
+        if e in full:
+            break
+        _say(name, "oracle router gradient of expert", e, "rows", len(toks))
+        fe = O.moe_forward(inp["x"][toks], ids_ref[toks], w_ref[toks], inp["w_gate"], inp["w_up"], inp["w_down"],
+                           dtype=dt, act=wl.act)
+        be = O.moe_backward(inp["dy"][toks], inp["x"][toks], inp["wg"], ids_ref[toks], w_ref[toks],
+                            inp["w_gate"], inp["w_up"], inp["w_down"], fe, z32[toks].astype(np.float64), dtype=dt,
+                            act=wl.act, saved=SAVED, router_only=True)
+        assert_close(f"dwg[{e}]", to_np(buf.dwg[e]), be["dwg"][e])
+        break
+    for e in np.nonzero(counts == 0)[0]:
+        for key in ("dw_gate", "dw_down", "dwg") + (("dw_up",) if gated else ()):
+            assert float(getattr(buf, key)[int(e)].abs().max()) == 0.0, (key, e)
+    _say(name, "done")
+    return counts
 
 
 @pytest.mark.timeout(900)
@@ -39,110 +225,34 @@ def test_workload_full_size(idx):
         pytest.skip("no GPU")
     wl = synth.WORKLOADS[idx]
     _say("workload", idx, wl.name, "generate")
-    T, d, E, K, h, dt = wl.T, wl.d, wl.E, wl.K, wl.h, wl.dtype
-    gated = wl.act == "swiglu"
     tensors = ("x", "wg", "w_gate", "w_up", "w_down") + (("dy",) if wl.backward else ())
     inp = synth.make_inputs(wl, tensors=tensors)
-    dev = {k: (Lyr.to_device(inp[k], dt) if inp[k] is not None else None) for k in tensors}
-    bias = torch.from_numpy(inp["bias"]).cuda() if inp["bias"] is not None else None
-    buf = Lyr.MoEBuffers(T, d, E, K, h, dt, backward=wl.backward, act=wl.act, saved=SAVED, save=wl.backward)
-
-    def run():
-        Lyr.forward(buf, dev["x"], dev["wg"], bias, dev["w_gate"], dev["w_up"], dev["w_down"])
-        if wl.backward:
-            Lyr.backward(buf, dev["dy"], dev["x"], dev["wg"], dev["w_gate"], dev["w_up"], dev["w_down"])
-        torch.cuda.synchronize()
-
-    _say("workload", idx, "gpu run 1")
-    run()
-    assert buf.device_error_words() == [0, 0][: 2 if wl.backward else 1] or all(
-        e == 0 for e in buf.device_error_words())
-    keep = {k: getattr(buf, k).clone() for k in ("out",) + (("dx", "dw_gate", "dw_down", "dwg")
-                                                            + (("dw_up",) if gated else ()) if wl.backward else ())}
-    _say("workload", idx, "gpu run 2 (repeatability)")
-    run()
-    for k, v in keep.items():
-        assert torch.equal(v, getattr(buf, k)), f"run-to-run difference in {k}"
-    del keep
-
-    _say("workload", idx, "oracle routing")
+    buf = _run_layer(wl, inp)
     z = O.router_logits(inp["x"], inp["wg"], inp["bias"])
-    zg = to_np(buf.logits)
-    dz = float(np.abs(zg - z).max())
-    assert dz < 1e-4, dz
-    z32 = z.astype(np.float32)
-    ids_ref = O.topk_select(z32, K)
-    ids_gpu = to_np(buf.topk_ids)
-    mism = np.nonzero((ids_gpu != ids_ref).any(axis=1))[0]
-    margin = topk_margin(z32, K)
-    assert np.all(margin[mism] <= 4 * dz), "routing differs away from a near tie"
-    _say("workload", idx, "near-tie tokens:", len(mism), "max |dz|:", dz)
-    w_ref = O.topk_weights(z32.astype(np.float64), ids_ref)
-    counts = np.bincount(ids_ref.reshape(-1), minlength=E)
-    if len(mism) == 0:
-        ix = O.build_index(ids_ref, E)
-        assert np.array_equal(to_np(buf.offsets), ix["offsets"])
-        assert np.array_equal(to_np(buf.eti), ix["expert_token_indices"])
-        assert np.array_equal(to_np(buf.tim), ix["token_index_map"])
-        np.testing.assert_allclose(to_np(buf.topk_w), w_ref, rtol=1e-4, atol=1e-7)
+    counts = _check(wl, inp, buf, z, given=False)
     if wl.zipf_s:
-        share = counts.max() / counts.sum()
-        # the Zipf(1.2) logit offset puts one expert in nearly every token's set
-        # and leaves the least popular experts with only a few tens of rows
-        assert share > 0.10 and counts.min() < 32, (share, counts.min())
+        share = counts / counts.sum()
+        hot, cold = int((share > HOT_SHARE).sum()), int((counts < COLD_ROWS).sum())
+        assert hot >= FEW_HOT and cold >= SEVERAL_COLD, (hot, cold, counts.min())
 
-    rng = np.random.default_rng(idx)
-    ok_tokens = np.setdiff1d(np.arange(T), mism)
-    sub = np.sort(rng.choice(ok_tokens, size=min(32, len(ok_tokens)), replace=False))
-    _say("workload", idx, "oracle sampled tokens")
-    f = O.moe_forward(inp["x"][sub], ids_ref[sub], w_ref[sub], inp["w_gate"], inp["w_up"], inp["w_down"], dtype=dt,
-                      act=wl.act)
-    assert_close("out[sample]", to_np(buf.out[torch.from_numpy(sub).cuda()]), f["out"])
-    pos = to_np(buf.tim).reshape(T, K)[sub]
-    yv = to_np(buf.y_swi[torch.from_numpy(pos.reshape(-1)).cuda()]).reshape(len(sub), K, -1)
-    assert_close("y[sample]", yv, f["y_s"])
-    if buf.h_ab is not None:   # a forward-only workload saves nothing
-        hab = to_np(buf.h_ab[torch.from_numpy(pos.reshape(-1)).cuda()]).reshape(len(sub), K, -1)
-        assert_close("a[sample]", hab[..., :h], f["a_s"])
-        if gated:
-            assert_close("b[sample]", hab[..., h:], f["b_s"])
-    if not wl.backward:
-        return
-    b = O.moe_backward(inp["dy"][sub], inp["x"][sub], inp["wg"], ids_ref[sub], w_ref[sub], inp["w_gate"],
-                       inp["w_up"], inp["w_down"], f, z32[sub].astype(np.float64), dtype=dt, act=wl.act,
-                       saved=SAVED)
-    assert_close("dx[sample]", to_np(buf.dx[torch.from_numpy(sub).cuda()]), b["dx"])
-    assert_close("ds[sample]", to_np(buf.ds)[sub], b["ds_router"])
 
-    nz = np.nonzero(counts > 0)[0]
-    e_small = int(nz[np.argmin(counts[nz])])
-    e_big = int(np.argmax(counts))
-    for e in sorted({e_small, e_big}):
-        toks = np.nonzero((ids_ref == e).any(axis=1))[0]
-        if np.isin(toks, mism).any():
-            continue
-        if e == e_big and e != e_small and len(toks) * h * d > 4e10:
-            continue   # the largest expert of the widest shapes: too slow for the float64 oracle
-        _say("workload", idx, "oracle expert", e, "rows", len(toks))
-        full_k = e == e_small
-        fe = O.moe_forward(inp["x"][toks], ids_ref[toks], w_ref[toks], inp["w_gate"], inp["w_up"], inp["w_down"],
-                           dtype=dt, only_experts=None if full_k else [e], act=wl.act)
-        be = O.moe_backward(inp["dy"][toks], inp["x"][toks], inp["wg"], ids_ref[toks], w_ref[toks], inp["w_gate"],
-                            inp["w_up"], inp["w_down"], fe, z32[toks].astype(np.float64), dtype=dt,
-                            only_experts=None if full_k else [e], act=wl.act, saved=SAVED)
-        it = ids_ref[toks]
-        fl = stored_flip_bounds(fe, be, w_ref[toks], dt, wl.act, SAVED)
-
-        def allow(key, rows, transpose=False):
-            return dw_flip_allowance(fl[key], it, rows, E, transpose, experts=[e])[e]
-
-        assert_close(f"dw_gate[{e}]", to_np(buf.dw_gate[e]), be["dw_gate"][e], allow=allow("da", inp["x"][toks]))
-        if gated:
-            assert_close(f"dw_up[{e}]", to_np(buf.dw_up[e]), be["dw_up"][e], allow=allow("db", inp["x"][toks]))
-        assert_close(f"dw_down[{e}]", to_np(buf.dw_down[e]), be["dw_down"][e],
-                     allow=allow("ap", inp["dy"][toks], True))
-        if full_k:
-            assert_close(f"dwg[{e}]", to_np(buf.dwg[e]), be["dwg"][e])
-    for e in np.nonzero(counts == 0)[0]:
-        for key in ("dw_gate", "dw_down", "dwg") + (("dw_up",) if gated else ()):
-            assert float(getattr(buf, key)[int(e)].abs().max()) == 0.0, (key, e)
+@pytest.mark.timeout(900)
+def test_skewed_shape_extreme_routing():
+    """The skewed workload's shape (T=16384, d=4096, E=64, K=6, h=1536) under
+    routing that empties three experts, gives three others 1, 5 and 15 rows
+    and puts two experts in nearly every token's set (the stress test of
+    extreme imbalance the MoEBlaze analysis page proposes, sec. 7 item 6).
+    It runs the 256 x 256 gate/up and dW tiles and both folds on the
+    128 x 256 tile with experts of 0, 1, 5 and 15 rows."""
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    base = synth.WORKLOADS[5]
+    wl = synth.Workload("skewed_shape_sparse_experts", base.T, base.d, base.E, base.K, base.h, "bf16", True,
+                        seed=1105)
+    _say(wl.name, "generate")
+    inp = synth.make_inputs(wl)
+    z = synth.structured_logits(wl.T, wl.E, wl.K, "sparse_experts", seed=1105).astype(np.float64)
+    buf = _run_layer(wl, inp, logits32=z.astype(np.float32))
+    counts = _check(wl, inp, buf, z, given=True)
+    assert (counts == 0).sum() >= 3 and ((counts > 0) & (counts < COLD_ROWS)).sum() >= 3, counts
+    assert (counts / counts.sum() > HOT_SHARE).sum() >= 2, counts
