@@ -207,7 +207,7 @@ class ClockSampler:
                           f"for {self.duration:g} s after the timed steps (first {self.settle:g} s dropped)"}
 
 
-def cpu_baseline(wl, inp, sample_tokens):
+def cpu_baseline(wl, inp, sample_tokens, saved="ab"):
     """The CPU oracle (float64 numpy) on the first ``sample_tokens`` tokens of
     the same workload, forward + backward."""
     import numpy as np
@@ -226,7 +226,7 @@ def cpu_baseline(wl, inp, sample_tokens):
     f = O.moe_forward(x, ids, w, inp["w_gate"], inp["w_up"], inp["w_down"], dtype=wl.dtype, act=wl.act)
     if wl.backward:
         O.moe_backward(dy, x, inp["wg"], ids, w, inp["w_gate"], inp["w_up"], inp["w_down"], f, z, dtype=wl.dtype,
-                       act=wl.act)
+                       act=wl.act, saved=saved)
     dt = time.perf_counter() - t0
     return {"value": n / dt, "unit": "tokens/s", "cores": int(cores), "kind": "oracle",
             "sample": f"first {n} tokens of the workload, router+index+forward" + ("+backward" if wl.backward else "")
@@ -238,8 +238,9 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=3)
-    ap.add_argument("--workload", type=int, default=3, help="1..9 (default 3: fine-grained fwd+bwd; 6..9: MoEBlaze's shapes, SiLU experts)")
-    ap.add_argument("--cpu-sample", type=int, default=64, help="tokens for the CPU oracle baseline (0 = skip)")
+    ap.add_argument("--workload", type=int, default=4,
+                    help="1..9 (default 4: large-d fwd+bwd, the largest workload; 6..9: MoEBlaze's shapes, SiLU experts)")
+    ap.add_argument("--cpu-sample", type=int, default=32, help="tokens for the CPU oracle baseline (0 = skip)")
     ap.add_argument("--saved", default="ab", choices=("aby", "ab"),
                     help="saved for backward: H-only (a and b; y recomputed; default) or a, b and y")
     ap.add_argument("--combine", default="fold", choices=("fold", "staged"),
@@ -336,6 +337,7 @@ def main():
         torch.cuda.synchronize()
         del src, dst
     errs = buf.device_error_words()
+    buf.check_device_errors()   # a fold that gave up leaves out / dx invalid: no number is reported then
 
     ms = (t1 - t0) * 1e3 / args.steps
     gated = wl.act == "swiglu"
@@ -347,21 +349,43 @@ def main():
     for name, t in recs:
         per.setdefault(name, []).append(t)
     per_kernel = {k: {"avg_ms": float(np.mean(v)), "launches": len(v)} for k, v in per.items()}
+    peak = PEAK_BF16_TFLOPS if dt == "bf16" else PEAK_F32_MFMA_TFLOPS
+    eb = 2 if dt == "bf16" else 4
+
+    def floors(k):
+        """The kernel's two roofline floors (ms): its model FLOP at the MFMA
+        peak and its algorithmic bytes at the HBM peak (None where not
+        defined); the larger one binds."""
+        fl = kernel_flops(k, T, d, E, K, h, gated)
+        by = kernel_bytes(k, T, d, E, K, h, eb, gated)
+        f_mfma = fl / (peak * 1e12) * 1e3 if fl is not None else None
+        f_hbm = by / (PEAK_HBM_GBS * 1e9) * 1e3 if by is not None else None
+        if f_mfma is None and f_hbm is None:
+            return None, None, None
+        bound = "mfma" if f_hbm is None or (f_mfma is not None and f_mfma >= f_hbm) else "hbm"
+        return f_mfma, f_hbm, bound
+
     roofline = None
     gemms = {k: v for k, v in per_kernel.items() if kernel_flops(k, T, d, E, K, h, gated) is not None and k != "router_logits"}
     if gemms:
         dom = max(gemms, key=lambda k: gemms[k]["avg_ms"] * gemms[k]["launches"])
         fl = kernel_flops(dom, T, d, E, K, h, gated)
-        ach = fl / (gemms[dom]["avg_ms"] * 1e-3) / 1e12
-        peak = PEAK_BF16_TFLOPS if dt == "bf16" else PEAK_F32_MFMA_TFLOPS
-        roofline = {"bound": "mfma", "kernel": dom, "achieved": round(ach, 2), "peak": peak, "unit": "TFLOP/s",
-                    "frac": round(ach / peak, 4), "traffic": committed_traffic(wl.name, dom),
-                    "avg_launch_ms": round(gemms[dom]["avg_ms"], 4), "algorithmic_flop_per_launch": fl,
+        by = kernel_bytes(dom, T, d, E, K, h, eb, gated)
+        f_mfma, f_hbm, bound = floors(dom)
+        t = gemms[dom]["avg_ms"]
+        if bound == "mfma":
+            ach, pk, unit = fl / (t * 1e-3) / 1e12, peak, "TFLOP/s"
+        else:
+            ach, pk, unit = by / (t * 1e-3) / 1e9, PEAK_HBM_GBS, "GB/s"
+        roofline = {"bound": bound, "kernel": dom, "achieved": round(ach, 2), "peak": pk, "unit": unit,
+                    "frac": round(ach / pk, 4), "traffic": committed_traffic(wl.name, dom),
+                    "avg_launch_ms": round(t, 4), "algorithmic_flop_per_launch": fl,
+                    "algorithmic_bytes_per_launch": by,
+                    "floor_ms": {"mfma": round(f_mfma, 4) if f_mfma else None,
+                                 "hbm": round(f_hbm, 4) if f_hbm else None},
                     "src_sha": kernel_source_hash(),
-                    "peak_at_measured_clock": round(peak * cscale, 1) if cscale else None,
-                    "frac_at_measured_clock": round(ach / (peak * cscale), 4) if cscale else None}
-    peak = PEAK_BF16_TFLOPS if dt == "bf16" else PEAK_F32_MFMA_TFLOPS
-    eb = 2 if dt == "bf16" else 4
+                    "peak_at_measured_clock": round(pk * cscale, 1) if (cscale and bound == "mfma") else None,
+                    "frac_at_measured_clock": round(ach / (pk * cscale), 4) if (cscale and bound == "mfma") else None}
     kernels = {}
     for k, v in per_kernel.items():
         rec = {"avg_ms": round(v["avg_ms"], 4)}
@@ -373,9 +397,13 @@ def main():
         if by is not None:
             rec["gbs"] = round(by / (v["avg_ms"] * 1e-3) / 1e9, 1)
             rec["hbm_peak_frac"] = round(rec["gbs"] / PEAK_HBM_GBS, 4)
+        f_mfma, f_hbm, bound = floors(k)
+        if bound is not None:
+            rec["bound"] = bound
+            rec["floor_frac"] = round(max(x for x in (f_mfma, f_hbm) if x is not None) / v["avg_ms"], 4)
         kernels[k] = rec
     counts = np.diff(buf.offsets.cpu().numpy())
-    cpu = cpu_baseline(wl, inp, args.cpu_sample) if args.cpu_sample > 0 else None
+    cpu = cpu_baseline(wl, inp, args.cpu_sample, args.saved) if args.cpu_sample > 0 else None
     out = {
         "metric": METRIC,
         "value": round(T / (ms * 1e-3), 1),
