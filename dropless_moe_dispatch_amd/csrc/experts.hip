@@ -94,16 +94,52 @@ static int forced_tile() {
   }();
   return v;
 }
-// Row blocks per tile group of the non-fold kernels (see grouped_tile); 8
-// gains a few percent at large d on MI355X.  MOE_DISPATCH_GROUP_ROWS
-// overrides it for tuning.
-static int tile_group_rows() {
-  static int v = [] {
-    const char* e = getenv("MOE_DISPATCH_GROUP_ROWS");
-    const int r = e ? atoi(e) : 0;
+// Tile order of the varlen-M kernels (gate/up, plain-expert forward, dH,
+// staged down projection): groups of R = 8 row blocks (grouped_tile), and
+// over each group an XCD grid (tile_of): workgroups go to the eight XCDs in
+// turn, so in launch order all XCDs work on the same group -- one expert's
+// weights and rows, which the memory-side cache then serves to all of them --
+// and each XCD takes a 2-D part of it (xg row residues x 8/xg column residues)
+// for reuse in its own L2.  The host takes xg = 2, else 4, else 8, the first
+// that divides the group.  Measured on MI355X at T=32768, d=6144, E=64, K=4,
+// h=2048: gate/up 7.47 -> 6.81 ms and dH 4.12 -> 3.78 ms against the earlier
+// order (each XCD a contiguous range of groups, one expert per XCD at a
+// time); xg = 4 and 8 land within 1% of xg = 2.
+// Tuning switches, read once per process:
+//   MOE_DISPATCH_GROUP_ROWS=R (1..64), MOE_DISPATCH_GROUP_XCD=1|2|4|8 forces
+//   xg, MOE_DISPATCH_GROUP_XCD=0 turns the grid off and runs the earlier
+//   orders: contiguous XCD ranges (MOE_DISPATCH_XCD_SWIZZLE=1, default) or
+//   launch order (=0), with groups inside each expert
+//   (MOE_DISPATCH_EXPERT_GROUPS=1, default) or over the global row blocks (=0).
+static int env_int(const char* name, int dflt) {
+  const char* e = getenv(name);
+  return e ? atoi(e) : dflt;
+}
+struct TileOrder {
+  int nblk;  // block count for the XCD swizzle (0: launch order)
+  int grp;   // group rows: > 0 global groups, < 0 groups inside each expert
+  int xg;    // XCD grid rows over a group (0: none)
+};
+static TileOrder tile_order(long long nblk, int nbn) {
+  static const int R = [] {
+    const int r = env_int("MOE_DISPATCH_GROUP_ROWS", 8);
     return r >= 1 && r <= 64 ? r : 8;
   }();
-  return v;
+  static const int force_xg = env_int("MOE_DISPATCH_GROUP_XCD", -1);
+  static const bool swizzle = env_int("MOE_DISPATCH_XCD_SWIZZLE", 1) != 0;
+  static const bool expert_groups = env_int("MOE_DISPATCH_EXPERT_GROUPS", 1) != 0;
+  int xg = 0;
+  if (force_xg == 1 || force_xg == 2 || force_xg == 4 || force_xg == 8) {
+    xg = force_xg;
+  } else if (force_xg != 0) {
+    for (int c : {2, 4, 8})
+      if (R % c == 0 && nbn % (8 / c) == 0) {
+        xg = c;
+        break;
+      }
+  }
+  if (xg) return {0, R, xg};
+  return {swizzle ? (int)nblk : 0, expert_groups ? -R : R, 0};
 }
 static bool pick_large(bool auto_choice) {
   const int f = forced_tile();
@@ -147,13 +183,13 @@ __global__ __launch_bounds__(C::NT, C::WAVES_PER_EU) void gate_up_kernel(
     const typename C::T* __restrict__ x, const int32_t* __restrict__ offsets, const int32_t* __restrict__ eti,
     const int32_t* __restrict__ mb_off, const typename C::T* __restrict__ w_gate,
     const typename C::T* __restrict__ w_up, typename C::T* __restrict__ h_ab, typename C::T* __restrict__ y_swi,
-    int T, int d, int E, int h, int nbn, int nblk, int grp) {
+    int T, int d, int E, int h, int nbn, int nblk, int grp, int xg) {
   __shared__ __attribute__((aligned(16))) char smem[smem_bytes<C>()];
   using TIN = typename C::T;
   constexpr int HB = C::BN / 2;     // gate (= up) columns per tile
   constexpr int HF = C::FN / 2;     // gate fragments per wave
   int g, nb;
-  if (!grouped_tile(xcd_swizzle(blockIdx.x, nblk), mb_off[E], nbn, grp, g, nb)) return;
+  if (!tile_of(xcd_swizzle(blockIdx.x, nblk), mb_off, E, nbn, grp, xg, g, nb)) return;
   const RowTile rt = decode_row_tile<C::BM>(mb_off, offsets, E, g);
   const int wave = threadIdx.x >> 6, wm = wave / C::WN, wn = wave % C::WN;
   const uint32_t ldx = (uint32_t)d * sizeof(TIN);
@@ -223,9 +259,10 @@ static hipError_t gate_up_t(const Shape& s, const void* x, const int32_t* offset
   const int nbn = col_blocks(s.h, C::BN / 2);
   long long nblk = max_row_blocks(s, BM) * nbn;
   nblk = (nblk + 7) / 8 * 8;
+  const TileOrder to = tile_order(nblk, nbn);
   gate_up_kernel<C><<<dim3((unsigned)nblk), dim3(C::NT), 0, st>>>(
       (const TIN*)x, offsets, eti, ws.tile_map(BM), (const TIN*)w_gate, (const TIN*)w_up, (TIN*)h_ab, (TIN*)y_swi,
-      s.T, s.d, s.E, s.h, nbn, (int)nblk, tile_group_rows());
+      s.T, s.d, s.E, s.h, nbn, to.nblk, to.grp, to.xg);
   return hipGetLastError();
 }
 
@@ -236,11 +273,11 @@ template <class C>
 __global__ __launch_bounds__(C::NT, C::WAVES_PER_EU) void up_act_kernel(
     const typename C::T* __restrict__ x, const int32_t* __restrict__ offsets, const int32_t* __restrict__ eti,
     const int32_t* __restrict__ mb_off, const typename C::T* __restrict__ w1, typename C::T* __restrict__ h_a,
-    typename C::T* __restrict__ y_swi, int T, int d, int E, int h, int act, int nbn, int nblk, int grp) {
+    typename C::T* __restrict__ y_swi, int T, int d, int E, int h, int act, int nbn, int nblk, int grp, int xg) {
   __shared__ __attribute__((aligned(16))) char smem[smem_bytes<C>()];
   using TIN = typename C::T;
   int g, nb;
-  if (!grouped_tile(xcd_swizzle(blockIdx.x, nblk), mb_off[E], nbn, grp, g, nb)) return;
+  if (!tile_of(xcd_swizzle(blockIdx.x, nblk), mb_off, E, nbn, grp, xg, g, nb)) return;
   const RowTile rt = decode_row_tile<C::BM>(mb_off, offsets, E, g);
   const int wave = threadIdx.x >> 6, wm = wave / C::WN, wn = wave % C::WN;
   const uint32_t ldx = (uint32_t)d * sizeof(TIN);
@@ -303,9 +340,10 @@ static hipError_t up_act_t(const Shape& s, const void* x, const int32_t* offsets
   const int nbn = col_blocks(s.h, C::BN);
   long long nblk = max_row_blocks(s, BM) * nbn;
   nblk = (nblk + 7) / 8 * 8;
+  const TileOrder to = tile_order(nblk, nbn);
   up_act_kernel<C><<<dim3((unsigned)nblk), dim3(C::NT), 0, st>>>(
       (const TIN*)x, offsets, eti, ws.tile_map(BM), (const TIN*)w1, (TIN*)h_a, (TIN*)y_swi, s.T, s.d, s.E, s.h,
-      s.act, nbn, (int)nblk, tile_group_rows());
+      s.act, nbn, to.nblk, to.grp, to.xg);
   return hipGetLastError();
 }
 
@@ -694,12 +732,12 @@ template <class C>
 __global__ __launch_bounds__(C::NT, C::WAVES_PER_EU) void down_staged_kernel(
     const typename C::T* __restrict__ y_swi, const typename C::T* __restrict__ w_down,
     const int32_t* __restrict__ offsets, const int32_t* __restrict__ mb_off, typename C::T* __restrict__ ystage,
-    int d, int E, int h, int nbn, int nblk, int grp) {
+    int d, int E, int h, int nbn, int nblk, int grp, int xg) {
   static_assert(C::BM == 128 && C::BN == 128 && C::NT == NTHREADS, "128 x 128 tile, four waves");
   __shared__ __attribute__((aligned(16))) char smem[smem_bytes<C>()];
   using TIN = typename C::T;
   int g, nb;
-  if (!grouped_tile(xcd_swizzle(blockIdx.x, nblk), mb_off[E], nbn, grp, g, nb)) return;
+  if (!tile_of(xcd_swizzle(blockIdx.x, nblk), mb_off, E, nbn, grp, xg, g, nb)) return;
   const RowTile rt = decode_row_tile<C::BM>(mb_off, offsets, E, g);
   const int wave = threadIdx.x >> 6, wm = wave / C::WN, wn = wave % C::WN;
   const uint32_t ldy = (uint32_t)h * sizeof(TIN);
@@ -809,10 +847,11 @@ static hipError_t combine_staged_t(const Shape& s, const void* y_swi, const void
   using C = GCfg<TIN, TILE_S>;
   const int nbn = col_blocks(s.d, TILE_S);
   const long long nblk = (max_row_blocks(s, TILE_S) * nbn + 7) / 8 * 8;
+  const TileOrder to = tile_order(nblk, nbn);
   timing_mark(st, "down_staged", true);
   down_staged_kernel<C><<<dim3((unsigned)nblk), dim3(C::NT), 0, st>>>(
       (const TIN*)y_swi, (const TIN*)w_down, offsets, ws.tile_map(TILE_S), (TIN*)ws.ystage, s.d, s.E, s.h, nbn,
-      (int)nblk, tile_group_rows());
+      to.nblk, to.grp, to.xg);
   timing_mark(st, "down_staged", false);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
@@ -894,11 +933,11 @@ __global__ __launch_bounds__(C::NT, C::WAVES_PER_EU) void dh_kernel(
     const typename C::T* __restrict__ h_ab, const typename C::T* __restrict__ y_swi,
     const int32_t* __restrict__ offsets, const int32_t* __restrict__ eti, const int32_t* __restrict__ mb_off,
     const float* __restrict__ w_pos, typename C::T* __restrict__ dh, float* __restrict__ ds_part,
-    typename C::T* __restrict__ a_prime, int T, int d, int E, int h, int act, int nbn, int nblk, int grp) {
+    typename C::T* __restrict__ a_prime, int T, int d, int E, int h, int act, int nbn, int nblk, int grp, int xg) {
   __shared__ __attribute__((aligned(16))) char smem[smem_bytes<C>()];
   using TIN = typename C::T;
   int g, nb;
-  if (!grouped_tile(xcd_swizzle(blockIdx.x, nblk), mb_off[E], nbn, grp, g, nb)) return;
+  if (!tile_of(xcd_swizzle(blockIdx.x, nblk), mb_off, E, nbn, grp, xg, g, nb)) return;
   const RowTile rt = decode_row_tile<C::BM>(mb_off, offsets, E, g);
   const int wave = threadIdx.x >> 6, wm = wave / C::WN, wn = wave % C::WN;
   const uint32_t ldd = (uint32_t)d * sizeof(TIN);
@@ -1313,6 +1352,26 @@ MOE_DEV void split_rows(int q0, int q1, int& p0, int& p1) {
   p1 = min_i(q1, p0 + len);
 }
 
+// Tile of a dW GEMM's workgroup.  Workgroups go to the eight XCDs in turn
+// (linear block id mod 8), and a dW grid has E (and split) planes of nmb x nnb
+// tiles.  With gr x gc = 8 (host-chosen; 0 keeps launch order), XCD x takes the
+// row blocks = x / gc (mod gr) and column blocks = x % gc (mod gc) of every
+// plane, in row-major order: an XCD's L2 then serves nmb / gr row blocks and
+// nnb / gc column blocks of an expert, and each operand block is fetched by gc
+// (A) or gr (B) XCDs, not by all eight.  Needs nmb % gr == nnb % gc == 0,
+// which also makes the plane size a multiple of 8.
+MOE_DEV void dw_tile(int bx, int nmb, int nnb, int gr, int gc, int& mb, int& nb) {
+  if (gr == 0) {
+    mb = bx / nnb;
+    nb = bx % nnb;
+    return;
+  }
+  const int x = bx & 7, j = bx >> 3;  // the XCD of the block and its turn there
+  const int cols = nnb / gc;          // column blocks of one XCD
+  mb = x / gc + gr * (j / cols);
+  nb = x % gc + gc * (j % cols);
+}
+
 // dW from its chunk partials [ns][E][M][N]: the sum over chunks in chunk
 // order; rows m < M0 of expert e go to out0 ([E][M0][N]), the others to out1
 // ([E][M - M0][N]).  Four floats per thread (N is a multiple of 128).
@@ -1346,12 +1405,13 @@ template <class C, bool SCALE>
 __global__ __launch_bounds__(C::NT, C::WAVES_PER_EU) void dw_down_kernel(
     const typename C::T* __restrict__ dout, const typename C::T* __restrict__ y_swi,
     const int32_t* __restrict__ offsets, const int32_t* __restrict__ eti, const float* __restrict__ w_pos,
-    float* __restrict__ dw_down, float* __restrict__ part, int T, int d, int h) {
+    float* __restrict__ dw_down, float* __restrict__ part, int T, int d, int h, int gr, int gc) {
   __shared__ __attribute__((aligned(16))) char smem[smem_bytes<C>()];
   using TIN = typename C::T;
   const int nnb = col_blocks(h, C::BN);
   const int e = blockIdx.y;
-  const int mb = blockIdx.x / nnb, nb = blockIdx.x % nnb;
+  int mb, nb;
+  dw_tile(blockIdx.x, col_blocks(d, C::BM), nnb, gr, gc, mb, nb);
   int p0, p1;
   split_rows<C::BK>(offsets[e], offsets[e + 1], p0, p1);
   const int wave = threadIdx.x >> 6, wm = wave / C::WN, wn = wave % C::WN;
@@ -1394,12 +1454,13 @@ template <class C>
 __global__ __launch_bounds__(C::NT, C::WAVES_PER_EU) void dw_gate_up_kernel(
     const typename C::T* __restrict__ dh, const typename C::T* __restrict__ x, const int32_t* __restrict__ offsets,
     const int32_t* __restrict__ eti, float* __restrict__ dw_gate, float* __restrict__ dw_up, float* __restrict__ part,
-    int T, int d, int h, int hw) {
+    int T, int d, int h, int hw, int gr, int gc) {
   __shared__ __attribute__((aligned(16))) char smem[smem_bytes<C>()];
   using TIN = typename C::T;
   const int nnb = col_blocks(d, C::BN);
   const int e = blockIdx.y;
-  const int mb = blockIdx.x / nnb, nb = blockIdx.x % nnb;
+  int mb, nb;
+  dw_tile(blockIdx.x, col_blocks(hw, C::BM), nnb, gr, gc, mb, nb);
   int p0, p1;
   split_rows<C::BK>(offsets[e], offsets[e + 1], p0, p1);
   const int wave = threadIdx.x >> 6, wm = wave / C::WN, wn = wave % C::WN;
@@ -1478,16 +1539,45 @@ __global__ __launch_bounds__(C::NT, C::WAVES_PER_EU) void dx_fold_kernel(
                           counters + ERR_BWD, spin_limit, smem);
 }
 
+// MOE_DISPATCH_DW_XCD=0 keeps the dW GEMMs' tiles in launch order (tuning aid).
+static bool dw_xcd_map_on() {
+  static int v = [] {
+    const char* e = getenv("MOE_DISPATCH_DW_XCD");
+    return e ? (atoi(e) ? 1 : 0) : 1;
+  }();
+  return v == 1;
+}
+// XCD grid gr x gc = 8 for a dW GEMM of nmb x nnb tiles per expert: the one
+// that fetches the fewest operand bytes into the eight L2s, gc * a_bytes +
+// gr * b_bytes (a_bytes, b_bytes: an expert's A and B operands), among those
+// dividing the tile grid; {0, 0} (launch order) if none does.
+static void dw_xcd_grid(int nmb, int nnb, double a_bytes, double b_bytes, int& gr, int& gc) {
+  gr = gc = 0;
+  if (!dw_xcd_map_on()) return;
+  double best = 0.0;
+  for (int r = 1; r <= 8; r *= 2) {
+    const int c = 8 / r;
+    if (nmb % r || nnb % c) continue;
+    const double cost = c * a_bytes + r * b_bytes;
+    if (gr == 0 || cost < best) {
+      best = cost;
+      gr = r;
+      gc = c;
+    }
+  }
+}
+
 template <typename TIN, int BM, int BN, bool HONLY>
 static void launch_dh(const Shape& s, const void* dout, const void* w_down, const void* h_ab, const void* y_swi,
                       void* a_prime, const int32_t* offsets, const int32_t* eti, const ExpertWs& ws, hipStream_t st) {
   using C = KCfg<TIN, BM, BN, false, true>;
   const int nbn = col_blocks(s.h, BN);
   const long long nblk = (max_row_blocks(s, BM) * nbn + 7) / 8 * 8;
+  const TileOrder to = tile_order(nblk, nbn);
   dh_kernel<C, HONLY><<<dim3((unsigned)nblk), dim3(C::NT), 0, st>>>(
       (const TIN*)dout, (const TIN*)w_down, (const TIN*)h_ab, (const TIN*)y_swi, offsets, eti, ws.tile_map(BM),
-      ws.w_pos, (TIN*)ws.dh, ws.ds_part, (TIN*)a_prime, s.T, s.d, s.E, s.h, s.act, nbn, (int)nblk,
-      tile_group_rows());
+      ws.w_pos, (TIN*)ws.dh, ws.ds_part, (TIN*)a_prime, s.T, s.d, s.E, s.h, s.act, nbn, to.nblk,
+      to.grp, to.xg);
 }
 
 template <typename TIN, int BM, int BN>
@@ -1576,13 +1666,16 @@ static hipError_t backward_t(const Shape& s, const void* dout, const void* x, co
   timing_mark(st, "dw_down", true);
   {
     const int ns = dw_down_split(s);
-    const dim3 grid(col_blocks(s.d, CL::BM) * col_blocks(s.h, CL::BN), s.E, ns);
+    const int nmb = col_blocks(s.d, CL::BM), nnb = col_blocks(s.h, CL::BN);
+    int gr, gc;  // A: dO rows (d columns), B: A' rows (h columns)
+    dw_xcd_grid(nmb, nnb, (double)s.d, (double)s.h, gr, gc);
+    const dim3 grid(nmb * nnb, s.E, ns);
     if (honly)
-      dw_down_kernel<CL, false><<<grid, dim3(CL::NT), 0, st>>>((const TIN*)dout, (const TIN*)ap, offsets,
-                                                               eti, ws.w_pos, dw_down, ws.dw_part, s.T, s.d, s.h);
+      dw_down_kernel<CL, false><<<grid, dim3(CL::NT), 0, st>>>((const TIN*)dout, (const TIN*)ap, offsets, eti,
+                                                               ws.w_pos, dw_down, ws.dw_part, s.T, s.d, s.h, gr, gc);
     else
       dw_down_kernel<CL, true><<<grid, dim3(CL::NT), 0, st>>>((const TIN*)dout, (const TIN*)y_swi, offsets, eti,
-                                                              ws.w_pos, dw_down, ws.dw_part, s.T, s.d, s.h);
+                                                              ws.w_pos, dw_down, ws.dw_part, s.T, s.d, s.h, gr, gc);
     if (ns > 1) launch_dw_split_reduce(ws.dw_part, ns, s.E, s.d, s.d, s.h, dw_down, nullptr, st);
   }
   timing_mark(st, "dw_down", false);
@@ -1591,9 +1684,11 @@ static hipError_t backward_t(const Shape& s, const void* dout, const void* x, co
   timing_mark(st, "dw_gate_up", true);
   {
     const int ns = dw_gate_up_split(s);
-    dw_gate_up_kernel<CL><<<dim3(col_blocks(s.hw(), CL::BM) * col_blocks(s.d, CL::BN), s.E, ns), dim3(CL::NT), 0,
-                            st>>>((const TIN*)ws.dh, (const TIN*)x, offsets, eti, dw_gate, dw_up, ws.dw_part, s.T,
-                                  s.d, s.h, s.hw());
+    const int nmb = col_blocks(s.hw(), CL::BM), nnb = col_blocks(s.d, CL::BN);
+    int gr, gc;  // A: dH rows (hw columns), B: gathered x rows (d columns)
+    dw_xcd_grid(nmb, nnb, (double)s.hw(), (double)s.d, gr, gc);
+    dw_gate_up_kernel<CL><<<dim3(nmb * nnb, s.E, ns), dim3(CL::NT), 0, st>>>(
+        (const TIN*)ws.dh, (const TIN*)x, offsets, eti, dw_gate, dw_up, ws.dw_part, s.T, s.d, s.h, s.hw(), gr, gc);
     if (ns > 1) launch_dw_split_reduce(ws.dw_part, ns, s.E, s.hw(), s.h, s.d, dw_gate, dw_up, st);
   }
   timing_mark(st, "dw_gate_up", false);

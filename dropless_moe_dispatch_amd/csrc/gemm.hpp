@@ -533,7 +533,50 @@ MOE_DEV bool grouped_tile(int id, int ng, int nbn, int R, int& g, int& nb) {
   return true;
 }
 
+// The same order inside each expert's own tiles (the ids of expert e are
+// [mb_off[e], mb_off[e+1]) * nbn), so that a group of R row blocks never
+// spans two experts and the tiles an XCD runs together share one expert's
+// weights.  grp > 0: groups over the global row blocks (R = grp); grp < 0:
+// groups inside each expert (R = -grp).
+//
+// xg (1, 2, 4 or 8; 0 = off, global groups only): the tiles of a group are
+// handed out so that the eight XCDs (workgroups go to them in turn) form an
+// xg x (8 / xg) grid over the group's R row blocks x nbn column blocks: XCD
+// (xr, xc) takes the row blocks = xr (mod xg) and the column blocks = xc
+// (mod 8 / xg) of the group, row-major.  All XCDs then work on the same
+// group -- one expert's weights and rows, shared through the memory-side
+// cache -- each on a 2-D part of it.  Groups that do not divide (the last,
+// short one) keep the plain order.
+MOE_DEV bool tile_of(int id, const int32_t* __restrict__ mb_off, int E, int nbn, int grp, int xg, int& g, int& nb) {
+  if (grp > 0 && xg > 0) {
+    const int ng = mb_off[E];
+    if (id >= ng * nbn) return false;
+    const int g0 = id / (grp * nbn) * grp;
+    const int rows = ng - g0 < grp ? ng - g0 : grp;
+    const int rem = id - g0 * nbn;
+    const int xc = 8 / xg;
+    if (rows == grp && grp % xg == 0 && nbn % xc == 0) {
+      const int x = rem & 7, j = rem >> 3, cols = nbn / xc;
+      g = g0 + x / xc + xg * (j / cols);
+      nb = x % xc + xc * (j % cols);
+    } else {
+      nb = rem / rows;
+      g = g0 + rem % rows;
+    }
+    return true;
+  }
+  if (grp > 0) return grouped_tile(id, mb_off[E], nbn, grp, g, nb);
+  if (id >= mb_off[E] * nbn) return false;
+  const int e = find_expert(mb_off, E, id / nbn);
+  const int base = mb_off[e];
+  int gl;
+  grouped_tile(id - base * nbn, mb_off[e + 1] - base, nbn, -grp, gl, nb);
+  g = base + gl;
+  return true;
+}
+
 MOE_DEV int xcd_swizzle(int bid, int nblk) {
+  if (nblk <= 0) return bid;  // launch order (the launcher's tuning switch)
   const int per = nblk >> 3;  // nblk is padded to a multiple of 8 by the launcher
   return (bid & 7) * per + (bid >> 3);
 }
