@@ -57,6 +57,8 @@ def lib():
         L.moe_route_topk.argtypes = [sp, _P, _P, _P, _P, _P, _P, _P]
         L.moe_build_index.argtypes = [sp, _P, _P, _P, _P, _P, ctypes.c_size_t, _P]
         L.moe_build_index_dense.argtypes = [sp, _P, _P, _P, _P, _P, ctypes.c_size_t, _P]
+        L.moe_build_index_noalloc.argtypes = [sp, _P, _P, _P, _P, _P]
+        L.moe_build_index_noalloc.restype = ctypes.c_int
         L.moe_expert_fwd.argtypes = [sp, _P, _P, _P, _P, _P, _P, _P, _P, ctypes.c_size_t, _P]
         L.moe_combine.argtypes = [sp, _P, _P, _P, _P, _P, _P, _P, _P, _P, ctypes.c_size_t, _P]
         L.moe_combine_staged.argtypes = [sp, _P, _P, _P, _P, _P, _P, _P, _P, _P, ctypes.c_size_t, _P]
@@ -125,6 +127,15 @@ def moe_build_index(s, topk_ids, offsets, eti, tim, ws, stream=None, check=True,
                                _nbytes(ws) if ws_bytes is None else ws_bytes, _stream(stream))
     if check:
         _check("moe_build_index", rc)
+    return rc
+
+
+def moe_build_index_noalloc(s, topk_ids, offsets, eti, tim, stream=None, check=True):
+    """moe_build_index with the library's static per-GPU scratch instead of a workspace."""
+    rc = lib().moe_build_index_noalloc(ctypes.byref(s), _ptr(topk_ids), _ptr(offsets), _ptr(eti), _ptr(tim),
+                                       _stream(stream))
+    if check:
+        _check("moe_build_index_noalloc", rc)
     return rc
 
 

@@ -175,6 +175,23 @@ int moe_build_index(const moe_shape* s, const int32_t* topk_ids, int32_t* offset
                                        (hipStream_t)stream));
 }
 
+int moe_build_index_noalloc(const moe_shape* s, const int32_t* topk_ids, int32_t* offsets,
+                            int32_t* expert_token_indices, int32_t* token_index_map, void* stream) {
+  Shape sh;
+  int rc = check_shape(s, &sh);
+  if (rc) return rc;
+  REQ(topk_ids);
+  REQ(offsets);
+  REQ(expert_token_indices);
+  REQ(token_index_map);
+  if (index_ws(sh, nullptr).bytes > index_scratch_bytes()) return MOE_ERR_WORKSPACE;
+  void* p = nullptr;
+  if (index_scratch_ptr(&p) != hipSuccess) return MOE_ERR_HIP;
+  const IndexWs w = index_ws(sh, p);
+  return hip_status(launch_build_index(sh, topk_ids, offsets, expert_token_indices, token_index_map, w,
+                                       (hipStream_t)stream));
+}
+
 int moe_build_index_dense(const moe_shape* s, const int32_t* topk_ids, int32_t* offsets,
                           int32_t* expert_token_indices, int32_t* token_index_map, void* ws, size_t ws_bytes,
                           void* stream) {

@@ -21,10 +21,48 @@
 //      expert_token_offsets); a token's position is its expert's offset plus
 //      its (expert, chunk) base plus the popcount of the lower tokens' bits in
 //      the same masks; every destination is written exactly once.
+#include <mutex>
+
+#include "../../include/moe_dispatch.h"
 #include "common.hpp"
 #include "layout.hpp"
 
 namespace moe {
+
+// ---------------------------------------------------------------------------
+// Static scratch of moe_build_index_noalloc: the index workspace of callers
+// that cannot allocate.  Each GPU the library runs on holds its own copy
+// until the process ends.  Host code never uses the array's name as an
+// address: the device address of this device's copy comes from
+// hipGetSymbolAddress, looked up once per device (with that device current)
+// on the entry point's first call there.  The index kernels write every byte
+// of the workspace they read (masks, counts, totals), so nothing is cleared
+// between calls; calls that overlap in time on one GPU share the array and
+// race.
+// ---------------------------------------------------------------------------
+static __device__ __align__(256) char scratch[MOE_NOALLOC_INDEX_MAX_BYTES];
+
+size_t index_scratch_bytes() { return sizeof(scratch); }
+
+hipError_t index_scratch_ptr(void** out) {
+  constexpr int MAX_DEVICES = 64;
+  static std::mutex mu;
+  static void* ptrs[MAX_DEVICES] = {};
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= MAX_DEVICES) return hipErrorInvalidDevice;
+  std::lock_guard<std::mutex> lk(mu);
+  if (ptrs[dev] == nullptr) {
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return e;
+    if (p == nullptr) return hipErrorInvalidSymbol;
+    ptrs[dev] = p;
+  }
+  *out = ptrs[dev];
+  return hipSuccess;
+}
 
 // Step 1 + counts.  Each lane first turns its token's K expert ids into an
 // E-bit set (NW words of 64 experts); the mask of expert e is then the ballot

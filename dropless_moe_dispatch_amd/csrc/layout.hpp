@@ -203,6 +203,11 @@ hipError_t launch_backward(const Shape& s, const void* dout, const void* x, cons
                            const void* y_swi, void* a_prime, void* dx, float* dwg, float* dw_gate, float* dw_up,
                            float* dw_down, float* ds, const ExpertWs& ws, int spin_limit, hipStream_t st);
 
+// Static index scratch of moe_build_index_noalloc (index.hip): its size, and
+// the device address of the current device's copy (looked up once per device).
+size_t index_scratch_bytes();
+hipError_t index_scratch_ptr(void** out);
+
 // Optional per-kernel timing hooks (set by the C-ABI timing calls).
 void timing_mark(hipStream_t st, const char* name, bool begin);
 

@@ -159,6 +159,23 @@ int moe_route_topk(const moe_shape* s, const void* x, const void* wg, const floa
 int moe_build_index(const moe_shape* s, const int32_t* topk_ids, int32_t* offsets, int32_t* expert_token_indices,
                     int32_t* token_index_map, void* ws, size_t ws_bytes, void* stream);
 
+/* moe_build_index without a caller workspace, for callers that cannot
+ * allocate device memory (code under HIP graph capture that must not
+ * allocate, tight serving loops, harnesses that forbid hipMalloc).  Same
+ * arguments (minus ws), outputs and errors as moe_build_index; the index
+ * workspace lives in a static device array of the library, one per GPU,
+ * MOE_NOALLOC_INDEX_MAX_BYTES long (about 0.14 * T * E bytes are needed:
+ * e.g. T = 32768 with E = 1024), held until the process ends.  A shape whose
+ * MOE_WS_INDEX workspace is larger returns MOE_ERR_WORKSPACE before anything
+ * is enqueued.  The call allocates nothing (no hipMalloc, no library
+ * allocation); its first call on a device looks up that device's copy of the
+ * array.  Every call on a GPU shares that GPU's array: calls that overlap in
+ * time on one GPU (other streams, other threads) race and give undefined
+ * results; calls ordered on one stream are fine. */
+#define MOE_NOALLOC_INDEX_MAX_BYTES (8u << 20)
+int moe_build_index_noalloc(const moe_shape* s, const int32_t* topk_ids, int32_t* offsets,
+                            int32_t* expert_token_indices, int32_t* token_index_map, void* stream);
+
 /* The same routing index, built by MoEBlaze's three steps taken literally
  * (MoEBlaze analysis page, "Dispatch Data Structure Construction: The
  * Atomic-Free Three-Step Algorithm"): a dense token-expert map [E][T]

@@ -113,6 +113,16 @@ hipError_t launch_build_index(const Shape& s, const int32_t*, int32_t*, int32_t*
   CHECK(w.nchunks == (s.T + 255) / 256);
   return hipSuccess;
 }
+// the no-alloc index's static scratch: a heap block of the same size here
+size_t index_scratch_bytes() { return MOE_NOALLOC_INDEX_MAX_BYTES; }
+hipError_t index_scratch_ptr(void** out) {
+  static char* block = nullptr;
+  if (!block) block = (char*)malloc(MOE_NOALLOC_INDEX_MAX_BYTES);
+  g_ws = block;
+  g_ws_bytes = MOE_NOALLOC_INDEX_MAX_BYTES;
+  *out = block;
+  return hipSuccess;
+}
 hipError_t launch_build_index_dense(const Shape& s, const int32_t*, int32_t*, int32_t*, int32_t*,
                                     const DenseIndexWs& w, hipStream_t) {
   ++g_launches;
@@ -229,6 +239,19 @@ void valid_calls(const moe_shape& s) {
     free(g_ws);
     g_ws = nullptr;
   }
+  // the no-alloc index: within the static scratch, or refused before any launch
+  {
+    const int before = g_launches;
+    const int rc = moe_build_index_noalloc(&s, (int32_t*)F, (int32_t*)F, (int32_t*)F, (int32_t*)F, nullptr);
+    if (moe_workspace_bytes(&s, MOE_WS_INDEX) <= MOE_NOALLOC_INDEX_MAX_BYTES) {
+      CHECK(rc == MOE_OK);
+      CHECK(g_launches == before + 1);
+    } else {
+      CHECK(rc == MOE_ERR_WORKSPACE);
+      CHECK(g_launches == before);
+    }
+    g_ws = nullptr;
+  }
   // the shared-workspace rule: the backward's kind is the largest of the expert calls
   CHECK(moe_workspace_bytes(&s, MOE_WS_EXPERT_BWD) >= moe_workspace_bytes(&s, MOE_WS_COMBINE));
   CHECK(moe_workspace_bytes(&s, MOE_WS_COMBINE) >= moe_workspace_bytes(&s, MOE_WS_EXPERT_FWD));
@@ -311,6 +334,11 @@ int main() {
                 g_case = "carving";
                 valid_calls(shape(T, d, E, K, h, dt, act));
               }
+  {
+    g_case = "no-alloc index limit";  // 0.14 * T * E bytes against the static scratch
+    valid_calls(shape(32768, 128, 1024, 8, 128));
+    valid_calls(shape(65536, 128, 1024, 8, 128));
+  }
   {
     g_case = "dW row split";  // few experts, many rows: the dW GEMMs split their rows
     valid_calls(shape(8192, 256, 2, 2, 256));
