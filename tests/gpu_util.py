@@ -182,7 +182,7 @@ def stored_flip_bounds(fwd, bw, w, dtype, act="swiglu", saved="aby", win=None):
                              P * np.abs(bw["a_prime_u"]))
     live = np.abs(fwd["a_u"]) > 0   # assignments the oracle evaluated
     n = int(live.sum())
-    if n:
+    if n and dtype == "bf16":       # (in fp32 storage every value is within the window: not a useful share)
         FLIP_MARKED.append(float(np.mean([np.count_nonzero(m[live]) / n for m in marked])))
     return dict(da=da, db=db, ap=ap)
 
@@ -231,7 +231,7 @@ def allowance_summary():
     elems = sum(x[1] for x in ALLOWANCE_LOG)
     total = sum(x[2] for x in ALLOWANCE_LOG)
     largest = max((x[3] for x in ALLOWANCE_LOG), default=0.0)
-    marked = f", {100 * np.mean(FLIP_MARKED):.2f}% of stored values marked able to flip" if FLIP_MARKED else ""
+    marked = f", {100 * np.mean(FLIP_MARKED):.2f}% of stored bf16 values marked able to flip" if FLIP_MARKED else ""
     return (f"rounding-flip allowance: {elems} of {total} weight-gradient elements in {len(drew)} of {checks} "
             f"checks drew on it (largest {largest:.2e} of the max_rel scale){marked}")
 
