@@ -155,13 +155,17 @@ static bool pick_mid(const Shape& s, bool auto_choice) {
   if (!s.bf16 || forced_tile()) return false;
   return v >= 0 ? v == 1 : auto_choice;
 }
-// The folds can run the 256 x 256 tile (eight waves, parked and folded in two
-// 128-row passes) in bf16 when d is a multiple of 256.  It pays where each
-// tile's reduction (kdim) is long next to its two-pass fold: measured on
-// MI355X, down-combine 1.62 -> 1.35 ms at d = 4096, h = 14336, but 20-45%
-// slower at d = 4096-6144 with a reduction of 1536-4096.
+// The folds can run the 256 x 256 tile in bf16 when d is a multiple of 256:
+// its eight waves park their accumulators in LDS and four of them fold the two
+// 128-column halves side by side.  It pays where each tile's reduction (kdim)
+// is long next to the fold.  Measured on MI355X against the 128 x 256 tile:
+// dX fold 7.4% faster at d = 6144, kdim = 4096 and 3% at d = 4096,
+// kdim = 3072; down-combine 1.62 -> 1.35 ms at d = 4096, kdim = 14336, but
+// 3-8% slower at kdim = 1536-2048 and 15-30% slower at d = 2048.
 static bool wide_fold(const Shape& s, int kdim) {
-  return s.bf16 && s.d % TILE_L == 0 && pick_large(s.d >= 4096 && kdim >= 8192);
+  static const int force = env_int("MOE_DISPATCH_WIDE_FOLD", -1);  // tuning aid: 1 on, 0 off
+  const bool auto_choice = force >= 0 ? force == 1 : (s.d >= 4096 && kdim >= 3072);
+  return s.bf16 && s.d % TILE_L == 0 && pick_large(auto_choice);
 }
 // Otherwise the folds take the 128 x 256 tile where d is a multiple of 256
 // (it folds its two 128-column halves against their own turn columns).
@@ -575,10 +579,15 @@ MOE_DEV void fold_epilogue(const f32x16_t (&acc)[C::FM][C::FN], const RowTile& r
     fold_rows<INIT_FIRST>(group ? s_c1 : s_c0, s_t, s_w, s_rank, rows, wave & 3, 2 * nb + group, 2 * NB, K, d, turn,
                           accws, out, counters, spin_limit);
   } else {
-    // 256 x 256 tile, eight waves of 64 x 128: two passes of 128 rows.  In
-    // pass hp the waves holding rows hp*128 .. +127 park both 128-column
-    // halves; waves 0-3 then fold half 0 (column block 2 nb of the 128-wide
-    // turn grid) and waves 4-7 half 1 (column block 2 nb + 1).
+    // 256 x 256 tile, eight waves of 64 x 128: two passes of 128 rows.  The
+    // waves holding rows 0..127 (wm < 2) park both 128-column halves and fold
+    // them (column blocks 2 nb and 2 nb + 1 of the 128-wide turn grid), four
+    // waves for both halves; then the waves holding rows 128..255 park theirs
+    // and all eight fold (waves 0-3 half 0, 4-7 half 1).  The two kinds of
+    // wave take separate branches, each through the same four workgroup
+    // barriers, so no fold code runs while a wave still holds accumulators:
+    // in one shared pass sequence the second half's accumulators would stay
+    // live through the first pass's fold and spill.
     static_assert(C::BM == 256 && C::BN == 256 && C::NT == 512 && C::WM == 4 && C::WN == 2, "eight-wave 256 tile");
     static_assert(2 * 128 * FOLD_LD * 4 + 3 * 128 * 4 <= C::LDS_BYTES, "two parked halves fit the LDS stages");
     float* s_c0 = (float*)smem;
@@ -587,33 +596,53 @@ MOE_DEV void fold_epilogue(const f32x16_t (&acc)[C::FM][C::FN], const RowTile& r
     float* s_w = (float*)(s_t + 128);
     int* s_rank = (int*)(s_w + 128);
     const int wave = tid >> 6, group = wave >> 2;
-#pragma unroll 1
-    for (int hp = 0; hp < 2; ++hp) {
-      const int left = rt.r1 - rt.r0 - hp * 128;
-      const int rows = left < 0 ? 0 : left > 128 ? 128 : left;
-      __syncthreads();  // the LDS stages (pass 0) or the previous half (pass 1) are reused below
-      for (int i = tid; i < 128; i += C::NT) {
-        const int p = rt.r0 + hp * 128 + i;
-        const bool in = i < rows;
-        s_t[i] = in ? eti[p] : 0;
-        s_w[i] = in && w_pos ? w_pos[p] : 1.0f;
-        s_rank[i] = in ? rank_pos[p] : 0;
+    const int all = rt.r1 - rt.r0;
+    const int rows0 = all > 128 ? 128 : all, rows1 = all > 128 ? all - 128 : 0;
+    // per-row token, weight and rank of rows hp*128 .. +127 (threads 0..127,
+    // which are waves 0 and 1: the first kind)
+    auto meta = [&](int hp, int rows) {
+      if (tid < 128) {
+        const int p = rt.r0 + hp * 128 + tid;
+        const bool in = tid < rows;
+        s_t[tid] = in ? eti[p] : 0;
+        s_w[tid] = in && w_pos ? w_pos[p] : 1.0f;
+        s_rank[tid] = in ? rank_pos[p] : 0;
       }
-      if ((wm >> 1) == hp) {
-        float* s_c = wn ? s_c1 : s_c0;
+    };
+    auto park = [&]() {
+      float* s_c = wn ? s_c1 : s_c0;
 #pragma unroll
-        for (int fm = 0; fm < C::FM; ++fm)
+      for (int fm = 0; fm < C::FM; ++fm)
 #pragma unroll
-          for (int fn = 0; fn < C::FN; ++fn)
+        for (int fn = 0; fn < C::FN; ++fn)
 #pragma unroll
-            for (int r = 0; r < 16; ++r)
-              s_c[((wm & 1) * 64 + fm * 32 + frag_row(r, l)) * FOLD_LD + fn * 32 + frag_col(l)] = acc[fm][fn][r];
+          for (int r = 0; r < 16; ++r)
+            s_c[((wm & 1) * 64 + fm * 32 + frag_row(r, l)) * FOLD_LD + fn * 32 + frag_col(l)] = acc[fm][fn][r];
+    };
+    if ((wm >> 1) == 0) {
+      __syncthreads();  // 1: the LDS stages are free
+      meta(0, rows0);
+      park();
+      __syncthreads();  // 2: rows 0..127 parked
+      if (rows0 > 0) {
+        fold_rows<INIT_FIRST>(s_c0, s_t, s_w, s_rank, rows0, wave, 2 * nb, 2 * NB, K, d, turn, accws, out, counters,
+                              spin_limit);
+        fold_rows<INIT_FIRST>(s_c1, s_t, s_w, s_rank, rows0, wave, 2 * nb + 1, 2 * NB, K, d, turn, accws, out,
+                              counters, spin_limit);
       }
-      __syncthreads();
-      if (rows > 0)
-        fold_rows<INIT_FIRST>(group ? s_c1 : s_c0, s_t, s_w, s_rank, rows, wave & 3, 2 * nb + group, 2 * NB, K, d,
-                              turn, accws, out, counters, spin_limit);
+      __syncthreads();  // 3: the first pass has read its rows
+      meta(1, rows1);
+      __syncthreads();  // 4: rows 128..255 parked
+    } else {
+      __syncthreads();  // 1
+      __syncthreads();  // 2
+      __syncthreads();  // 3
+      park();
+      __syncthreads();  // 4
     }
+    if (rows1 > 0)
+      fold_rows<INIT_FIRST>(group ? s_c1 : s_c0, s_t, s_w, s_rank, rows1, wave & 3, 2 * nb + group, 2 * NB, K, d,
+                            turn, accws, out, counters, spin_limit);
   }
 }
 
