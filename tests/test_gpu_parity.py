@@ -185,6 +185,13 @@ LAYER_CASES = [
     # d = 6144: dH on the 128 x 256 tile (a long reduction), with h = 384 an
     # odd multiple of 128, so its last column block runs past h
     ("dh_mid_d6144", 200, 6144, 4, 2, 384, "bf16", None),
+    # the skewed workload's tile choices at a small T: the dX fold on the
+    # 256 x 256 tile with a reduction of 2h = 3072, six ranks per token, Zipf
+    # skew (22 to 291 rows per expert, ragged in every 256-row block)
+    ("wide_dx_k6", 300, 4096, 16, 6, 1536, "bf16", 1.2),
+    # the large-d workload's tile choices: gate/up and the dW GEMMs on 256 x 256,
+    # dH and down-combine on 128 x 256, the dX fold on 256 x 256 (reduction 4096)
+    ("large_d_tiles", 200, 6144, 8, 4, 2048, "bf16", None),
 ]
 
 
