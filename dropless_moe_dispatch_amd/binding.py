@@ -18,6 +18,7 @@ MOE_F32, MOE_BF16 = 0, 1
 MOE_WS_INDEX, MOE_WS_EXPERT_FWD, MOE_WS_COMBINE, MOE_WS_EXPERT_BWD, MOE_WS_EXPERT_BWD_H = 0, 1, 2, 3, 4
 MOE_WS_COMBINE_STAGED = 5
 MOE_WS_INDEX_DENSE = 6
+MOE_WS_EXPERT_BWD_LEAN = 7
 
 
 MOE_ACT_SWIGLU, MOE_ACT_SILU, MOE_ACT_RELU = 0, 1, 2
@@ -62,7 +63,7 @@ def lib():
         L.moe_expert_fwd.argtypes = [sp, _P, _P, _P, _P, _P, _P, _P, _P, ctypes.c_size_t, _P]
         L.moe_combine.argtypes = [sp, _P, _P, _P, _P, _P, _P, _P, _P, _P, ctypes.c_size_t, _P]
         L.moe_combine_staged.argtypes = [sp, _P, _P, _P, _P, _P, _P, _P, _P, _P, ctypes.c_size_t, _P]
-        L.moe_expert_bwd.argtypes = [sp] + [_P] * 21 + [ctypes.c_size_t, _P]
+        L.moe_expert_bwd.argtypes = [sp] + [_P] * 22 + [ctypes.c_size_t, _P]
         for f in ("moe_route_topk", "moe_build_index", "moe_build_index_dense", "moe_expert_fwd", "moe_combine", "moe_combine_staged", "moe_expert_bwd"):
             getattr(L, f).restype = ctypes.c_int
         L.moe_status_string.argtypes = [ctypes.c_int]
@@ -174,11 +175,12 @@ def moe_combine_staged(s, y_swi, w_down, offsets, eti, tim, topk_ids, topk_w, ou
 
 
 def moe_expert_bwd(s, dout, x, wg, w_gate, w_up, w_down, topk_ids, topk_w, offsets, eti, tim, h_ab, y_swi,
-                   a_prime, dx, dwg, dw_gate, dw_up, dw_down, ds, ws, stream=None, check=True):
+                   a_prime, dh, dx, dwg, dw_gate, dw_up, dw_down, ds, ws, stream=None, check=True):
     rc = lib().moe_expert_bwd(ctypes.byref(s), _ptr(dout), _ptr(x), _ptr(wg), _ptr(w_gate), _ptr(w_up),
                               _ptr(w_down), _ptr(topk_ids), _ptr(topk_w), _ptr(offsets), _ptr(eti), _ptr(tim),
-                              _ptr(h_ab), _ptr(y_swi), _ptr(a_prime), _ptr(dx), _ptr(dwg), _ptr(dw_gate),
-                              _ptr(dw_up), _ptr(dw_down), _ptr(ds), _ptr(ws), _nbytes(ws), _stream(stream))
+                              _ptr(h_ab), _ptr(y_swi), _ptr(a_prime), _ptr(dh), _ptr(dx), _ptr(dwg),
+                              _ptr(dw_gate), _ptr(dw_up), _ptr(dw_down), _ptr(ds), _ptr(ws), _nbytes(ws),
+                              _stream(stream))
     if check:
         _check("moe_expert_bwd", rc)
     return rc

@@ -118,6 +118,7 @@ size_t moe_workspace_bytes(const moe_shape* s, int which) {
     case MOE_WS_EXPERT_BWD_H: return expert_ws(sh, WS_EXPERT_BWD_H, nullptr).bytes;
     case MOE_WS_COMBINE_STAGED: return expert_ws(sh, WS_COMBINE_STAGED, nullptr).bytes;
     case MOE_WS_INDEX_DENSE: return dense_index_ws(sh, nullptr).bytes;
+    case MOE_WS_EXPERT_BWD_LEAN: return expert_ws(sh, WS_EXPERT_BWD_LEAN, nullptr).bytes;
     default: return 0;
   }
 }
@@ -282,8 +283,9 @@ int moe_combine_staged(const moe_shape* s, const void* y_swi, const void* w_down
 int moe_expert_bwd(const moe_shape* s, const void* dout, const void* x, const void* wg, const void* w_gate,
                    const void* w_up, const void* w_down, const int32_t* topk_ids, const float* topk_w,
                    const int32_t* offsets, const int32_t* expert_token_indices, const int32_t* token_index_map,
-                   const void* h_ab, const void* y_swi, void* a_prime, void* dx, float* dwg, float* dw_gate,
-                   float* dw_up, float* dw_down, float* ds, void* ws, size_t ws_bytes, void* stream) {
+                   const void* h_ab, const void* y_swi, void* a_prime, void* dh, void* dx, float* dwg,
+                   float* dw_gate, float* dw_up, float* dw_down, float* ds, void* ws, size_t ws_bytes,
+                   void* stream) {
   Shape sh;
   int rc = check_shape(s, &sh);
   if (rc) return rc;
@@ -304,6 +306,9 @@ int moe_expert_bwd(const moe_shape* s, const void* dout, const void* x, const vo
   OPT(a_prime);  // H-only: where A' goes (else the workspace); must be NULL with a saved y_swi
   if (y_swi && a_prime) return MOE_ERR_INVALID_ARG;
   if (a_prime && a_prime == h_ab) return MOE_ERR_INVALID_ARG;
+  OPT(dh);  // where dH goes (else the workspace); may be h_ab itself
+  if (dh && !y_swi && !a_prime) return MOE_ERR_INVALID_ARG;  // a lean workspace has no room for A'
+  if (dh && (dh == y_swi || dh == a_prime || dh == dout || dh == x || dh == dx)) return MOE_ERR_INVALID_ARG;
   REQ(dx);
   REQ(dwg);
   REQ(dw_gate);
@@ -312,14 +317,16 @@ int moe_expert_bwd(const moe_shape* s, const void* dout, const void* x, const vo
   REQ(dw_down);
   OPT(ds);
   REQ(ws);
-  const ExpertWs w = expert_ws(sh, (y_swi || a_prime) ? WS_EXPERT_BWD : WS_EXPERT_BWD_H, ws);
+  const int kind = dh ? WS_EXPERT_BWD_LEAN : (y_swi || a_prime) ? WS_EXPERT_BWD : WS_EXPERT_BWD_H;
+  const ExpertWs w = expert_ws(sh, kind, ws);
   if (ws_bytes < w.bytes) return MOE_ERR_WORKSPACE;
   hipStream_t st = (hipStream_t)stream;
   rc = hip_status(launch_prep(sh, w, offsets, topk_ids, topk_w, token_index_map, true, ERR_BWD, st));
   if (rc) return rc;
   return hip_status(launch_backward(sh, dout, x, wg, w_gate, w_up, w_down, topk_ids, topk_w, offsets,
-                                    expert_token_indices, token_index_map, h_ab, y_swi, a_prime, dx, dwg, dw_gate,
-                                    dw_up, dw_down, ds, w, g_spin_limit.load(std::memory_order_relaxed), st));
+                                    expert_token_indices, token_index_map, h_ab, y_swi, a_prime, dh, dx, dwg,
+                                    dw_gate, dw_up, dw_down, ds, w, g_spin_limit.load(std::memory_order_relaxed),
+                                    st));
 }
 
 int moe_timing_enable(int on) {

@@ -959,9 +959,9 @@ MOE_DEV int min_i(int a, int b) { return a < b ? a : b; }
 template <class C, bool HONLY>
 __global__ __launch_bounds__(C::NT, C::WAVES_PER_EU) void dh_kernel(
     const typename C::T* __restrict__ dout, const typename C::T* __restrict__ w_down,
-    const typename C::T* __restrict__ h_ab, const typename C::T* __restrict__ y_swi,
+    const typename C::T* h_ab, const typename C::T* __restrict__ y_swi,
     const int32_t* __restrict__ offsets, const int32_t* __restrict__ eti, const int32_t* __restrict__ mb_off,
-    const float* __restrict__ w_pos, typename C::T* __restrict__ dh, float* __restrict__ ds_part,
+    const float* __restrict__ w_pos, typename C::T* dh, float* __restrict__ ds_part,
     typename C::T* __restrict__ a_prime, int T, int d, int E, int h, int act, int nbn, int nblk, int grp, int xg) {
   __shared__ __attribute__((aligned(16))) char smem[smem_bytes<C>()];
   using TIN = typename C::T;
@@ -989,7 +989,9 @@ __global__ __launch_bounds__(C::NT, C::WAVES_PER_EU) void dh_kernel(
   {
     // Park dA' (fp32) in LDS, 128 rows at a time; then each thread takes
     // 16-byte row chunks, so a, b, y are read and dA, dB (and A') written as
-    // whole chunks (a, b and the outputs with the non-temporal policy: each
+    // whole chunks.  dh may be h_ab itself (no __restrict__ on either): each
+    // chunk of a and b is loaded by the thread that later stores da and db at
+    // the same place, from those very values, and no other chunk is touched (a, b and the outputs with the non-temporal policy: each
     // is touched once here; measured 1-3% faster).  dS of a row is reduced over the row's chunk-owning lanes
     // in a fixed order.
     constexpr int PR = 128, PITCH = C::BN + 8;
@@ -1741,13 +1743,20 @@ static hipError_t backward_t(const Shape& s, const void* dout, const void* x, co
 hipError_t launch_backward(const Shape& s, const void* dout, const void* x, const void* wg, const void* w_gate,
                            const void* w_up, const void* w_down, const int32_t* ids, const float* topk_w,
                            const int32_t* offsets, const int32_t* eti, const int32_t* tim, const void* h_ab,
-                           const void* y_swi, void* a_prime, void* dx, float* dwg, float* dw_gate, float* dw_up,
-                           float* dw_down, float* ds, const ExpertWs& ws, int spin_limit, hipStream_t st) {
+                           const void* y_swi, void* a_prime, void* dh, void* dx, float* dwg, float* dw_gate,
+                           float* dw_up, float* dw_down, float* ds, const ExpertWs& ws, int spin_limit,
+                           hipStream_t st) {
+  // dH goes to the caller's buffer when one is passed (possibly h_ab itself:
+  // the dH kernel reads each element of H before it writes the gradient
+  // element at the same place, and nothing after it reads H), else to the
+  // workspace
+  ExpertWs w = ws;
+  if (dh) w.dh = dh;
   if (s.bf16)
     return backward_t<bf16_t>(s, dout, x, wg, w_gate, w_up, w_down, ids, topk_w, offsets, eti, tim, h_ab, y_swi,
-                              a_prime, dx, dwg, dw_gate, dw_up, dw_down, ds, ws, spin_limit, st);
+                              a_prime, dx, dwg, dw_gate, dw_up, dw_down, ds, w, spin_limit, st);
   return backward_t<float>(s, dout, x, wg, w_gate, w_up, w_down, ids, topk_w, offsets, eti, tim, h_ab, y_swi,
-                           a_prime, dx, dwg, dw_gate, dw_up, dw_down, ds, ws, spin_limit, st);
+                           a_prime, dx, dwg, dw_gate, dw_up, dw_down, ds, w, spin_limit, st);
 }
 
 }  // namespace moe

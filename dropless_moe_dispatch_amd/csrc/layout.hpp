@@ -132,7 +132,8 @@ struct ExpertWs {
   float* dz_tok;       // [A] the same per (token, slot), token-major (backward)
   float* dwg_part;     // dWg partial sums (backward): bf16 [token chunks][E][d], fp32 [row blocks of 128][d]
   float* dw_part;      // [split][E][m][n] dW chunk partials when a dW GEMM splits its rows (backward)
-  void* dh;            // [A][hw] activation-dtype gradient of the pre-activations (backward)
+  void* dh;            // [A][hw] activation-dtype gradient of the pre-activations (backward,
+                       // unless the caller passes a buffer for it)
   void* a_prime;       // [A][h] activation-dtype A' = w * y recomputed from a, b (H-only backward,
                        // unless the caller passes a buffer for it)
   void* ystage;        // [A][d] activation-dtype staged expert outputs (staged-Y combine ablation)
@@ -140,7 +141,8 @@ struct ExpertWs {
   int E;
   const int32_t* tile_map(int bm) const { return mb_off + (bm == TILE_L ? E + 1 : 0); }
 };
-enum { WS_EXPERT_FWD = 1, WS_COMBINE = 2, WS_EXPERT_BWD = 3, WS_EXPERT_BWD_H = 4, WS_COMBINE_STAGED = 5 };
+enum { WS_EXPERT_FWD = 1, WS_COMBINE = 2, WS_EXPERT_BWD = 3, WS_EXPERT_BWD_H = 4, WS_COMBINE_STAGED = 5,
+       WS_EXPERT_BWD_LEAN = 7 };
 
 inline ExpertWs expert_ws(const Shape& s, int which, void* p) {
   ExpertWs w{};
@@ -150,7 +152,7 @@ inline ExpertWs expert_ws(const Shape& s, int which, void* p) {
   auto take = [&](size_t bytes) { void* q = ws_at(p, off); off = align_up(off + bytes, 256); return q; };
   w.counters = (int32_t*)take(N_COUNTERS * 4);
   w.mb_off = (int32_t*)take((size_t)2 * (s.E + 1) * 4);
-  const bool bwd = which == WS_EXPERT_BWD || which == WS_EXPERT_BWD_H;
+  const bool bwd = which == WS_EXPERT_BWD || which == WS_EXPERT_BWD_H || which == WS_EXPERT_BWD_LEAN;
   if (which == WS_COMBINE || bwd) {
     w.w_pos = (float*)take(A * 4);
     w.rank_pos = (int32_t*)take(A * 4);
@@ -167,7 +169,7 @@ inline ExpertWs expert_ws(const Shape& s, int which, void* p) {
     const size_t pd = sd > 1 ? (size_t)sd * s.E * s.d * s.h : 0;
     const size_t pg = sg > 1 ? (size_t)sg * s.E * s.hw() * s.d : 0;
     if (pd || pg) w.dw_part = (float*)take((pd > pg ? pd : pg) * 4);
-    w.dh = take(A * (size_t)s.hw() * s.elem());
+    if (which != WS_EXPERT_BWD_LEAN) w.dh = take(A * (size_t)s.hw() * s.elem());  // the last item: LEAN is a prefix
   }
   if (which == WS_EXPERT_BWD_H) w.a_prime = take(A * (size_t)s.h * s.elem());
   if (which == WS_COMBINE_STAGED) w.ystage = take(A * (size_t)s.d * s.elem());
@@ -200,8 +202,9 @@ hipError_t launch_combine_staged(const Shape& s, const void* y_swi, const void* 
 hipError_t launch_backward(const Shape& s, const void* dout, const void* x, const void* wg, const void* w_gate,
                            const void* w_up, const void* w_down, const int32_t* ids, const float* topk_w,
                            const int32_t* offsets, const int32_t* eti, const int32_t* tim, const void* h_ab,
-                           const void* y_swi, void* a_prime, void* dx, float* dwg, float* dw_gate, float* dw_up,
-                           float* dw_down, float* ds, const ExpertWs& ws, int spin_limit, hipStream_t st);
+                           const void* y_swi, void* a_prime, void* dh, void* dx, float* dwg, float* dw_gate,
+                           float* dw_up, float* dw_down, float* ds, const ExpertWs& ws, int spin_limit,
+                           hipStream_t st);
 
 // Static index scratch of moe_build_index_noalloc (index.hip): its size, and
 // the device address of the current device's copy (looked up once per device).

@@ -9,6 +9,9 @@ Memory: the expert forward, the combine and the backward share one workspace
 (the library allows it for calls ordered on one stream), and under H-only
 saving the backward writes A' = w * y into the forward's y_swi buffer, which
 is dead once the combine has read it.  So y_swi holds A' after a backward.
+By default the backward also writes dH over the saved H (``dh_over_h``): the
+dH kernel is the last reader of H, so the workspace needs no [T*K, 2h] dH
+buffer, and h_ab holds dH after a backward.
 """
 from __future__ import annotations
 
@@ -47,6 +50,9 @@ class MoEBuffers:
     # keep a|b from the forward (always, when a backward follows); a forward
     # alone may save nothing (h_ab is then None and not written)
     save: bool = True
+    # the backward writes dH over the saved H (h_ab), its last reader being
+    # the dH kernel: no dH buffer in the workspace, and H is gone afterwards
+    dh_over_h: bool = True
 
     def __post_init__(self):
         dev, td = self.device, torch_dtype(self.dtype)
@@ -70,9 +76,11 @@ class MoEBuffers:
         if self.saved not in ("aby", "ab"):
             raise ValueError(f"saved must be 'aby' or 'ab', not {self.saved!r}")
         # one workspace for the expert forward, the ordered combine and the
-        # backward (H-only: A' goes to y_swi, so the smaller backward kind)
+        # backward (H-only: A' goes to y_swi, so the smaller backward kind;
+        # dH over H: the lean one, without a dH buffer)
+        bwd_kind = B.MOE_WS_EXPERT_BWD_LEAN if self.dh_over_h else B.MOE_WS_EXPERT_BWD
         kinds = [B.MOE_WS_EXPERT_FWD] + ([B.MOE_WS_COMBINE] if self.combine == "fold" else []) \
-            + ([B.MOE_WS_EXPERT_BWD] if self.backward else [])
+            + ([bwd_kind] if self.backward else [])
         self.ws_main = self._ws(*kinds)
         self.ws_comb = self.ws_main if self.combine == "fold" else self._ws(B.MOE_WS_COMBINE_STAGED)
         if self.backward:
@@ -144,11 +152,13 @@ def forward(buf: MoEBuffers, x, wg, bias, w_gate, w_up, w_down, logits_in: bool 
 
 def backward(buf: MoEBuffers, dy, x, wg, w_gate, w_up, w_down, stream=None, want_ds: bool = True):
     """H-only saving: y_swi is not passed as y, and receives A' (it is dead
-    after the forward's combine)."""
+    after the forward's combine).  With ``dh_over_h`` dH is written over
+    h_ab."""
     honly = buf.saved == "ab"
     B.moe_expert_bwd(buf.shape, dy, x, wg, w_gate, w_up, w_down, buf.topk_ids, buf.topk_w, buf.offsets, buf.eti,
-                     buf.tim, buf.h_ab, None if honly else buf.y_swi, buf.y_swi if honly else None, buf.dx, buf.dwg,
-                     buf.dw_gate, buf.dw_up, buf.dw_down, buf.ds if want_ds else None, buf.ws_main, stream)
+                     buf.tim, buf.h_ab, None if honly else buf.y_swi, buf.y_swi if honly else None,
+                     buf.h_ab if buf.dh_over_h else None, buf.dx, buf.dwg, buf.dw_gate, buf.dw_up, buf.dw_down,
+                     buf.ds if want_ds else None, buf.ws_main, stream)
     return buf.dx
 
 

@@ -52,7 +52,7 @@
  *   - One workspace may serve moe_expert_fwd, moe_combine and
  *     moe_expert_bwd of the same shape (their layouts share a prefix and no
  *     call reads what an earlier one left there), sized as the largest of
- *     MOE_WS_EXPERT_FWD, MOE_WS_COMBINE and MOE_WS_EXPERT_BWD(_H).  Calls
+ *     MOE_WS_EXPERT_FWD, MOE_WS_COMBINE and MOE_WS_EXPERT_BWD(_H, _LEAN).  Calls
  *     that share a workspace must not overlap in time (enqueue them on one
  *     stream, or order their streams).
  *   - Device error words (int32, in the workspace): bytes 0-3 belong to
@@ -119,7 +119,10 @@ typedef enum {
   MOE_WS_EXPERT_BWD_H = 4, /* moe_expert_bwd with y_swi == NULL (H-only saving):
                               MOE_WS_EXPERT_BWD plus a [T*K, h] dtype buffer */
   MOE_WS_COMBINE_STAGED = 5, /* moe_combine_staged: holds a [T*K, d] dtype buffer */
-  MOE_WS_INDEX_DENSE = 6     /* moe_build_index_dense: two [E, T] int32 maps */
+  MOE_WS_INDEX_DENSE = 6,    /* moe_build_index_dense: two [E, T] int32 maps */
+  MOE_WS_EXPERT_BWD_LEAN = 7 /* moe_expert_bwd with dh given (and a_prime given under
+                                H-only saving): MOE_WS_EXPERT_BWD without its
+                                [T*K, 2h] (plain experts: [T*K, h]) dtype dH buffer */
 } moe_workspace_kind;
 
 /* Bytes of device workspace the call of kind `which` needs for shape *s
@@ -262,12 +265,26 @@ int moe_combine_staged(const moe_shape* s, const void* y_swi, const void* w_down
  *     intended one.  With a_prime == NULL, A' lives in the workspace, which
  *     must then be MOE_WS_EXPERT_BWD_H; with a_prime given, MOE_WS_EXPERT_BWD
  *     suffices.  It is overwritten, must not overlap any other argument, and
- *     must be NULL when y_swi is passed (MOE_ERR_INVALID_ARG otherwise). */
+ *     must be NULL when y_swi is passed (MOE_ERR_INVALID_ARG otherwise).
+ *   dh [T*K, 2h] dtype (nullable; [T*K, h] for the plain experts): where the
+ *     gradient of the pre-activations, dH = [da | db], is written (the same
+ *     layout as h_ab), for the dW_gate/dW_up and dX GEMMs that read it.  NULL:
+ *     the workspace holds it (MOE_WS_EXPERT_BWD or _H).  Given, the workspace
+ *     needs only MOE_WS_EXPERT_BWD_LEAN, and under H-only saving a_prime must
+ *     be given too (MOE_ERR_INVALID_ARG otherwise).  dh may be h_ab itself:
+ *     the saved H is then overwritten by its own gradient, which the backward
+ *     allows because each element of H is read (once, by the dH kernel)
+ *     before the gradient element at the same place is written, and nothing
+ *     after the dH kernel reads H.  That saves the [T*K, 2h] buffer; the
+ *     saved H is gone after the call.  Otherwise dh must not overlap any
+ *     other argument (dh equal to y_swi, a_prime, dout, x or dx is
+ *     MOE_ERR_INVALID_ARG). */
 int moe_expert_bwd(const moe_shape* s, const void* dout, const void* x, const void* wg, const void* w_gate,
                    const void* w_up, const void* w_down, const int32_t* topk_ids, const float* topk_w,
                    const int32_t* offsets, const int32_t* expert_token_indices, const int32_t* token_index_map,
-                   const void* h_ab, const void* y_swi, void* a_prime, void* dx, float* dwg, float* dw_gate,
-                   float* dw_up, float* dw_down, float* ds, void* ws, size_t ws_bytes, void* stream);
+                   const void* h_ab, const void* y_swi, void* a_prime, void* dh, void* dx, float* dwg,
+                   float* dw_gate, float* dw_up, float* dw_down, float* ds, void* ws, size_t ws_bytes,
+                   void* stream);
 
 /* Static string for a moe_status value (host). */
 const char* moe_status_string(int code);

@@ -70,7 +70,7 @@ void check_expert_ws(const moe::Shape& s, const moe::ExpertWs& w) {
     rs.push_back({w.turn, (size_t)s.T * ((s.d + 127) / 128) * 4});
     rs.push_back({w.acc, (size_t)s.T * s.d * 4});
   }
-  if (w.dh) {
+  if (w.ds_part) {  // a backward kind (the lean one has no dH buffer)
     rs.push_back({w.ds_part, A * ((s.h + 127) / 128) * 4});
     rs.push_back({w.dz_pos, A * 4});
     rs.push_back({w.dz_tok, A * 4});
@@ -79,7 +79,7 @@ void check_expert_ws(const moe::Shape& s, const moe::ExpertWs& w) {
     const size_t pd = moe::dw_down_split(s) > 1 ? (size_t)moe::dw_down_split(s) * s.E * s.d * s.h : 0;
     const size_t pg = moe::dw_gate_up_split(s) > 1 ? (size_t)moe::dw_gate_up_split(s) * s.E * s.hw() * s.d : 0;
     rs.push_back({w.dw_part, (pd > pg ? pd : pg) * 4});
-    rs.push_back({w.dh, A * s.hw() * eb});
+    rs.push_back({w.dh, w.dh ? A * s.hw() * eb : 0});
   }
   rs.push_back({w.a_prime, w.a_prime ? A * s.h * eb : 0});
   rs.push_back({w.ystage, w.ystage ? A * s.d * eb : 0});
@@ -158,12 +158,13 @@ hipError_t launch_combine_staged(const Shape& s, const void*, const void*, const
 }
 hipError_t launch_backward(const Shape& s, const void*, const void*, const void*, const void*, const void*,
                            const void*, const int32_t*, const float*, const int32_t*, const int32_t*,
-                           const int32_t*, const void*, const void* y_swi, void* a_prime, void*, float*, float*,
-                           float*, float*, float*, const ExpertWs& w, int spin, hipStream_t) {
+                           const int32_t*, const void*, const void* y_swi, void* a_prime, void* dh, void*, float*,
+                           float*, float*, float*, float*, const ExpertWs& w, int spin, hipStream_t) {
   ++g_launches;
   CHECK(spin > 0);
   CHECK(!(y_swi && a_prime));
   CHECK(y_swi || a_prime || w.a_prime);  // H-only: A' has somewhere to go
+  CHECK(dh || w.dh);                     // and so has dH
   check_expert_ws(s, w);
   return hipSuccess;
 }
@@ -181,8 +182,8 @@ moe_shape shape(int T, int d, int E, int K, int h, int dtype = MOE_BF16, int act
 
 // one call of every entry point with a workspace of exactly the reported size
 void valid_calls(const moe_shape& s) {
-  const int kinds[] = {MOE_WS_INDEX, MOE_WS_EXPERT_FWD, MOE_WS_COMBINE, MOE_WS_EXPERT_BWD, MOE_WS_EXPERT_BWD_H,
-                       MOE_WS_COMBINE_STAGED, MOE_WS_INDEX_DENSE};
+  const int kinds[] = {MOE_WS_INDEX,          MOE_WS_EXPERT_FWD,  MOE_WS_COMBINE,        MOE_WS_EXPERT_BWD,
+                       MOE_WS_EXPERT_BWD_H,   MOE_WS_COMBINE_STAGED, MOE_WS_INDEX_DENSE, MOE_WS_EXPERT_BWD_LEAN};
   const bool gated = s.act == MOE_ACT_SWIGLU;
   for (int kind : kinds) {
     const size_t n = moe_workspace_bytes(&s, kind);
@@ -215,13 +216,23 @@ void valid_calls(const moe_shape& s) {
       case MOE_WS_EXPERT_BWD_H: {
         const bool honly = kind == MOE_WS_EXPERT_BWD_H;
         rc = moe_expert_bwd(&s, F, F, F, F, up, F, (int32_t*)F, (float*)F, (int32_t*)F, (int32_t*)F, (int32_t*)F,
-                            (char*)F + 0x100, honly ? nullptr : F, nullptr, F, (float*)F, (float*)F,
+                            (char*)F + 0x100, honly ? nullptr : F, nullptr, nullptr, F, (float*)F, (float*)F,
                             gated ? (float*)F : nullptr, (float*)F, nullptr, g_ws, n, nullptr);
         if (!honly) {  // H-only with a buffer of its own for A' fits the smaller workspace
           rc |= moe_expert_bwd(&s, F, F, F, F, up, F, (int32_t*)F, (float*)F, (int32_t*)F, (int32_t*)F,
-                               (int32_t*)F, (char*)F + 0x100, nullptr, (char*)F + 0x200, F, (float*)F, (float*)F,
-                               gated ? (float*)F : nullptr, (float*)F, nullptr, g_ws, n, nullptr);
+                               (int32_t*)F, (char*)F + 0x100, nullptr, (char*)F + 0x200, nullptr, F, (float*)F,
+                               (float*)F, gated ? (float*)F : nullptr, (float*)F, nullptr, g_ws, n, nullptr);
         }
+        break;
+      }
+      case MOE_WS_EXPERT_BWD_LEAN: {
+        // dH over the saved H, with a saved y and (H-only) with A' in a buffer of its own
+        rc = moe_expert_bwd(&s, F, F, F, F, up, F, (int32_t*)F, (float*)F, (int32_t*)F, (int32_t*)F, (int32_t*)F,
+                            (char*)F + 0x100, F, nullptr, (char*)F + 0x100, F, (float*)F, (float*)F,
+                            gated ? (float*)F : nullptr, (float*)F, nullptr, g_ws, n, nullptr);
+        rc |= moe_expert_bwd(&s, F, F, F, F, up, F, (int32_t*)F, (float*)F, (int32_t*)F, (int32_t*)F, (int32_t*)F,
+                             (char*)F + 0x100, nullptr, (char*)F + 0x200, (char*)F + 0x100, F, (float*)F,
+                             (float*)F, gated ? (float*)F : nullptr, (float*)F, nullptr, g_ws, n, nullptr);
         break;
       }
     }
@@ -254,6 +265,8 @@ void valid_calls(const moe_shape& s) {
   }
   // the shared-workspace rule: the backward's kind is the largest of the expert calls
   CHECK(moe_workspace_bytes(&s, MOE_WS_EXPERT_BWD) >= moe_workspace_bytes(&s, MOE_WS_COMBINE));
+  CHECK(moe_workspace_bytes(&s, MOE_WS_EXPERT_BWD_LEAN) >= moe_workspace_bytes(&s, MOE_WS_COMBINE));
+  CHECK(moe_workspace_bytes(&s, MOE_WS_EXPERT_BWD_LEAN) < moe_workspace_bytes(&s, MOE_WS_EXPERT_BWD));
   CHECK(moe_workspace_bytes(&s, MOE_WS_COMBINE) >= moe_workspace_bytes(&s, MOE_WS_EXPERT_FWD));
 }
 
@@ -309,11 +322,17 @@ int main() {
                           nullptr) == MOE_ERR_INVALID_ARG);
     const size_t n = moe_workspace_bytes(&s, MOE_WS_EXPERT_BWD);
     CHECK(moe_expert_bwd(&s, F, F, F, F, F, F, (int32_t*)F, (float*)F, (int32_t*)F, (int32_t*)F, (int32_t*)F, F,
-                         F, F, F, (float*)F, (float*)F, (float*)F, (float*)F, nullptr, F, n,
+                         F, F, nullptr, F, (float*)F, (float*)F, (float*)F, (float*)F, nullptr, F, n,
                          nullptr) == MOE_ERR_INVALID_ARG);  // y_swi and a_prime both given
     CHECK(moe_expert_bwd(&s, F, F, F, F, F, F, (int32_t*)F, (float*)F, (int32_t*)F, (int32_t*)F, (int32_t*)F, F,
-                         nullptr, F, F, (float*)F, (float*)F, (float*)F, (float*)F, nullptr, F, n,
+                         nullptr, F, nullptr, F, (float*)F, (float*)F, (float*)F, (float*)F, nullptr, F, n,
                          nullptr) == MOE_ERR_INVALID_ARG);  // A' over h_ab
+    CHECK(moe_expert_bwd(&s, F, F, F, F, F, F, (int32_t*)F, (float*)F, (int32_t*)F, (int32_t*)F, (int32_t*)F, F,
+                         nullptr, nullptr, (char*)F + 0x100, F, (float*)F, (float*)F, (float*)F, (float*)F, nullptr,
+                         F, n, nullptr) == MOE_ERR_INVALID_ARG);  // dH given, H-only, no A' buffer
+    CHECK(moe_expert_bwd(&s, F, F, F, F, F, F, (int32_t*)F, (float*)F, (int32_t*)F, (int32_t*)F, (int32_t*)F, F,
+                         (char*)F + 0x100, nullptr, (char*)F + 0x100, F, (float*)F, (float*)F, (float*)F, (float*)F,
+                         nullptr, F, n, nullptr) == MOE_ERR_INVALID_ARG);  // dH over y_swi
     CHECK(g_launches == before);
     CHECK(moe_set_spin_limit(0) > 0);
   }

@@ -232,7 +232,7 @@ def allowance_summary():
     total = sum(x[2] for x in ALLOWANCE_LOG)
     largest = max((x[3] for x in ALLOWANCE_LOG), default=0.0)
     marked = f", {100 * np.mean(FLIP_MARKED):.2f}% of stored bf16 values marked able to flip" if FLIP_MARKED else ""
-    return (f"rounding-flip allowance: {elems} of {total} weight-gradient elements in {len(drew)} of {checks} "
+    return (f"rounding-flip allowance: {elems} of {total} gradient elements in {len(drew)} of {checks} "
             f"checks drew on it (largest {largest:.2e} of the max_rel scale){marked}")
 
 

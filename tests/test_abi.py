@@ -35,9 +35,11 @@ def test_status_strings():
 
 def test_workspace_sizes_depend_on_shape_only():
     s = B.shape(16384, 2048, 128, 8, 768)
-    sizes = [B.workspace_bytes(s, w) for w in range(7)]
+    sizes = [B.workspace_bytes(s, w) for w in range(8)]
     assert all(n > 0 for n in sizes)
-    assert B.workspace_bytes(s, 7) == 0
+    assert B.workspace_bytes(s, 8) == 0 and B.workspace_bytes(s, -1) == 0
+    # the lean backward workspace is the full one without the [T*K, 2h] dH buffer
+    assert sizes[B.MOE_WS_EXPERT_BWD] - sizes[B.MOE_WS_EXPERT_BWD_LEAN] == 16384 * 8 * 2 * 768 * 2
     # the H-only backward workspace adds exactly the [T*K, h] A' buffer (256-byte aligned)
     extra = sizes[B.MOE_WS_EXPERT_BWD_H] - sizes[B.MOE_WS_EXPERT_BWD]
     assert 16384 * 8 * 768 * 2 <= extra < 16384 * 8 * 768 * 2 + 256
@@ -92,12 +94,13 @@ def test_pointer_and_workspace_validation():
     need = B.workspace_bytes(s, B.MOE_WS_EXPERT_BWD)
 
     def bwd_args():
-        a = [FAKE] * 19          # dout .. dw_down
+        a = [FAKE] * 20          # dout .. dw_down
         a[13] = None             # a_prime: only with H-only saving
+        a[14] = None             # dh: optional (the workspace holds it)
         return a
     req = bwd_args()
     assert L.moe_expert_bwd(sp, *req, None, FAKE, need - 1, 0) == B.MOE_ERR_WORKSPACE   # ds is optional
-    req[15] = None               # dwg missing
+    req[16] = None               # dwg missing
     assert L.moe_expert_bwd(sp, *req, None, FAKE, need, 0) == B.MOE_ERR_INVALID_ARG
     # y_swi == NULL (H-only saving) needs the larger MOE_WS_EXPERT_BWD_H workspace ...
     req = bwd_args()
@@ -118,6 +121,29 @@ def test_pointer_and_workspace_validation():
     req = bwd_args()
     req[13] = FAKE + 0x100       # a saved y and an A' buffer: ambiguous
     assert L.moe_expert_bwd(sp, *req, None, FAKE, need, 0) == B.MOE_ERR_INVALID_ARG
+    # dH in a caller buffer: the lean workspace, dH's [T*K, 2h] smaller, suffices
+    lean = B.workspace_bytes(s, B.MOE_WS_EXPERT_BWD_LEAN)
+    assert lean == need - (64 * 2 * 2 * 128 * 2)
+
+    def distinct_args():         # every buffer at an address of its own
+        a = [FAKE + 0x1000 * i for i in range(20)]
+        a[13] = a[14] = None
+        return a
+    req = distinct_args()
+    req[14] = FAKE + 0x100000
+    assert L.moe_expert_bwd(sp, *req, None, FAKE, lean - 1, 0) == B.MOE_ERR_WORKSPACE
+    req[14] = req[11]            # dH over the saved a|b: allowed
+    assert L.moe_expert_bwd(sp, *req, None, FAKE, lean - 1, 0) == B.MOE_ERR_WORKSPACE
+    for bad in (req[12], req[0], req[1], req[15], FAKE + 0x100004):   # y_swi, dout, x, dx, misaligned
+        req[14] = bad
+        assert L.moe_expert_bwd(sp, *req, None, FAKE, need, 0) == B.MOE_ERR_INVALID_ARG
+    req = distinct_args()
+    req[12], req[14] = None, req[11]          # H-only with dH given needs an A' buffer too
+    assert L.moe_expert_bwd(sp, *req, None, FAKE, need_h, 0) == B.MOE_ERR_INVALID_ARG
+    req[13] = FAKE + 0x200000
+    assert L.moe_expert_bwd(sp, *req, None, FAKE, lean - 1, 0) == B.MOE_ERR_WORKSPACE
+    req[14] = req[13]            # dH over A'
+    assert L.moe_expert_bwd(sp, *req, None, FAKE, need_h, 0) == B.MOE_ERR_INVALID_ARG
 
 
 def test_activation_kind_validation():
@@ -160,3 +186,6 @@ def test_one_workspace_serves_forward_combine_and_backward():
     # it does not repeat the fp32 [T, d] accumulator
     dh = 16384 * 8 * 2 * 768 * 2
     assert dh <= bwd - comb < dh + 16384 * 2048 * 4
+    # with dH in a caller buffer the backward needs the same carving without it
+    lean = B.workspace_bytes(s, B.MOE_WS_EXPERT_BWD_LEAN)
+    assert lean == bwd - dh and comb < lean

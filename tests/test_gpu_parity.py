@@ -195,10 +195,10 @@ LAYER_CASES = [
 ]
 
 
-def _gpu_layer(inp, wl, logits32=None, backward=True, saved="aby", combine="fold"):
+def _gpu_layer(inp, wl, logits32=None, backward=True, saved="aby", combine="fold", dh_over_h=True):
     dt = wl.dtype
     buf = Lyr.MoEBuffers(wl.T, wl.d, wl.E, wl.K, wl.h, dt, backward=backward, saved=saved, combine=combine,
-                         act=wl.act)
+                         act=wl.act, dh_over_h=dh_over_h)
     dev = {k: (Lyr.to_device(inp[k], dt) if inp[k] is not None else None)
            for k in ("x", "wg", "w_gate", "w_up", "w_down", "dy") if k in inp}
     bias = torch.from_numpy(inp["bias"]).cuda() if inp.get("bias") is not None else None
@@ -207,6 +207,7 @@ def _gpu_layer(inp, wl, logits32=None, backward=True, saved="aby", combine="fold
     Lyr.forward(buf, dev["x"], dev["wg"], bias, dev["w_gate"], dev["w_up"], dev["w_down"],
                 logits_in=logits32 is not None)
     buf.y_fwd = buf.y_swi.clone()       # an H-only backward writes A' over y_swi
+    buf.h_fwd = buf.h_ab.clone() if buf.h_ab is not None else None   # the backward writes dH over h_ab
     if backward:
         Lyr.backward(buf, dev["dy"], dev["x"], dev["wg"], dev["w_gate"], dev["w_up"], dev["w_down"])
     torch.cuda.synchronize()
@@ -226,10 +227,11 @@ def _compare_layer(buf, inp, wl, z32, backward=True, report=None, w_rtol=2e-6, s
     gated = wl.act == "swiglu"
     f = O.moe_forward(inp["x"], ids, w, inp["w_gate"], inp["w_up"], inp["w_down"], dtype=wl.dtype, act=wl.act)
     pos = ix["token_index_map"].reshape(T, K)
-    hab = to_np(buf.h_ab)[pos]          # [T,K,2h] (gated) or [T,K,h]
-    assert_close("a", hab[..., :h], f["a_s"], report=report)
-    if gated:
-        assert_close("b", hab[..., h:], f["b_s"], report=report)
+    if getattr(buf, "h_fwd", None) is not None:   # H as the forward left it (the backward writes dH over it)
+        hab = to_np(buf.h_fwd)[pos]     # [T,K,2h] (gated) or [T,K,h]
+        assert_close("a", hab[..., :h], f["a_s"], report=report)
+        if gated:
+            assert_close("b", hab[..., h:], f["b_s"], report=report)
     if getattr(buf, "y_fwd", None) is not None:   # y as the forward left it (an H-only backward overwrites it)
         assert_close("y_swi", to_np(buf.y_fwd)[pos], f["y_s"], report=report)
     assert_close("out", to_np(buf.out), f["out"], report=report)
@@ -250,6 +252,11 @@ def _compare_layer(buf, inp, wl, z32, backward=True, report=None, w_rtol=2e-6, s
                      allow=dw_flip_allowance(fl["db"], ids, inp["x"], E))
     assert_close("dw_down", to_np(buf.dw_down), bw["dw_down"], report=report,
                  allow=dw_flip_allowance(fl["ap"], ids, inp["dy"], E, transpose=True))
+    if buf.dh_over_h:                   # h_ab now holds dH = [dA | dB], stored in the activation dtype
+        dh = to_np(buf.h_ab)[pos]
+        assert_close("dA", dh[..., :h], bw["dh_a"], report=report, allow=fl["da"])
+        if gated:
+            assert_close("dB", dh[..., h:], bw["dh_b"], report=report, allow=fl["db"])
     # experts without rows: exact zeros
     empty = np.nonzero(np.diff(ix["offsets"]) == 0)[0]
     for key in ("dw_gate", "dw_down", "dwg") + (("dw_up",) if gated else ()):
@@ -395,9 +402,30 @@ def test_bitwise_repeatable():
     inp = synth.make_inputs(wl)
     b1, _ = _gpu_layer(inp, wl)
     b2, _ = _gpu_layer(inp, wl)
-    for key in ("topk_ids", "topk_w", "eti", "tim", "h_ab", "y_fwd", "y_swi", "out", "dx", "dwg", "dw_gate",
-                "dw_up", "dw_down", "ds"):
+    for key in ("topk_ids", "topk_w", "eti", "tim", "h_fwd", "h_ab", "y_fwd", "y_swi", "out", "dx", "dwg",
+                "dw_gate", "dw_up", "dw_down", "ds"):
         assert torch.equal(getattr(b1, key), getattr(b2, key)), key
+
+
+@pytest.mark.parametrize("saved", ["aby", "ab"])
+def test_dh_over_saved_h_matches_the_workspace_dh(saved):
+    """dH written over the saved H (the lean backward workspace) gives the
+    same gradients, bit for bit, as dH in the workspace; in the first case
+    h_ab then holds dH, in the second it still holds H."""
+    T, d, E, K, h = 700, 1024, 16, 4, 512
+    _say("dh_over_h", saved, T, d, E, K, h)
+    wl = synth.small_workload(T, d, E, K, h, seed=29, zipf_s=1.2)
+    inp = synth.make_inputs(wl)
+    z32 = O.router_logits(inp["x"], inp["wg"], inp["bias"]).astype(np.float32)
+    lean, _ = _gpu_layer(inp, wl, logits32=z32, saved=saved, dh_over_h=True)
+    full, _ = _gpu_layer(inp, wl, logits32=z32, saved=saved, dh_over_h=False)
+    assert lean.ws_main.numel() < full.ws_main.numel()
+    assert lean.device_error_words() == [0, 0] and full.device_error_words() == [0, 0]
+    for key in ("h_fwd", "y_fwd", "y_swi", "out", "dx", "dwg", "dw_gate", "dw_up", "dw_down", "ds"):
+        assert torch.equal(getattr(lean, key), getattr(full, key)), key
+    assert torch.equal(full.h_ab, full.h_fwd)
+    assert not torch.equal(lean.h_ab, lean.h_fwd)
+    _compare_layer(lean, inp, wl, z32, saved=saved)
 
 
 def test_bounded_wait_reports_and_finishes():

@@ -64,6 +64,7 @@ def _run_layer(wl, inp, logits32=None):
         Lyr.forward(buf, dev["x"], dev["wg"], bias, dev["w_gate"], dev["w_up"], dev["w_down"],
                     logits_in=logits32 is not None)
         buf.y_fwd = buf.y_swi.clone()   # the H-only backward writes A' over y_swi
+        buf.h_fwd = buf.h_ab.clone() if buf.h_ab is not None else None   # and dH over h_ab
         if wl.backward:
             Lyr.backward(buf, dev["dy"], dev["x"], dev["wg"], dev["w_gate"], dev["w_up"], dev["w_down"])
         torch.cuda.synchronize()
@@ -137,7 +138,7 @@ def _check(wl, inp, buf, z, given):
     pos = torch.from_numpy(to_np(buf.tim).reshape(T, K)[sub].reshape(-1)).cuda()
     assert_close("y[sample]", to_np(buf.y_fwd[pos]).reshape(len(sub), K, -1), f["y_s"])
     if buf.h_ab is not None:   # a forward-only workload saves nothing
-        hab = to_np(buf.h_ab[pos]).reshape(len(sub), K, -1)
+        hab = to_np(buf.h_fwd[pos]).reshape(len(sub), K, -1)
         assert_close("a[sample]", hab[..., :h], f["a_s"])
         if gated:
             assert_close("b[sample]", hab[..., h:], f["b_s"])
@@ -148,6 +149,14 @@ def _check(wl, inp, buf, z, given):
                        saved=SAVED)
     assert_close(f"dx[sample] {tag}", to_np(buf.dx[subd]), b["dx"])
     assert_close("ds[sample]", to_np(buf.ds)[sub], b["ds_router"])
+    if buf.dh_over_h:   # h_ab holds dH = [dA | dB] after the backward
+        win = fp32_windows(inp["x"][sub], inp["dy"][sub], ids_ref[sub], inp["w_gate"], inp["w_up"], inp["w_down"],
+                           act=wl.act)
+        fl = stored_flip_bounds(f, b, w_ref[sub], dt, wl.act, SAVED, win)
+        dhs = to_np(buf.h_ab[pos]).reshape(len(sub), K, -1)
+        assert_close("dA[sample]", dhs[..., :h], b["dh_a"], allow=fl["da"])
+        if gated:
+            assert_close("dB[sample]", dhs[..., h:], b["dh_b"], allow=fl["db"])
 
     def toks_of(e):
         toks = np.nonzero((ids_ref == e).any(axis=1))[0]
