@@ -1059,8 +1059,10 @@ __global__ __launch_bounds__(C::NT, C::WAVES_PER_EU) void dh_kernel(
             } else {  // plain expert: dA = dy * sigma'(a), from the saved pre-activation
 #pragma unroll
               for (int v = 0; v < VPC; ++v) {
-                if constexpr (HONLY) y[v] = act_fwd(a[v], act);
-                da[v] = w[i] * dapr[v] * act_grad(a[v], act);
+                float yv, gv;
+                act_fwd_grad(a[v], act, yv, gv);
+                if constexpr (HONLY) y[v] = yv;
+                da[v] = w[i] * dapr[v] * gv;
                 dsum += dapr[v] * y[v];
               }
             }
