@@ -17,11 +17,14 @@ typedef uint32_t u32x2_t __attribute__((ext_vector_type(2)));
 
 MOE_DEV float bf16_to_f32(uint32_t v) { return __uint_as_float(v << 16); }
 
-MOE_DEV uint32_t f32_to_bf16(float f) {
-  const uint32_t u = __float_as_uint(f);
-  const uint32_t rounded = (u + 0x7fffu + ((u >> 16) & 1u)) >> 16;
-  return (u & 0x7fffffffu) > 0x7f800000u ? (u >> 16) | 0x40u : rounded;  // NaN stays a quiet NaN
+// fp32 -> bf16, rounded to nearest even: gfx950 converts two values in one
+// v_cvt_pk_bf16_f32 (low half a, high half b).  A NaN stays a NaN.
+typedef __bf16 bf16x2_v __attribute__((ext_vector_type(2)));
+typedef float f32x2_v __attribute__((ext_vector_type(2)));
+MOE_DEV uint32_t pack_bf16x2(float a, float b) {
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector((f32x2_v){a, b}, bf16x2_v));
 }
+MOE_DEV uint32_t f32_to_bf16(float f) { return pack_bf16x2(f, 0.0f) & 0xffffu; }
 
 template <typename T> struct ElemT;
 template <> struct ElemT<float> {
@@ -52,7 +55,7 @@ MOE_DEV void ld16(const float* p, float (&v)[4]) {
 MOE_DEV void st16(bf16_t* p, const float (&v)[8]) {
   u32x4_t q;
 #pragma unroll
-  for (int i = 0; i < 4; ++i) q[i] = f32_to_bf16(v[2 * i]) | (f32_to_bf16(v[2 * i + 1]) << 16);
+  for (int i = 0; i < 4; ++i) q[i] = pack_bf16x2(v[2 * i], v[2 * i + 1]);
   *(u32x4_t*)p = q;
 }
 MOE_DEV void st16(float* p, const float (&v)[4]) { *(f32x4_t*)p = f32x4_t{v[0], v[1], v[2], v[3]}; }
@@ -90,7 +93,7 @@ MOE_DEV void unpack16(const u32x4_t& q, float (&v)[4]) {  // 4 fp32
 MOE_DEV void st16nt(bf16_t* p, const float (&v)[8]) {
   u32x4_t q;
 #pragma unroll
-  for (int i = 0; i < 4; ++i) q[i] = f32_to_bf16(v[2 * i]) | (f32_to_bf16(v[2 * i + 1]) << 16);
+  for (int i = 0; i < 4; ++i) q[i] = pack_bf16x2(v[2 * i], v[2 * i + 1]);
   __builtin_nontemporal_store(q, (u32x4_t*)p);
 }
 MOE_DEV void st16nt(float* p, const float (&v)[4]) {

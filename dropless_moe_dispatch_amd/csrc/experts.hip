@@ -422,7 +422,7 @@ MOE_DEV void coherent_store2(float* p, float a, float b) {
   __hip_atomic_store((uint64_t*)p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 MOE_DEV void store2(float* p, float a, float b) { *(float2*)p = make_float2(a, b); }
-MOE_DEV void store2(bf16_t* p, float a, float b) { *(uint32_t*)p = f32_to_bf16(a) | (f32_to_bf16(b) << 16); }
+MOE_DEV void store2(bf16_t* p, float a, float b) { *(uint32_t*)p = pack_bf16x2(a, b); }
 
 constexpr int FOLD_ROWS_PER_WAVE = 32;
 constexpr int FOLD_BATCH = 16;
@@ -811,7 +811,7 @@ __global__ __launch_bounds__(C::NT, C::WAVES_PER_EU) void down_staged_kernel(
     if constexpr (sizeof(TIN) == 2) {
       u32x4_t v;
 #pragma unroll
-      for (int q = 0; q < 4; ++q) v[q] = f32_to_bf16(src[2 * q]) | (f32_to_bf16(src[2 * q + 1]) << 16);
+      for (int q = 0; q < 4; ++q) v[q] = pack_bf16x2(src[2 * q], src[2 * q + 1]);
       *(u32x4_t*)dst = v;
     } else {
       *(f32x4_t*)dst = *(const f32x4_t*)src;
@@ -860,7 +860,7 @@ __global__ __launch_bounds__(256) void gather_sum_kernel(const TIN* __restrict__
     if constexpr (sizeof(TIN) == 2) {
       u32x4_t q;
 #pragma unroll
-      for (int v = 0; v < 4; ++v) q[v] = f32_to_bf16(acc[2 * v]) | (f32_to_bf16(acc[2 * v + 1]) << 16);
+      for (int v = 0; v < 4; ++v) q[v] = pack_bf16x2(acc[2 * v], acc[2 * v + 1]);
       *(u32x4_t*)o = q;
     } else {
       *(f32x4_t*)o = f32x4_t{acc[0], acc[1], acc[2], acc[3]};

@@ -227,9 +227,7 @@ struct KRowLoader {
 #pragma unroll
             for (int q = 0; q < 4; ++q) {
               const uint32_t v = r[j][q];
-              const uint32_t lo = f32_to_bf16(bf16_to_f32(v & 0xffffu) * sdat[SET][j]);
-              const uint32_t hi = f32_to_bf16(bf16_to_f32(v >> 16) * sdat[SET][j]);
-              r[j][q] = lo | (hi << 16);
+              r[j][q] = pack_bf16x2(bf16_to_f32(v & 0xffffu) * sdat[SET][j], bf16_to_f32(v >> 16) * sdat[SET][j]);
             }
           }
         }
@@ -308,9 +306,7 @@ struct KLoader {
       if constexpr (SCALED) {
 #pragma unroll
         for (int q = 0; q < 4; ++q) {
-          const uint32_t lo = f32_to_bf16(bf16_to_f32(v[q] & 0xffffu) * sdat[SET][i]);
-          const uint32_t hi = f32_to_bf16(bf16_to_f32(v[q] >> 16) * sdat[SET][i]);
-          v[q] = lo | (hi << 16);
+          v[q] = pack_bf16x2(bf16_to_f32(v[q] & 0xffffu) * sdat[SET][i], bf16_to_f32(v[q] >> 16) * sdat[SET][i]);
         }
       }
       *(u32x4_t*)(lds + kr(i) * G::PITCH + cc() * 16) = v;
