@@ -61,7 +61,23 @@ def build(verbose: bool = False, jobs: int = 4) -> str:
         print(" ".join(cmd), flush=True)
     subprocess.run(cmd, check=True)
     os.replace(tmp, LIB)
+    build_pack_check(verbose)
     return LIB
+
+
+PACK_CHECK_SRC = os.path.join(os.path.dirname(HERE), "tests", "bf16_pack_check.hip")
+PACK_CHECK = os.path.join(OUT_DIR, "bf16_pack_check")
+
+
+def build_pack_check(verbose: bool = False) -> str:
+    """The GPU test program that checks the library's bf16 packing rounds to
+    nearest even (tests/test_gpu_bf16_pack.py runs it)."""
+    cmd = [hipcc(), *[f for f in compile_flags() if f != "-fPIC"], PACK_CHECK_SRC, "-o", PACK_CHECK + ".tmp"]
+    if verbose:
+        print(" ".join(cmd), flush=True)
+    subprocess.run(cmd, check=True, capture_output=not verbose)
+    os.replace(PACK_CHECK + ".tmp", PACK_CHECK)
+    return PACK_CHECK
 
 
 if __name__ == "__main__":
