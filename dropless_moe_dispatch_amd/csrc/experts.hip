@@ -442,6 +442,7 @@ MOE_DEV void fold_rows(const float* s_c, const int* s_t, const float* s_w, const
   const bool mine = l < 32 && my_row < rows;
   const int my_t = mine ? s_t[my_row] : 0;
   const int my_rank = mine ? s_rank[my_row] : 0;
+  const float my_w = mine ? s_w[my_row] : 1.0f;
   int32_t* my_turn = turn + (size_t)my_t * NB + nb;
   const int col = 2 * l;  // each lane folds two adjacent columns of a row
   const size_t cofs = (size_t)nb * 128 + col;
@@ -463,25 +464,35 @@ MOE_DEV void fold_rows(const float* s_c, const int* s_t, const float* s_w, const
     // In batches of 16 rows: read the accumulator of every row of the batch
     // without branches (a row that is not ready yet, or past the tile, reads
     // a value that is never stored), combine, then store the ready rows, so
-    // that no store waits on a load.
+    // that no store waits on a load.  A row's token, rank and weight come
+    // from the lane that watches it (readlane: scalars, with no LDS read and
+    // no wait per row); the row's two parked values are read from LDS for the
+    // whole batch at once.
 #pragma unroll
     for (int b0 = 0; b0 < FOLD_ROWS_PER_WAVE; b0 += FOLD_BATCH) {
       if (((m >> b0) & ((1ull << FOLD_BATCH) - 1)) == 0) continue;
-      u32x2_t prev[FOLD_BATCH];
-#pragma unroll
-      for (int i = 0; i < FOLD_BATCH; ++i)
-        prev[i] = coherent_load2(accws + (size_t)s_t[wave + 4 * (b0 + i)] * d + cofs);
+      int t_r[FOLD_BATCH], rank_r[FOLD_BATCH];
+      float w_r[FOLD_BATCH];
 #pragma unroll
       for (int i = 0; i < FOLD_BATCH; ++i) {
-        const int row = wave + 4 * (b0 + i);
-        const float w = s_w[row];
-        const float2 c = *(const float2*)(s_c + row * FOLD_LD + col);
-        const bool fresh = INIT_FIRST && s_rank[row] == 0;  // rank 0 starts the sum (forward)
-        const float a = (fresh ? 0.0f : __uint_as_float(prev[i][0])) + w * c.x;
-        const float b = (fresh ? 0.0f : __uint_as_float(prev[i][1])) + w * c.y;
+        t_r[i] = __builtin_amdgcn_readlane(my_t, b0 + i);
+        rank_r[i] = __builtin_amdgcn_readlane(my_rank, b0 + i);
+        w_r[i] = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(my_w), b0 + i));
+      }
+      u32x2_t prev[FOLD_BATCH];
+#pragma unroll
+      for (int i = 0; i < FOLD_BATCH; ++i) prev[i] = coherent_load2(accws + (size_t)t_r[i] * d + cofs);
+      float2 c[FOLD_BATCH];
+#pragma unroll
+      for (int i = 0; i < FOLD_BATCH; ++i) c[i] = *(const float2*)(s_c + (wave + 4 * (b0 + i)) * FOLD_LD + col);
+#pragma unroll
+      for (int i = 0; i < FOLD_BATCH; ++i) {
+        const bool fresh = INIT_FIRST && rank_r[i] == 0;  // rank 0 starts the sum (forward)
+        const float a = (fresh ? 0.0f : __uint_as_float(prev[i][0])) + w_r[i] * c[i].x;
+        const float b = (fresh ? 0.0f : __uint_as_float(prev[i][1])) + w_r[i] * c[i].y;
         if ((m >> (b0 + i)) & 1) {
-          const size_t o = (size_t)s_t[row] * d + cofs;
-          if (s_rank[row] == K - 1) store2(out + o, a, b);
+          const size_t o = (size_t)t_r[i] * d + cofs;
+          if (rank_r[i] == K - 1) store2(out + o, a, b);
           else coherent_store2(accws + o, a, b);
         }
       }
