@@ -425,7 +425,11 @@ MOE_DEV void store2(float* p, float a, float b) { *(float2*)p = make_float2(a, b
 MOE_DEV void store2(bf16_t* p, float a, float b) { *(uint32_t*)p = pack_bf16x2(a, b); }
 
 constexpr int FOLD_ROWS_PER_WAVE = 32;
-constexpr int FOLD_BATCH = 16;
+// Rows per batch of a wave's fold: 16 in the forward, all 32 in the dX fold.
+// Measured on MI355X at large d against 16 everywhere: the dX fold 0.9%
+// faster with 32, down-combine 1.1% slower.
+template <bool INIT_FIRST>
+constexpr int fold_batch() { return INIT_FIRST ? 16 : 32; }
 
 // Fold of one parked 128 x 128 block (rows of 136 floats in s_c, per-row
 // token, weight and rank in s_t, s_w, s_rank) into the 128 accumulator
@@ -435,6 +439,7 @@ template <bool INIT_FIRST, typename TOUT>
 MOE_DEV void fold_rows(const float* s_c, const int* s_t, const float* s_w, const int* s_rank, int rows, int wave,
                        int nb, int NB, int K, int d, int32_t* turn, float* __restrict__ accws, TOUT* __restrict__ out,
                        int32_t* err, int spin_limit) {
+  constexpr int BATCH = fold_batch<INIT_FIRST>();
   const int l = lane_id();
   // wave w folds tile rows w, w + 4, ..., w + 124; lane j < 32 watches row w + 4j
   const int j = l & 31;
@@ -445,7 +450,9 @@ MOE_DEV void fold_rows(const float* s_c, const int* s_t, const float* s_w, const
   const float my_w = mine ? s_w[my_row] : 1.0f;
   int32_t* my_turn = turn + (size_t)my_t * NB + nb;
   const int col = 2 * l;  // each lane folds two adjacent columns of a row
-  const size_t cofs = (size_t)nb * 128 + col;
+  // byte offset of the lane's two columns in a row: a 32-bit lane offset on a
+  // scalar row address
+  const uint32_t cbyte = (uint32_t)(nb * 128 + col) * 4u;
   uint64_t pending = __builtin_amdgcn_ballot_w64(mine);
   int spins = 0;
   while (pending) {
@@ -461,7 +468,7 @@ MOE_DEV void fold_rows(const float* s_c, const int* s_t, const float* s_w, const
       continue;
     }
     spins = 0;
-    // In batches of 16 rows: read the accumulator of every row of the batch
+    // In batches of BATCH rows: read the accumulator of every row of the batch
     // without branches (a row that is not ready yet, or past the tile, reads
     // a value that is never stored), combine, then store the ready rows, so
     // that no store waits on a load.  A row's token, rank and weight come
@@ -469,31 +476,32 @@ MOE_DEV void fold_rows(const float* s_c, const int* s_t, const float* s_w, const
     // no wait per row); the row's two parked values are read from LDS for the
     // whole batch at once.
 #pragma unroll
-    for (int b0 = 0; b0 < FOLD_ROWS_PER_WAVE; b0 += FOLD_BATCH) {
-      if (((m >> b0) & ((1ull << FOLD_BATCH) - 1)) == 0) continue;
-      int t_r[FOLD_BATCH], rank_r[FOLD_BATCH];
-      float w_r[FOLD_BATCH];
+    for (int b0 = 0; b0 < FOLD_ROWS_PER_WAVE; b0 += BATCH) {
+      if (((m >> b0) & ((1ull << BATCH) - 1)) == 0) continue;
+      int t_r[BATCH], rank_r[BATCH];
+      float w_r[BATCH];
 #pragma unroll
-      for (int i = 0; i < FOLD_BATCH; ++i) {
+      for (int i = 0; i < BATCH; ++i) {
         t_r[i] = __builtin_amdgcn_readlane(my_t, b0 + i);
         rank_r[i] = __builtin_amdgcn_readlane(my_rank, b0 + i);
         w_r[i] = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(my_w), b0 + i));
       }
-      u32x2_t prev[FOLD_BATCH];
+      u32x2_t prev[BATCH];
 #pragma unroll
-      for (int i = 0; i < FOLD_BATCH; ++i) prev[i] = coherent_load2(accws + (size_t)t_r[i] * d + cofs);
-      float2 c[FOLD_BATCH];
+      for (int i = 0; i < BATCH; ++i)
+        prev[i] = coherent_load2((const float*)((const char*)(accws + (size_t)t_r[i] * d) + cbyte));
+      float2 c[BATCH];
 #pragma unroll
-      for (int i = 0; i < FOLD_BATCH; ++i) c[i] = *(const float2*)(s_c + (wave + 4 * (b0 + i)) * FOLD_LD + col);
+      for (int i = 0; i < BATCH; ++i) c[i] = *(const float2*)(s_c + (wave + 4 * (b0 + i)) * FOLD_LD + col);
 #pragma unroll
-      for (int i = 0; i < FOLD_BATCH; ++i) {
+      for (int i = 0; i < BATCH; ++i) {
         const bool fresh = INIT_FIRST && rank_r[i] == 0;  // rank 0 starts the sum (forward)
         const float a = (fresh ? 0.0f : __uint_as_float(prev[i][0])) + w_r[i] * c[i].x;
         const float b = (fresh ? 0.0f : __uint_as_float(prev[i][1])) + w_r[i] * c[i].y;
         if ((m >> (b0 + i)) & 1) {
-          const size_t o = (size_t)t_r[i] * d + cofs;
-          if (rank_r[i] == K - 1) store2(out + o, a, b);
-          else coherent_store2(accws + o, a, b);
+          const size_t row = (size_t)t_r[i] * d;
+          if (rank_r[i] == K - 1) store2((TOUT*)((char*)(out + row) + cbyte / (4 / sizeof(TOUT))), a, b);
+          else coherent_store2((float*)((char*)(accws + row) + cbyte), a, b);
         }
       }
     }
