@@ -450,9 +450,10 @@ MOE_DEV void fold_rows(const float* s_c, const int* s_t, const float* s_w, const
   const float my_w = mine ? s_w[my_row] : 1.0f;
   int32_t* my_turn = turn + (size_t)my_t * NB + nb;
   const int col = 2 * l;  // each lane folds two adjacent columns of a row
-  // byte offset of the lane's two columns in a row: a 32-bit lane offset on a
-  // scalar row address
-  const uint32_t cbyte = (uint32_t)(nb * 128 + col) * 4u;
+  // byte offsets of the lane's two columns in an accumulator row and in an
+  // output row: 32-bit lane offsets on scalar row addresses
+  const uint32_t cbyte = (uint32_t)(nb * 128 + col) * (uint32_t)sizeof(float);
+  const uint32_t obyte = (uint32_t)(nb * 128 + col) * (uint32_t)sizeof(TOUT);
   uint64_t pending = __builtin_amdgcn_ballot_w64(mine);
   int spins = 0;
   while (pending) {
@@ -500,7 +501,7 @@ MOE_DEV void fold_rows(const float* s_c, const int* s_t, const float* s_w, const
         const float b = (fresh ? 0.0f : __uint_as_float(prev[i][1])) + w_r[i] * c[i].y;
         if ((m >> (b0 + i)) & 1) {
           const size_t row = (size_t)t_r[i] * d;
-          if (rank_r[i] == K - 1) store2((TOUT*)((char*)(out + row) + cbyte / (4 / sizeof(TOUT))), a, b);
+          if (rank_r[i] == K - 1) store2((TOUT*)((char*)(out + row) + obyte), a, b);
           else coherent_store2((float*)((char*)(accws + row) + cbyte), a, b);
         }
       }
