@@ -410,8 +410,9 @@ def test_bitwise_repeatable():
 @pytest.mark.parametrize("saved", ["aby", "ab"])
 def test_dh_over_saved_h_matches_the_workspace_dh(saved):
     """dH written over the saved H (the lean backward workspace) gives the
-    same gradients, bit for bit, as dH in the workspace; in the first case
-    h_ab then holds dH, in the second it still holds H."""
+    same gradients, bit for bit, as dH in the workspace, and as dH in a
+    caller buffer of its own; h_ab then holds dH in the first case and still
+    holds H in the others."""
     T, d, E, K, h = 700, 1024, 16, 4, 512
     _say("dh_over_h", saved, T, d, E, K, h)
     wl = synth.small_workload(T, d, E, K, h, seed=29, zipf_s=1.2)
@@ -426,6 +427,23 @@ def test_dh_over_saved_h_matches_the_workspace_dh(saved):
     assert torch.equal(full.h_ab, full.h_fwd)
     assert not torch.equal(lean.h_ab, lean.h_fwd)
     _compare_layer(lean, inp, wl, z32, saved=saved)
+    # dH in a buffer of its own (neither h_ab nor the workspace): the same dH
+    # and gradients, with the saved H left as it was
+    sep, dev = _gpu_layer(inp, wl, logits32=z32, saved=saved, dh_over_h=False)
+    dh = torch.full_like(sep.h_ab, -7.0)
+    for key in ("dx", "dwg", "dw_gate", "dw_up", "dw_down", "ds"):   # every output written again
+        getattr(sep, key).fill_(float("nan"))
+    honly = saved == "ab"
+    B.moe_expert_bwd(sep.shape, dev["dy"], dev["x"], dev["wg"], dev["w_gate"], dev["w_up"], dev["w_down"],
+                     sep.topk_ids, sep.topk_w, sep.offsets, sep.eti, sep.tim, sep.h_ab,
+                     None if honly else sep.y_swi, sep.y_swi if honly else None, dh, sep.dx, sep.dwg, sep.dw_gate,
+                     sep.dw_up, sep.dw_down, sep.ds, sep.ws_main)
+    torch.cuda.synchronize()
+    assert sep.device_error_words() == [0, 0]
+    assert torch.equal(dh, lean.h_ab)
+    assert torch.equal(sep.h_ab, sep.h_fwd)
+    for key in ("dx", "dwg", "dw_gate", "dw_up", "dw_down", "ds"):
+        assert torch.equal(getattr(sep, key), getattr(lean, key)), key
 
 
 def test_bounded_wait_reports_and_finishes():
