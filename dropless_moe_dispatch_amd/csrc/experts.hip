@@ -159,12 +159,15 @@ static bool pick_mid(const Shape& s, bool auto_choice) {
 // its eight waves park their accumulators in LDS and four of them fold the two
 // 128-column halves side by side.  It pays where each tile's reduction (kdim)
 // is long next to the fold.  Measured on MI355X against the 128 x 256 tile:
-// dX fold 7.4% faster at d = 6144, kdim = 4096 and 3% at d = 4096,
-// kdim = 3072; down-combine 1.62 -> 1.35 ms at d = 4096, kdim = 14336, but
-// 3-8% slower at kdim = 1536-2048 and 15-30% slower at d = 2048.
-static bool wide_fold(const Shape& s, int kdim) {
+// dX fold 7.4% faster at d = 6144, kdim = 4096, 3% at d = 4096, kdim = 3072,
+// and faster at d = 1024-2048 with kdim = 4096-8192 too (MoEBlaze's conf3
+// and conf4), but 15% slower at d = 2048, kdim = 1536; down-combine
+// 1.62 -> 1.35 ms at d = 4096, kdim = 14336, but 3-8% slower at
+// kdim = 1536-2048 and 7.5% slower at d = 1024, kdim = 4096.  dx: the dX fold
+// (else down-combine).
+static bool wide_fold(const Shape& s, int kdim, bool dx) {
   static const int force = env_int("MOE_DISPATCH_WIDE_FOLD", -1);  // tuning aid: 1 on, 0 off
-  const bool auto_choice = force >= 0 ? force == 1 : (s.d >= 4096 && kdim >= 3072);
+  const bool auto_choice = force >= 0 ? force == 1 : (kdim >= 3072 && (dx || s.d >= 4096));
   return s.bf16 && s.d % TILE_L == 0 && pick_large(auto_choice);
 }
 // Otherwise the folds take the 128 x 256 tile where d is a multiple of 256
@@ -175,8 +178,8 @@ static bool wide_fold(const Shape& s, int kdim) {
 // 0.5-1.7% slower on skewed and conf3.  The gate/up and dH kernels measured
 // 2-14% slower on it and keep 128 x 128 (dH except for a long reduction,
 // see the backward).
-static bool mid_fold(const Shape& s, int kdim) {
-  return !wide_fold(s, kdim) && s.d % TILE_L == 0 && pick_mid(s, true);
+static bool mid_fold(const Shape& s, int kdim, bool dx) {
+  return !wide_fold(s, kdim, dx) && s.d % TILE_L == 0 && pick_mid(s, true);
 }
 
 // ===========================================================================
@@ -356,8 +359,10 @@ hipError_t launch_gate_up(const Shape& s, const void* x, const int32_t* offsets,
                           hipStream_t st) {
   timing_mark(st, "gate_up", true);
   // measured on MI355X: the large tile wins from d = 4096 on (the small one
-  // wastes less on partial row tiles for short reductions)
-  const bool big = pick_large(s.d >= 4096);
+  // wastes less on partial row tiles for short reductions); a plain expert's
+  // first layer (one projection, N = h) takes it at every d in bf16: 4-8.5%
+  // faster at d = 512-2048, h = 4d (MoEBlaze's conf1, conf3, conf4)
+  const bool big = pick_large(s.d >= 4096 || (!s.gated() && s.bf16));
   const bool mid = !big && pick_mid(s, false);
   hipError_t e;
   if (!s.gated()) {
@@ -762,8 +767,8 @@ hipError_t launch_down_combine(const Shape& s, const void* y_swi, const void* w_
   timing_mark(st, "down_combine", true);
   const hipError_t e =
       !s.bf16               ? down_combine_t<float, TILE_S, TILE_S>(s, y_swi, w_down, offsets, eti, out, ws, spin_limit, st)
-      : wide_fold(s, s.h) ? down_combine_t<bf16_t, TILE_L, TILE_L>(s, y_swi, w_down, offsets, eti, out, ws, spin_limit, st)
-      : mid_fold(s, s.h)  ? down_combine_t<bf16_t, TILE_S, TILE_L>(s, y_swi, w_down, offsets, eti, out, ws, spin_limit, st)
+      : wide_fold(s, s.h, false) ? down_combine_t<bf16_t, TILE_L, TILE_L>(s, y_swi, w_down, offsets, eti, out, ws, spin_limit, st)
+      : mid_fold(s, s.h, false)  ? down_combine_t<bf16_t, TILE_S, TILE_L>(s, y_swi, w_down, offsets, eti, out, ws, spin_limit, st)
                           : down_combine_t<bf16_t, TILE_S, TILE_S>(s, y_swi, w_down, offsets, eti, out, ws, spin_limit, st);
   timing_mark(st, "down_combine", false);
   return e;
@@ -1752,8 +1757,8 @@ static hipError_t backward_t(const Shape& s, const void* dout, const void* x, co
   // weight slot is never read
   const void* w2 = s.gated() ? w_up : w_gate;
   if constexpr (sizeof(TIN) == 2) {
-    if (wide_fold(s, s.hw())) launch_dx_fold<TIN, TILE_L, TILE_L>(s, w_gate, w2, offsets, eti, dx, ws, spin_limit, st);
-    else if (mid_fold(s, s.hw())) launch_dx_fold<TIN, TILE_S, TILE_L>(s, w_gate, w2, offsets, eti, dx, ws, spin_limit, st);
+    if (wide_fold(s, s.hw(), true)) launch_dx_fold<TIN, TILE_L, TILE_L>(s, w_gate, w2, offsets, eti, dx, ws, spin_limit, st);
+    else if (mid_fold(s, s.hw(), true)) launch_dx_fold<TIN, TILE_S, TILE_L>(s, w_gate, w2, offsets, eti, dx, ws, spin_limit, st);
     else launch_dx_fold<TIN, TILE_S, TILE_S>(s, w_gate, w2, offsets, eti, dx, ws, spin_limit, st);
   } else {
     launch_dx_fold<TIN, TILE_S, TILE_S>(s, w_gate, w2, offsets, eti, dx, ws, spin_limit, st);

@@ -344,6 +344,9 @@ PLAIN_CASES = [
     ("silu_f32", 256, 128, 8, 2, 256, "f32", "silu", "aby"),
     ("relu_k1", 200, 128, 4, 1, 128, "bf16", "relu", "aby"),
     ("silu_h_only_split_k", 8192, 256, 4, 1, 256, "bf16", "silu", "ab"),  # dW rows in 4 chunks
+    # h = 4d as in MoEBlaze's shapes: the first layer and the dX fold (a
+    # reduction of 4096) on the 256 x 256 tile, rows ragged in every expert
+    ("silu_h4d_wide", 700, 1024, 8, 4, 4096, "bf16", "silu", "ab"),
 ]
 
 
