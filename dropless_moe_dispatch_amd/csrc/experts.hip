@@ -746,7 +746,7 @@ __global__ __launch_bounds__(C::NT, C::WAVES_PER_EU) void down_combine_kernel(
   }
   const FoldRowMeta meta = C::BM == 128 ? fold_row_meta(rt, eti, w_pos, rank_pos) : FoldRowMeta{};
   f32x16_t acc[C::FM][C::FN];
-  gemm_mainloop<C>(la, lb, h / C::BK, smem, acc, wm, wn);
+  gemm_mainloop<C, false>(la, lb, h / C::BK, smem, acc, wm, wn);
   fold_epilogue<C, true>(acc, rt, nb, NB, wm, wn, meta, eti, w_pos, rank_pos, K, d, turn, accws, out,
                          counters + ERR_COMBINE, spin_limit, smem);
 }
@@ -1589,7 +1589,7 @@ __global__ __launch_bounds__(C::NT, C::WAVES_PER_EU) void dx_fold_kernel(
   lb.src.kpt = C::BK;
   lb.ncols = min_i(C::BN, d - nb * C::BN);
   f32x16_t acc[C::FM][C::FN];
-  gemm_mainloop<C>(la, lb, hw / C::BK, smem, acc, wm, wn);
+  gemm_mainloop<C, false>(la, lb, hw / C::BK, smem, acc, wm, wn);
   // fetched after the main loop here: before it, down-combine gained 1% and
   // this kernel lost 0.2-0.5% (MI355X, three workloads)
   const FoldRowMeta meta = C::BM == 128 ? fold_row_meta(rt, eti, nullptr, rank_pos) : FoldRowMeta{};
