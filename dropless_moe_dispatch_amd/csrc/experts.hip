@@ -161,13 +161,18 @@ static bool pick_mid(const Shape& s, bool auto_choice) {
 // is long next to the fold.  Measured on MI355X against the 128 x 256 tile:
 // dX fold 7.4% faster at d = 6144, kdim = 4096, 3% at d = 4096, kdim = 3072,
 // and faster at d = 1024-2048 with kdim = 4096-8192 too (MoEBlaze's conf3
-// and conf4), but 15% slower at d = 2048, kdim = 1536; down-combine
-// 1.62 -> 1.35 ms at d = 4096, kdim = 14336, but 3-8% slower at
-// kdim = 1536-2048 and 7.5% slower at d = 1024, kdim = 4096.  dx: the dX fold
-// (else down-combine).
+// and conf4), but 15% slower at d = 2048, kdim = 1536.  Down-combine (its
+// main loop loading a whole iteration ahead): 4.32 -> 4.22 ms at d = 6144,
+// kdim = 2048, 2-4% faster at d = 1024-2048, kdim = 4096-8192 with 4096 or
+// more tiles and at d = 4096, kdim = 14336 (512 tiles), but 4-8% slower with
+// 512-1024 tiles at kdim = 2048-8192 and level at d = 4096, kdim = 1536.
+// dx: the dX fold (else down-combine).
 static bool wide_fold(const Shape& s, int kdim, bool dx) {
   static const int force = env_int("MOE_DISPATCH_WIDE_FOLD", -1);  // tuning aid: 1 on, 0 off
-  const bool auto_choice = force >= 0 ? force == 1 : (kdim >= 3072 && (dx || s.d >= 4096));
+  const long long tiles = s.A() / TILE_L * (s.d / TILE_L);
+  const bool auto_choice = force >= 0 ? force == 1
+                           : dx      ? kdim >= 3072
+                                     : (kdim >= 3072 && s.d >= 4096) || (kdim >= 2048 && tiles >= 4096);
   return s.bf16 && s.d % TILE_L == 0 && pick_large(auto_choice);
 }
 // Otherwise the folds take the 128 x 256 tile where d is a multiple of 256
@@ -746,7 +751,7 @@ __global__ __launch_bounds__(C::NT, C::WAVES_PER_EU) void down_combine_kernel(
   }
   const FoldRowMeta meta = C::BM == 128 ? fold_row_meta(rt, eti, w_pos, rank_pos) : FoldRowMeta{};
   f32x16_t acc[C::FM][C::FN];
-  gemm_mainloop<C, false>(la, lb, h / C::BK, smem, acc, wm, wn);
+  gemm_mainloop<C>(la, lb, h / C::BK, smem, acc, wm, wn);
   fold_epilogue<C, true>(acc, rt, nb, NB, wm, wn, meta, eti, w_pos, rank_pos, K, d, turn, accws, out,
                          counters + ERR_COMBINE, spin_limit, smem);
 }
