@@ -14,7 +14,8 @@
 //
 // Pipeline: two LDS stages, one barrier per k-tile.  Global loads go through
 // registers (two sets on the 128-row tiles, one on the 256 tile) and are written to
-// the free stage between the MFMA k-steps (after the last one on the 256 tile).  Loaders whose rows come through an
+// the free stage between the MFMA k-steps (on the 256 tile after the last one,
+// with the next load issued right after, except in the dX fold).  Loaders whose rows come through an
 // index (gathered k-rows of the weight-gradient GEMMs) fetch the indices one
 // stage ahead and form the byte offsets only when they load.
 //
